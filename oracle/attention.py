@@ -1,0 +1,145 @@
+"""Oracle: biased multi-head attention forward and backward in float64 (test infrastructure).
+
+Follows the MegaGraph pages' statement that each Graph-Transformer layer
+forms an attention score matrix plus a topology-aware bias matrix (abstract),
+with the bias read as B[h,i,j] = table[h, code(i,j)] and the scores as
+QK^T/sqrt(D) + B. Both matrices are materialised here, one block of query
+rows at a time; softmax is the two-pass definition over the whole row.
+
+Layouts: q, k, v, dout, out, dq, dk, dv are [rows or N, H, D]; lse is [rows, H];
+codes is [rows, N] uint8 (row = query node, column = key node); table and
+dtable are [H, NB]. A code >= NB is clamped to NB - 1.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _bias(table: np.ndarray, codes: np.ndarray, h: int) -> np.ndarray:
+    nb = table.shape[1]
+    return table[h][np.minimum(codes, nb - 1)]
+
+
+def forward(q, k, v, codes, table):
+    """out [R,H,D], lse [R,H] for the R query rows given (q and codes hold those rows)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    table = np.asarray(table, np.float64)
+    R, H, D = q.shape
+    out = np.empty((R, H, D))
+    lse = np.empty((R, H))
+    for h in range(H):
+        S = q[:, h, :] @ k[:, h, :].T / np.sqrt(D) + _bias(table, codes, h)
+        m = S.max(axis=1, keepdims=True)
+        E = np.exp(S - m)
+        l = E.sum(axis=1, keepdims=True)
+        P = E / l
+        out[:, h, :] = P @ v[:, h, :]
+        lse[:, h] = m[:, 0] + np.log(l[:, 0])
+    return out, lse
+
+
+def backward(q, k, v, codes, table, dout):
+    """Forward and backward for the R query rows given.
+
+    Returns out, lse, dq for those rows, plus the contributions of those rows to
+    dk [N,H,D], dv [N,H,D] and dtable [H,NB] (sums over rows; add blocks to get
+    the full gradients). The loss is sum(dout * out).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    table = np.asarray(table, np.float64)
+    R, H, D = q.shape
+    N = k.shape[0]
+    NB = table.shape[1]
+    sc = 1.0 / np.sqrt(D)
+    cl = np.minimum(codes, NB - 1)
+    out = np.empty((R, H, D))
+    lse = np.empty((R, H))
+    dq = np.empty((R, H, D))
+    dk = np.zeros((N, H, D))
+    dv = np.zeros((N, H, D))
+    dtable = np.zeros((H, NB))
+    for h in range(H):
+        S = q[:, h, :] @ k[:, h, :].T * sc + table[h][cl]
+        m = S.max(axis=1, keepdims=True)
+        E = np.exp(S - m)
+        l = E.sum(axis=1, keepdims=True)
+        P = E / l
+        out[:, h, :] = P @ v[:, h, :]
+        lse[:, h] = m[:, 0] + np.log(l[:, 0])
+        dO = dout[:, h, :]
+        dv[:, h, :] = P.T @ dO
+        dP = dO @ v[:, h, :].T
+        delta = (P * dP).sum(axis=1, keepdims=True)
+        dS = P * (dP - delta)
+        dq[:, h, :] = dS @ k[:, h, :] * sc
+        dk[:, h, :] = dS.T @ q[:, h, :] * sc
+        dtable[h] = np.bincount(cl.ravel(), weights=dS.ravel(), minlength=NB)
+    return out, lse, dq, dk, dv, dtable
+
+
+def sum_dtable_rows(dtable_blocks):
+    return np.sum(np.stack(dtable_blocks), axis=0)
+
+
+_G = {}
+
+
+def _pool_init(q, k, v, codes, table, dout):
+    _G.update(q=q, k=k, v=v, codes=codes, table=table, dout=dout)
+
+
+def _pool_block(span):
+    r0, r1 = span
+    g = _G
+    o, l, dq, dk, dv, dt = backward(g["q"][r0:r1], g["k"], g["v"], g["codes"][r0:r1],
+                                    g["table"], g["dout"][r0:r1])
+    return r0, o, l, dq, dk, dv, dt
+
+
+def full_backward(q, k, v, codes, table, dout, block: int = 256, workers: int = 1, rows=None):
+    """Forward + backward over all N query rows, in row blocks.
+
+    codes must be the full [N, N] matrix. If ``rows`` is given, it selects the
+    query rows processed (dk/dv/dtable are then the contributions of those rows
+    only). Blocks may be spread over a process pool; each block is the plain
+    definition above and the partial sums are added in block order.
+    """
+    N = k.shape[0]
+    H, D = k.shape[1], k.shape[2]
+    NB = np.asarray(table).shape[1]
+    if rows is None:
+        rows = np.arange(N)
+        qs, cs, ds = np.asarray(q), np.asarray(codes), np.asarray(dout)
+    else:
+        rows = np.asarray(rows)
+        qs, cs, ds = np.asarray(q)[rows], np.asarray(codes)[rows], np.asarray(dout)[rows]
+    spans = [(r0, min(r0 + block, len(rows))) for r0 in range(0, len(rows), block)]
+    out = np.empty((len(rows), H, D))
+    lse = np.empty((len(rows), H))
+    dq = np.empty((len(rows), H, D))
+    dk = np.zeros((N, H, D))
+    dv = np.zeros((N, H, D))
+    dtable = np.zeros((H, NB))
+    if workers <= 1:
+        _pool_init(qs, k, v, cs, table, ds)
+        results = map(_pool_block, spans)
+    else:
+        import multiprocessing as mp
+        ctx = mp.get_context("fork")
+        pool = ctx.Pool(workers, initializer=_pool_init, initargs=(qs, k, v, cs, table, ds))
+        results = pool.imap(_pool_block, spans)  # in block order
+    for r0, o, l, dqb, dkb, dvb, dtb in results:
+        r1 = r0 + o.shape[0]
+        out[r0:r1], lse[r0:r1], dq[r0:r1] = o, l, dqb
+        dk += dkb
+        dv += dvb
+        dtable += dtb
+    if workers > 1:
+        pool.close()
+        pool.join()
+    return out, lse, dq, dk, dv, dtable
