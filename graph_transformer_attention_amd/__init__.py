@@ -1,0 +1,186 @@
+"""Python binding of libgt_attn.so — biased full-graph attention on gfx950.
+
+Argument marshalling only: every step runs in the library's HIP kernels (or, for
+``spd_build``, its native host code). PyTorch provides device memory and the
+current stream. There is no fallback: if the library is not built, every call
+raises.
+
+    out, lse = fwd(q, k, v, spd, table)
+    dq, dk, dv, dtable = bwd(q, k, v, spd, table, out, lse, dout)
+    spd = spd_build(indptr, indices, N, C)          # host numpy, uint8 [N, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgt_attn.so")
+GT_F32, GT_BF16 = 0, 1
+GT_OK, GT_EINVAL, GT_EUNSUPPORTED, GT_EHIP = 0, -1, -2, -3
+
+_lib = None
+
+
+class GtError(RuntimeError):
+    def __init__(self, name: str, code: int, msg: str):
+        super().__init__(f"{name} failed with status {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m graph_transformer_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.gt_attn_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I32, I32, P]
+        L.gt_attn_fwd.restype = ctypes.c_int
+        L.gt_attn_bwd_workspace_bytes.argtypes = [I64, I32, I32, I32, I32]
+        L.gt_attn_bwd_workspace_bytes.restype = SZ
+        L.gt_attn_bwd.argtypes = [P] * 13 + [SZ, I64, I32, I32, I32, I32, P]
+        L.gt_attn_bwd.restype = ctypes.c_int
+        L.gt_spd_build.argtypes = [P, P, I64, I32, P, I32]
+        L.gt_spd_build.restype = ctypes.c_int
+        L.gt_last_error.argtypes = []
+        L.gt_last_error.restype = ctypes.c_char_p
+        L.gt_version.argtypes = []
+        L.gt_version.restype = ctypes.c_char_p
+        L.gt_trace_enable.argtypes = [I32]
+        L.gt_trace_enable.restype = ctypes.c_int
+        L.gt_trace_collect.argtypes = [P, P, I32]
+        L.gt_trace_collect.restype = ctypes.c_int
+        L.gt_kernel_name.argtypes = [I32]
+        L.gt_kernel_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().gt_last_error().decode()
+
+
+def _check(name: str, rc: int):
+    if rc != GT_OK:
+        raise GtError(name, rc, last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return GT_F32
+    if t.dtype == torch.bfloat16:
+        return GT_BF16
+    raise TypeError(f"q/k/v/dout must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def fwd(q, k, v, spd, table, out=None, lse=None, stream=None):
+    """Forward: q, k, v [N,H,D] (float32 or bfloat16), spd [N,N] uint8, table [H,NB] float32.
+    Returns (out [N,H,D] in q's dtype, lse [N,H] float32)."""
+    import torch
+    N, H, D = q.shape
+    NB = table.shape[1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, H), dtype=torch.float32, device=q.device)
+    args = [_dev(q, "q", q.dtype, (N, H, D)), _dev(k, "k", q.dtype, (N, H, D)),
+            _dev(v, "v", q.dtype, (N, H, D)), _dev(spd, "spd", torch.uint8, (N, N)),
+            _dev(table, "table", torch.float32, (H, NB)), _dev(out, "out", q.dtype, (N, H, D)),
+            _dev(lse, "lse", torch.float32, (N, H))]
+    _check("gt_attn_fwd", lib().gt_attn_fwd(*args, N, H, D, NB, dt, _stream(stream)))
+    return out, lse
+
+
+def bwd_workspace_bytes(N: int, H: int, D: int, NB: int, dtype: int) -> int:
+    return int(lib().gt_attn_bwd_workspace_bytes(N, H, D, NB, dtype))
+
+
+def bwd(q, k, v, spd, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=None,
+        workspace=None, stream=None):
+    """Backward of fwd for loss sum(dout*out). Returns (dq, dk, dv [N,H,D] float32, dtable [H,NB])."""
+    import torch
+    N, H, D = q.shape
+    NB = table.shape[1]
+    dt = _dtype_code(q)
+    f32 = torch.float32
+    dq = torch.empty((N, H, D), dtype=f32, device=q.device) if dq is None else dq
+    dk = torch.empty((N, H, D), dtype=f32, device=q.device) if dk is None else dk
+    dv = torch.empty((N, H, D), dtype=f32, device=q.device) if dv is None else dv
+    dtable = torch.empty((H, NB), dtype=f32, device=q.device) if dtable is None else dtable
+    wsb = bwd_workspace_bytes(N, H, D, NB, dt)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=q.device)
+    args = [_dev(q, "q", q.dtype, (N, H, D)), _dev(k, "k", q.dtype, (N, H, D)),
+            _dev(v, "v", q.dtype, (N, H, D)), _dev(spd, "spd", torch.uint8, (N, N)),
+            _dev(table, "table", f32, (H, NB)), _dev(out, "out", q.dtype, (N, H, D)),
+            _dev(lse, "lse", f32, (N, H)), _dev(dout, "dout", q.dtype, (N, H, D)),
+            _dev(dq, "dq", f32, (N, H, D)), _dev(dk, "dk", f32, (N, H, D)),
+            _dev(dv, "dv", f32, (N, H, D)), _dev(dtable, "dtable", f32, (H, NB)),
+            _dev(workspace, "workspace")]
+    _check("gt_attn_bwd", lib().gt_attn_bwd(*args, workspace.numel() * workspace.element_size(),
+                                            N, H, D, NB, dt, _stream(stream)))
+    return dq, dk, dv, dtable
+
+
+def spd_build(indptr, indices, N: int, C: int, nthreads: int = 0, out=None) -> np.ndarray:
+    """Clipped hop-distance codes uint8 [N, N] of an undirected CSR graph (host, native)."""
+    indptr = np.ascontiguousarray(indptr, dtype=np.int64)
+    indices = np.ascontiguousarray(indices, dtype=np.int32)
+    if indptr.shape != (N + 1,):
+        raise ValueError("indptr must have N+1 entries")
+    if out is None:
+        out = np.empty((N, N), dtype=np.uint8)
+    if out.dtype != np.uint8 or out.shape != (N, N) or not out.flags.c_contiguous:
+        raise ValueError("out must be a C-contiguous uint8 [N, N] array")
+    ip = indices.ctypes.data if indices.size else None
+    _check("gt_spd_build", lib().gt_spd_build(indptr.ctypes.data, ip, N, C, out.ctypes.data, nthreads))
+    return out
+
+
+def version() -> str:
+    return lib().gt_version().decode()
+
+
+KERNEL_COUNT = 5
+
+
+def kernel_names():
+    return [lib().gt_kernel_name(i).decode() for i in range(KERNEL_COUNT)]
+
+
+def trace(on: bool):
+    """Bracket every kernel the library enqueues from this thread with HIP events."""
+    _check("gt_trace_enable", lib().gt_trace_enable(1 if on else 0))
+
+
+def trace_collect() -> dict:
+    """Wait for traced kernels; {kernel name: (launches, total ms)} since the last collect."""
+    counts = (ctypes.c_int32 * KERNEL_COUNT)()
+    ms = (ctypes.c_double * KERNEL_COUNT)()
+    _check("gt_trace_collect", lib().gt_trace_collect(counts, ms, KERNEL_COUNT))
+    return {n: (int(counts[i]), float(ms[i])) for i, n in enumerate(kernel_names()) if counts[i]}

@@ -1,0 +1,481 @@
+// General biased-attention kernels on the vector ALU (any supported H and D, float32
+// or bfloat16 storage). One thread owns one (node, head) pair; tiles of the other
+// operand and of the uint8 code matrix are staged in LDS, and the bias table
+// (premultiplied by log2 e) sits in LDS for the whole kernel.
+//
+// MegaGraph pages, Fig. 4 caption: attention is computed block by block over the
+// keys with the bias columns sliced to each block — here each key tile of the
+// forward pulls exactly the matching code columns and merges its softmax
+// statistics into a running (max, sum) pair.
+#include "gt_internal.h"
+
+#include <algorithm>
+
+namespace gt {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr size_t kLdsDefault = 65536;
+
+__device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld(const uint16_t* p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void st(uint16_t* p, int64_t i, float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest, ties to even
+  p[i] = static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------------
+// Forward: thread (r, h) owns query row i = blockIdx.x*R + r and head h.
+// LDS: table*log2e [H*NB] | K tile [BN][H][D] | V tile | codes [R][BN].
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void fwd_valu_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const uint8_t* __restrict__ spd, const float* __restrict__ table, T* __restrict__ out,
+    float* __restrict__ lse, int64_t N, int H, int NB, int BN, float qscale) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int HD = H * D;
+  const int R = kThreads / H;
+  float* tb = reinterpret_cast<float*>(smem);
+  float* Ks = tb + ((H * NB + 3) & ~3);
+  float* Vs = Ks + BN * HD;
+  uint8_t* cs = reinterpret_cast<uint8_t*>(Vs + BN * HD);
+
+  const int t = threadIdx.x;
+  const int r = t / H, h = t - r * H;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * R;
+  const int64_t i = row0 + r;
+  const bool valid = (r < R) && (i < N);
+
+  for (int x = t; x < H * NB; x += kThreads) tb[x] = table[x] * kLog2e;
+
+  float qr[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qr[d] = valid ? ld(q, (i * H + h) * D + d) * qscale : 0.f;
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const float* tbh = tb + h * NB;
+
+  for (int64_t j0 = 0; j0 < N; j0 += BN) {
+    const int nk = static_cast<int>(std::min<int64_t>(BN, N - j0));
+    __syncthreads();
+    for (int x = t; x < BN * HD; x += kThreads) {
+      const int jj = x / HD;
+      float kx = 0.f, vx = 0.f;
+      if (jj < nk) {
+        const int64_t g = (j0 + jj) * HD + (x - jj * HD);
+        kx = ld(k, g);
+        vx = ld(v, g);
+      }
+      Ks[x] = kx;
+      Vs[x] = vx;
+    }
+    for (int x = t; x < R * BN; x += kThreads) {
+      const int rr = x / BN, jj = x - rr * BN;
+      const int64_t ii = row0 + rr;
+      cs[x] = (ii < N && jj < nk) ? spd[ii * N + j0 + jj] : 0;
+    }
+    __syncthreads();
+    if (!valid) continue;
+    const uint8_t* crow = cs + r * BN;
+    for (int jc = 0; jc < nk; jc += 8) {
+      float s[8];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = jc + u;
+        float sv = -INFINITY;
+        if (j < nk) {
+          const float* kp = Ks + (j * H + h) * D;
+          float dot = 0.f;
+#pragma unroll
+          for (int d = 0; d < D; ++d) dot = fmaf(qr[d], kp[d], dot);
+          const int code = min(static_cast<int>(crow[j]), NB - 1);
+          sv = dot + tbh[code];
+        }
+        s[u] = sv;
+        cmax = fmaxf(cmax, sv);
+      }
+      const float mn = fmaxf(m, cmax);
+      const float alpha = exp2_hw(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = jc + u;
+        if (j < nk) {
+          const float p = exp2_hw(s[u] - mn);
+          l += p;
+          const float* vp = Vs + (j * H + h) * D;
+#pragma unroll
+          for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vp[d], acc[d]);
+        }
+      }
+      m = mn;
+    }
+  }
+  if (valid) {
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int d = 0; d < D; ++d) st(out, (i * H + h) * D + d, acc[d] * inv);
+    lse[i * H + h] = (m + log2f(l)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Backward, step 1: delta[i,h] = sum_d dout[i,h,d] * out[i,h,d].
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const T* __restrict__ out,
+                                                             const T* __restrict__ dout,
+                                                             float* __restrict__ delta,
+                                                             int64_t NH) {
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (x >= NH) return;
+  float s = 0.f;
+#pragma unroll
+  for (int d = 0; d < D; ++d) s = fmaf(ld(dout, x * D + d), ld(out, x * D + d), s);
+  delta[x] = s;
+}
+
+// Backward, step 2 (key-outer): thread (c, h) owns key j = blockIdx.x*CK + c and head h,
+// loops over all query rows and accumulates dK, dV and per-thread bucket sums of dS.
+// LDS: table*log2e | bins [NB][256] | Q tile [BM][H][D] | dO tile | lse*log2e [BM][H]
+//      | delta [BM][H] | codes [BM][CK].
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_kv_valu_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const uint8_t* __restrict__ spd, const float* __restrict__ table,
+    const float* __restrict__ lse, const float* __restrict__ delta, const T* __restrict__ dout,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ partial, int64_t N,
+    int H, int NB, int BM, float qscale, float scale) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int HD = H * D;
+  const int CK = kThreads / H;
+  float* tb = reinterpret_cast<float*>(smem);
+  float* bins = tb + ((H * NB + 3) & ~3);
+  float* Qs = bins + NB * kThreads;
+  float* Os = Qs + BM * HD;
+  float* Ls = Os + BM * HD;
+  float* Ds = Ls + BM * H;
+  uint8_t* cs = reinterpret_cast<uint8_t*>(Ds + BM * H);
+
+  const int t = threadIdx.x;
+  const int c = t / H, h = t - c * H;
+  const int64_t col0 = static_cast<int64_t>(blockIdx.x) * CK;
+  const int64_t j = col0 + c;
+  const bool valid = (c < CK) && (j < N);
+
+  for (int x = t; x < H * NB; x += kThreads) tb[x] = table[x] * kLog2e;
+  for (int b = 0; b < NB; ++b) bins[b * kThreads + t] = 0.f;
+
+  float kr[D], vr[D], dka[D], dva[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    kr[d] = valid ? ld(k, (j * H + h) * D + d) : 0.f;
+    vr[d] = valid ? ld(v, (j * H + h) * D + d) : 0.f;
+    dka[d] = 0.f;
+    dva[d] = 0.f;
+  }
+  const float* tbh = tb + h * NB;
+
+  for (int64_t i0 = 0; i0 < N; i0 += BM) {
+    const int nq = static_cast<int>(std::min<int64_t>(BM, N - i0));
+    __syncthreads();
+    for (int x = t; x < BM * HD; x += kThreads) {
+      const int ii = x / HD;
+      float qx = 0.f, ox = 0.f;
+      if (ii < nq) {
+        const int64_t g = (i0 + ii) * HD + (x - ii * HD);
+        qx = ld(q, g);
+        ox = ld(dout, g);
+      }
+      Qs[x] = qx;
+      Os[x] = ox;
+    }
+    for (int x = t; x < BM * H; x += kThreads) {
+      const int ii = x / H;
+      const bool ok = ii < nq;
+      Ls[x] = ok ? lse[i0 * H + x] * kLog2e : 0.f;
+      Ds[x] = ok ? delta[i0 * H + x] : 0.f;
+    }
+    for (int x = t; x < BM * CK; x += kThreads) {
+      const int ii = x / CK, cc = x - ii * CK;
+      cs[x] = (ii < nq && col0 + cc < N) ? spd[(i0 + ii) * N + col0 + cc] : 0;
+    }
+    __syncthreads();
+    if (!valid) continue;
+    for (int ii = 0; ii < nq; ++ii) {
+      const float* qp = Qs + (ii * H + h) * D;
+      const float* op = Os + (ii * H + h) * D;
+      float dot = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        dot = fmaf(qp[d], kr[d], dot);
+        dp = fmaf(op[d], vr[d], dp);
+      }
+      const int code = min(static_cast<int>(cs[ii * CK + c]), NB - 1);
+      const float p = exp2_hw(fmaf(dot, qscale, tbh[code]) - Ls[ii * H + h]);
+      const float ds = p * (dp - Ds[ii * H + h]);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        dva[d] = fmaf(p, op[d], dva[d]);
+        dka[d] = fmaf(ds, qp[d], dka[d]);
+      }
+      bins[code * kThreads + t] += ds;
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      dk[(j * H + h) * D + d] = dka[d] * scale;
+      dv[(j * H + h) * D + d] = dva[d];
+    }
+  }
+  __syncthreads();
+  for (int x = t; x < H * NB; x += kThreads) {
+    const int hh = x / NB, b = x - hh * NB;
+    float s = 0.f;
+    for (int cc = 0; cc < CK; ++cc) s += bins[b * kThreads + cc * H + hh];
+    partial[static_cast<int64_t>(blockIdx.x) * H * NB + x] = s;
+  }
+}
+
+// Backward, step 3 (query-outer): thread (r, h) owns query row i and head h and
+// accumulates dQ over all keys. LDS: table*log2e | K tile | V tile | codes [R][BN].
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const uint8_t* __restrict__ spd, const float* __restrict__ table,
+    const float* __restrict__ lse, const float* __restrict__ delta, const T* __restrict__ dout,
+    float* __restrict__ dq, int64_t N, int H, int NB, int BN, float qscale, float scale) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int HD = H * D;
+  const int R = kThreads / H;
+  float* tb = reinterpret_cast<float*>(smem);
+  float* Ks = tb + ((H * NB + 3) & ~3);
+  float* Vs = Ks + BN * HD;
+  uint8_t* cs = reinterpret_cast<uint8_t*>(Vs + BN * HD);
+
+  const int t = threadIdx.x;
+  const int r = t / H, h = t - r * H;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * R;
+  const int64_t i = row0 + r;
+  const bool valid = (r < R) && (i < N);
+
+  for (int x = t; x < H * NB; x += kThreads) tb[x] = table[x] * kLog2e;
+  float qr[D], orr[D], dqa[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qr[d] = valid ? ld(q, (i * H + h) * D + d) : 0.f;
+    orr[d] = valid ? ld(dout, (i * H + h) * D + d) : 0.f;
+    dqa[d] = 0.f;
+  }
+  const float l2 = valid ? lse[i * H + h] * kLog2e : 0.f;
+  const float dl = valid ? delta[i * H + h] : 0.f;
+  const float* tbh = tb + h * NB;
+
+  for (int64_t j0 = 0; j0 < N; j0 += BN) {
+    const int nk = static_cast<int>(std::min<int64_t>(BN, N - j0));
+    __syncthreads();
+    for (int x = t; x < BN * HD; x += kThreads) {
+      const int jj = x / HD;
+      float kx = 0.f, vx = 0.f;
+      if (jj < nk) {
+        const int64_t g = (j0 + jj) * HD + (x - jj * HD);
+        kx = ld(k, g);
+        vx = ld(v, g);
+      }
+      Ks[x] = kx;
+      Vs[x] = vx;
+    }
+    for (int x = t; x < R * BN; x += kThreads) {
+      const int rr = x / BN, jj = x - rr * BN;
+      const int64_t ii = row0 + rr;
+      cs[x] = (ii < N && jj < nk) ? spd[ii * N + j0 + jj] : 0;
+    }
+    __syncthreads();
+    if (!valid) continue;
+    const uint8_t* crow = cs + r * BN;
+    for (int jj = 0; jj < nk; ++jj) {
+      const float* kp = Ks + (jj * H + h) * D;
+      const float* vp = Vs + (jj * H + h) * D;
+      float dot = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        dot = fmaf(qr[d], kp[d], dot);
+        dp = fmaf(orr[d], vp[d], dp);
+      }
+      const int code = min(static_cast<int>(crow[jj]), NB - 1);
+      const float p = exp2_hw(fmaf(dot, qscale, tbh[code]) - l2);
+      const float ds = p * (dp - dl);
+#pragma unroll
+      for (int d = 0; d < D; ++d) dqa[d] = fmaf(ds, kp[d], dqa[d]);
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) dq[(i * H + h) * D + d] = dqa[d] * scale;
+  }
+}
+
+// Backward, step 4: dtable[x] = sum over key blocks of partial[block][x], in block
+// order within each thread and a fixed tree across the workgroup (deterministic).
+__global__ __launch_bounds__(kThreads) void dtable_reduce_kernel(const float* __restrict__ partial,
+                                                                 float* __restrict__ dtable,
+                                                                 int64_t nblocks, int HNB) {
+  __shared__ float red[kThreads];
+  const int x = blockIdx.x;
+  float s = 0.f;
+  for (int64_t b = threadIdx.x; b < nblocks; b += kThreads) s += partial[b * HNB + x];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dtable[x] = red[0];
+}
+
+int fwd_tile_keys(int H, int D, int NB) {
+  const int HD = H * D;
+  int bn = std::max(8, std::min(64, 4096 / HD));
+  bn &= ~7;
+  const size_t fixed = 4 * ((H * NB + 3) & ~3);
+  while (bn > 8 && fixed + 8ull * bn * HD + static_cast<size_t>(kThreads / H) * bn > kLdsDefault)
+    bn -= 8;
+  return bn;
+}
+
+size_t fwd_lds(int H, int D, int NB, int BN) {
+  return 4 * ((H * NB + 3) & ~3) + 8ull * BN * H * D + static_cast<size_t>(kThreads / H) * BN;
+}
+
+size_t kv_lds(int H, int D, int NB, int BM) {
+  const int CK = kThreads / H;
+  return 4 * ((H * NB + 3) & ~3) + 4ull * NB * kThreads + 8ull * BM * H * D + 8ull * BM * H +
+         static_cast<size_t>(BM) * CK;
+}
+
+int kv_tile_rows(int H, int D, int NB) {
+  int bm = 32;
+  while (bm > 1 && kv_lds(H, D, NB, bm) > kLdsDefault) bm >>= 1;
+  return bm;
+}
+
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  if (bytes <= kLdsDefault) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+template <typename T, int D>
+hipError_t fwd_typed(const FwdArgs& a, hipStream_t s) {
+  const int BN = fwd_tile_keys(a.H, D, a.NB);
+  const size_t lds = fwd_lds(a.H, D, a.NB, BN);
+  const int R = kThreads / a.H;
+  const unsigned grid = static_cast<unsigned>((a.N + R - 1) / R);
+  const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+  trace_begin(0, s);
+  hipLaunchKernelGGL((fwd_valu_kernel<T, D>), dim3(grid), dim3(kThreads), lds, s,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), a.spd, a.table, static_cast<T*>(a.out), a.lse,
+                     a.N, a.H, a.NB, BN, qscale);
+  const hipError_t e = hipGetLastError();
+  trace_end(0, s);
+  return e;
+}
+
+template <typename T, int D>
+hipError_t bwd_typed(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
+  char* ws = static_cast<char*>(a.workspace);
+  float* delta = reinterpret_cast<float*>(ws + w.delta_off);
+  float* partial = reinterpret_cast<float*>(ws + w.partial_off);
+  const int64_t NH = a.N * a.H;
+  const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+  const float scale = 1.f / sqrtf(static_cast<float>(D));
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  const T* dout = static_cast<const T*>(a.dout);
+
+  trace_begin(1, s);
+  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(static_cast<unsigned>((NH + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, static_cast<const T*>(a.out), dout, delta, NH);
+  hipError_t e = hipGetLastError();
+  trace_end(1, s);
+  if (e != hipSuccess) return e;
+
+  const int BM = kv_tile_rows(a.H, D, a.NB);
+  const size_t lds_kv = kv_lds(a.H, D, a.NB, BM);
+  e = allow_lds(bwd_kv_valu_kernel<T, D>, lds_kv);
+  if (e != hipSuccess) return e;
+  trace_begin(2, s);
+  hipLaunchKernelGGL((bwd_kv_valu_kernel<T, D>), dim3(static_cast<unsigned>(w.n_kv_blocks)),
+                     dim3(kThreads), lds_kv, s, q, k, v, a.spd, a.table, a.lse, delta, dout, a.dk,
+                     a.dv, partial, a.N, a.H, a.NB, BM, qscale, scale);
+  e = hipGetLastError();
+  trace_end(2, s);
+  if (e != hipSuccess) return e;
+
+  const int BN = fwd_tile_keys(a.H, D, a.NB);
+  const size_t lds_q = fwd_lds(a.H, D, a.NB, BN);
+  const int R = kThreads / a.H;
+  trace_begin(3, s);
+  hipLaunchKernelGGL((bwd_q_valu_kernel<T, D>), dim3(static_cast<unsigned>((a.N + R - 1) / R)),
+                     dim3(kThreads), lds_q, s, q, k, v, a.spd, a.table, a.lse, delta, dout, a.dq,
+                     a.N, a.H, a.NB, BN, qscale, scale);
+  e = hipGetLastError();
+  trace_end(3, s);
+  if (e != hipSuccess) return e;
+
+  trace_begin(4, s);
+  hipLaunchKernelGGL(dtable_reduce_kernel, dim3(static_cast<unsigned>(a.H * a.NB)), dim3(kThreads),
+                     0, s, partial, a.dtable, w.n_kv_blocks, a.H * a.NB);
+  e = hipGetLastError();
+  trace_end(4, s);
+  return e;
+}
+
+template <typename T>
+hipError_t fwd_by_d(const FwdArgs& a, hipStream_t s) {
+  switch (a.D) {
+    case 8: return fwd_typed<T, 8>(a, s);
+    case 16: return fwd_typed<T, 16>(a, s);
+    case 32: return fwd_typed<T, 32>(a, s);
+    default: return fwd_typed<T, 64>(a, s);
+  }
+}
+
+template <typename T>
+hipError_t bwd_by_d(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
+  switch (a.D) {
+    case 8: return bwd_typed<T, 8>(a, w, s);
+    case 16: return bwd_typed<T, 16>(a, w, s);
+    case 32: return bwd_typed<T, 32>(a, w, s);
+    default: return bwd_typed<T, 64>(a, w, s);
+  }
+}
+
+}  // namespace
+
+int64_t valu_kv_block(int H) { return kThreads / H; }
+
+hipError_t launch_fwd_valu(const FwdArgs& a, hipStream_t s) {
+  return a.dtype == 0 ? fwd_by_d<float>(a, s) : fwd_by_d<uint16_t>(a, s);
+}
+
+hipError_t launch_bwd_valu(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
+  return a.dtype == 0 ? bwd_by_d<float>(a, w, s) : bwd_by_d<uint16_t>(a, w, s);
+}
+
+}  // namespace gt

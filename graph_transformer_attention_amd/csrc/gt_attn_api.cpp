@@ -1,0 +1,237 @@
+// C ABI of libgt_attn.so: argument validation, workspace sizing, kernel dispatch and
+// per-thread error messages. Validation runs on the host before anything is
+// enqueued, so every argument error is reported without touching the GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/gt_attn.h"
+#include "gt_internal.h"
+
+namespace gt {
+std::string spd_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C);
+void spd_fill(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C, uint8_t* spd,
+              int nthreads);
+}  // namespace gt
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by all device entry points; returns GT_OK or an error.
+int check_shape(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  if (N < 1 || N > 0x7FFFFFFFll) return fail(GT_EINVAL, "N=%lld must lie in [1, 2^31-1]", (long long)N);
+  if (H < 1) return fail(GT_EINVAL, "H=%d must be >= 1", H);
+  if (D < 1) return fail(GT_EINVAL, "D=%d must be >= 1", D);
+  if (NB < 2 || NB > 255) return fail(GT_EINVAL, "NB=%d must lie in [2, 255]", NB);
+  if (dtype != GT_F32 && dtype != GT_BF16) return fail(GT_EINVAL, "dtype=%d is not GT_F32 or GT_BF16", dtype);
+  if (D != 8 && D != 16 && D != 32 && D != 64)
+    return fail(GT_EUNSUPPORTED, "D=%d: supported head dimensions are 8, 16, 32, 64", D);
+  if (H > 64 || H * D > 512) return fail(GT_EUNSUPPORTED, "H=%d, D=%d: needs H <= 64 and H*D <= 512", H, D);
+  if (NB > 64 || H * NB > 4096)
+    return fail(GT_EUNSUPPORTED, "NB=%d, H=%d: needs NB <= 64 and H*NB <= 4096", NB, H);
+  return GT_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(GT_EINVAL, "%s is null", name);
+  if (!aligned16(p)) return fail(GT_EINVAL, "%s is not 16-byte aligned", name);
+  return GT_OK;
+}
+
+#define GT_CHECK(expr)          \
+  do {                          \
+    const int rc_ = (expr);     \
+    if (rc_ != GT_OK) return rc_; \
+  } while (0)
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GT_OK;
+  return fail(GT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Kernel timing records of the calling thread (gt_trace_enable / gt_trace_collect).
+struct TraceRec {
+  int id;
+  hipEvent_t begin, end;
+};
+thread_local bool g_trace_on = false;
+thread_local bool g_trace_failed = false;
+thread_local std::vector<hipEvent_t> g_trace_pool;
+thread_local std::vector<TraceRec> g_trace_recs;
+thread_local hipEvent_t g_trace_open = nullptr;
+
+hipEvent_t trace_event() {
+  if (!g_trace_pool.empty()) {
+    hipEvent_t e = g_trace_pool.back();
+    g_trace_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    g_trace_failed = true;
+    return nullptr;
+  }
+  return e;
+}
+
+const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd", "bwd_delta", "bwd_kv", "bwd_q", "bwd_dtable"};
+
+}  // namespace
+
+namespace gt {
+
+void trace_begin(int kernel_id, hipStream_t s) {
+  (void)kernel_id;
+  if (!g_trace_on) return;
+  g_trace_open = trace_event();
+  if (g_trace_open != nullptr && hipEventRecord(g_trace_open, s) != hipSuccess) g_trace_failed = true;
+}
+
+void trace_end(int kernel_id, hipStream_t s) {
+  if (!g_trace_on || g_trace_open == nullptr) return;
+  hipEvent_t e = trace_event();
+  if (e == nullptr) return;
+  if (hipEventRecord(e, s) != hipSuccess) g_trace_failed = true;
+  g_trace_recs.push_back({kernel_id, g_trace_open, e});
+  g_trace_open = nullptr;
+}
+
+BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype) {
+  BwdWorkspace w{};
+  (void)D;
+  (void)dtype;
+  const int64_t kb = valu_kv_block(H);
+  w.n_kv_blocks = (N + kb - 1) / kb;
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  w.delta_off = 0;
+  w.partial_off = up(static_cast<size_t>(N) * H * sizeof(float));
+  w.bytes = w.partial_off + up(static_cast<size_t>(w.n_kv_blocks) * H * NB * sizeof(float));
+  return w;
+}
+
+bool use_mfma(int H, int D, int dtype) {
+  (void)H;
+  (void)D;
+  (void)dtype;
+  return false;
+}
+
+}  // namespace gt
+
+extern "C" {
+
+const char* gt_last_error(void) { return g_error.c_str(); }
+
+const char* gt_version(void) { return "gt_attn 0.1 (gfx950)"; }
+
+int gt_trace_enable(int32_t on) {
+  g_trace_on = on != 0;
+  return GT_OK;
+}
+
+int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n) {
+  for (int32_t i = 0; i < n; ++i) {
+    if (counts) counts[i] = 0;
+    if (total_ms) total_ms[i] = 0.0;
+  }
+  int rc = GT_OK;
+  for (const TraceRec& r : g_trace_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.end) != hipSuccess || hipEventElapsedTime(&ms, r.begin, r.end) != hipSuccess)
+      rc = fail(GT_EHIP, "gt_trace_collect: could not read a kernel timing event");
+    if (r.id >= 0 && r.id < n) {
+      if (counts) counts[r.id] += 1;
+      if (total_ms) total_ms[r.id] += ms;
+    }
+    g_trace_pool.push_back(r.begin);
+    g_trace_pool.push_back(r.end);
+  }
+  g_trace_recs.clear();
+  if (g_trace_failed) {
+    g_trace_failed = false;
+    rc = fail(GT_EHIP, "gt_trace: an event could not be created or recorded");
+  }
+  return rc;
+}
+
+const char* gt_kernel_name(int32_t id) {
+  return (id >= 0 && id < GT_KERNEL_COUNT) ? kKernelNames[id] : "";
+}
+
+int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd, const float* table,
+                void* out, float* lse, int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype,
+                void* stream) {
+  GT_CHECK(check_shape(N, H, D, NB, dtype));
+  GT_CHECK(check_ptr(q, "q"));
+  GT_CHECK(check_ptr(k, "k"));
+  GT_CHECK(check_ptr(v, "v"));
+  GT_CHECK(check_ptr(spd, "spd"));
+  GT_CHECK(check_ptr(table, "table"));
+  GT_CHECK(check_ptr(out, "out"));
+  GT_CHECK(check_ptr(lse, "lse"));
+  gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype};
+  return hip_status(gt::launch_fwd_valu(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd launch");
+}
+
+size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  const std::string saved = g_error;
+  const int rc = check_shape(N, H, D, NB, dtype);
+  g_error = saved;
+  if (rc != GT_OK) return 0;
+  return gt::bwd_workspace(N, H, D, NB, dtype).bytes;
+}
+
+int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd, const float* table,
+                const void* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                float* dtable, void* workspace, size_t workspace_bytes, int64_t N, int32_t H,
+                int32_t D, int32_t NB, int32_t dtype, void* stream) {
+  GT_CHECK(check_shape(N, H, D, NB, dtype));
+  GT_CHECK(check_ptr(q, "q"));
+  GT_CHECK(check_ptr(k, "k"));
+  GT_CHECK(check_ptr(v, "v"));
+  GT_CHECK(check_ptr(spd, "spd"));
+  GT_CHECK(check_ptr(table, "table"));
+  GT_CHECK(check_ptr(out, "out"));
+  GT_CHECK(check_ptr(lse, "lse"));
+  GT_CHECK(check_ptr(dout, "dout"));
+  GT_CHECK(check_ptr(dq, "dq"));
+  GT_CHECK(check_ptr(dk, "dk"));
+  GT_CHECK(check_ptr(dv, "dv"));
+  GT_CHECK(check_ptr(dtable, "dtable"));
+  if (workspace == nullptr) return fail(GT_EINVAL, "workspace is null");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GT_EINVAL, "workspace is not 256-byte aligned");
+  const gt::BwdWorkspace w = gt::bwd_workspace(N, H, D, NB, dtype);
+  if (workspace_bytes < w.bytes)
+    return fail(GT_EINVAL, "workspace_bytes=%zu < %zu required", workspace_bytes, w.bytes);
+  gt::BwdArgs a{q, k, v, spd, table, out, lse, dout, dq, dk, dv, dtable, workspace, N, H, D, NB, dtype};
+  return hip_status(gt::launch_bwd_valu(a, w, static_cast<hipStream_t>(stream)), "gt_attn_bwd launch");
+}
+
+int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C, uint8_t* spd,
+                 int32_t nthreads) {
+  if (indptr == nullptr) return fail(GT_EINVAL, "indptr is null");
+  if (spd == nullptr) return fail(GT_EINVAL, "spd is null");
+  const std::string why = gt::spd_validate(indptr, indices, N, C);
+  if (!why.empty()) return fail(GT_EINVAL, "gt_spd_build: %s", why.c_str());
+  gt::spd_fill(indptr, indices, N, C, spd, nthreads);
+  return GT_OK;
+}
+
+}  // extern "C"

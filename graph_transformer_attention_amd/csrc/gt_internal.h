@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI layer (gt_attn_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gt {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* spd;
+  const float* table;
+  void* out;
+  float* lse;
+  int64_t N;
+  int H, D, NB, dtype;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* spd;
+  const float* table;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dtable;
+  void* workspace;
+  int64_t N;
+  int H, D, NB, dtype;
+};
+
+// Workspace layout of the backward: delta [N*H] float, then per-workgroup bucket
+// partial sums [n_kv_blocks * H * NB] float; each region starts 256-byte aligned.
+struct BwdWorkspace {
+  size_t delta_off, partial_off, bytes;
+  int64_t n_kv_blocks;
+};
+
+// Which kernel family serves a shape: the MFMA kernels (bf16, D in {8, 32}, H = 8)
+// or the general vector-ALU kernels.
+bool use_mfma(int H, int D, int dtype);
+
+// Kernel timing hook (gt_trace_enable): bracket one launch with events on its stream.
+void trace_begin(int kernel_id, hipStream_t s);
+void trace_end(int kernel_id, hipStream_t s);
+
+BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype);
+
+hipError_t launch_fwd_valu(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_valu(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
+int64_t valu_kv_block(int H);
+
+}  // namespace gt

@@ -1,0 +1,128 @@
+/* gt_attn.h — C ABI of the biased full-graph attention library (libgt_attn.so), gfx950.
+ *
+ * Method (MegaGraph pages, abstract: every Graph-Transformer layer forms an
+ * attention score matrix together with a topology-aware bias matrix; Fig. 4
+ * caption: the bias is processed column-block by column-block, each slice
+ * matched to the key/value block it is used with). Read here as
+ *
+ *     B[h,i,j] = table[h, code(i,j)]            code = clipped hop distance (gt_spd_build)
+ *     S[h,i,j] = <q[i,h,:], k[j,h,:]> / sqrt(D) + B[h,i,j]
+ *     out[i,h,:] = sum_j softmax_j(S[h,i,:]) v[j,h,:],   lse[i,h] = log sum_j exp S[h,i,j]
+ *
+ * over all N x N node pairs (no mask; unreachable pairs use their own bucket).
+ * Neither S nor B is ever stored: kernels rebuild each bias tile from the
+ * uint8 code tile and a copy of the table held on chip.
+ *
+ * Conventions shared by every entry point
+ *   - Layouts (row-major, node-major):
+ *       q, k, v, out, dout, dq, dk, dv   [N, H, D]   (= [N, H*D], hidden index h*D + d)
+ *       lse                              [N, H]      float32, natural log
+ *       spd                              [N, N]      uint8, row = query node i, column = key node j
+ *       table, dtable                    [H, NB]     float32
+ *   - dtype selects the storage type of q, k, v, out and dout: GT_F32 (float)
+ *     or GT_BF16 (bfloat16 bits). Arithmetic is float32 throughout; table,
+ *     lse and every gradient are float32.
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library never allocates, frees or synchronises device memory, and keeps
+ *     no state between calls. Every base pointer must be 16-byte aligned.
+ *   - A code >= NB in spd is a caller error; kernels clamp it to NB-1.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *     null stream) and return once the kernels are enqueued. Device faults
+ *     surface at the caller's next synchronisation.
+ *   - Return value: GT_OK, or a negative gt_status. Argument errors are
+ *     reported before anything is enqueued. gt_last_error() then returns a
+ *     message for the calling thread.
+ *   - No exception crosses this interface. All calls are re-entrant.
+ *   - Supported shapes: 1 <= N < 2^31, 1 <= H <= 64, D in {8, 16, 32, 64},
+ *     H*D <= 512, 2 <= NB <= 64, H*NB <= 4096. Other sizes return
+ *     GT_EUNSUPPORTED (the bucket-gradient partial sums are kept per thread in
+ *     on-chip memory, which bounds NB).
+ */
+#ifndef GT_ATTN_H
+#define GT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GT_F32 = 0, GT_BF16 = 1 } gt_dtype;
+
+typedef enum {
+  GT_OK = 0,
+  GT_EINVAL = -1,        /* null or misaligned pointer, size out of range, workspace too small */
+  GT_EUNSUPPORTED = -2,  /* valid arguments this build has no kernel for (D, H*D, dtype) */
+  GT_EHIP = -3           /* the HIP runtime refused a launch */
+} gt_status;
+
+/* Forward of one biased attention layer (abstract and Fig. 4 of the MegaGraph pages).
+ *   q, k, v  device [N,H,D] dtype        spd    device [N,N] uint8
+ *   table    device [H,NB] float32       out    device [N,H,D] dtype (overwritten)
+ *   lse      device [N,H] float32 (overwritten; the backward needs it)            */
+int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
+                const float* table, void* out, float* lse, int64_t N, int32_t H,
+                int32_t D, int32_t NB, int32_t dtype, void* stream);
+
+/* Bytes of device workspace gt_attn_bwd needs for these sizes (0 on invalid sizes). */
+size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype);
+
+/* Backward of gt_attn_fwd for the loss sum(dout * out): recomputes the scores and the
+ * softmax from q, k, spd, table and lse (the forward's outputs out and lse are inputs).
+ *   dout                   device [N,H,D] dtype
+ *   dq, dk, dv             device [N,H,D] float32 (overwritten)
+ *   dtable                 device [H,NB]  float32 (overwritten, not accumulated):
+ *                          dtable[h,b] = sum over pairs (i,j) with code b of dS[h,i,j]
+ *   workspace              device, >= gt_attn_bwd_workspace_bytes(...) bytes, 256-byte
+ *                          aligned, contents ignored on entry; calls that share one
+ *                          workspace must be ordered on one stream.
+ * Results are bitwise reproducible run to run (no floating-point atomics).           */
+int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
+                const float* table, const void* out, const float* lse, const void* dout,
+                float* dq, float* dk, float* dv, float* dtable, void* workspace,
+                size_t workspace_bytes, int64_t N, int32_t H, int32_t D, int32_t NB,
+                int32_t dtype, void* stream);
+
+/* Clipped hop-distance codes on the host (the topology that "topology-aware" refers to).
+ *   indptr   host int64 [N+1], indices host int32 [indptr[N]]: an undirected graph in
+ *            CSR form (both directions stored; neighbour order is free).
+ *   spd      host uint8 [N,N] (overwritten): spd[i,j] = min(dist(i,j), C-1) if j is
+ *            reachable from i (dist(i,i) = 0), else C.
+ *   nthreads host threads to use (<= 0: all hardware threads).
+ * Synchronous. Errors: GT_EINVAL for C outside [1,254], a malformed CSR, or an
+ * adjacency that is not symmetric.                                                    */
+int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C,
+                 uint8_t* spd, int32_t nthreads);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* gt_last_error(void);
+
+/* Library version string. */
+const char* gt_version(void);
+
+/* Kernel timing for benchmarks and profiling. While tracing is on for the calling
+ * thread, every kernel the library enqueues from that thread is bracketed by a pair
+ * of HIP events recorded on the kernel's own stream. gt_trace_collect waits for
+ * those events, writes per-kernel launch counts and total milliseconds into
+ * counts[id] / total_ms[id] for id < n (ids below; n >= GT_KERNEL_COUNT covers
+ * all), and clears the record. Tracing adds two event records per launch.
+ * gt_trace_enable returns GT_OK; gt_trace_collect returns GT_OK, or GT_EHIP if
+ * an event could not be created or read.                                          */
+enum {
+  GT_KERNEL_FWD = 0,        /* forward (scores, bias, online softmax, PV)          */
+  GT_KERNEL_BWD_DELTA = 1,  /* backward: delta = rowsum(dout * out)                */
+  GT_KERNEL_BWD_KV = 2,     /* backward: key-outer dK, dV and bucket partial sums  */
+  GT_KERNEL_BWD_Q = 3,      /* backward: query-outer dQ                            */
+  GT_KERNEL_BWD_DTABLE = 4, /* backward: reduction of bucket partials to dtable    */
+  GT_KERNEL_COUNT = 5
+};
+int gt_trace_enable(int32_t on);
+int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n);
+const char* gt_kernel_name(int32_t id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GT_ATTN_H */

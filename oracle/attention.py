@@ -102,26 +102,28 @@ def _pool_block(span):
 
 
 def full_backward(q, k, v, codes, table, dout, block: int = 256, workers: int = 1, rows=None):
-    """Forward + backward over all N query rows, in row blocks.
+    """Forward + backward over query rows, in row blocks.
 
-    codes must be the full [N, N] matrix. If ``rows`` is given, it selects the
-    query rows processed (dk/dv/dtable are then the contributions of those rows
-    only). Blocks may be spread over a process pool; each block is the plain
-    definition above and the partial sums are added in block order.
+    q, codes and dout hold R query rows (codes [R, N]); k and v hold all N keys.
+    With q/codes/dout covering all N rows the results are the full gradients. If
+    ``rows`` is given it selects a subset of those R rows. dk/dv/dtable are the
+    contributions of the rows processed. Blocks may be spread over a process pool;
+    each block is the plain definition above and the partial sums are added in
+    block order.
     """
-    N = k.shape[0]
+    N = np.asarray(k).shape[0]
     H, D = k.shape[1], k.shape[2]
     NB = np.asarray(table).shape[1]
     if rows is None:
-        rows = np.arange(N)
         qs, cs, ds = np.asarray(q), np.asarray(codes), np.asarray(dout)
     else:
         rows = np.asarray(rows)
         qs, cs, ds = np.asarray(q)[rows], np.asarray(codes)[rows], np.asarray(dout)[rows]
-    spans = [(r0, min(r0 + block, len(rows))) for r0 in range(0, len(rows), block)]
-    out = np.empty((len(rows), H, D))
-    lse = np.empty((len(rows), H))
-    dq = np.empty((len(rows), H, D))
+    R = qs.shape[0]
+    spans = [(r0, min(r0 + block, R)) for r0 in range(0, R, block)]
+    out = np.empty((R, H, D))
+    lse = np.empty((R, H))
+    dq = np.empty((R, H, D))
     dk = np.zeros((N, H, D))
     dv = np.zeros((N, H, D))
     dtable = np.zeros((H, NB))

@@ -1,0 +1,47 @@
+"""Helpers for GPU parity tests: moving stored inputs to the device and comparing
+against the float64 oracle at the stated tolerances.
+
+Tolerances, per output tensor T in {out, lse, dq, dk, dv, dtable}:
+  float32 inputs:  max |T_gpu - T_ref| <= 1e-4
+  bfloat16 inputs: max |T_gpu - T_ref| / rms(T_ref) <= 2e-2   (float32 accumulation)
+"""
+import numpy as np
+import torch
+
+TOL_F32_ABS = 1e-4
+TOL_BF16_REL = 2e-2
+
+
+def dev(stored):
+    """A workloads.Stored tensor on cuda:0 in its storage type."""
+    if stored.dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(stored.raw)).cuda()
+    bits = np.ascontiguousarray(stored.raw).view(np.int16)
+    return torch.from_numpy(bits).cuda().view(torch.bfloat16)
+
+
+def host64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def err(got, ref, dtype):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    e = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    if dtype == "f32":
+        return e, e <= TOL_F32_ABS
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    if rms == 0.0:
+        return e, e == 0.0
+    return e / rms, e / rms <= TOL_BF16_REL
+
+
+def check(name, got, ref, dtype, report=None):
+    e, ok = err(got, ref, dtype)
+    if report is not None:
+        report[name] = e
+    bound = TOL_F32_ABS if dtype == "f32" else TOL_BF16_REL
+    kind = "max-abs" if dtype == "f32" else "max-abs/rms"
+    assert ok, f"{name}: {kind} error {e:.3e} exceeds {bound:.0e}"
+    return e

@@ -1,0 +1,175 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every declared symbol,
+rejects bad arguments before anything is enqueued, and its native distance-code
+builder agrees bit for bit with the oracle's breadth-first search."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import graph_transformer_attention_amd as gta
+from workloads import graphs, make_inputs, small_case
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gt_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gt_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"gt_attn_fwd", "gt_attn_bwd", "gt_attn_bwd_workspace_bytes", "gt_spd_build",
+            "gt_last_error", "gt_version"} <= set(names)
+    L = gta.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in gta.version()
+
+
+P = 0x10000  # a 16-byte-aligned stand-in address; these calls never reach the GPU
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, spd=P, table=P, out=P, lse=P, N=100, H=8, D=8, NB=33, dt=1)
+    a.update(kw)
+    return gta.lib().gt_attn_fwd(a["q"], a["k"], a["v"], a["spd"], a["table"], a["out"], a["lse"],
+                                 a["N"], a["H"], a["D"], a["NB"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), gta.GT_EINVAL, "q is null"),
+    (dict(spd=None), gta.GT_EINVAL, "spd is null"),
+    (dict(lse=P + 4), gta.GT_EINVAL, "aligned"),
+    (dict(N=0), gta.GT_EINVAL, "N="),
+    (dict(N=1 << 31), gta.GT_EINVAL, "N="),
+    (dict(H=0), gta.GT_EINVAL, "H="),
+    (dict(NB=1), gta.GT_EINVAL, "NB="),
+    (dict(NB=256), gta.GT_EINVAL, "NB="),
+    (dict(dt=7), gta.GT_EINVAL, "dtype"),
+    (dict(D=12), gta.GT_EUNSUPPORTED, "D=12"),
+    (dict(H=65), gta.GT_EUNSUPPORTED, "H=65"),
+    (dict(H=16, D=64), gta.GT_EUNSUPPORTED, "H*D"),
+    (dict(NB=100), gta.GT_EUNSUPPORTED, "NB=100"),
+])
+def test_fwd_argument_errors(kw, code, msg):
+    assert _fwd(**kw) == code
+    assert msg in gta.last_error()
+
+
+def test_bwd_argument_errors():
+    L = gta.lib()
+    N, H, D, NB = 1000, 8, 8, 33
+    need = L.gt_attn_bwd_workspace_bytes(N, H, D, NB, 1)
+    assert need >= N * H * 4
+    assert L.gt_attn_bwd_workspace_bytes(0, H, D, NB, 1) == 0
+    assert L.gt_attn_bwd_workspace_bytes(N, H, 12, NB, 1) == 0
+
+    def call(ws=P, wsb=need, dout=P, dtable=P, **kw):
+        return L.gt_attn_bwd(P, P, P, P, P, P, P, dout, P, P, P, dtable, ws, wsb,
+                             kw.get("N", N), H, D, NB, 1, None)
+    assert call(wsb=need - 1) == gta.GT_EINVAL and "workspace_bytes" in gta.last_error()
+    assert call(ws=None) == gta.GT_EINVAL
+    assert call(ws=P + 16) == gta.GT_EINVAL and "256-byte" in gta.last_error()
+    assert call(dout=None) == gta.GT_EINVAL and "dout" in gta.last_error()
+    assert call(dtable=P + 8) == gta.GT_EINVAL
+    assert call(N=-5) == gta.GT_EINVAL
+
+
+def test_workspace_query_keeps_last_error():
+    _fwd(q=None)
+    before = gta.last_error()
+    gta.lib().gt_attn_bwd_workspace_bytes(0, 8, 8, 33, 1)
+    assert gta.last_error() == before
+
+
+def _oracle_all(indptr, indices, C):
+    n = len(indptr) - 1
+    return oracle.bfs_codes(indptr, indices, C, range(n))
+
+
+@pytest.mark.parametrize("case", ["er1", "path", "components", "single", "empty", "ragged"])
+def test_spd_build_matches_oracle_small(case):
+    if case == "er1":
+        inp = make_inputs(1)
+        ip, ix, C = inp.indptr, inp.indices, inp.workload.C
+    elif case == "path":
+        ip, ix = graphs.path_graph(150)
+        C = 30
+    elif case == "components":
+        a = graphs.path_graph(70)
+        b = graphs.erdos_renyi(90, 3.0, np.random.default_rng(1))
+        u = np.concatenate([np.repeat(np.arange(70), np.diff(a[0])), 70 + np.repeat(np.arange(90), np.diff(b[0]))])
+        v = np.concatenate([a[1], 70 + b[1]])
+        ip, ix = graphs.csr_from_edges(160, u, v)
+        C = 5
+    elif case == "single":
+        ip, ix, C = np.array([0, 0], np.int64), np.zeros(0, np.int32), 3
+    elif case == "empty":
+        ip, ix, C = np.zeros(11, np.int64), np.zeros(0, np.int32), 2
+    else:
+        inp = small_case(131, 1, 8, 4, "f32", seed=2, avg_degree=2.5)
+        ip, ix, C = inp.indptr, inp.indices, 4
+    n = len(ip) - 1
+    ref = _oracle_all(ip, ix, C)
+    for nt in (1, 3):
+        got = gta.spd_build(ip, ix, n, C, nthreads=nt)
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_spd_build_c1_small_clip():
+    inp = make_inputs(1)
+    for C in (1, 2, 3):
+        ref = _oracle_all(inp.indptr, inp.indices, C)
+        got = gta.spd_build(inp.indptr, inp.indices, 256, C)
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_spd_build_rgg4096_sampled_rows_and_certificate():
+    inp = make_inputs(2)
+    w = inp.workload
+    got = gta.spd_build(inp.indptr, inp.indices, w.N, w.C)
+    rows = np.random.default_rng(5).choice(w.N, 48, replace=False)
+    ref = oracle.bfs_codes(inp.indptr, inp.indices, w.C, rows)
+    np.testing.assert_array_equal(got[rows], ref)
+    assert oracle.certify_codes(inp.indptr, inp.indices, w.C, np.arange(w.N), got)
+    # unreachable pairs exist in this graph (two components)
+    assert (got == w.C).any()
+
+
+@pytest.mark.slow
+def test_spd_build_ba32768_full_certificate():
+    inp = make_inputs(4)
+    w = inp.workload
+    got = gta.spd_build(inp.indptr, inp.indices, w.N, w.C)
+    ref = oracle.bfs_codes(inp.indptr, inp.indices, w.C, inp.rows[:40])
+    np.testing.assert_array_equal(got[inp.rows[:40]], ref)
+    src = np.arange(0, w.N, 8)   # certificate on every 8th row keeps this under a minute
+    assert oracle.certify_codes(inp.indptr, inp.indices, w.C, src, got[src])
+
+
+@pytest.mark.parametrize("bad", ["asym", "range", "order", "C0", "C255"])
+def test_spd_build_rejects_malformed(bad):
+    ip, ix = graphs.path_graph(10)
+    C = 4
+    if bad == "asym":
+        ix = ix.copy()
+        ix[0] = 5            # 0 -> 5 without 5 -> 0
+    elif bad == "range":
+        ix = ix.copy()
+        ix[3] = 10
+    elif bad == "order":
+        ip = ip.copy()
+        ip[4] = ip[5] + 1
+    elif bad == "C0":
+        C = 0
+    else:
+        C = 255
+    with pytest.raises(gta.GtError) as e:
+        gta.spd_build(ip, ix, 10, C)
+    assert e.value.code == gta.GT_EINVAL
