@@ -42,13 +42,13 @@ def work_model(name: str, N: int, H: int, D: int, s_bytes: int):
     node = N * H * D * s_bytes
     f32node = N * H * D * 4
     if name == "fwd":
-        return E * (4 * D + 4), E, N * N + 3 * node + node + N * H * 4
+        return E * (4 * D + 4), E, N * N + 3 * node + f32node + N * H * 4
     if name == "bwd_kv":
         return E * (8 * D + 5), E, N * N + 4 * node + 2 * N * H * 4 + 2 * f32node
     if name == "bwd_q":
         return E * (6 * D + 4), E, N * N + 4 * node + 2 * N * H * 4 + f32node
     if name == "bwd_delta":
-        return N * H * 2 * D, 0, 2 * node + N * H * 4
+        return N * H * 2 * D, 0, node + f32node + N * H * 4
     return 0, 0, 0
 
 
@@ -84,7 +84,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ba32768-bf16")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -121,7 +121,7 @@ def main():
     spd = torch.from_numpy(spd_host).to(dev)
     hist = np.bincount(spd_host.ravel(), minlength=NB)
     del spd_host
-    out = torch.empty_like(q)
+    out = torch.empty((N, H, D), dtype=torch.float32, device=dev)
     lse = torch.empty((N, H), dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty((N, H, D), dtype=torch.float32, device=dev) for _ in range(3))
     dtab = torch.empty((H, NB), dtype=torch.float32, device=dev)

@@ -99,18 +99,18 @@ def _dev(t, name, dtype=None, shape=None):
 
 def fwd(q, k, v, spd, table, out=None, lse=None, stream=None):
     """Forward: q, k, v [N,H,D] (float32 or bfloat16), spd [N,N] uint8, table [H,NB] float32.
-    Returns (out [N,H,D] in q's dtype, lse [N,H] float32)."""
+    Returns (out [N,H,D] float32, lse [N,H] float32)."""
     import torch
     N, H, D = q.shape
     NB = table.shape[1]
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((N, H, D), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((N, H), dtype=torch.float32, device=q.device)
     args = [_dev(q, "q", q.dtype, (N, H, D)), _dev(k, "k", q.dtype, (N, H, D)),
             _dev(v, "v", q.dtype, (N, H, D)), _dev(spd, "spd", torch.uint8, (N, N)),
-            _dev(table, "table", torch.float32, (H, NB)), _dev(out, "out", q.dtype, (N, H, D)),
+            _dev(table, "table", torch.float32, (H, NB)), _dev(out, "out", torch.float32, (N, H, D)),
             _dev(lse, "lse", torch.float32, (N, H))]
     _check("gt_attn_fwd", lib().gt_attn_fwd(*args, N, H, D, NB, dt, _stream(stream)))
     return out, lse
@@ -137,7 +137,7 @@ def bwd(q, k, v, spd, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=N
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=q.device)
     args = [_dev(q, "q", q.dtype, (N, H, D)), _dev(k, "k", q.dtype, (N, H, D)),
             _dev(v, "v", q.dtype, (N, H, D)), _dev(spd, "spd", torch.uint8, (N, N)),
-            _dev(table, "table", f32, (H, NB)), _dev(out, "out", q.dtype, (N, H, D)),
+            _dev(table, "table", f32, (H, NB)), _dev(out, "out", f32, (N, H, D)),
             _dev(lse, "lse", f32, (N, H)), _dev(dout, "dout", q.dtype, (N, H, D)),
             _dev(dq, "dq", f32, (N, H, D)), _dev(dk, "dk", f32, (N, H, D)),
             _dev(dv, "dv", f32, (N, H, D)), _dev(dtable, "dtable", f32, (H, NB)),

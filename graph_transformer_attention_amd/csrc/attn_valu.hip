@@ -23,12 +23,6 @@ __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
-__device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
-__device__ __forceinline__ void st(uint16_t* p, int64_t i, float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest, ties to even
-  p[i] = static_cast<uint16_t>(u >> 16);
-}
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------------
@@ -37,7 +31,7 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const uint8_t* __restrict__ spd, const float* __restrict__ table, T* __restrict__ out,
+    const uint8_t* __restrict__ spd, const float* __restrict__ table, float* __restrict__ out,
     float* __restrict__ lse, int64_t N, int H, int NB, int BN, float qscale) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int HD = H * D;
@@ -126,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(
   if (valid) {
     const float inv = 1.f / l;
 #pragma unroll
-    for (int d = 0; d < D; ++d) st(out, (i * H + h) * D + d, acc[d] * inv);
+    for (int d = 0; d < D; ++d) out[(i * H + h) * D + d] = acc[d] * inv;
     lse[i * H + h] = (m + log2f(l)) * kLn2;
   }
 }
@@ -134,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(
 // ---------------------------------------------------------------------------------
 // Backward, step 1: delta[i,h] = sum_d dout[i,h,d] * out[i,h,d].
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const T* __restrict__ out,
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const float* __restrict__ out,
                                                              const T* __restrict__ dout,
                                                              float* __restrict__ delta,
                                                              int64_t NH) {
@@ -142,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const T* __restrict
   if (x >= NH) return;
   float s = 0.f;
 #pragma unroll
-  for (int d = 0; d < D; ++d) s = fmaf(ld(dout, x * D + d), ld(out, x * D + d), s);
+  for (int d = 0; d < D; ++d) s = fmaf(ld(dout, x * D + d), out[x * D + d], s);
   delta[x] = s;
 }
 
@@ -388,7 +382,7 @@ hipError_t fwd_typed(const FwdArgs& a, hipStream_t s) {
   trace_begin(0, s);
   hipLaunchKernelGGL((fwd_valu_kernel<T, D>), dim3(grid), dim3(kThreads), lds, s,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), a.spd, a.table, static_cast<T*>(a.out), a.lse,
+                     static_cast<const T*>(a.v), a.spd, a.table, a.out, a.lse,
                      a.N, a.H, a.NB, BN, qscale);
   const hipError_t e = hipGetLastError();
   trace_end(0, s);
@@ -410,7 +404,7 @@ hipError_t bwd_typed(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
 
   trace_begin(1, s);
   hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(static_cast<unsigned>((NH + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, static_cast<const T*>(a.out), dout, delta, NH);
+                     dim3(kThreads), 0, s, a.out, dout, delta, NH);
   hipError_t e = hipGetLastError();
   trace_end(1, s);
   if (e != hipSuccess) return e;

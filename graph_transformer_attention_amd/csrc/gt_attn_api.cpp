@@ -175,7 +175,7 @@ const char* gt_kernel_name(int32_t id) {
 }
 
 int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd, const float* table,
-                void* out, float* lse, int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype,
+                float* out, float* lse, int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype,
                 void* stream) {
   GT_CHECK(check_shape(N, H, D, NB, dtype));
   GT_CHECK(check_ptr(q, "q"));
@@ -198,7 +198,7 @@ size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, 
 }
 
 int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd, const float* table,
-                const void* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                const float* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
                 float* dtable, void* workspace, size_t workspace_bytes, int64_t N, int32_t H,
                 int32_t D, int32_t NB, int32_t dtype, void* stream) {
   GT_CHECK(check_shape(N, H, D, NB, dtype));

@@ -13,7 +13,7 @@ struct FwdArgs {
   const void* v;
   const uint8_t* spd;
   const float* table;
-  void* out;
+  float* out;
   float* lse;
   int64_t N;
   int H, D, NB, dtype;
@@ -25,7 +25,7 @@ struct BwdArgs {
   const void* v;
   const uint8_t* spd;
   const float* table;
-  const void* out;
+  const float* out;
   const float* lse;
   const void* dout;
   float* dq;

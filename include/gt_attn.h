@@ -19,9 +19,10 @@
  *       lse                              [N, H]      float32, natural log
  *       spd                              [N, N]      uint8, row = query node i, column = key node j
  *       table, dtable                    [H, NB]     float32
- *   - dtype selects the storage type of q, k, v, out and dout: GT_F32 (float)
- *     or GT_BF16 (bfloat16 bits). Arithmetic is float32 throughout; table,
- *     lse and every gradient are float32.
+ *   - dtype selects the storage type of the inputs q, k, v and dout: GT_F32
+ *     (float) or GT_BF16 (bfloat16 bits). Arithmetic is float32 throughout and
+ *     every output (out, lse, dq, dk, dv, dtable) is float32, so a bfloat16
+ *     caller loses nothing to output rounding; table is float32.
  *   - Pointers marked "device" are device memory owned by the caller; the
  *     library never allocates, frees or synchronises device memory, and keeps
  *     no state between calls. Every base pointer must be 16-byte aligned.
@@ -59,10 +60,10 @@ typedef enum {
 
 /* Forward of one biased attention layer (abstract and Fig. 4 of the MegaGraph pages).
  *   q, k, v  device [N,H,D] dtype        spd    device [N,N] uint8
- *   table    device [H,NB] float32       out    device [N,H,D] dtype (overwritten)
+ *   table    device [H,NB] float32       out    device [N,H,D] float32 (overwritten)
  *   lse      device [N,H] float32 (overwritten; the backward needs it)            */
 int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
-                const float* table, void* out, float* lse, int64_t N, int32_t H,
+                const float* table, float* out, float* lse, int64_t N, int32_t H,
                 int32_t D, int32_t NB, int32_t dtype, void* stream);
 
 /* Bytes of device workspace gt_attn_bwd needs for these sizes (0 on invalid sizes). */
@@ -70,6 +71,7 @@ size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, 
 
 /* Backward of gt_attn_fwd for the loss sum(dout * out): recomputes the scores and the
  * softmax from q, k, spd, table and lse (the forward's outputs out and lse are inputs).
+ *   out                    device [N,H,D] float32, as written by gt_attn_fwd
  *   dout                   device [N,H,D] dtype
  *   dq, dk, dv             device [N,H,D] float32 (overwritten)
  *   dtable                 device [H,NB]  float32 (overwritten, not accumulated):
@@ -79,7 +81,7 @@ size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, 
  *                          workspace must be ordered on one stream.
  * Results are bitwise reproducible run to run (no floating-point atomics).           */
 int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
-                const float* table, const void* out, const float* lse, const void* dout,
+                const float* table, const float* out, const float* lse, const void* dout,
                 float* dq, float* dk, float* dv, float* dtable, void* workspace,
                 size_t workspace_bytes, int64_t N, int32_t H, int32_t D, int32_t NB,
                 int32_t dtype, void* stream);

@@ -89,7 +89,18 @@ def sum_dtable_rows(dtable_blocks):
 _G = {}
 
 
-def _pool_init(q, k, v, codes, table, dout):
+def _one_blas_thread():
+    # one BLAS thread per pool worker, so the workers do not oversubscribe the cores
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
+def _pool_init(q, k, v, codes, table, dout, one_thread=False):
+    if one_thread:
+        _one_blas_thread()
     _G.update(q=q, k=k, v=v, codes=codes, table=table, dout=dout)
 
 
@@ -133,7 +144,7 @@ def full_backward(q, k, v, codes, table, dout, block: int = 256, workers: int = 
     else:
         import multiprocessing as mp
         ctx = mp.get_context("fork")
-        pool = ctx.Pool(workers, initializer=_pool_init, initargs=(qs, k, v, cs, table, ds))
+        pool = ctx.Pool(workers, initializer=_pool_init, initargs=(qs, k, v, cs, table, ds, True))
         results = pool.imap(_pool_block, spans)  # in block order
     for r0, o, l, dqb, dkb, dvb, dtb in results:
         r1 = r0 + o.shape[0]

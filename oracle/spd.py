@@ -52,7 +52,17 @@ def bfs_codes(indptr, indices, C: int, sources, adj=None) -> np.ndarray:
 _G = {}
 
 
+def _one_blas_thread():
+    # one BLAS thread per pool worker, so the workers do not oversubscribe the cores
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
 def _pool_init(indptr, indices, C):
+    _one_blas_thread()
     _G["adj"] = _adjacency(indptr, indices)
     _G["args"] = (indptr, indices, C)
 
