@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.gt_trace_enable.restype = ctypes.c_int
         L.gt_trace_collect.argtypes = [P, P, I32]
         L.gt_trace_collect.restype = ctypes.c_int
+        L.gt_probe_peak.argtypes = [I32, I32, I32, P, P]
+        L.gt_probe_peak.restype = ctypes.c_int
         L.gt_kernel_name.argtypes = [I32]
         L.gt_kernel_name.restype = ctypes.c_char_p
         _lib = L
@@ -184,3 +186,28 @@ def trace_collect() -> dict:
     ms = (ctypes.c_double * KERNEL_COUNT)()
     _check("gt_trace_collect", lib().gt_trace_collect(counts, ms, KERNEL_COUNT))
     return {n: (int(counts[i]), float(ms[i])) for i, n in enumerate(kernel_names()) if counts[i]}
+
+
+PROBES = {0: ("exp2", "Gop/s"), 1: ("fma", "Gop/s"), 2: ("exp2 with 4 fma", "Gexp/s"),
+          3: ("mfma 32x32x8 bf16", "TFLOP/s"), 4: ("mfma 32x32x16 bf16", "TFLOP/s")}
+
+
+def probe_peak(kind: int, blocks: int = 4096, iters: int = 2048, repeats: int = 3) -> float:
+    """Measured rate of one unit (see gt_probe_peak); best of `repeats` timed launches."""
+    import torch
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    best = None
+    for _ in range(repeats + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        _check("gt_probe_peak", lib().gt_probe_peak(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                                    ctypes.c_void_p(s.cuda_stream)))
+        b.record()
+        b.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    if kind in (0, 1, 2):
+        return blocks * 256 * iters * 8 / (best * 1e-3) / 1e9
+    flops = 16384 if kind == 3 else 32768
+    return blocks * 4 * iters * 4 * flops / (best * 1e-3) / 1e12

@@ -125,13 +125,6 @@ BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype) {
   return w;
 }
 
-bool use_mfma(int H, int D, int dtype) {
-  (void)H;
-  (void)D;
-  (void)dtype;
-  return false;
-}
-
 }  // namespace gt
 
 extern "C" {
@@ -170,6 +163,15 @@ int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n) {
   return rc;
 }
 
+int gt_probe_peak(int32_t kind, int32_t blocks, int32_t iters, float* sink, void* stream) {
+  if (kind < 0 || kind > 4) return fail(GT_EINVAL, "probe kind=%d must lie in [0, 4]", kind);
+  if (blocks < 1 || blocks > (1 << 20)) return fail(GT_EINVAL, "probe blocks=%d out of range", blocks);
+  if (iters < 1) return fail(GT_EINVAL, "probe iters=%d must be >= 1", iters);
+  if (sink == nullptr) return fail(GT_EINVAL, "probe sink is null");
+  return hip_status(gt::launch_probe(kind, blocks, iters, sink, static_cast<hipStream_t>(stream)),
+                    "gt_probe_peak launch");
+}
+
 const char* gt_kernel_name(int32_t id) {
   return (id >= 0 && id < GT_KERNEL_COUNT) ? kKernelNames[id] : "";
 }
@@ -186,7 +188,9 @@ int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(out, "out"));
   GT_CHECK(check_ptr(lse, "lse"));
   gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype};
-  return hip_status(gt::launch_fwd_valu(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd launch");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = gt::mfma_supported(H, D, dtype) ? gt::launch_fwd_mfma(a, s) : gt::launch_fwd_valu(a, s);
+  return hip_status(e, "gt_attn_fwd launch");
 }
 
 size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype) {

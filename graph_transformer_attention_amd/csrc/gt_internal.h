@@ -44,10 +44,6 @@ struct BwdWorkspace {
   int64_t n_kv_blocks;
 };
 
-// Which kernel family serves a shape: the MFMA kernels (bf16, D in {8, 32}, H = 8)
-// or the general vector-ALU kernels.
-bool use_mfma(int H, int D, int dtype);
-
 // Kernel timing hook (gt_trace_enable): bracket one launch with events on its stream.
 void trace_begin(int kernel_id, hipStream_t s);
 void trace_end(int kernel_id, hipStream_t s);
@@ -55,7 +51,10 @@ void trace_end(int kernel_id, hipStream_t s);
 BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype);
 
 hipError_t launch_fwd_valu(const FwdArgs& a, hipStream_t s);
+bool mfma_supported(int H, int D, int dtype);
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_valu(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 int64_t valu_kv_block(int H);
+hipError_t launch_probe(int kind, int blocks, int iters, float* sink, hipStream_t s);
 
 }  // namespace gt

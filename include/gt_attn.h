@@ -123,6 +123,19 @@ int gt_trace_enable(int32_t on);
 int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n);
 const char* gt_kernel_name(int32_t id);
 
+/* Unit-throughput probe, used to state the measured peaks the attention kernels are
+ * held against (the exp-throughput bound in particular). Launches `blocks` workgroups
+ * of 256 threads on `stream`; each thread runs `iters` steps of 8 independent chains.
+ *   kind 0: v_exp_f32 (hardware exp2)            ops = blocks*256*iters*8
+ *   kind 1: fp32 fused multiply-add               ops = blocks*256*iters*8
+ *   kind 2: one exp2 + four fma per chain step    ops = blocks*256*iters*8 exps
+ *   kind 3: bf16 MFMA 32x32x8                     flops = blocks*4*iters*4*16384
+ *   kind 4: bf16 MFMA 32x32x16                    flops = blocks*4*iters*4*32768
+ * sink: device float [blocks*256] (overwritten with values that keep the work live).
+ * The caller times the launch. Errors: GT_EINVAL for kind outside [0,4], blocks
+ * outside [1, 1<<20], iters < 1 or a null sink.                                      */
+int gt_probe_peak(int32_t kind, int32_t blocks, int32_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
