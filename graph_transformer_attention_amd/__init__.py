@@ -42,7 +42,7 @@ def lib() -> ctypes.CDLL:
         L.gt_attn_fwd.restype = ctypes.c_int
         L.gt_attn_bwd_workspace_bytes.argtypes = [I64, I32, I32, I32, I32]
         L.gt_attn_bwd_workspace_bytes.restype = SZ
-        L.gt_attn_bwd.argtypes = [P] * 13 + [SZ, I64, I32, I32, I32, I32, P]
+        L.gt_attn_bwd.argtypes = [P] * 14 + [SZ, I64, I32, I32, I32, I32, P]
         L.gt_attn_bwd.restype = ctypes.c_int
         L.gt_spd_build.argtypes = [P, P, I64, I32, P, I32]
         L.gt_spd_build.restype = ctypes.c_int
@@ -123,8 +123,10 @@ def bwd_workspace_bytes(N: int, H: int, D: int, NB: int, dtype: int) -> int:
 
 
 def bwd(q, k, v, spd, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=None,
-        workspace=None, stream=None):
-    """Backward of fwd for loss sum(dout*out). Returns (dq, dk, dv [N,H,D] float32, dtable [H,NB])."""
+        workspace=None, stream=None, spd_t=None):
+    """Backward of fwd for loss sum(dout*out). Returns (dq, dk, dv [N,H,D] float32, dtable [H,NB]).
+
+    spd_t is the transpose of spd; None means spd is symmetric (undirected graph)."""
     import torch
     N, H, D = q.shape
     NB = table.shape[1]
@@ -139,6 +141,7 @@ def bwd(q, k, v, spd, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=N
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=q.device)
     args = [_dev(q, "q", q.dtype, (N, H, D)), _dev(k, "k", q.dtype, (N, H, D)),
             _dev(v, "v", q.dtype, (N, H, D)), _dev(spd, "spd", torch.uint8, (N, N)),
+            _dev(spd if spd_t is None else spd_t, "spd_t", torch.uint8, (N, N)),
             _dev(table, "table", f32, (H, NB)), _dev(out, "out", f32, (N, H, D)),
             _dev(lse, "lse", f32, (N, H)), _dev(dout, "dout", q.dtype, (N, H, D)),
             _dev(dq, "dq", f32, (N, H, D)), _dev(dk, "dk", f32, (N, H, D)),

@@ -1,5 +1,12 @@
-// Biased attention on the bf16 matrix cores (gfx950 MFMA): head dimension 8, bf16
-// inputs, float32 accumulation and outputs.
+// Biased attention on the gfx950 matrix cores (MFMA): head dimension 8, 8 heads,
+// bfloat16 inputs, float32 accumulation and outputs.
+//
+// Precision: the scores QK^T and dO V^T multiply the bf16 inputs exactly. Softmax
+// probabilities P and score gradients dS enter the contractions over nodes (P.V,
+// P^T dO, dS^T Q, dS K) as IEEE half precision (11-bit significand; bf16's 8 bits
+// leave a max error near 4-7% of the gradients' RMS on heavy-tailed rows), and the
+// bf16 inputs they meet are converted to half exactly (inputs must lie within
+// half's range, |x| < 65504).
 //
 // MegaGraph pages, abstract: the score matrix and the topology-aware bias matrix are
 // what make full-graph attention expensive; Fig. 4 caption: work proceeds over key
@@ -38,6 +45,7 @@ constexpr int kHD = kH * kD;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -64,24 +72,33 @@ __device__ __forceinline__ s16x4 load_op4(const uint16_t* base, int64_t node, in
   return s16x4{0, 0, 0, 0};
 }
 
-__device__ __forceinline__ s16x8 pack_bf16x8(const f32x16& a, int first) {
-  bf16x8 r;
+__device__ __forceinline__ s16x8 pack_f16x8(const f32x16& a, int first) {
+  f16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(a[first + e]);
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<_Float16>(a[first + e]);
   return __builtin_bit_cast(s16x8, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Two bf16 in one dword -> two halves in one dword (same element order).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 r = {static_cast<_Float16>(bf16_lo(w)), static_cast<_Float16>(bf16_hi(w))};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ f32x16 mfma_x8(s16x4 a, s16x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x16 mfma_x16(s16x8 a, s16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                  c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma_h16(s16x8 a, s16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                 0, 0, 0);
 }
 
-// Stage the transposed tile T[hl][d][0..31] (bf16) of nodes n0..n0+31 for the wave's
-// heads h0, h0+1 from a node-major [N][H][D] bf16 tensor: lane (hl, group g of 4 nodes,
-// d-pair dp) loads 4 dwords and packs them into two 8-byte rows of the tile.
+// Stage the transposed half-precision tile T[hl][d][0..31] of nodes n0..n0+31 for the
+// wave's heads h0, h0+1 from a node-major [N][H][D] bf16 tensor: lane (hl, group g of 4
+// nodes, d-pair dp) loads 4 dwords, converts them and packs two 8-byte rows of the tile.
 __device__ __forceinline__ void stage_transposed(uint16_t* tile, const uint16_t* src, int64_t n0,
                                                  int64_t N, int h0, int lane) {
   const int hl = lane >> 5, g = (lane >> 2) & 7, dp = lane & 3;
@@ -89,7 +106,8 @@ __device__ __forceinline__ void stage_transposed(uint16_t* tile, const uint16_t*
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t n = n0 + 4 * g + r;
-    w[r] = n < N ? *reinterpret_cast<const uint32_t*>(src + n * kHD + (h0 + hl) * kD + 2 * dp) : 0u;
+    w[r] = n < N ? bf16x2_to_f16x2(*reinterpret_cast<const uint32_t*>(src + n * kHD + (h0 + hl) * kD + 2 * dp))
+                 : 0u;
   }
   // low halves are d = 2dp, high halves d = 2dp+1
   const u32x2 lo = {__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)};
@@ -98,18 +116,19 @@ __device__ __forceinline__ void stage_transposed(uint16_t* tile, const uint16_t*
   *reinterpret_cast<u32x2*>(tile + (hl * kD + 2 * dp + 1) * 32 + 4 * g) = hi;
 }
 
-// A operand of the contraction over 8 nodes: rows m < 8 are T[hl][m][first..first+7];
-// row 8 is all ones when `ones_row` (it yields the row sums); other rows are zero.
+// A operand of a half-precision contraction over 8 nodes: rows m < 8 are
+// T[hl][m][first..first+7]; row 8 is all ones when `ones_row` (it yields the row sums);
+// other rows are zero.
 __device__ __forceinline__ s16x8 read_operand_t(const uint16_t* tile, int hl, int m, int first, bool ones_row) {
   if (m < kD) return *reinterpret_cast<const s16x8*>(tile + (hl * kD + m) * 32 + first);
-  const short one = ones_row && m == kD ? static_cast<short>(0x3F80) : static_cast<short>(0);
+  const short one = ones_row && m == kD ? static_cast<short>(0x3C00) : static_cast<short>(0);
   return s16x8{one, one, one, one, one, one, one, one};
 }
 
 // ---------------------------------------------------------------------------------
 // Forward. S^T = K Q^T per 32-key tile (rows = keys in the order above, columns =
-// queries); running max and sum per query column; O^T += V^T P^T with a ones row in
-// V^T so the MFMA also accumulates the row sum l.
+// queries); running max per query column; O^T += V^T P^T with a ones row in V^T so
+// the MFMA also accumulates the row sum l.
 template <bool kAligned>
 __global__ __launch_bounds__(64) void fwd_mfma_d8_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
@@ -198,8 +217,8 @@ __global__ __launch_bounds__(64) void fwd_mfma_d8_kernel(const uint16_t* __restr
     for (int k1 = 0; k1 < 2; ++k1) {
       const s16x8 va = read_operand_t(vt, 0, c, 16 * hp + 8 * k1, true);
       const s16x8 vb = read_operand_t(vt, 1, c, 16 * hp + 8 * k1, true);
-      o0 = mfma_x16(va, pack_bf16x8(s0, 8 * k1), o0);
-      o1 = mfma_x16(vb, pack_bf16x8(s1, 8 * k1), o1);
+      o0 = mfma_h16(va, pack_f16x8(s0, 8 * k1), o0);
+      o1 = mfma_h16(vb, pack_f16x8(s1, 8 * k1), o1);
     }
   }
   // O^T rows: d = 4hp + e in entries e = 0..3; row 8 (lane half 0, entry 4) is l.
@@ -216,9 +235,300 @@ __global__ __launch_bounds__(64) void fwd_mfma_d8_kernel(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Backward operand copies, written once per call into the workspace for all Npad =
+// N rounded up to 32 nodes (rows past N padded so the main loops need no bounds
+// checks). Augmented half-precision rows [node][head][16] fold the per-query terms of
+// the backward into the score MFMAs (contraction index 8.. holds the extra columns):
+//   qa  = [q(8), -L_hi, -L_lo, 1, 0..]    L = lse * sqrt(D), split into two halves
+//   ka  = [k(8),  1,     1,  pen, 0..]    pen = 0, or -inf for padded keys
+//   doa = [do(8), -dl_hi, -dl_lo, 0..]    dl = delta = <dout, out>
+//   va  = [v(8),  1,     1,   0, 0..]
+// so that qa.ka = q.k - lse*sqrt(D) (+ -inf past N) and doa.va = dout.v - delta. Padded
+// queries get -L_hi = -inf. Transposed half copies [head][d][node] of q, k and dout are
+// the A operands of the contractions over nodes.
+struct BwdOps {
+  uint16_t *qa, *ka, *doa, *va, *qt, *kt, *ot;
+  int64_t npad;
+};
+
+__global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v,
+                                                               const float* __restrict__ out,
+                                                               const uint16_t* __restrict__ dout,
+                                                               const float* __restrict__ lse, BwdOps ops,
+                                                               int64_t N) {
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t npad = ops.npad;
+  if (x >= npad * kH) return;
+  const int h = static_cast<int>(x / npad);
+  const int64_t n = x - h * npad;
+  // Rows are assembled as raw half bit patterns (uint16) and stored as four dwordx4.
+  uint16_t qa[16] = {}, ka[16] = {}, da[16] = {}, va[16] = {};
+  auto hbits = [](float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); };
+  const uint16_t one = hbits(1.0f);
+  const uint16_t ninf = hbits(-INFINITY);
+  ka[8] = one;
+  ka[9] = one;
+  va[8] = one;
+  va[9] = one;
+  qa[10] = one;
+  if (n < N) {
+    const int64_t r = n * kH + h;
+    const u32x4 qw = *reinterpret_cast<const u32x4*>(q + r * kD);
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(k + r * kD);
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(v + r * kD);
+    const u32x4 dw = *reinterpret_cast<const u32x4*>(dout + r * kD);
+    const float4 o0 = *reinterpret_cast<const float4*>(out + r * kD);
+    const float4 o1 = *reinterpret_cast<const float4*>(out + r * kD + 4);
+    const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+    float delta = 0.f;
+#pragma unroll
+    for (int d = 0; d < kD; ++d) {
+      const int wi = d >> 1;
+      const float qf = (d & 1) ? bf16_hi(qw[wi]) : bf16_lo(qw[wi]);
+      const float kf = (d & 1) ? bf16_hi(kw[wi]) : bf16_lo(kw[wi]);
+      const float vf = (d & 1) ? bf16_hi(vw[wi]) : bf16_lo(vw[wi]);
+      const float df = (d & 1) ? bf16_hi(dw[wi]) : bf16_lo(dw[wi]);
+      delta = fmaf(df, ov[d], delta);
+      qa[d] = hbits(qf);
+      ka[d] = hbits(kf);
+      va[d] = hbits(vf);
+      da[d] = hbits(df);
+    }
+    const float L = lse[r] * sqrtf(static_cast<float>(kD));
+    const _Float16 lh = static_cast<_Float16>(L);
+    qa[8] = hbits(-static_cast<float>(lh));
+    qa[9] = hbits(-(L - static_cast<float>(lh)));
+    const _Float16 dh = static_cast<_Float16>(delta);
+    da[8] = hbits(-static_cast<float>(dh));
+    da[9] = hbits(-(delta - static_cast<float>(dh)));
+  } else {
+    qa[8] = ninf;
+    ka[10] = ninf;
+  }
+  auto pack = [](const uint16_t* e, int first) {
+    u32x4 w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      w[t] = static_cast<uint32_t>(e[first + 2 * t]) | (static_cast<uint32_t>(e[first + 2 * t + 1]) << 16);
+    return w;
+  };
+  const int64_t row = (n * kH + h) * 16;
+  u32x4* qa_out = reinterpret_cast<u32x4*>(ops.qa + row);
+  u32x4* ka_out = reinterpret_cast<u32x4*>(ops.ka + row);
+  u32x4* da_out = reinterpret_cast<u32x4*>(ops.doa + row);
+  u32x4* va_out = reinterpret_cast<u32x4*>(ops.va + row);
+  qa_out[0] = pack(qa, 0);
+  qa_out[1] = pack(qa, 8);
+  ka_out[0] = pack(ka, 0);
+  ka_out[1] = pack(ka, 8);
+  da_out[0] = pack(da, 0);
+  da_out[1] = pack(da, 8);
+  va_out[0] = pack(va, 0);
+  va_out[1] = pack(va, 8);
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    const int64_t t = (static_cast<int64_t>(h) * kD + d) * npad + n;
+    ops.qt[t] = qa[d];
+    ops.kt[t] = ka[d];
+    ops.ot[t] = da[d];
+  }
+}
+
+__device__ __forceinline__ s16x8 load_h8(const uint16_t* p) { return *reinterpret_cast<const s16x8*>(p); }
+
+// A operand rows m < 8 of a transposed [head][d][npad] half copy, 8 consecutive nodes.
+__device__ __forceinline__ s16x8 load_t8(const uint16_t* t, int64_t npad, int h, int m, int64_t first) {
+  if (m < kD) return *reinterpret_cast<const s16x8*>(t + (static_cast<int64_t>(h) * kD + m) * npad + first);
+  return s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+// Backward, step 2 (key-outer): a wave owns 32 keys x 2 heads and sweeps all query
+// tiles, reading the codes of its keys along rows of the transposed code matrix. S = Q K^T - lse and dP - delta = dO V^T - delta come out of two augmented
+// MFMAs with rows = queries (order a(r)) and columns = keys, so lane c keeps key c for
+// the whole kernel and its accumulator entries are queries 16*hp + 0..15; then
+// P = exp2(S log2e / sqrt(D)) and dS = P (dP - delta) need one multiply each.
+// dV^T += dO^T P and dK^T += Q^T dS contract over those queries. Bucket sums of dS
+// go to per-lane LDS bins ([head][bucket][lane]: no two lanes share an address),
+// reduced in a fixed order at the end.
+template <bool kAligned>
+__global__ __launch_bounds__(64) void bwd_kv_mfma_d8_kernel(const uint8_t* __restrict__ spd_t,
+                                                            const float* __restrict__ table, BwdOps ops,
+                                                            float* __restrict__ dk, float* __restrict__ dv,
+                                                            float* __restrict__ partial, int64_t N, int NB) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* bins = reinterpret_cast<float*>(smem);                 // [2][NB][64]
+  float* tb = bins + 2 * NB * 64;                                // [2][256]
+
+  const int lane = threadIdx.x;
+  const int c = lane & 31, hp = lane >> 5;
+  const int h0 = 2 * blockIdx.y;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 32;
+  const int64_t j = j0 + c;
+  const int64_t npad = ops.npad;
+  const float sqd = sqrtf(static_cast<float>(kD));
+  const float sc2 = kLog2e / sqd;
+
+  for (int x = lane; x < 512; x += 64) {
+    const int hl = x >> 8, b = x & 255;
+    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  }
+  for (int x = lane; x < 2 * NB * 64; x += 64) bins[x] = 0.f;
+  // B operands over the key columns: [k | 1, 1, pen] and [v | 1, 1], halves 8*hp..
+  const s16x8 kb0 = load_h8(ops.ka + (j * kH + h0) * 16 + 8 * hp);
+  const s16x8 kb1 = load_h8(ops.ka + (j * kH + h0 + 1) * 16 + 8 * hp);
+  const s16x8 vb0 = load_h8(ops.va + (j * kH + h0) * 16 + 8 * hp);
+  const s16x8 vb1 = load_h8(ops.va + (j * kH + h0 + 1) * 16 + 8 * hp);
+  f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
+  const int qr = node_of_row(c);  // the query this lane feeds as A-operand row c
+  const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
+  const bool kvalid = j < N;
+  const uint8_t* crow = spd_t + (kvalid ? j : 0) * N;
+  __syncthreads();
+
+  for (int64_t i0 = 0; i0 < npad; i0 += 32) {
+    const int64_t qrow = (i0 + qr) * kH;
+    const s16x8 qa0 = load_h8(ops.qa + (qrow + h0) * 16 + 8 * hp);
+    const s16x8 qa1 = load_h8(ops.qa + (qrow + h0 + 1) * 16 + 8 * hp);
+    const s16x8 oa0 = load_h8(ops.doa + (qrow + h0) * 16 + 8 * hp);
+    const s16x8 oa1 = load_h8(ops.doa + (qrow + h0 + 1) * 16 + 8 * hp);
+    const u32x4 cw = kvalid ? load_codes16<kAligned>(crow, i0 + 16 * hp, N) : u32x4{0u, 0u, 0u, 0u};
+    f32x16 s0, s1;
+    uint32_t code[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      code[e] = min(code_byte(cw, e), nbm1);
+      s0[e] = tb[code[e]];
+      s1[e] = tb[256 + code[e]];
+    }
+    s0 = mfma_h16(qa0, kb0, s0);
+    s1 = mfma_h16(qa1, kb1, s1);
+    f32x16 p0 = mfma_h16(oa0, vb0, f32x16{});
+    f32x16 p1 = mfma_h16(oa1, vb1, f32x16{});
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pa = __builtin_amdgcn_exp2f(s0[e] * sc2);
+      const float pb = __builtin_amdgcn_exp2f(s1[e] * sc2);
+      const float dsa = pa * p0[e];
+      const float dsb = pb * p1[e];
+      s0[e] = pa;
+      s1[e] = pb;
+      p0[e] = dsa;
+      p1[e] = dsb;
+      // private to this lane: plain read-add-write (LDS float atomics are far slower)
+      float* bin = bins + code[e] * 64 + lane;
+      bin[0] += dsa;
+      bin[NB * 64] += dsb;
+    }
+#pragma unroll
+    for (int k1 = 0; k1 < 2; ++k1) {
+      const int64_t first = i0 + 16 * hp + 8 * k1;
+      dv0 = mfma_h16(load_t8(ops.ot, npad, h0, c, first), pack_f16x8(s0, 8 * k1), dv0);
+      dv1 = mfma_h16(load_t8(ops.ot, npad, h0 + 1, c, first), pack_f16x8(s1, 8 * k1), dv1);
+      dk0 = mfma_h16(load_t8(ops.qt, npad, h0, c, first), pack_f16x8(p0, 8 * k1), dk0);
+      dk1 = mfma_h16(load_t8(ops.qt, npad, h0 + 1, c, first), pack_f16x8(p1, 8 * k1), dk1);
+    }
+  }
+  if (j < N) {
+    const float rs = 1.f / sqd;
+    float* kp = dk + j * kHD + h0 * kD + 4 * hp;
+    float* vp = dv + j * kHD + h0 * kD + 4 * hp;
+    *reinterpret_cast<float4*>(kp) = make_float4(dk0[0] * rs, dk0[1] * rs, dk0[2] * rs, dk0[3] * rs);
+    *reinterpret_cast<float4*>(kp + kD) = make_float4(dk1[0] * rs, dk1[1] * rs, dk1[2] * rs, dk1[3] * rs);
+    *reinterpret_cast<float4*>(vp) = make_float4(dv0[0], dv0[1], dv0[2], dv0[3]);
+    *reinterpret_cast<float4*>(vp + kD) = make_float4(dv1[0], dv1[1], dv1[2], dv1[3]);
+  }
+  __syncthreads();
+  for (int x = lane; x < 2 * NB; x += 64) {
+    float sum = 0.f;
+    for (int l = 0; l < 64; ++l) sum += bins[x * 64 + l];
+    const int hl = x / NB, b = x - hl * NB;
+    partial[(static_cast<int64_t>(blockIdx.x) * kH + h0 + hl) * NB + b] = sum;
+  }
+}
+
+// Backward, step 3 (query-outer): same orientation as the forward (lane c = query c);
+// S^T - lse and dP^T - delta from the augmented MFMAs, dQ^T += K^T dS^T per key tile.
+template <bool kAligned>
+__global__ __launch_bounds__(64) void bwd_q_mfma_d8_kernel(const uint8_t* __restrict__ spd,
+                                                           const float* __restrict__ table, BwdOps ops,
+                                                           float* __restrict__ dq, int64_t N, int NB) {
+  __shared__ float tb[2 * 256];
+  const int lane = threadIdx.x;
+  const int c = lane & 31, hp = lane >> 5;
+  const int h0 = 2 * blockIdx.y;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 32;
+  const int64_t i = i0 + c;
+  const bool qvalid = i < N;
+  const int64_t npad = ops.npad;
+  const float sqd = sqrtf(static_cast<float>(kD));
+  const float sc2 = kLog2e / sqd;
+
+  for (int x = lane; x < 512; x += 64) {
+    const int hl = x >> 8, b = x & 255;
+    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  }
+  const s16x8 qb0 = load_h8(ops.qa + (i * kH + h0) * 16 + 8 * hp);
+  const s16x8 qb1 = load_h8(ops.qa + (i * kH + h0 + 1) * 16 + 8 * hp);
+  const s16x8 ob0 = load_h8(ops.doa + (i * kH + h0) * 16 + 8 * hp);
+  const s16x8 ob1 = load_h8(ops.doa + (i * kH + h0 + 1) * 16 + 8 * hp);
+  const uint8_t* srow = spd + (qvalid ? i : 0) * N;
+  f32x16 dq0 = {}, dq1 = {};
+  const int kr = node_of_row(c);
+  __syncthreads();
+
+  for (int64_t j0 = 0; j0 < npad; j0 += 32) {
+    const u32x4 cw = qvalid ? load_codes16<kAligned>(srow, j0 + 16 * hp, N) : u32x4{0u, 0u, 0u, 0u};
+    const int64_t krow = (j0 + kr) * kH;
+    const s16x8 ka0 = load_h8(ops.ka + (krow + h0) * 16 + 8 * hp);
+    const s16x8 ka1 = load_h8(ops.ka + (krow + h0 + 1) * 16 + 8 * hp);
+    const s16x8 va0 = load_h8(ops.va + (krow + h0) * 16 + 8 * hp);
+    const s16x8 va1 = load_h8(ops.va + (krow + h0 + 1) * 16 + 8 * hp);
+    f32x16 s0, s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t cb = code_byte(cw, e);
+      s0[e] = tb[cb];
+      s1[e] = tb[256 + cb];
+    }
+    s0 = mfma_h16(ka0, qb0, s0);
+    s1 = mfma_h16(ka1, qb1, s1);
+    f32x16 p0 = mfma_h16(va0, ob0, f32x16{});
+    f32x16 p1 = mfma_h16(va1, ob1, f32x16{});
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p0[e] *= __builtin_amdgcn_exp2f(s0[e] * sc2);
+      p1[e] *= __builtin_amdgcn_exp2f(s1[e] * sc2);
+    }
+#pragma unroll
+    for (int k1 = 0; k1 < 2; ++k1) {
+      const int64_t first = j0 + 16 * hp + 8 * k1;
+      dq0 = mfma_h16(load_t8(ops.kt, npad, h0, c, first), pack_f16x8(p0, 8 * k1), dq0);
+      dq1 = mfma_h16(load_t8(ops.kt, npad, h0 + 1, c, first), pack_f16x8(p1, 8 * k1), dq1);
+    }
+  }
+  if (qvalid) {
+    const float rs = 1.f / sqd;
+    float* qp = dq + i * kHD + h0 * kD + 4 * hp;
+    *reinterpret_cast<float4*>(qp) = make_float4(dq0[0] * rs, dq0[1] * rs, dq0[2] * rs, dq0[3] * rs);
+    *reinterpret_cast<float4*>(qp + kD) = make_float4(dq1[0] * rs, dq1[1] * rs, dq1[2] * rs, dq1[3] * rs);
+  }
+}
+
+size_t kv_mfma_lds(int NB) { return 4ull * 2 * NB * 64 + 4ull * 512; }
+
 }  // namespace
 
 bool mfma_supported(int H, int D, int dtype) { return H == kH && D == kD && dtype == 1; }
+
+int64_t mfma_npad(int64_t N) { return (N + 31) / 32 * 32; }
+
+size_t mfma_ops_bytes(int64_t N) {
+  const size_t npad = static_cast<size_t>(mfma_npad(N));
+  return 4 * npad * kH * 16 * 2 + 3 * npad * kH * kD * 2;
+}
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.N + 31) / 32), kH / 2);
@@ -234,6 +544,56 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const hipError_t e = hipGetLastError();
   trace_end(0, s);
   return e;
+}
+
+hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
+  char* ws = static_cast<char*>(a.workspace);
+  float* partial = reinterpret_cast<float*>(ws + w.partial_off);
+  BwdOps ops;
+  ops.npad = mfma_npad(a.N);
+  const size_t big = static_cast<size_t>(ops.npad) * kH * 16;  // halves per augmented copy
+  const size_t small = static_cast<size_t>(ops.npad) * kH * kD;
+  uint16_t* base = reinterpret_cast<uint16_t*>(ws + w.ops_off);
+  ops.qa = base;
+  ops.ka = ops.qa + big;
+  ops.doa = ops.ka + big;
+  ops.va = ops.doa + big;
+  ops.qt = ops.va + big;
+  ops.kt = ops.qt + small;
+  ops.ot = ops.kt + small;
+  const bool aligned = a.N % 16 == 0;
+
+  trace_begin(1, s);
+  hipLaunchKernelGGL(bwd_prep_mfma_d8_kernel, dim3(static_cast<unsigned>((ops.npad * kH + 255) / 256)), dim3(256),
+                     0, s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.out, static_cast<const uint16_t*>(a.dout), a.lse, ops,
+                     a.N);
+  hipError_t e = hipGetLastError();
+  trace_end(1, s);
+  if (e != hipSuccess) return e;
+
+  const dim3 grid(static_cast<unsigned>(ops.npad / 32), kH / 2);
+  const size_t lds = kv_mfma_lds(a.NB);
+  trace_begin(2, s);
+  if (aligned)
+    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<true>, grid, dim3(64), lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
+                       partial, a.N, a.NB);
+  else
+    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<false>, grid, dim3(64), lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
+                       partial, a.N, a.NB);
+  e = hipGetLastError();
+  trace_end(2, s);
+  if (e != hipSuccess) return e;
+
+  trace_begin(3, s);
+  if (aligned)
+    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<true>, grid, dim3(64), 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
+  else
+    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<false>, grid, dim3(64), 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
+  e = hipGetLastError();
+  trace_end(3, s);
+  if (e != hipSuccess) return e;
+  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, s);
 }
 
 }  // namespace gt

@@ -432,12 +432,7 @@ hipError_t bwd_typed(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
   trace_end(3, s);
   if (e != hipSuccess) return e;
 
-  trace_begin(4, s);
-  hipLaunchKernelGGL(dtable_reduce_kernel, dim3(static_cast<unsigned>(a.H * a.NB)), dim3(kThreads),
-                     0, s, partial, a.dtable, w.n_kv_blocks, a.H * a.NB);
-  e = hipGetLastError();
-  trace_end(4, s);
-  return e;
+  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, a.H * a.NB, s);
 }
 
 template <typename T>
@@ -463,6 +458,15 @@ hipError_t bwd_by_d(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
 }  // namespace
 
 int64_t valu_kv_block(int H) { return kThreads / H; }
+
+hipError_t launch_dtable_reduce(const float* partial, float* dtable, int64_t nblocks, int HNB, hipStream_t s) {
+  trace_begin(4, s);
+  hipLaunchKernelGGL(dtable_reduce_kernel, dim3(static_cast<unsigned>(HNB)), dim3(kThreads), 0, s, partial,
+                     dtable, nblocks, HNB);
+  const hipError_t e = hipGetLastError();
+  trace_end(4, s);
+  return e;
+}
 
 hipError_t launch_fwd_valu(const FwdArgs& a, hipStream_t s) {
   return a.dtype == 0 ? fwd_by_d<float>(a, s) : fwd_by_d<uint16_t>(a, s);

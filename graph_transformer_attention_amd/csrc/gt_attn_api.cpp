@@ -114,13 +114,13 @@ void trace_end(int kernel_id, hipStream_t s) {
 
 BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype) {
   BwdWorkspace w{};
-  (void)D;
-  (void)dtype;
-  const int64_t kb = valu_kv_block(H);
-  w.n_kv_blocks = (N + kb - 1) / kb;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const bool mfma = mfma_supported(H, D, dtype);
+  const int64_t kb = mfma ? 32 : valu_kv_block(H);
+  w.n_kv_blocks = (N + kb - 1) / kb;
   w.delta_off = 0;
-  w.partial_off = up(static_cast<size_t>(N) * H * sizeof(float));
+  w.ops_off = up(static_cast<size_t>(N) * H * sizeof(float));
+  w.partial_off = w.ops_off + (mfma ? up(mfma_ops_bytes(N)) : 0);
   w.bytes = w.partial_off + up(static_cast<size_t>(w.n_kv_blocks) * H * NB * sizeof(float));
   return w;
 }
@@ -201,7 +201,8 @@ size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, 
   return gt::bwd_workspace(N, H, D, NB, dtype).bytes;
 }
 
-int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd, const float* table,
+int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd, const uint8_t* spd_t,
+                const float* table,
                 const float* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
                 float* dtable, void* workspace, size_t workspace_bytes, int64_t N, int32_t H,
                 int32_t D, int32_t NB, int32_t dtype, void* stream) {
@@ -210,6 +211,7 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(k, "k"));
   GT_CHECK(check_ptr(v, "v"));
   GT_CHECK(check_ptr(spd, "spd"));
+  GT_CHECK(check_ptr(spd_t, "spd_t"));
   GT_CHECK(check_ptr(table, "table"));
   GT_CHECK(check_ptr(out, "out"));
   GT_CHECK(check_ptr(lse, "lse"));
@@ -224,8 +226,10 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   const gt::BwdWorkspace w = gt::bwd_workspace(N, H, D, NB, dtype);
   if (workspace_bytes < w.bytes)
     return fail(GT_EINVAL, "workspace_bytes=%zu < %zu required", workspace_bytes, w.bytes);
-  gt::BwdArgs a{q, k, v, spd, table, out, lse, dout, dq, dk, dv, dtable, workspace, N, H, D, NB, dtype};
-  return hip_status(gt::launch_bwd_valu(a, w, static_cast<hipStream_t>(stream)), "gt_attn_bwd launch");
+  gt::BwdArgs a{q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, workspace, N, H, D, NB, dtype};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = gt::mfma_supported(H, D, dtype) ? gt::launch_bwd_mfma(a, w, s) : gt::launch_bwd_valu(a, w, s);
+  return hip_status(e, "gt_attn_bwd launch");
 }
 
 int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C, uint8_t* spd,

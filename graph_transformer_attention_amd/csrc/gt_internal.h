@@ -24,6 +24,7 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const uint8_t* spd;
+  const uint8_t* spd_t;
   const float* table;
   const float* out;
   const float* lse;
@@ -37,10 +38,11 @@ struct BwdArgs {
   int H, D, NB, dtype;
 };
 
-// Workspace layout of the backward: delta [N*H] float, then per-workgroup bucket
-// partial sums [n_kv_blocks * H * NB] float; each region starts 256-byte aligned.
+// Workspace layout of the backward (each region 256-byte aligned): delta [N*H] float
+// (vector-ALU kernels), operand copies of the MFMA kernels (mfma_ops_bytes), then
+// per-key-block bucket partial sums [n_kv_blocks * H * NB] float.
 struct BwdWorkspace {
-  size_t delta_off, partial_off, bytes;
+  size_t delta_off, ops_off, partial_off, bytes;
   int64_t n_kv_blocks;
 };
 
@@ -52,7 +54,11 @@ BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype);
 
 hipError_t launch_fwd_valu(const FwdArgs& a, hipStream_t s);
 bool mfma_supported(int H, int D, int dtype);
+int64_t mfma_npad(int64_t N);
+size_t mfma_ops_bytes(int64_t N);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
+hipError_t launch_dtable_reduce(const float* partial, float* dtable, int64_t nblocks, int HNB, hipStream_t s);
 hipError_t launch_bwd_valu(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 int64_t valu_kv_block(int H);
 hipError_t launch_probe(int kind, int blocks, int iters, float* sink, hipStream_t s);

@@ -81,7 +81,7 @@ size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, 
  *                          workspace must be ordered on one stream.
  * Results are bitwise reproducible run to run (no floating-point atomics).           */
 int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
-                const float* table, const float* out, const float* lse, const void* dout,
+                const uint8_t* spd_t, const float* table, const float* out, const float* lse, const void* dout,
                 float* dq, float* dk, float* dv, float* dtable, void* workspace,
                 size_t workspace_bytes, int64_t N, int32_t H, int32_t D, int32_t NB,
                 int32_t dtype, void* stream);

@@ -71,7 +71,7 @@ def test_bwd_argument_errors():
     assert L.gt_attn_bwd_workspace_bytes(N, H, 12, NB, 1) == 0
 
     def call(ws=P, wsb=need, dout=P, dtable=P, **kw):
-        return L.gt_attn_bwd(P, P, P, P, P, P, P, dout, P, P, P, dtable, ws, wsb,
+        return L.gt_attn_bwd(P, P, P, P, P, P, P, P, dout, P, P, P, dtable, ws, wsb,
                              kw.get("N", N), H, D, NB, 1, None)
     assert call(wsb=need - 1) == gta.GT_EINVAL and "workspace_bytes" in gta.last_error()
     assert call(ws=None) == gta.GT_EINVAL

@@ -113,3 +113,24 @@ def test_bad_arguments_raise_without_launch():
     assert e.value.code == gta.GT_EUNSUPPORTED
     with pytest.raises(ValueError):
         gta.fwd(q, q, q, spd[:, :8], table)
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 200), ("f32", 200), ("bf16", 93)])
+def test_asymmetric_codes_with_transpose(dtype, N):
+    """Codes of a directed relation (spd != spd^T): the backward reads the key-outer
+    codes from spd_t, which the caller passes as the transpose."""
+    inp = small_case(N, 8, 8, 10, dtype, seed=5)
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 11, size=(N, N)).astype(np.uint8)
+    assert not np.array_equal(codes, codes.T)
+    q, k, v, do, table = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.dout), dev(inp.table)
+    spd = torch.from_numpy(codes).cuda()
+    spd_t = spd.t().contiguous()
+    out, lse = gta.fwd(q, k, v, spd, table)
+    dq, dk, dv, dtab = gta.bwd(q, k, v, spd, table, out, lse, do, spd_t=spd_t)
+    torch.cuda.synchronize()
+    ref = oracle.full_backward(inp.q.value, inp.k.value, inp.v.value, codes, inp.table.value,
+                               inp.dout.value)
+    for name, got, r in zip(["out", "lse", "dq", "dk", "dv", "dtable"],
+                            [out, lse, dq, dk, dv, dtab], ref):
+        check(name, host64(got), r, dtype)
