@@ -19,7 +19,8 @@ ARCH = "gfx950"
 # Packed fp32 arithmetic is switched off for every HIP file.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function"]
+             "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form",
+             "-Wall", "-Wno-unused-function"]
 CXX_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
 
 

@@ -129,54 +129,116 @@ __device__ __forceinline__ s16x8 read_operand_t(const uint16_t* tile, int hl, in
 // Forward. S^T = K Q^T per 32-key tile (rows = keys in the order above, columns =
 // queries); running max per query column; O^T += V^T P^T with a ones row in V^T so
 // the MFMA also accumulates the row sum l.
+//
+// A workgroup is 4 waves = 128 queries x 2 heads; the waves share one transposed
+// half-precision V tile in LDS (double-buffered, one barrier per key tile; each wave
+// converts a quarter of it), and each wave prefetches the next tile's codes and K
+// operands into registers while it computes the current one. Only the last key tile
+// can be partial, so only it takes the guarded loads and the -inf mask.
+//
+// The running max is updated lazily: a wave rescales its accumulators only when some
+// lane's tile max exceeds its current max by more than kLazy (in log2 units), so the
+// probabilities fed to the MFMA stay below 2^kLazy and rescales are rare.
+constexpr float kLazy = 8.0f;
+constexpr int kFwdWaves = 4;
+
+struct FwdTile {
+  u32x4 cw;       // 16 codes: query row, keys 16*hp .. 16*hp+15 of the tile
+  s16x4 ka, kb;   // K operand rows (both heads) for MFMA row c
+  uint32_t vw;    // one dword of V (two d values of one key and head) to stage
+};
+
+template <bool kGuard, bool kAligned>
+__device__ __forceinline__ void fwd_load(FwdTile& t, const uint8_t* srow, const uint16_t* k,
+                                         const uint16_t* v, int64_t j0, int64_t N, int h0, int hp,
+                                         int kr, int sk, int shl, int sdp) {
+  if (kGuard || !kAligned) {
+    t.cw = load_codes16<false>(srow, j0 + 16 * hp, N);
+  } else {
+    t.cw = *reinterpret_cast<const u32x4*>(srow + j0 + 16 * hp);
+  }
+  const int64_t kn = j0 + kr, vn = j0 + sk;
+  if (!kGuard || kn < N) {
+    const uint16_t* kp = k + kn * kHD + h0 * kD + 4 * hp;
+    t.ka = *reinterpret_cast<const s16x4*>(kp);
+    t.kb = *reinterpret_cast<const s16x4*>(kp + kD);
+  } else {
+    t.ka = s16x4{0, 0, 0, 0};
+    t.kb = s16x4{0, 0, 0, 0};
+  }
+  t.vw = (!kGuard || vn < N) ? *reinterpret_cast<const uint32_t*>(v + vn * kHD + (h0 + shl) * kD + 2 * sdp) : 0u;
+}
+
 template <bool kAligned>
-__global__ __launch_bounds__(64) void fwd_mfma_d8_kernel(const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v,
-                                                         const uint8_t* __restrict__ spd,
-                                                         const float* __restrict__ table,
-                                                         float* __restrict__ out, float* __restrict__ lse,
-                                                         int64_t N, int NB) {
+__global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint16_t* __restrict__ q,
+                                                                    const uint16_t* __restrict__ k,
+                                                                    const uint16_t* __restrict__ v,
+                                                                    const uint8_t* __restrict__ spd,
+                                                                    const float* __restrict__ table,
+                                                                    float* __restrict__ out,
+                                                                    float* __restrict__ lse, int64_t N, int NB) {
   __shared__ float tb[2 * 256];
-  __shared__ __align__(16) uint16_t vt[2 * kD * 32];
-  const int lane = threadIdx.x;
+  __shared__ __align__(16) uint16_t vt[2][2][kD + 1][32];  // [buffer][head][d or ones][key]
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
   const int c = lane & 31, hp = lane >> 5;
   const int h0 = 2 * blockIdx.y;
-  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 32;
-  const int64_t i = i0 + c;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * (32 * kFwdWaves) + 32 * w + c;
   const bool qvalid = i < N;
+  const int64_t irow = qvalid ? i : N - 1;
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
+  const float lazy_raw = kLazy / sc2;
 
-  for (int x = lane; x < 512; x += 64) {
+  for (int x = tid; x < 512; x += 64 * kFwdWaves) {
     const int hl = x >> 8, b = x & 255;
     tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
   }
-  const s16x4 qop0 = load_op4(q, qvalid ? i : N, N, h0, hp);
-  const s16x4 qop1 = load_op4(q, qvalid ? i : N, N, h0 + 1, hp);
-  const uint8_t* srow = spd + (qvalid ? i : 0) * N;
+  for (int x = tid; x < 2 * 2 * 32; x += 64 * kFwdWaves) vt[x >> 6][(x >> 5) & 1][kD][x & 31] = 0x3C00;  // 1.0
+  s16x4 qop0 = s16x4{0, 0, 0, 0}, qop1 = s16x4{0, 0, 0, 0};
+  if (qvalid) {
+    const uint16_t* qp = q + i * kHD + h0 * kD + 4 * hp;
+    qop0 = *reinterpret_cast<const s16x4*>(qp);
+    qop1 = *reinterpret_cast<const s16x4*>(qp + kD);
+  }
+  const uint8_t* srow = spd + irow * N;
+  const int kr = node_of_row(c);
+  // staging role: key sk of the tile, head shl, d pair sdp (one dword per thread)
+  const int sk = 8 * w + (lane >> 3), shl = (lane >> 2) & 1, sdp = lane & 3;
+  auto stage = [&](int buf, uint32_t vw) {
+    const uint32_t hh = bf16x2_to_f16x2(vw);
+    vt[buf][shl][2 * sdp][sk] = static_cast<uint16_t>(hh & 0xffffu);
+    vt[buf][shl][2 * sdp + 1][sk] = static_cast<uint16_t>(hh >> 16);
+  };
+
+  const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
+  FwdTile cur, nxt;
+  if (nfull > 0)
+    fwd_load<false, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, sk, shl, sdp);
+  else
+    fwd_load<true, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, sk, shl, sdp);
+  stage(0, cur.vw);
+  __syncthreads();
 
   f32x16 o0 = {}, o1 = {};
   float m0 = -INFINITY, m1 = -INFINITY;
-  const int kr = node_of_row(c);  // the key this lane feeds as A-operand row c
-
-  for (int64_t j0 = 0; j0 < N; j0 += 32) {
-    const bool tail = j0 + 32 > N;
-    const u32x4 cw = qvalid ? load_codes16<kAligned>(srow, j0 + 16 * hp, N) : u32x4{0u, 0u, 0u, 0u};
-    const s16x4 kop0 = load_op4(k, j0 + kr, N, h0, hp);
-    const s16x4 kop1 = load_op4(k, j0 + kr, N, h0 + 1, hp);
-    __syncthreads();
-    stage_transposed(vt, v, j0, N, h0, lane);
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t j0 = t * 32;
+    const int buf = static_cast<int>(t & 1);
+    if (t + 1 < nfull)
+      fwd_load<false, kAligned>(nxt, srow, k, v, j0 + 32, N, h0, hp, kr, sk, shl, sdp);
+    else if (t + 1 < ntiles)
+      fwd_load<true, kAligned>(nxt, srow, k, v, j0 + 32, N, h0, hp, kr, sk, shl, sdp);
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const uint32_t cb = code_byte(cw, e);
+      const uint32_t cb = code_byte(cur.cw, e);
       s0[e] = tb[cb];
       s1[e] = tb[256 + cb];
     }
-    s0 = mfma_x8(kop0, qop0, s0);
-    s1 = mfma_x8(kop1, qop1, s1);
-    if (tail) {
+    s0 = mfma_x8(cur.ka, qop0, s0);
+    s1 = mfma_x8(cur.kb, qop1, s1);
+    if (t >= nfull) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         if (j0 + 16 * hp + e >= N) {
@@ -193,17 +255,16 @@ __global__ __launch_bounds__(64) void fwd_mfma_d8_kernel(const uint16_t* __restr
     }
     x0 = fmaxf(x0, __shfl_xor(x0, 32));
     x1 = fmaxf(x1, __shfl_xor(x1, 32));
-    const float n0 = fmaxf(m0, x0), n1 = fmaxf(m1, x1);
-    if (n0 > m0) {
+    if (__any(x0 > m0 + lazy_raw || x1 > m1 + lazy_raw)) {
+      const float n0 = fmaxf(m0, x0), n1 = fmaxf(m1, x1);
       const float a0 = __builtin_amdgcn_exp2f((m0 - n0) * sc2);
-#pragma unroll
-      for (int e = 0; e < 5; ++e) o0[e] *= a0;
-      m0 = n0;
-    }
-    if (n1 > m1) {
       const float a1 = __builtin_amdgcn_exp2f((m1 - n1) * sc2);
 #pragma unroll
-      for (int e = 0; e < 5; ++e) o1[e] *= a1;
+      for (int e = 0; e < 5; ++e) {
+        o0[e] *= a0;
+        o1[e] *= a1;
+      }
+      m0 = n0;
       m1 = n1;
     }
     const float b0 = -m0 * sc2, b1 = -m1 * sc2;
@@ -212,14 +273,20 @@ __global__ __launch_bounds__(64) void fwd_mfma_d8_kernel(const uint16_t* __restr
       s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, b0));
       s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, b1));
     }
-    __syncthreads();
+    // rows >= 9 of the V^T operand only feed output rows that are never read
+    const int vr = min(c, kD);
 #pragma unroll
     for (int k1 = 0; k1 < 2; ++k1) {
-      const s16x8 va = read_operand_t(vt, 0, c, 16 * hp + 8 * k1, true);
-      const s16x8 vb = read_operand_t(vt, 1, c, 16 * hp + 8 * k1, true);
+      const s16x8 va = *reinterpret_cast<const s16x8*>(&vt[buf][0][vr][16 * hp + 8 * k1]);
+      const s16x8 vb = *reinterpret_cast<const s16x8*>(&vt[buf][1][vr][16 * hp + 8 * k1]);
       o0 = mfma_h16(va, pack_f16x8(s0, 8 * k1), o0);
       o1 = mfma_h16(vb, pack_f16x8(s1, 8 * k1), o1);
     }
+    if (t + 1 < ntiles) {
+      stage(buf ^ 1, nxt.vw);
+      cur = nxt;
+    }
+    __syncthreads();
   }
   // O^T rows: d = 4hp + e in entries e = 0..3; row 8 (lane half 0, entry 4) is l.
   const float l0 = __shfl(o0[4], c), l1 = __shfl(o1[4], c);
@@ -339,27 +406,57 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
 
 __device__ __forceinline__ s16x8 load_h8(const uint16_t* p) { return *reinterpret_cast<const s16x8*>(p); }
 
-// A operand rows m < 8 of a transposed [head][d][npad] half copy, 8 consecutive nodes.
+// A operand of a contraction over 8 nodes from a transposed [head][d][npad] half copy:
+// lane row m reads d = m & 7 (rows >= 8 only feed output rows that are never read).
 __device__ __forceinline__ s16x8 load_t8(const uint16_t* t, int64_t npad, int h, int m, int64_t first) {
-  if (m < kD) return *reinterpret_cast<const s16x8*>(t + (static_cast<int64_t>(h) * kD + m) * npad + first);
-  return s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  return *reinterpret_cast<const s16x8*>(t + (static_cast<int64_t>(h) * kD + (m & 7)) * npad + first);
+}
+
+// Per-lane pointers of the backward's inner loops. Each loop step advances every
+// pointer by one 32-node tile, so no 64-bit address is recomputed per load.
+struct BwdPtrs {
+  const uint8_t* code;   // this lane's 16 codes
+  const uint16_t* a;     // augmented score row, head h0 (head h0+1 at +16)
+  const uint16_t* g;     // augmented gradient row, head h0 (head h0+1 at +16)
+  const uint16_t* t;     // transposed operand, head h0, d = c & 7 (head h0+1 at +8*npad)
+  const uint16_t* u;     // second transposed operand (key-outer kernel)
+};
+
+struct ScoreOps {
+  u32x4 cw;
+  s16x8 a0, a1, g0, g1;
+};
+
+template <bool kGuard, bool kAligned>
+__device__ __forceinline__ void load_score_ops(ScoreOps& o, const BwdPtrs& p, int64_t col, int64_t N) {
+  if (kGuard || !kAligned)
+    o.cw = load_codes16<false>(p.code - col, col, N);  // p.code points at column col
+  else
+    o.cw = *reinterpret_cast<const u32x4*>(p.code);
+  o.a0 = load_h8(p.a);
+  o.a1 = load_h8(p.a + 16);
+  o.g0 = load_h8(p.g);
+  o.g1 = load_h8(p.g + 16);
 }
 
 // Backward, step 2 (key-outer): a wave owns 32 keys x 2 heads and sweeps all query
-// tiles, reading the codes of its keys along rows of the transposed code matrix. S = Q K^T - lse and dP - delta = dO V^T - delta come out of two augmented
-// MFMAs with rows = queries (order a(r)) and columns = keys, so lane c keeps key c for
-// the whole kernel and its accumulator entries are queries 16*hp + 0..15; then
-// P = exp2(S log2e / sqrt(D)) and dS = P (dP - delta) need one multiply each.
-// dV^T += dO^T P and dK^T += Q^T dS contract over those queries. Bucket sums of dS
-// go to per-lane LDS bins ([head][bucket][lane]: no two lanes share an address),
-// reduced in a fixed order at the end.
+// tiles, reading the codes of its keys along rows of the transposed code matrix.
+// S = Q K^T - lse and dP - delta = dO V^T - delta come out of two augmented MFMAs
+// with rows = queries (order a(r)) and columns = keys, so lane c keeps key c for the
+// whole kernel and its accumulator entries are queries 16*hp + 0..15; then
+// P = exp2(S log2e / sqrt(D)) and dS = P (dP - delta) take one multiply each.
+// dV^T += dO^T P and dK^T += Q^T dS contract over those queries; their transposed
+// operands are loaded only by the 16 lanes whose rows (d < 8) reach the outputs.
+// Bucket sums of dS go to per-lane LDS bins laid out [bucket][head][lane]: no two
+// lanes share an address, so a plain read-add-write suffices (both heads' bins of
+// one code sit 256 bytes apart), reduced in a fixed order at the end.
 template <bool kAligned>
 __global__ __launch_bounds__(64) void bwd_kv_mfma_d8_kernel(const uint8_t* __restrict__ spd_t,
                                                             const float* __restrict__ table, BwdOps ops,
                                                             float* __restrict__ dk, float* __restrict__ dv,
                                                             float* __restrict__ partial, int64_t N, int NB) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* bins = reinterpret_cast<float*>(smem);                 // [2][NB][64]
+  float* bins = reinterpret_cast<float*>(smem);                 // [NB][2][64]
   float* tb = bins + 2 * NB * 64;                                // [2][256]
 
   const int lane = threadIdx.x;
@@ -384,52 +481,80 @@ __global__ __launch_bounds__(64) void bwd_kv_mfma_d8_kernel(const uint8_t* __res
   f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
   const int qr = node_of_row(c);  // the query this lane feeds as A-operand row c
   const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
-  const bool kvalid = j < N;
-  const uint8_t* crow = spd_t + (kvalid ? j : 0) * N;
+  const bool trow = c < kD;       // this lane's transposed-operand row reaches the outputs
+  float* mybins = bins + lane;
+  BwdPtrs p;
+  p.code = spd_t + (j < N ? j : N - 1) * N + 16 * hp;
+  p.a = ops.qa + (static_cast<int64_t>(qr) * kH + h0) * 16 + 8 * hp;
+  p.g = ops.doa + (static_cast<int64_t>(qr) * kH + h0) * 16 + 8 * hp;
+  p.t = ops.ot + (static_cast<int64_t>(h0) * kD + (c & 7)) * npad + 16 * hp;
+  p.u = ops.qt + (static_cast<int64_t>(h0) * kD + (c & 7)) * npad + 16 * hp;
+  const int64_t hstride = kD * npad;
   __syncthreads();
 
-  for (int64_t i0 = 0; i0 < npad; i0 += 32) {
-    const int64_t qrow = (i0 + qr) * kH;
-    const s16x8 qa0 = load_h8(ops.qa + (qrow + h0) * 16 + 8 * hp);
-    const s16x8 qa1 = load_h8(ops.qa + (qrow + h0 + 1) * 16 + 8 * hp);
-    const s16x8 oa0 = load_h8(ops.doa + (qrow + h0) * 16 + 8 * hp);
-    const s16x8 oa1 = load_h8(ops.doa + (qrow + h0 + 1) * 16 + 8 * hp);
-    const u32x4 cw = kvalid ? load_codes16<kAligned>(crow, i0 + 16 * hp, N) : u32x4{0u, 0u, 0u, 0u};
+  const int64_t ntiles = npad / 32, nfull = N / 32;
+  ScoreOps cur, nxt;
+  if (nfull > 0)
+    load_score_ops<false, kAligned>(cur, p, 16 * hp, N);
+  else
+    load_score_ops<true, kAligned>(cur, p, 16 * hp, N);
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t i0 = t * 32;
+    s16x8 t00 = {}, t01 = {}, t10 = {}, t11 = {}, u00 = {}, u01 = {}, u10 = {}, u11 = {};
+    if (trow) {
+      t00 = load_h8(p.t);
+      t01 = load_h8(p.t + 8);
+      t10 = load_h8(p.t + hstride);
+      t11 = load_h8(p.t + hstride + 8);
+      u00 = load_h8(p.u);
+      u01 = load_h8(p.u + 8);
+      u10 = load_h8(p.u + hstride);
+      u11 = load_h8(p.u + hstride + 8);
+    }
+    BwdPtrs pn = p;
+    pn.code += 32;
+    pn.a += 32 * kH * 16;
+    pn.g += 32 * kH * 16;
+    pn.t += 32;
+    pn.u += 32;
+    if (t + 1 < nfull)
+      load_score_ops<false, kAligned>(nxt, pn, i0 + 32 + 16 * hp, N);
+    else if (t + 1 < ntiles)
+      load_score_ops<true, kAligned>(nxt, pn, i0 + 32 + 16 * hp, N);
     f32x16 s0, s1;
     uint32_t code[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      code[e] = min(code_byte(cw, e), nbm1);
+      code[e] = min(code_byte(cur.cw, e), nbm1);
       s0[e] = tb[code[e]];
       s1[e] = tb[256 + code[e]];
     }
-    s0 = mfma_h16(qa0, kb0, s0);
-    s1 = mfma_h16(qa1, kb1, s1);
-    f32x16 p0 = mfma_h16(oa0, vb0, f32x16{});
-    f32x16 p1 = mfma_h16(oa1, vb1, f32x16{});
+    s0 = mfma_h16(cur.a0, kb0, s0);
+    s1 = mfma_h16(cur.a1, kb1, s1);
+    f32x16 p0 = mfma_h16(cur.g0, vb0, f32x16{});
+    f32x16 p1 = mfma_h16(cur.g1, vb1, f32x16{});
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float pa = __builtin_amdgcn_exp2f(s0[e] * sc2);
       const float pb = __builtin_amdgcn_exp2f(s1[e] * sc2);
-      const float dsa = pa * p0[e];
-      const float dsb = pb * p1[e];
       s0[e] = pa;
       s1[e] = pb;
-      p0[e] = dsa;
-      p1[e] = dsb;
-      // private to this lane: plain read-add-write (LDS float atomics are far slower)
-      float* bin = bins + code[e] * 64 + lane;
-      bin[0] += dsa;
-      bin[NB * 64] += dsb;
+      p0[e] *= pa;
+      p1[e] *= pb;
+      float* bin = mybins + code[e] * 128;
+      bin[0] += p0[e];
+      bin[64] += p1[e];
     }
-#pragma unroll
-    for (int k1 = 0; k1 < 2; ++k1) {
-      const int64_t first = i0 + 16 * hp + 8 * k1;
-      dv0 = mfma_h16(load_t8(ops.ot, npad, h0, c, first), pack_f16x8(s0, 8 * k1), dv0);
-      dv1 = mfma_h16(load_t8(ops.ot, npad, h0 + 1, c, first), pack_f16x8(s1, 8 * k1), dv1);
-      dk0 = mfma_h16(load_t8(ops.qt, npad, h0, c, first), pack_f16x8(p0, 8 * k1), dk0);
-      dk1 = mfma_h16(load_t8(ops.qt, npad, h0 + 1, c, first), pack_f16x8(p1, 8 * k1), dk1);
-    }
+    dv0 = mfma_h16(t00, pack_f16x8(s0, 0), dv0);
+    dv0 = mfma_h16(t01, pack_f16x8(s0, 8), dv0);
+    dv1 = mfma_h16(t10, pack_f16x8(s1, 0), dv1);
+    dv1 = mfma_h16(t11, pack_f16x8(s1, 8), dv1);
+    dk0 = mfma_h16(u00, pack_f16x8(p0, 0), dk0);
+    dk0 = mfma_h16(u01, pack_f16x8(p0, 8), dk0);
+    dk1 = mfma_h16(u10, pack_f16x8(p1, 0), dk1);
+    dk1 = mfma_h16(u11, pack_f16x8(p1, 8), dk1);
+    cur = nxt;
+    p = pn;
   }
   if (j < N) {
     const float rs = 1.f / sqd;
@@ -442,9 +567,10 @@ __global__ __launch_bounds__(64) void bwd_kv_mfma_d8_kernel(const uint8_t* __res
   }
   __syncthreads();
   for (int x = lane; x < 2 * NB; x += 64) {
-    float sum = 0.f;
-    for (int l = 0; l < 64; ++l) sum += bins[x * 64 + l];
     const int hl = x / NB, b = x - hl * NB;
+    const float* src = bins + (b * 2 + hl) * 64;
+    float sum = 0.f;
+    for (int l = 0; l < 64; ++l) sum += src[l];
     partial[(static_cast<int64_t>(blockIdx.x) * kH + h0 + hl) * NB + b] = sum;
   }
 }
@@ -474,40 +600,64 @@ __global__ __launch_bounds__(64) void bwd_q_mfma_d8_kernel(const uint8_t* __rest
   const s16x8 qb1 = load_h8(ops.qa + (i * kH + h0 + 1) * 16 + 8 * hp);
   const s16x8 ob0 = load_h8(ops.doa + (i * kH + h0) * 16 + 8 * hp);
   const s16x8 ob1 = load_h8(ops.doa + (i * kH + h0 + 1) * 16 + 8 * hp);
-  const uint8_t* srow = spd + (qvalid ? i : 0) * N;
   f32x16 dq0 = {}, dq1 = {};
   const int kr = node_of_row(c);
+  const bool trow = c < kD;
+  BwdPtrs p;
+  p.code = spd + (qvalid ? i : N - 1) * N + 16 * hp;
+  p.a = ops.ka + (static_cast<int64_t>(kr) * kH + h0) * 16 + 8 * hp;
+  p.g = ops.va + (static_cast<int64_t>(kr) * kH + h0) * 16 + 8 * hp;
+  p.t = ops.kt + (static_cast<int64_t>(h0) * kD + (c & 7)) * npad + 16 * hp;
+  p.u = nullptr;
+  const int64_t hstride = kD * npad;
   __syncthreads();
 
-  for (int64_t j0 = 0; j0 < npad; j0 += 32) {
-    const u32x4 cw = qvalid ? load_codes16<kAligned>(srow, j0 + 16 * hp, N) : u32x4{0u, 0u, 0u, 0u};
-    const int64_t krow = (j0 + kr) * kH;
-    const s16x8 ka0 = load_h8(ops.ka + (krow + h0) * 16 + 8 * hp);
-    const s16x8 ka1 = load_h8(ops.ka + (krow + h0 + 1) * 16 + 8 * hp);
-    const s16x8 va0 = load_h8(ops.va + (krow + h0) * 16 + 8 * hp);
-    const s16x8 va1 = load_h8(ops.va + (krow + h0 + 1) * 16 + 8 * hp);
+  const int64_t ntiles = npad / 32, nfull = N / 32;
+  ScoreOps cur, nxt;
+  if (nfull > 0)
+    load_score_ops<false, kAligned>(cur, p, 16 * hp, N);
+  else
+    load_score_ops<true, kAligned>(cur, p, 16 * hp, N);
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t j0 = t * 32;
+    s16x8 t00 = {}, t01 = {}, t10 = {}, t11 = {};
+    if (trow) {
+      t00 = load_h8(p.t);
+      t01 = load_h8(p.t + 8);
+      t10 = load_h8(p.t + hstride);
+      t11 = load_h8(p.t + hstride + 8);
+    }
+    BwdPtrs pn = p;
+    pn.code += 32;
+    pn.a += 32 * kH * 16;
+    pn.g += 32 * kH * 16;
+    pn.t += 32;
+    if (t + 1 < nfull)
+      load_score_ops<false, kAligned>(nxt, pn, j0 + 32 + 16 * hp, N);
+    else if (t + 1 < ntiles)
+      load_score_ops<true, kAligned>(nxt, pn, j0 + 32 + 16 * hp, N);
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const uint32_t cb = code_byte(cw, e);
+      const uint32_t cb = code_byte(cur.cw, e);
       s0[e] = tb[cb];
       s1[e] = tb[256 + cb];
     }
-    s0 = mfma_h16(ka0, qb0, s0);
-    s1 = mfma_h16(ka1, qb1, s1);
-    f32x16 p0 = mfma_h16(va0, ob0, f32x16{});
-    f32x16 p1 = mfma_h16(va1, ob1, f32x16{});
+    s0 = mfma_h16(cur.a0, qb0, s0);
+    s1 = mfma_h16(cur.a1, qb1, s1);
+    f32x16 p0 = mfma_h16(cur.g0, ob0, f32x16{});
+    f32x16 p1 = mfma_h16(cur.g1, ob1, f32x16{});
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       p0[e] *= __builtin_amdgcn_exp2f(s0[e] * sc2);
       p1[e] *= __builtin_amdgcn_exp2f(s1[e] * sc2);
     }
-#pragma unroll
-    for (int k1 = 0; k1 < 2; ++k1) {
-      const int64_t first = j0 + 16 * hp + 8 * k1;
-      dq0 = mfma_h16(load_t8(ops.kt, npad, h0, c, first), pack_f16x8(p0, 8 * k1), dq0);
-      dq1 = mfma_h16(load_t8(ops.kt, npad, h0 + 1, c, first), pack_f16x8(p1, 8 * k1), dq1);
-    }
+    dq0 = mfma_h16(t00, pack_f16x8(p0, 0), dq0);
+    dq0 = mfma_h16(t01, pack_f16x8(p0, 8), dq0);
+    dq1 = mfma_h16(t10, pack_f16x8(p1, 0), dq1);
+    dq1 = mfma_h16(t11, pack_f16x8(p1, 8), dq1);
+    cur = nxt;
+    p = pn;
   }
   if (qvalid) {
     const float rs = 1.f / sqd;
@@ -531,14 +681,14 @@ size_t mfma_ops_bytes(int64_t N) {
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((a.N + 31) / 32), kH / 2);
+  const dim3 grid(static_cast<unsigned>((a.N + 32 * kFwdWaves - 1) / (32 * kFwdWaves)), kH / 2);
   trace_begin(0, s);
   if (a.N % 16 == 0)
-    hipLaunchKernelGGL(fwd_mfma_d8_kernel<true>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(a.q),
+    hipLaunchKernelGGL(fwd_mfma_d8_kernel<true>, grid, dim3(64 * kFwdWaves), 0, s, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table,
                        a.out, a.lse, a.N, a.NB);
   else
-    hipLaunchKernelGGL(fwd_mfma_d8_kernel<false>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(a.q),
+    hipLaunchKernelGGL(fwd_mfma_d8_kernel<false>, grid, dim3(64 * kFwdWaves), 0, s, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table,
                        a.out, a.lse, a.N, a.NB);
   const hipError_t e = hipGetLastError();
