@@ -25,8 +25,32 @@ import numpy as np
 
 METRIC = "biased-attn fwd+bwd ms & Gpairs/s at N=32768,H=8,d=8; SPD-stream GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3
-BF16_MFMA_PEAK_TFLOPS = 2500.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["graph_transformer_attention_amd/csrc/attn_mfma.hip",
+                  "graph_transformer_attention_amd/csrc/attn_valu.hip"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def work_model(name: str, N: int, H: int, D: int, s_bytes: int):
@@ -48,7 +72,7 @@ def work_model(name: str, N: int, H: int, D: int, s_bytes: int):
     if name == "bwd_q":
         return E * (6 * D + 4), E, N * N + 4 * node + 2 * N * H * 4 + f32node
     if name == "bwd_delta":
-        return N * H * 2 * D, 0, node + f32node + N * H * 4
+        return N * H * 2 * D, 0, 4 * node + f32node + N * H * 4
     return 0, 0, 0
 
 
@@ -86,6 +110,8 @@ def main():
     ap.add_argument("--workload", default="ba32768-bf16")
     ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (the reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
@@ -137,6 +163,16 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
+    exp_peak = gta.probe_peak(0) / 1e3   # T exp2/s, this device, this run
+    print(f"[bench] measured v_exp_f32 rate {exp_peak:.2f} T/s", file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     gta.trace(True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -173,11 +209,14 @@ def main():
     dom = max(per_kernel, key=lambda n: per_kernel[n][1])
     fl, ex, by = work_model(dom, N, H, D, s_bytes)
     dom_s = per_kernel[dom][1] / per_kernel[dom][0] * 1e-3
-    achieved = fl / dom_s / 1e12
-    roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3),
-                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
-                "flops_per_launch": fl, "avg_launch_ms": round(dom_s * 1e3, 4)}
+    achieved = ex / dom_s / 1e12
+    roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved, 4),
+                "peak": round(exp_peak, 3), "unit": "TFLOP/s",
+                "frac": round(achieved / exp_peak, 4),
+                "traffic": recorded_traffic(dom, w.name),
+                "op": "exp2 (one per score entry and pass; peak = measured v_exp_f32 rate)",
+                "ops_per_launch": ex, "algorithmic_bytes_per_launch": by,
+                "avg_launch_ms": round(dom_s * 1e3, 4)}
 
     pairs = H * N * N
     fwd_ms = kern.get("fwd", {}).get("avg_ms", 0.0)
@@ -194,7 +233,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if (w.dtype == "bf16" and H == 8 and D == 8) else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "graph": f"{w.family} {w.graph_args}", "N": N, "H": H,
                    "D": D, "NB": NB, "storage": w.dtype, "layers": 1},
@@ -206,6 +245,9 @@ def main():
         "kernels": kern,
         "roofline": roofline,
         "spd_build_host_s": round(t_spd, 2),
+        "exp_peak_tops": round(exp_peak, 3),
+        "exp_frac_of_step": round(3 * pairs / (ms_step * 1e-3) / (exp_peak * 1e12), 4),
+        "kernel_source_hash": kernel_source_hash(),
         "checks": checks,
     }
     if not args.no_cpu_baseline:

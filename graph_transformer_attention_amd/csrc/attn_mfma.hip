@@ -412,151 +412,209 @@ __device__ __forceinline__ s16x8 load_t8(const uint16_t* t, int64_t npad, int h,
   return *reinterpret_cast<const s16x8*>(t + (static_cast<int64_t>(h) * kD + (m & 7)) * npad + first);
 }
 
-// Per-lane pointers of the backward's inner loops. Each loop step advances every
-// pointer by one 32-node tile, so no 64-bit address is recomputed per load.
-struct BwdPtrs {
-  const uint8_t* code;   // this lane's 16 codes
-  const uint16_t* a;     // augmented score row, head h0 (head h0+1 at +16)
-  const uint16_t* g;     // augmented gradient row, head h0 (head h0+1 at +16)
-  const uint16_t* t;     // transposed operand, head h0, d = c & 7 (head h0+1 at +8*npad)
-  const uint16_t* u;     // second transposed operand (key-outer kernel)
-};
-
-struct ScoreOps {
-  u32x4 cw;
-  s16x8 a0, a1, g0, g1;
-};
-
-template <bool kGuard, bool kAligned>
-__device__ __forceinline__ void load_score_ops(ScoreOps& o, const BwdPtrs& p, int64_t col, int64_t N) {
-  if (kGuard || !kAligned)
-    o.cw = load_codes16<false>(p.code - col, col, N);  // p.code points at column col
-  else
-    o.cw = *reinterpret_cast<const u32x4*>(p.code);
-  o.a0 = load_h8(p.a);
-  o.a1 = load_h8(p.a + 16);
-  o.g0 = load_h8(p.g);
-  o.g1 = load_h8(p.g + 16);
+// Workgroup -> (node block, head pair) mapping. Workgroups are dispatched round-robin
+// over the 8 XCDs (each with its own L2). The 4 head pairs of one node block read
+// the same code rows, so they are placed on one XCD, in consecutive dispatch slots.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_map(int wg, int nblocks, int& blk, int& hpair) {
+  const int xcd = wg % kXcds, slot = wg / kXcds;
+  hpair = slot & 3;
+  blk = (slot >> 2) * kXcds + xcd;
+  if (blk >= nblocks) blk = -1;  // padding workgroup (grid rounded up to whole groups)
+}
+__host__ __device__ constexpr int xcd_grid(int nblocks) {
+  return ((nblocks + kXcds - 1) / kXcds) * kXcds * 4;
 }
 
-// Backward, step 2 (key-outer): a wave owns 32 keys x 2 heads and sweeps all query
-// tiles, reading the codes of its keys along rows of the transposed code matrix.
-// S = Q K^T - lse and dP - delta = dO V^T - delta come out of two augmented MFMAs
-// with rows = queries (order a(r)) and columns = keys, so lane c keeps key c for the
-// whole kernel and its accumulator entries are queries 16*hp + 0..15; then
-// P = exp2(S log2e / sqrt(D)) and dS = P (dP - delta) take one multiply each.
-// dV^T += dO^T P and dK^T += Q^T dS contract over those queries; their transposed
-// operands are loaded only by the 16 lanes whose rows (d < 8) reach the outputs.
-// Bucket sums of dS go to per-lane LDS bins laid out [bucket][head][lane]: no two
-// lanes share an address, so a plain read-add-write suffices (both heads' bins of
-// one code sit 256 bytes apart), reduced in a fixed order at the end.
-template <bool kAligned>
-__global__ __launch_bounds__(64) void bwd_kv_mfma_d8_kernel(const uint8_t* __restrict__ spd_t,
-                                                            const float* __restrict__ table, BwdOps ops,
-                                                            float* __restrict__ dk, float* __restrict__ dv,
-                                                            float* __restrict__ partial, int64_t N, int NB) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* bins = reinterpret_cast<float*>(smem);                 // [NB][2][64]
-  float* tb = bins + 2 * NB * 64;                                // [2][256]
+constexpr int kBwdWaves = 4;              // waves per backward workgroup: 4 x 32 nodes, one head pair
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kTileHalves = 32 * 2 * 16;  // one staged [32 nodes][2 heads][16] augmented tile
+constexpr int kTTileHalves = 2 * kD * 32; // one staged transposed [2 heads][8][32] tile
+constexpr int kStageHalves = 2 * kTileHalves + 2 * kTTileHalves;  // one buffer of the double buffer
 
-  const int lane = threadIdx.x;
+// One 32-node tile of backward operands of a head pair, staged into LDS: two
+// augmented-row tiles [node][head][16] and one or two transposed tiles [head][d][node].
+// The tiles are cut into 16-byte chunks; chunk x lands at halves 8x of the buffer:
+// x in [0,128) first augmented, [128,256) second augmented, [256,320) first
+// transposed, [320,384) second transposed. Thread t moves chunks t, t + 256, ...
+struct StageSrc {
+  const uint16_t* row0;  // first augmented rows (qa or ka) at node 0, head h0
+  const uint16_t* row1;  // second augmented rows (doa or va) at node 0, head h0
+  const uint16_t* tr0;   // first transposed copy at head h0, d 0, node 0
+  const uint16_t* tr1;   // second transposed copy (unused when only one is staged)
+};
+
+// chunk c of an augmented tile: node = c >> 2, head = (c >> 1) & 1, half = c & 1
+__device__ __forceinline__ const uint16_t* aug_chunk(const uint16_t* base, int64_t n0, int c) {
+  return base + ((n0 + (c >> 2)) * kH + ((c >> 1) & 1)) * 16 + 8 * (c & 1);
+}
+// chunk c of a transposed tile: head = c >> 5, d = (c >> 2) & 7, 8 nodes from (c & 3)*8
+__device__ __forceinline__ const uint16_t* tr_chunk(const uint16_t* base, int64_t npad, int64_t n0, int c) {
+  return base + ((c >> 5) * kD + ((c >> 2) & 7)) * npad + n0 + 8 * (c & 3);
+}
+__device__ __forceinline__ const uint16_t* stage_chunk(const StageSrc& s, int64_t npad, int64_t n0, int x) {
+  if (x < 128) return aug_chunk(s.row0, n0, x);
+  if (x < 256) return aug_chunk(s.row1, n0, x - 128);
+  if (x < 320) return tr_chunk(s.tr0, npad, n0, x - 256);
+  return tr_chunk(s.tr1, npad, n0, x - 320);
+}
+
+template <int kChunks>
+constexpr int stage_per_thread() { return (kChunks + kBwdThreads - 1) / kBwdThreads; }
+
+template <int kChunks>
+__device__ __forceinline__ void stage_load(s16x8 (&r)[stage_per_thread<kChunks>()], const StageSrc& s,
+                                           int64_t npad, int64_t n0, int tid) {
+#pragma unroll
+  for (int u = 0; u < stage_per_thread<kChunks>(); ++u) {
+    const int x = tid + u * kBwdThreads;
+    if (x < kChunks) r[u] = load_h8(stage_chunk(s, npad, n0, x));
+  }
+}
+
+template <int kChunks>
+__device__ __forceinline__ void stage_store(uint16_t* buf, const s16x8 (&r)[stage_per_thread<kChunks>()],
+                                            int tid) {
+#pragma unroll
+  for (int u = 0; u < stage_per_thread<kChunks>(); ++u) {
+    const int x = tid + u * kBwdThreads;
+    if (x < kChunks) *reinterpret_cast<s16x8*>(buf + 8 * x) = r[u];
+  }
+}
+
+// Read from a staged tile: augmented row of node n, head hl, half hp.
+__device__ __forceinline__ s16x8 staged_aug(const uint16_t* aug, int n, int hl, int hp) {
+  return *reinterpret_cast<const s16x8*>(aug + (n * 2 + hl) * 16 + 8 * hp);
+}
+// Transposed operand: head hl, d = m & 7, nodes first .. first+7.
+__device__ __forceinline__ s16x8 staged_tr(const uint16_t* tr, int hl, int m, int first) {
+  return *reinterpret_cast<const s16x8*>(tr + (hl * kD + (m & 7)) * 32 + first);
+}
+
+// 16 codes of one row from column col (col is a multiple of 16); kGuard zero-fills past N.
+template <bool kGuard, bool kAligned>
+__device__ __forceinline__ u32x4 codes_at(const uint8_t* row, int64_t col, int64_t N) {
+  if (kGuard || !kAligned) return load_codes16<false>(row, col, N);
+  return *reinterpret_cast<const u32x4*>(row + col);
+}
+
+// Backward, step 2 (key-outer). A workgroup is 4 waves = 128 keys x one head pair;
+// each wave owns 32 keys (lane c keeps key c for the whole sweep) and all waves share
+// each staged query tile (augmented q and dout rows, transposed q and dout) in LDS,
+// double-buffered. Codes come along rows of the transposed code matrix.
+// S = Q K^T - lse and dP - delta = dO V^T - delta come out of two augmented MFMAs with
+// rows = queries (order a(r)) and columns = keys, so a lane's accumulator entries
+// are queries 16*hp + 0..15; then P = exp2(S log2e / sqrt(D)) and dS = P (dP - delta)
+// take one multiply each. dV^T += dO^T P and dK^T += Q^T dS contract over those
+// queries. Bucket sums of dS go to per-lane LDS bins laid out [bucket][head][lane]
+// (no two lanes share an address, so a plain read-add-write suffices), reduced in a
+// fixed order at the end.
+template <bool kAligned>
+__global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
+    const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ partial, int64_t N, int NB) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 64);      // [NB][2][64] per wave
+  float* tb = reinterpret_cast<float*>(smem) + kBwdWaves * 2 * NB * 64;  // [2][64] by clamped code
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + 128);               // [2][kStageHalves]
+
+  const int npad32 = static_cast<int>(ops.npad / 32);
+  const int nkb = (npad32 + kBwdWaves - 1) / kBwdWaves;
+  int kb, hpair;
+  xcd_map(blockIdx.x, nkb, kb, hpair);
+  if (kb < 0) return;
   const int c = lane & 31, hp = lane >> 5;
-  const int h0 = 2 * blockIdx.y;
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 32;
-  const int64_t j = j0 + c;
+  const int h0 = 2 * hpair;
+  const int64_t jw = static_cast<int64_t>(kb) * (32 * kBwdWaves) + 32 * w;  // this wave's first key
+  const int64_t j = jw + c;
+  const bool wave_live = jw < ops.npad;
+  const int64_t jj = wave_live ? j : 0;
   const int64_t npad = ops.npad;
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
-  for (int x = lane; x < 512; x += 64) {
-    const int hl = x >> 8, b = x & 255;
+  for (int x = tid; x < 128; x += kBwdThreads) {
+    const int hl = x >> 6, b = x & 63;
     tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
   }
   for (int x = lane; x < 2 * NB * 64; x += 64) bins[x] = 0.f;
-  // B operands over the key columns: [k | 1, 1, pen] and [v | 1, 1], halves 8*hp..
-  const s16x8 kb0 = load_h8(ops.ka + (j * kH + h0) * 16 + 8 * hp);
-  const s16x8 kb1 = load_h8(ops.ka + (j * kH + h0 + 1) * 16 + 8 * hp);
-  const s16x8 vb0 = load_h8(ops.va + (j * kH + h0) * 16 + 8 * hp);
-  const s16x8 vb1 = load_h8(ops.va + (j * kH + h0 + 1) * 16 + 8 * hp);
+  const s16x8 kb0 = load_h8(ops.ka + (jj * kH + h0) * 16 + 8 * hp);
+  const s16x8 kb1 = load_h8(ops.ka + (jj * kH + h0 + 1) * 16 + 8 * hp);
+  const s16x8 vb0 = load_h8(ops.va + (jj * kH + h0) * 16 + 8 * hp);
+  const s16x8 vb1 = load_h8(ops.va + (jj * kH + h0 + 1) * 16 + 8 * hp);
   f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
-  const int qr = node_of_row(c);  // the query this lane feeds as A-operand row c
+  const int qr = node_of_row(c);
   const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
-  const bool trow = c < kD;       // this lane's transposed-operand row reaches the outputs
   float* mybins = bins + lane;
-  BwdPtrs p;
-  p.code = spd_t + (j < N ? j : N - 1) * N + 16 * hp;
-  p.a = ops.qa + (static_cast<int64_t>(qr) * kH + h0) * 16 + 8 * hp;
-  p.g = ops.doa + (static_cast<int64_t>(qr) * kH + h0) * 16 + 8 * hp;
-  p.t = ops.ot + (static_cast<int64_t>(h0) * kD + (c & 7)) * npad + 16 * hp;
-  p.u = ops.qt + (static_cast<int64_t>(h0) * kD + (c & 7)) * npad + 16 * hp;
-  const int64_t hstride = kD * npad;
+  const uint8_t* crow = spd_t + (j < N ? j : N - 1) * N;
+  const int64_t cc = 16 * hp;  // this lane's first code column within a tile
+
+  StageSrc src;
+  src.row0 = ops.qa + h0 * 16;
+  src.row1 = ops.doa + h0 * 16;
+  src.tr0 = ops.qt + static_cast<int64_t>(h0) * kD * npad;
+  src.tr1 = ops.ot + static_cast<int64_t>(h0) * kD * npad;
+  const int64_t ntiles = npad / 32, nfull = N / 32;
+  constexpr int kCh = 384;  // qa, doa, q^T, dout^T
+  s16x8 sr[stage_per_thread<kCh>()];
+  stage_load<kCh>(sr, src, npad, 0, tid);
+  stage_store<kCh>(stage, sr, tid);
+  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
   __syncthreads();
 
-  const int64_t ntiles = npad / 32, nfull = N / 32;
-  ScoreOps cur, nxt;
-  if (nfull > 0)
-    load_score_ops<false, kAligned>(cur, p, 16 * hp, N);
-  else
-    load_score_ops<true, kAligned>(cur, p, 16 * hp, N);
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t i0 = t * 32;
-    s16x8 t00 = {}, t01 = {}, t10 = {}, t11 = {}, u00 = {}, u01 = {}, u10 = {}, u11 = {};
-    if (trow) {
-      t00 = load_h8(p.t);
-      t01 = load_h8(p.t + 8);
-      t10 = load_h8(p.t + hstride);
-      t11 = load_h8(p.t + hstride + 8);
-      u00 = load_h8(p.u);
-      u01 = load_h8(p.u + 8);
-      u10 = load_h8(p.u + hstride);
-      u11 = load_h8(p.u + hstride + 8);
+    const uint16_t* cur = stage + (t & 1) * kStageHalves;
+    u32x4 cwn = cw;
+    if (t + 1 < ntiles) {
+      stage_load<kCh>(sr, src, npad, i0 + 32, tid);
+      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(crow, i0 + 32 + cc, N)
+                            : codes_at<true, kAligned>(crow, i0 + 32 + cc, N);
     }
-    BwdPtrs pn = p;
-    pn.code += 32;
-    pn.a += 32 * kH * 16;
-    pn.g += 32 * kH * 16;
-    pn.t += 32;
-    pn.u += 32;
-    if (t + 1 < nfull)
-      load_score_ops<false, kAligned>(nxt, pn, i0 + 32 + 16 * hp, N);
-    else if (t + 1 < ntiles)
-      load_score_ops<true, kAligned>(nxt, pn, i0 + 32 + 16 * hp, N);
-    f32x16 s0, s1;
-    uint32_t code[16];
+    if (wave_live) {
+      const uint16_t* qa_t = cur;
+      const uint16_t* doa_t = cur + kTileHalves;
+      const uint16_t* qt_t = cur + 2 * kTileHalves;
+      const uint16_t* ot_t = qt_t + kTTileHalves;
+      f32x16 s0, s1;
+      uint32_t code[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      code[e] = min(code_byte(cur.cw, e), nbm1);
-      s0[e] = tb[code[e]];
-      s1[e] = tb[256 + code[e]];
-    }
-    s0 = mfma_h16(cur.a0, kb0, s0);
-    s1 = mfma_h16(cur.a1, kb1, s1);
-    f32x16 p0 = mfma_h16(cur.g0, vb0, f32x16{});
-    f32x16 p1 = mfma_h16(cur.g1, vb1, f32x16{});
+      for (int e = 0; e < 16; ++e) {
+        code[e] = min(code_byte(cw, e), nbm1);
+        s0[e] = tb[code[e]];
+        s1[e] = tb[64 + code[e]];
+      }
+      s0 = mfma_h16(staged_aug(qa_t, qr, 0, hp), kb0, s0);
+      s1 = mfma_h16(staged_aug(qa_t, qr, 1, hp), kb1, s1);
+      f32x16 p0 = mfma_h16(staged_aug(doa_t, qr, 0, hp), vb0, f32x16{});
+      f32x16 p1 = mfma_h16(staged_aug(doa_t, qr, 1, hp), vb1, f32x16{});
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pa = __builtin_amdgcn_exp2f(s0[e] * sc2);
-      const float pb = __builtin_amdgcn_exp2f(s1[e] * sc2);
-      s0[e] = pa;
-      s1[e] = pb;
-      p0[e] *= pa;
-      p1[e] *= pb;
-      float* bin = mybins + code[e] * 128;
-      bin[0] += p0[e];
-      bin[64] += p1[e];
+      for (int e = 0; e < 16; ++e) {
+        const float pa = __builtin_amdgcn_exp2f(s0[e] * sc2);
+        const float pb = __builtin_amdgcn_exp2f(s1[e] * sc2);
+        s0[e] = pa;
+        s1[e] = pb;
+        p0[e] *= pa;
+        p1[e] *= pb;
+        float* bin = mybins + code[e] * 128;
+        bin[0] += p0[e];
+        bin[64] += p1[e];
+      }
+#pragma unroll
+      for (int k1 = 0; k1 < 2; ++k1) {
+        const int f = 16 * hp + 8 * k1;
+        dv0 = mfma_h16(staged_tr(ot_t, 0, c, f), pack_f16x8(s0, 8 * k1), dv0);
+        dv1 = mfma_h16(staged_tr(ot_t, 1, c, f), pack_f16x8(s1, 8 * k1), dv1);
+        dk0 = mfma_h16(staged_tr(qt_t, 0, c, f), pack_f16x8(p0, 8 * k1), dk0);
+        dk1 = mfma_h16(staged_tr(qt_t, 1, c, f), pack_f16x8(p1, 8 * k1), dk1);
+      }
     }
-    dv0 = mfma_h16(t00, pack_f16x8(s0, 0), dv0);
-    dv0 = mfma_h16(t01, pack_f16x8(s0, 8), dv0);
-    dv1 = mfma_h16(t10, pack_f16x8(s1, 0), dv1);
-    dv1 = mfma_h16(t11, pack_f16x8(s1, 8), dv1);
-    dk0 = mfma_h16(u00, pack_f16x8(p0, 0), dk0);
-    dk0 = mfma_h16(u01, pack_f16x8(p0, 8), dk0);
-    dk1 = mfma_h16(u10, pack_f16x8(p1, 0), dk1);
-    dk1 = mfma_h16(u11, pack_f16x8(p1, 8), dk1);
-    cur = nxt;
-    p = pn;
+    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kStageHalves, sr, tid);
+    cw = cwn;
+    __syncthreads();
   }
-  if (j < N) {
+  if (wave_live && j < N) {
     const float rs = 1.f / sqd;
     float* kp = dk + j * kHD + h0 * kD + 4 * hp;
     float* vp = dv + j * kHD + h0 * kD + 4 * hp;
@@ -565,101 +623,112 @@ __global__ __launch_bounds__(64) void bwd_kv_mfma_d8_kernel(const uint8_t* __res
     *reinterpret_cast<float4*>(vp) = make_float4(dv0[0], dv0[1], dv0[2], dv0[3]);
     *reinterpret_cast<float4*>(vp + kD) = make_float4(dv1[0], dv1[1], dv1[2], dv1[3]);
   }
-  __syncthreads();
+  // per-wave bins -> one partial row per 32-key block and head; a wave past the last
+  // key block writes its (zero) bins too, so every partial row is defined
   for (int x = lane; x < 2 * NB; x += 64) {
     const int hl = x / NB, b = x - hl * NB;
-    const float* src = bins + (b * 2 + hl) * 64;
+    const float* srcb = bins + (b * 2 + hl) * 64;
     float sum = 0.f;
-    for (int l = 0; l < 64; ++l) sum += src[l];
-    partial[(static_cast<int64_t>(blockIdx.x) * kH + h0 + hl) * NB + b] = sum;
+    for (int l = 0; l < 64; ++l) sum += srcb[l];
+    partial[((jw / 32) * kH + h0 + hl) * NB + b] = sum;
   }
 }
 
-// Backward, step 3 (query-outer): same orientation as the forward (lane c = query c);
-// S^T - lse and dP^T - delta from the augmented MFMAs, dQ^T += K^T dS^T per key tile.
+// Backward, step 3 (query-outer). A workgroup is 4 waves = 128 queries x one head
+// pair (lane c keeps query c); all waves share each staged key tile (augmented k and
+// v rows, transposed k) in LDS, double-buffered. S^T - lse and dP^T - delta come from
+// the augmented MFMAs and dQ^T += K^T dS^T per key tile.
 template <bool kAligned>
-__global__ __launch_bounds__(64) void bwd_q_mfma_d8_kernel(const uint8_t* __restrict__ spd,
-                                                           const float* __restrict__ table, BwdOps ops,
-                                                           float* __restrict__ dq, int64_t N, int NB) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_t* __restrict__ spd,
+                                                                      const float* __restrict__ table,
+                                                                      BwdOps ops, float* __restrict__ dq,
+                                                                      int64_t N, int NB) {
   __shared__ float tb[2 * 256];
-  const int lane = threadIdx.x;
+  __shared__ __align__(16) uint16_t stage[2 * kStageHalves];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int npad32 = static_cast<int>(ops.npad / 32);
+  const int nqb = (npad32 + kBwdWaves - 1) / kBwdWaves;
+  int qb, hpair;
+  xcd_map(blockIdx.x, nqb, qb, hpair);
+  if (qb < 0) return;
   const int c = lane & 31, hp = lane >> 5;
-  const int h0 = 2 * blockIdx.y;
-  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 32;
-  const int64_t i = i0 + c;
+  const int h0 = 2 * hpair;
+  const int64_t iw = static_cast<int64_t>(qb) * (32 * kBwdWaves) + 32 * w;
+  const int64_t i = iw + c;
+  const bool wave_live = iw < ops.npad;
+  const int64_t ii = wave_live ? i : 0;
   const bool qvalid = i < N;
   const int64_t npad = ops.npad;
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
-  for (int x = lane; x < 512; x += 64) {
+  for (int x = tid; x < 512; x += kBwdThreads) {
     const int hl = x >> 8, b = x & 255;
     tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
   }
-  const s16x8 qb0 = load_h8(ops.qa + (i * kH + h0) * 16 + 8 * hp);
-  const s16x8 qb1 = load_h8(ops.qa + (i * kH + h0 + 1) * 16 + 8 * hp);
-  const s16x8 ob0 = load_h8(ops.doa + (i * kH + h0) * 16 + 8 * hp);
-  const s16x8 ob1 = load_h8(ops.doa + (i * kH + h0 + 1) * 16 + 8 * hp);
+  const s16x8 qb0 = load_h8(ops.qa + (ii * kH + h0) * 16 + 8 * hp);
+  const s16x8 qb1 = load_h8(ops.qa + (ii * kH + h0 + 1) * 16 + 8 * hp);
+  const s16x8 ob0 = load_h8(ops.doa + (ii * kH + h0) * 16 + 8 * hp);
+  const s16x8 ob1 = load_h8(ops.doa + (ii * kH + h0 + 1) * 16 + 8 * hp);
   f32x16 dq0 = {}, dq1 = {};
   const int kr = node_of_row(c);
-  const bool trow = c < kD;
-  BwdPtrs p;
-  p.code = spd + (qvalid ? i : N - 1) * N + 16 * hp;
-  p.a = ops.ka + (static_cast<int64_t>(kr) * kH + h0) * 16 + 8 * hp;
-  p.g = ops.va + (static_cast<int64_t>(kr) * kH + h0) * 16 + 8 * hp;
-  p.t = ops.kt + (static_cast<int64_t>(h0) * kD + (c & 7)) * npad + 16 * hp;
-  p.u = nullptr;
-  const int64_t hstride = kD * npad;
+  const uint8_t* srow = spd + (qvalid ? i : N - 1) * N;
+  const int64_t cc = 16 * hp;
+
+  StageSrc src;
+  src.row0 = ops.ka + h0 * 16;
+  src.row1 = ops.va + h0 * 16;
+  src.tr0 = ops.kt + static_cast<int64_t>(h0) * kD * npad;
+  src.tr1 = nullptr;
+  const int64_t ntiles = npad / 32, nfull = N / 32;
+  constexpr int kCh = 320;  // ka, va, k^T
+  s16x8 sr[stage_per_thread<kCh>()];
+  stage_load<kCh>(sr, src, npad, 0, tid);
+  stage_store<kCh>(stage, sr, tid);
+  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(srow, cc, N) : codes_at<true, kAligned>(srow, cc, N);
   __syncthreads();
 
-  const int64_t ntiles = npad / 32, nfull = N / 32;
-  ScoreOps cur, nxt;
-  if (nfull > 0)
-    load_score_ops<false, kAligned>(cur, p, 16 * hp, N);
-  else
-    load_score_ops<true, kAligned>(cur, p, 16 * hp, N);
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t j0 = t * 32;
-    s16x8 t00 = {}, t01 = {}, t10 = {}, t11 = {};
-    if (trow) {
-      t00 = load_h8(p.t);
-      t01 = load_h8(p.t + 8);
-      t10 = load_h8(p.t + hstride);
-      t11 = load_h8(p.t + hstride + 8);
+    const uint16_t* cur = stage + (t & 1) * kStageHalves;
+    u32x4 cwn = cw;
+    if (t + 1 < ntiles) {
+      stage_load<kCh>(sr, src, npad, j0 + 32, tid);
+      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(srow, j0 + 32 + cc, N)
+                            : codes_at<true, kAligned>(srow, j0 + 32 + cc, N);
     }
-    BwdPtrs pn = p;
-    pn.code += 32;
-    pn.a += 32 * kH * 16;
-    pn.g += 32 * kH * 16;
-    pn.t += 32;
-    if (t + 1 < nfull)
-      load_score_ops<false, kAligned>(nxt, pn, j0 + 32 + 16 * hp, N);
-    else if (t + 1 < ntiles)
-      load_score_ops<true, kAligned>(nxt, pn, j0 + 32 + 16 * hp, N);
-    f32x16 s0, s1;
+    if (wave_live) {
+      const uint16_t* ka_t = cur;
+      const uint16_t* va_t = cur + kTileHalves;
+      const uint16_t* kt_t = cur + 2 * kTileHalves;
+      f32x16 s0, s1;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t cb = code_byte(cur.cw, e);
-      s0[e] = tb[cb];
-      s1[e] = tb[256 + cb];
-    }
-    s0 = mfma_h16(cur.a0, qb0, s0);
-    s1 = mfma_h16(cur.a1, qb1, s1);
-    f32x16 p0 = mfma_h16(cur.g0, ob0, f32x16{});
-    f32x16 p1 = mfma_h16(cur.g1, ob1, f32x16{});
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t cb = code_byte(cw, e);
+        s0[e] = tb[cb];
+        s1[e] = tb[256 + cb];
+      }
+      s0 = mfma_h16(staged_aug(ka_t, kr, 0, hp), qb0, s0);
+      s1 = mfma_h16(staged_aug(ka_t, kr, 1, hp), qb1, s1);
+      f32x16 p0 = mfma_h16(staged_aug(va_t, kr, 0, hp), ob0, f32x16{});
+      f32x16 p1 = mfma_h16(staged_aug(va_t, kr, 1, hp), ob1, f32x16{});
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p0[e] *= __builtin_amdgcn_exp2f(s0[e] * sc2);
-      p1[e] *= __builtin_amdgcn_exp2f(s1[e] * sc2);
+      for (int e = 0; e < 16; ++e) {
+        p0[e] *= __builtin_amdgcn_exp2f(s0[e] * sc2);
+        p1[e] *= __builtin_amdgcn_exp2f(s1[e] * sc2);
+      }
+#pragma unroll
+      for (int k1 = 0; k1 < 2; ++k1) {
+        const int f = 16 * hp + 8 * k1;
+        dq0 = mfma_h16(staged_tr(kt_t, 0, c, f), pack_f16x8(p0, 8 * k1), dq0);
+        dq1 = mfma_h16(staged_tr(kt_t, 1, c, f), pack_f16x8(p1, 8 * k1), dq1);
+      }
     }
-    dq0 = mfma_h16(t00, pack_f16x8(p0, 0), dq0);
-    dq0 = mfma_h16(t01, pack_f16x8(p0, 8), dq0);
-    dq1 = mfma_h16(t10, pack_f16x8(p1, 0), dq1);
-    dq1 = mfma_h16(t11, pack_f16x8(p1, 8), dq1);
-    cur = nxt;
-    p = pn;
+    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kStageHalves, sr, tid);
+    cw = cwn;
+    __syncthreads();
   }
-  if (qvalid) {
+  if (wave_live && qvalid) {
     const float rs = 1.f / sqd;
     float* qp = dq + i * kHD + h0 * kD + 4 * hp;
     *reinterpret_cast<float4*>(qp) = make_float4(dq0[0] * rs, dq0[1] * rs, dq0[2] * rs, dq0[3] * rs);
@@ -667,13 +736,26 @@ __global__ __launch_bounds__(64) void bwd_q_mfma_d8_kernel(const uint8_t* __rest
   }
 }
 
-size_t kv_mfma_lds(int NB) { return 4ull * 2 * NB * 64 + 4ull * 512; }
+size_t kv_mfma_lds(int NB) { return 4ull * kBwdWaves * 2 * NB * 64 + 4ull * 128 + 2ull * 2 * kStageHalves; }
+
+template <typename K>
+hipError_t allow_lds_mfma(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(bytes));
+}
 
 }  // namespace
 
 bool mfma_supported(int H, int D, int dtype) { return H == kH && D == kD && dtype == 1; }
 
 int64_t mfma_npad(int64_t N) { return (N + 31) / 32 * 32; }
+
+// dtable partial rows: one per 32-key block (padded to whole key workgroups)
+int64_t mfma_kv_blocks(int64_t N) {
+  const int64_t nblk = (mfma_npad(N) / 32 + kBwdWaves - 1) / kBwdWaves;
+  return nblk * kBwdWaves;
+}
 
 size_t mfma_ops_bytes(int64_t N) {
   const size_t npad = static_cast<size_t>(mfma_npad(N));
@@ -722,14 +804,19 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   trace_end(1, s);
   if (e != hipSuccess) return e;
 
-  const dim3 grid(static_cast<unsigned>(ops.npad / 32), kH / 2);
+  const int nblk = static_cast<int>((ops.npad / 32 + kBwdWaves - 1) / kBwdWaves);
+  const dim3 grid(static_cast<unsigned>(xcd_grid(nblk)));
+  const dim3 block(kBwdThreads);
   const size_t lds = kv_mfma_lds(a.NB);
+  e = allow_lds_mfma(bwd_kv_mfma_d8_kernel<true>, lds);
+  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d8_kernel<false>, lds);
+  if (e != hipSuccess) return e;
   trace_begin(2, s);
   if (aligned)
-    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<true>, grid, dim3(64), lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
+    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<true>, grid, block, lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
                        partial, a.N, a.NB);
   else
-    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<false>, grid, dim3(64), lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
+    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<false>, grid, block, lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
                        partial, a.N, a.NB);
   e = hipGetLastError();
   trace_end(2, s);
@@ -737,9 +824,9 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
 
   trace_begin(3, s);
   if (aligned)
-    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<true>, grid, dim3(64), 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
+    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<true>, grid, block, 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
   else
-    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<false>, grid, dim3(64), 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
+    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<false>, grid, block, 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
   e = hipGetLastError();
   trace_end(3, s);
   if (e != hipSuccess) return e;

@@ -116,8 +116,8 @@ BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype) {
   BwdWorkspace w{};
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const bool mfma = mfma_supported(H, D, dtype);
-  const int64_t kb = mfma ? 32 : valu_kv_block(H);
-  w.n_kv_blocks = (N + kb - 1) / kb;
+  const int64_t kb = valu_kv_block(H);
+  w.n_kv_blocks = mfma ? mfma_kv_blocks(N) : (N + kb - 1) / kb;
   w.delta_off = 0;
   w.ops_off = up(static_cast<size_t>(N) * H * sizeof(float));
   w.partial_off = w.ops_off + (mfma ? up(mfma_ops_bytes(N)) : 0);
