@@ -52,6 +52,13 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int node_of_row(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued once before a
+// software-pipelined loop: with a load of the first tile still pending at loop entry,
+// the compiler's wait analysis would otherwise merge that state into the loop header
+// and wait for every outstanding load (the next tile's prefetch included) at the top
+// of each iteration.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // 16 consecutive codes of one row starting at column col; zero past column `limit`.
 template <bool kAligned>
 __device__ __forceinline__ u32x4 load_codes16(const uint8_t* row, int64_t col, int64_t limit) {
@@ -125,13 +132,27 @@ __device__ __forceinline__ s16x8 read_operand_t(const uint16_t* tile, int hl, in
   return s16x8{one, one, one, one, one, one, one, one};
 }
 
+// Workgroup -> (node block, head pair) mapping. Workgroups are dispatched round-robin
+// over the 8 XCDs (each with its own L2). The 4 head pairs of one node block read
+// the same code rows, so they are placed on one XCD, in consecutive dispatch slots.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_map(int wg, int nblocks, int& blk, int& hpair) {
+  const int xcd = wg % kXcds, slot = wg / kXcds;
+  hpair = slot & 3;
+  blk = (slot >> 2) * kXcds + xcd;
+  if (blk >= nblocks) blk = -1;  // padding workgroup (grid rounded up to whole groups)
+}
+__host__ __device__ constexpr int xcd_grid(int nblocks) {
+  return ((nblocks + kXcds - 1) / kXcds) * kXcds * 4;
+}
+
 // ---------------------------------------------------------------------------------
 // Forward. S^T = K Q^T per 32-key tile (rows = keys in the order above, columns =
 // queries); running max per query column; O^T += V^T P^T with a ones row in V^T so
 // the MFMA also accumulates the row sum l.
 //
-// A workgroup is 4 waves = 128 queries x 2 heads; the waves share one transposed
-// half-precision V tile in LDS (double-buffered, one barrier per key tile; each wave
+// A workgroup is 4 waves = 128 queries x 2 heads (ordered as in xcd_map); the waves
+// share one transposed half-precision V tile in LDS (double-buffered, one barrier per key tile; each wave
 // converts a quarter of it), and each wave prefetches the next tile's codes and K
 // operands into registers while it computes the current one. Only the last key tile
 // can be partial, so only it takes the guarded loads and the -inf mask.
@@ -182,8 +203,12 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int c = lane & 31, hp = lane >> 5;
-  const int h0 = 2 * blockIdx.y;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * (32 * kFwdWaves) + 32 * w + c;
+  const int nqb = static_cast<int>((N + 32 * kFwdWaves - 1) / (32 * kFwdWaves));
+  int qb, hpair;
+  xcd_map(blockIdx.x, nqb, qb, hpair);
+  if (qb < 0) return;
+  const int h0 = 2 * hpair;
+  const int64_t i = static_cast<int64_t>(qb) * (32 * kFwdWaves) + 32 * w + c;
   const bool qvalid = i < N;
   const int64_t irow = qvalid ? i : N - 1;
   const float sqd = sqrtf(static_cast<float>(kD));
@@ -218,6 +243,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
   else
     fwd_load<true, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, sk, shl, sdp);
   stage(0, cur.vw);
+  wait_vm0();
   __syncthreads();
 
   f32x16 o0 = {}, o1 = {};
@@ -412,31 +438,24 @@ __device__ __forceinline__ s16x8 load_t8(const uint16_t* t, int64_t npad, int h,
   return *reinterpret_cast<const s16x8*>(t + (static_cast<int64_t>(h) * kD + (m & 7)) * npad + first);
 }
 
-// Workgroup -> (node block, head pair) mapping. Workgroups are dispatched round-robin
-// over the 8 XCDs (each with its own L2). The 4 head pairs of one node block read
-// the same code rows, so they are placed on one XCD, in consecutive dispatch slots.
-constexpr int kXcds = 8;
-__device__ __forceinline__ void xcd_map(int wg, int nblocks, int& blk, int& hpair) {
-  const int xcd = wg % kXcds, slot = wg / kXcds;
-  hpair = slot & 3;
-  blk = (slot >> 2) * kXcds + xcd;
-  if (blk >= nblocks) blk = -1;  // padding workgroup (grid rounded up to whole groups)
-}
-__host__ __device__ constexpr int xcd_grid(int nblocks) {
-  return ((nblocks + kXcds - 1) / kXcds) * kXcds * 4;
-}
-
 constexpr int kBwdWaves = 4;              // waves per backward workgroup: 4 x 32 nodes, one head pair
 constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kTileHalves = 32 * 2 * 16;  // one staged [32 nodes][2 heads][16] augmented tile
-constexpr int kTTileHalves = 2 * kD * 32; // one staged transposed [2 heads][8][32] tile
-constexpr int kStageHalves = 2 * kTileHalves + 2 * kTTileHalves;  // one buffer of the double buffer
 
 // One 32-node tile of backward operands of a head pair, staged into LDS: two
-// augmented-row tiles [node][head][16] and one or two transposed tiles [head][d][node].
-// The tiles are cut into 16-byte chunks; chunk x lands at halves 8x of the buffer:
-// x in [0,128) first augmented, [128,256) second augmented, [256,320) first
-// transposed, [320,384) second transposed. Thread t moves chunks t, t + 256, ...
+// augmented-row tiles and one or two transposed tiles. Each tile is 32 rows of 64
+// bytes (4 chunks of 16 bytes):
+//   augmented:  row = slot s holding node a(s) (the MFMA row order), chunk = 2*head + half
+//   transposed: row = 8*head + d, chunk = 8-node group
+// Chunk k of row r is stored at chunk position k ^ ((r >> 1) & 3), so that the eight
+// lanes of one LDS cycle, which read rows 0..7 (or 8..15, ...) at one chunk index,
+// hit 8 distinct 16-byte bank groups instead of two.
+// The global source is cut into 16-byte chunks x: [0,128) first augmented, [128,256)
+// second augmented, [256,320) first transposed, [320,384) second transposed; thread t
+// moves chunks t, t + 256, ...
+constexpr int kAugHalves = 32 * 32;             // one augmented tile, halves
+constexpr int kTrHalves = 2 * kD * 32;          // one transposed tile [2 heads][8][32], halves
+constexpr int kStageHalves = 2 * kAugHalves + 2 * kTrHalves;  // one buffer of the double buffer
+
 struct StageSrc {
   const uint16_t* row0;  // first augmented rows (qa or ka) at node 0, head h0
   const uint16_t* row1;  // second augmented rows (doa or va) at node 0, head h0
@@ -444,11 +463,16 @@ struct StageSrc {
   const uint16_t* tr1;   // second transposed copy (unused when only one is staged)
 };
 
-// chunk c of an augmented tile: node = c >> 2, head = (c >> 1) & 1, half = c & 1
+__host__ __device__ constexpr int slot_of_node(int n) {  // inverse of node_of_row
+  return (((n >> 2) & 3) << 3) | (((n >> 4) & 1) << 2) | (n & 3);
+}
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 32 + 8 * (chunk ^ ((row >> 1) & 3)); }
+
+// global chunk c of an augmented tile: node = c >> 2, chunk = c & 3 (head = bit 1, half = bit 0)
 __device__ __forceinline__ const uint16_t* aug_chunk(const uint16_t* base, int64_t n0, int c) {
   return base + ((n0 + (c >> 2)) * kH + ((c >> 1) & 1)) * 16 + 8 * (c & 1);
 }
-// chunk c of a transposed tile: head = c >> 5, d = (c >> 2) & 7, 8 nodes from (c & 3)*8
+// global chunk c of a transposed tile: row = c >> 2 (head = c >> 5, d = (c >> 2) & 7), 8 nodes from 8*(c & 3)
 __device__ __forceinline__ const uint16_t* tr_chunk(const uint16_t* base, int64_t npad, int64_t n0, int c) {
   return base + ((c >> 5) * kD + ((c >> 2) & 7)) * npad + n0 + 8 * (c & 3);
 }
@@ -457,6 +481,15 @@ __device__ __forceinline__ const uint16_t* stage_chunk(const StageSrc& s, int64_
   if (x < 256) return aug_chunk(s.row1, n0, x - 128);
   if (x < 320) return tr_chunk(s.tr0, npad, n0, x - 256);
   return tr_chunk(s.tr1, npad, n0, x - 320);
+}
+// LDS position (halves) of global chunk x within one stage buffer
+__device__ __forceinline__ int stage_pos(int x) {
+  if (x < 256) {
+    const int c = x & 127;
+    return (x >> 7) * kAugHalves + swz(slot_of_node(c >> 2), c & 3);
+  }
+  const int c = (x - 256) & 63;
+  return 2 * kAugHalves + ((x - 256) >> 6) * kTrHalves + swz(c >> 2, c & 3);
 }
 
 template <int kChunks>
@@ -478,17 +511,17 @@ __device__ __forceinline__ void stage_store(uint16_t* buf, const s16x8 (&r)[stag
 #pragma unroll
   for (int u = 0; u < stage_per_thread<kChunks>(); ++u) {
     const int x = tid + u * kBwdThreads;
-    if (x < kChunks) *reinterpret_cast<s16x8*>(buf + 8 * x) = r[u];
+    if (x < kChunks) *reinterpret_cast<s16x8*>(buf + stage_pos(x)) = r[u];
   }
 }
 
-// Read from a staged tile: augmented row of node n, head hl, half hp.
-__device__ __forceinline__ s16x8 staged_aug(const uint16_t* aug, int n, int hl, int hp) {
-  return *reinterpret_cast<const s16x8*>(aug + (n * 2 + hl) * 16 + 8 * hp);
+// Staged augmented operand of MFMA row c (node a(c)): head hl, half hp.
+__device__ __forceinline__ s16x8 staged_aug(const uint16_t* aug, int c, int hl, int hp) {
+  return *reinterpret_cast<const s16x8*>(aug + swz(c, 2 * hl + hp));
 }
-// Transposed operand: head hl, d = m & 7, nodes first .. first+7.
-__device__ __forceinline__ s16x8 staged_tr(const uint16_t* tr, int hl, int m, int first) {
-  return *reinterpret_cast<const s16x8*>(tr + (hl * kD + (m & 7)) * 32 + first);
+// Staged transposed operand: head hl, d = m & 7, nodes 8g .. 8g+7.
+__device__ __forceinline__ s16x8 staged_tr(const uint16_t* tr, int hl, int m, int g) {
+  return *reinterpret_cast<const s16x8*>(tr + swz(hl * kD + (m & 7), g));
 }
 
 // 16 codes of one row from column col (col is a multiple of 16); kGuard zero-fills past N.
@@ -506,16 +539,16 @@ __device__ __forceinline__ u32x4 codes_at(const uint8_t* row, int64_t col, int64
 // rows = queries (order a(r)) and columns = keys, so a lane's accumulator entries
 // are queries 16*hp + 0..15; then P = exp2(S log2e / sqrt(D)) and dS = P (dP - delta)
 // take one multiply each. dV^T += dO^T P and dK^T += Q^T dS contract over those
-// queries. Bucket sums of dS go to per-lane LDS bins laid out [bucket][head][lane]
-// (no two lanes share an address, so a plain read-add-write suffices), reduced in a
-// fixed order at the end.
+// queries. Bucket sums of dS go to per-lane LDS bins laid out [bucket][lane][head]
+// (no two lanes share an address, so a plain read-add-write suffices; one 8-byte
+// read-add-write updates both heads), reduced in a fixed order at the end.
 template <bool kAligned>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
     const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ partial, int64_t N, int NB) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 64);      // [NB][2][64] per wave
+  float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 64);      // [NB][64 lanes][2 heads] per wave
   float* tb = reinterpret_cast<float*>(smem) + kBwdWaves * 2 * NB * 64;  // [2][64] by clamped code
   uint16_t* stage = reinterpret_cast<uint16_t*>(tb + 128);               // [2][kStageHalves]
 
@@ -544,9 +577,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   const s16x8 vb0 = load_h8(ops.va + (jj * kH + h0) * 16 + 8 * hp);
   const s16x8 vb1 = load_h8(ops.va + (jj * kH + h0 + 1) * 16 + 8 * hp);
   f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
-  const int qr = node_of_row(c);
   const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
-  float* mybins = bins + lane;
+  float2* mybins = reinterpret_cast<float2*>(bins) + lane;
   const uint8_t* crow = spd_t + (j < N ? j : N - 1) * N;
   const int64_t cc = 16 * hp;  // this lane's first code column within a tile
 
@@ -561,6 +593,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   stage_load<kCh>(sr, src, npad, 0, tid);
   stage_store<kCh>(stage, sr, tid);
   u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
+  wait_vm0();
   __syncthreads();
 
   for (int64_t t = 0; t < ntiles; ++t) {
@@ -574,9 +607,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
     }
     if (wave_live) {
       const uint16_t* qa_t = cur;
-      const uint16_t* doa_t = cur + kTileHalves;
-      const uint16_t* qt_t = cur + 2 * kTileHalves;
-      const uint16_t* ot_t = qt_t + kTTileHalves;
+      const uint16_t* doa_t = cur + kAugHalves;
+      const uint16_t* qt_t = cur + 2 * kAugHalves;
+      const uint16_t* ot_t = qt_t + kTrHalves;
       f32x16 s0, s1;
       uint32_t code[16];
 #pragma unroll
@@ -585,10 +618,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
         s0[e] = tb[code[e]];
         s1[e] = tb[64 + code[e]];
       }
-      s0 = mfma_h16(staged_aug(qa_t, qr, 0, hp), kb0, s0);
-      s1 = mfma_h16(staged_aug(qa_t, qr, 1, hp), kb1, s1);
-      f32x16 p0 = mfma_h16(staged_aug(doa_t, qr, 0, hp), vb0, f32x16{});
-      f32x16 p1 = mfma_h16(staged_aug(doa_t, qr, 1, hp), vb1, f32x16{});
+      s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), kb0, s0);
+      s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), kb1, s1);
+      f32x16 p0 = mfma_h16(staged_aug(doa_t, c, 0, hp), vb0, f32x16{});
+      f32x16 p1 = mfma_h16(staged_aug(doa_t, c, 1, hp), vb1, f32x16{});
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pa = __builtin_amdgcn_exp2f(s0[e] * sc2);
@@ -597,17 +630,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
         s1[e] = pb;
         p0[e] *= pa;
         p1[e] *= pb;
-        float* bin = mybins + code[e] * 128;
-        bin[0] += p0[e];
-        bin[64] += p1[e];
+        float2 bin = mybins[code[e] * 64];
+        bin.x += p0[e];
+        bin.y += p1[e];
+        mybins[code[e] * 64] = bin;
       }
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
-        const int f = 16 * hp + 8 * k1;
-        dv0 = mfma_h16(staged_tr(ot_t, 0, c, f), pack_f16x8(s0, 8 * k1), dv0);
-        dv1 = mfma_h16(staged_tr(ot_t, 1, c, f), pack_f16x8(s1, 8 * k1), dv1);
-        dk0 = mfma_h16(staged_tr(qt_t, 0, c, f), pack_f16x8(p0, 8 * k1), dk0);
-        dk1 = mfma_h16(staged_tr(qt_t, 1, c, f), pack_f16x8(p1, 8 * k1), dk1);
+        const int g = 2 * hp + k1;
+        dv0 = mfma_h16(staged_tr(ot_t, 0, c, g), pack_f16x8(s0, 8 * k1), dv0);
+        dv1 = mfma_h16(staged_tr(ot_t, 1, c, g), pack_f16x8(s1, 8 * k1), dv1);
+        dk0 = mfma_h16(staged_tr(qt_t, 0, c, g), pack_f16x8(p0, 8 * k1), dk0);
+        dk1 = mfma_h16(staged_tr(qt_t, 1, c, g), pack_f16x8(p1, 8 * k1), dk1);
       }
     }
     if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kStageHalves, sr, tid);
@@ -627,9 +661,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   // key block writes its (zero) bins too, so every partial row is defined
   for (int x = lane; x < 2 * NB; x += 64) {
     const int hl = x / NB, b = x - hl * NB;
-    const float* srcb = bins + (b * 2 + hl) * 64;
+    const float* srcb = bins + b * 128 + hl;
     float sum = 0.f;
-    for (int l = 0; l < 64; ++l) sum += srcb[l];
+    for (int l = 0; l < 64; ++l) sum += srcb[2 * l];
     partial[((jw / 32) * kH + h0 + hl) * NB + b] = sum;
   }
 }
@@ -671,7 +705,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   const s16x8 ob0 = load_h8(ops.doa + (ii * kH + h0) * 16 + 8 * hp);
   const s16x8 ob1 = load_h8(ops.doa + (ii * kH + h0 + 1) * 16 + 8 * hp);
   f32x16 dq0 = {}, dq1 = {};
-  const int kr = node_of_row(c);
   const uint8_t* srow = spd + (qvalid ? i : N - 1) * N;
   const int64_t cc = 16 * hp;
 
@@ -686,6 +719,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   stage_load<kCh>(sr, src, npad, 0, tid);
   stage_store<kCh>(stage, sr, tid);
   u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(srow, cc, N) : codes_at<true, kAligned>(srow, cc, N);
+  wait_vm0();
   __syncthreads();
 
   for (int64_t t = 0; t < ntiles; ++t) {
@@ -699,8 +733,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
     }
     if (wave_live) {
       const uint16_t* ka_t = cur;
-      const uint16_t* va_t = cur + kTileHalves;
-      const uint16_t* kt_t = cur + 2 * kTileHalves;
+      const uint16_t* va_t = cur + kAugHalves;
+      const uint16_t* kt_t = cur + 2 * kAugHalves;
       f32x16 s0, s1;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -708,10 +742,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
         s0[e] = tb[cb];
         s1[e] = tb[256 + cb];
       }
-      s0 = mfma_h16(staged_aug(ka_t, kr, 0, hp), qb0, s0);
-      s1 = mfma_h16(staged_aug(ka_t, kr, 1, hp), qb1, s1);
-      f32x16 p0 = mfma_h16(staged_aug(va_t, kr, 0, hp), ob0, f32x16{});
-      f32x16 p1 = mfma_h16(staged_aug(va_t, kr, 1, hp), ob1, f32x16{});
+      s0 = mfma_h16(staged_aug(ka_t, c, 0, hp), qb0, s0);
+      s1 = mfma_h16(staged_aug(ka_t, c, 1, hp), qb1, s1);
+      f32x16 p0 = mfma_h16(staged_aug(va_t, c, 0, hp), ob0, f32x16{});
+      f32x16 p1 = mfma_h16(staged_aug(va_t, c, 1, hp), ob1, f32x16{});
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         p0[e] *= __builtin_amdgcn_exp2f(s0[e] * sc2);
@@ -719,9 +753,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
       }
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
-        const int f = 16 * hp + 8 * k1;
-        dq0 = mfma_h16(staged_tr(kt_t, 0, c, f), pack_f16x8(p0, 8 * k1), dq0);
-        dq1 = mfma_h16(staged_tr(kt_t, 1, c, f), pack_f16x8(p1, 8 * k1), dq1);
+        const int g = 2 * hp + k1;
+        dq0 = mfma_h16(staged_tr(kt_t, 0, c, g), pack_f16x8(p0, 8 * k1), dq0);
+        dq1 = mfma_h16(staged_tr(kt_t, 1, c, g), pack_f16x8(p1, 8 * k1), dq1);
       }
     }
     if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kStageHalves, sr, tid);
@@ -763,7 +797,7 @@ size_t mfma_ops_bytes(int64_t N) {
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((a.N + 32 * kFwdWaves - 1) / (32 * kFwdWaves)), kH / 2);
+  const dim3 grid(static_cast<unsigned>(xcd_grid(static_cast<int>((a.N + 32 * kFwdWaves - 1) / (32 * kFwdWaves)))));
   trace_begin(0, s);
   if (a.N % 16 == 0)
     hipLaunchKernelGGL(fwd_mfma_d8_kernel<true>, grid, dim3(64 * kFwdWaves), 0, s, static_cast<const uint16_t*>(a.q),
