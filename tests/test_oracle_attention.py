@@ -272,3 +272,36 @@ def test_stack_finite_differences_without_rounding():
             lm = loss(args["x"], args["w"], args["t"])
             fd = (lp - lm) / (2 * eps)
             assert abs(fd - grad[ix]) <= 1e-6 * max(1.0, abs(grad[ix])), (name, ix, fd, grad[ix])
+
+
+def test_projection_identity_weights_round_inputs():
+    # W_t = I: Q = K = V = store(X), so each is X rounded to bfloat16 (or X itself)
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((11, 16))
+    w = np.stack([np.eye(16)] * 3)
+    for t in oracle.qkv_projection(x, w):
+        np.testing.assert_array_equal(t, oracle.round_bf16(x))
+    for t in oracle.qkv_projection(x, w, rounding=False):
+        np.testing.assert_array_equal(t, x)
+
+
+def test_projection_backward_finite_differences():
+    # loss = sum_t <G_t, X W_t>: its gradients are dW_t = X^T G_t and dX = sum_t G_t W_t^T
+    rng = np.random.default_rng(32)
+    N, hid = 7, 8
+    x = rng.standard_normal((N, hid))
+    w = rng.standard_normal((3, hid, hid))
+    g = rng.standard_normal((3, N, hid))
+    dx, dw = oracle.qkv_projection_backward(x, w, g[0], g[1], g[2])
+
+    def loss(x_, w_):
+        return sum(float((g[t] * tt).sum()) for t, tt in enumerate(oracle.qkv_projection(x_, w_, rounding=False)))
+
+    eps = 1e-6
+    for name, arr, grad in [("x", x, dx), ("w", w, dw)]:
+        for ix in [tuple(rng.integers(s) for s in arr.shape) for _ in range(10)]:
+            p, m = arr.copy(), arr.copy()
+            p[ix] += eps
+            m[ix] -= eps
+            fd = (loss(p, w) - loss(m, w)) / (2 * eps) if name == "x" else (loss(x, p) - loss(x, m)) / (2 * eps)
+            assert abs(fd - grad[ix]) <= 1e-7 * max(1.0, abs(grad[ix])), (name, ix, fd, grad[ix])
