@@ -8,6 +8,9 @@ raises.
     out, lse = fwd(q, k, v, spd, table)
     dq, dk, dv, dtable = bwd(q, k, v, spd, table, out, lse, dout)
     spd = spd_build(indptr, indices, N, C)          # host numpy, uint8 [N, N]
+    q, k, v = qkv_fwd(x, w)                         # one layer's projections
+    dx, dw = qkv_bwd(x, w, dq, dk, dv)
+    x_last, dx0, dw, dtable = stack_fwd_bwd(x0, w, tables, spd, dout, H)
 """
 from __future__ import annotations
 
@@ -58,6 +61,18 @@ def lib() -> ctypes.CDLL:
         L.gt_probe_peak.restype = ctypes.c_int
         L.gt_kernel_name.argtypes = [I32]
         L.gt_kernel_name.restype = ctypes.c_char_p
+        L.gt_qkv_fwd.argtypes = [P, P, P, P, P, I64, I32, I32, P]
+        L.gt_qkv_fwd.restype = ctypes.c_int
+        L.gt_qkv_bwd_workspace_bytes.argtypes = [I64, I32]
+        L.gt_qkv_bwd_workspace_bytes.restype = SZ
+        L.gt_qkv_bwd.argtypes = [P] * 8 + [SZ, I64, I32, I32, P]
+        L.gt_qkv_bwd.restype = ctypes.c_int
+        L.gt_store.argtypes = [P, P, I64, I32, P]
+        L.gt_store.restype = ctypes.c_int
+        L.gt_stack_workspace_bytes.argtypes = [I64, I32, I32, I32, I32, I32]
+        L.gt_stack_workspace_bytes.restype = SZ
+        L.gt_stack_fwd_bwd.argtypes = [P] * 11 + [SZ, I64, I32, I32, I32, I32, I32, P]
+        L.gt_stack_fwd_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -171,7 +186,87 @@ def version() -> str:
     return lib().gt_version().decode()
 
 
-KERNEL_COUNT = 5
+def _empty_like_shape(shape, dtype, device):
+    import torch
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def qkv_fwd(x, w, q=None, k=None, v=None, stream=None):
+    """One layer's projections: x [N, hid], w [3, hid, hid] (float32 or bfloat16).
+    Returns q, k, v [N, hid] in x's dtype (float32 accumulation, then rounded)."""
+    N, hid = x.shape
+    dt = _dtype_code(x)
+    q, k, v = (_empty_like_shape((N, hid), x.dtype, x.device) if t is None else t for t in (q, k, v))
+    args = [_dev(x, "x", x.dtype, (N, hid)), _dev(w, "w", x.dtype, (3, hid, hid)),
+            _dev(q, "q", x.dtype, (N, hid)), _dev(k, "k", x.dtype, (N, hid)), _dev(v, "v", x.dtype, (N, hid))]
+    _check("gt_qkv_fwd", lib().gt_qkv_fwd(*args, N, hid, dt, _stream(stream)))
+    return q, k, v
+
+
+def qkv_bwd(x, w, dq, dk, dv, dx=None, dw=None, workspace=None, stream=None):
+    """Backward of qkv_fwd for float32 dq, dk, dv [N, hid]: returns dx [N, hid], dw [3, hid, hid]."""
+    import torch
+    N, hid = x.shape
+    dt = _dtype_code(x)
+    f32 = torch.float32
+    dx = _empty_like_shape((N, hid), f32, x.device) if dx is None else dx
+    dw = _empty_like_shape((3, hid, hid), f32, x.device) if dw is None else dw
+    if workspace is None:
+        workspace = torch.empty(max(int(lib().gt_qkv_bwd_workspace_bytes(N, hid)), 256), dtype=torch.uint8,
+                                device=x.device)
+    args = [_dev(x, "x", x.dtype, (N, hid)), _dev(w, "w", x.dtype, (3, hid, hid)),
+            _dev(dq, "dq", f32, (N, hid)), _dev(dk, "dk", f32, (N, hid)), _dev(dv, "dv", f32, (N, hid)),
+            _dev(dx, "dx", f32, (N, hid)), _dev(dw, "dw", f32, (3, hid, hid)), _dev(workspace, "workspace")]
+    _check("gt_qkv_bwd", lib().gt_qkv_bwd(*args, _nbytes(workspace), N, hid, dt, _stream(stream)))
+    return dx, dw
+
+
+def store(src, dtype, dst=None, stream=None):
+    """float32 tensor -> dtype (torch.bfloat16: round to nearest even; torch.float32: copy)."""
+    import torch
+    dt = GT_BF16 if dtype == torch.bfloat16 else GT_F32
+    dst = _empty_like_shape(tuple(src.shape), dtype, src.device) if dst is None else dst
+    args = [_dev(src, "src", torch.float32), _dev(dst, "dst", dtype, tuple(src.shape))]
+    _check("gt_store", lib().gt_store(*args, src.numel(), dt, _stream(stream)))
+    return dst
+
+
+def stack_workspace_bytes(N: int, L: int, H: int, D: int, NB: int, dtype: int) -> int:
+    return int(lib().gt_stack_workspace_bytes(N, L, H, D, NB, dtype))
+
+
+def stack_fwd_bwd(x0, w, tables, spd, dout, H: int, spd_t=None, workspace=None, stream=None):
+    """Forward and backward of L stacked layers (see gt_stack_fwd_bwd) for loss sum(dout * X_L).
+    x0, dout [N, hid]; w [L, 3, hid, hid]; tables [L, H, NB] float32; spd [N, N] uint8.
+    Returns (x_last [N, hid] in x0's dtype, dx0 [N, hid], dw [L, 3, hid, hid], dtable [L, H, NB])."""
+    import torch
+    N, hid = x0.shape
+    L, _, NB = tables.shape
+    D = hid // H
+    dt = _dtype_code(x0)
+    f32 = torch.float32
+    x_last = _empty_like_shape((N, hid), x0.dtype, x0.device)
+    dx0 = _empty_like_shape((N, hid), f32, x0.device)
+    dw = _empty_like_shape((L, 3, hid, hid), f32, x0.device)
+    dtable = _empty_like_shape((L, H, NB), f32, x0.device)
+    wsb = stack_workspace_bytes(N, L, H, D, NB, dt)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x0.device)
+    args = [_dev(x0, "x0", x0.dtype, (N, hid)), _dev(w, "w", x0.dtype, (L, 3, hid, hid)),
+            _dev(tables, "tables", f32, (L, H, NB)), _dev(spd, "spd", torch.uint8, (N, N)),
+            _dev(spd if spd_t is None else spd_t, "spd_t", torch.uint8, (N, N)),
+            _dev(dout, "dout", x0.dtype, (N, hid)), _dev(x_last, "x_last"), _dev(dx0, "dx0"), _dev(dw, "dw"),
+            _dev(dtable, "dtable"), _dev(workspace, "workspace")]
+    _check("gt_stack_fwd_bwd", lib().gt_stack_fwd_bwd(*args, _nbytes(workspace), N, L, H, D, NB, dt,
+                                                      _stream(stream)))
+    return x_last, dx0, dw, dtable
+
+
+KERNEL_COUNT = 9
 
 
 def kernel_names():

@@ -90,7 +90,84 @@ hipEvent_t trace_event() {
   return e;
 }
 
-const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd", "bwd_delta", "bwd_kv", "bwd_q", "bwd_dtable"};
+const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd",     "bwd_delta",  "bwd_kv",     "bwd_q", "bwd_dtable",
+                                                   "qkv_fwd", "qkv_bwd_dx", "qkv_bwd_dw", "store"};
+
+int check_dtype(int32_t dtype) {
+  if (dtype != GT_F32 && dtype != GT_BF16) return fail(GT_EINVAL, "dtype=%d is not GT_F32 or GT_BF16", dtype);
+  return GT_OK;
+}
+
+int check_proj(int64_t N, int32_t hid, int32_t dtype) {
+  if (N < 1 || N > 0x7FFFFFFFll) return fail(GT_EINVAL, "N=%lld must lie in [1, 2^31-1]", (long long)N);
+  if (hid < 8 || hid > 512 || hid % 8 != 0) return fail(GT_EINVAL, "hid=%d must be a multiple of 8 in [8, 512]", hid);
+  return check_dtype(dtype);
+}
+
+int check_workspace(const void* ws, size_t have, size_t need) {
+  if (ws == nullptr) return fail(GT_EINVAL, "workspace is null");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(GT_EINVAL, "workspace is not 256-byte aligned");
+  if (have < need) return fail(GT_EINVAL, "workspace_bytes=%zu < %zu required", have, need);
+  return GT_OK;
+}
+
+size_t up256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Workspace of gt_stack_fwd_bwd: per layer the saved activations (Q, K, V and the
+// next layer's input in storage type, out and lse in float32), then the backward's
+// scratch shared by all layers.
+struct StackLayout {
+  size_t q, k, v, out, lse, xn, layer;    // offsets within one layer's block, block size
+  size_t g, dob, dq, dk, dv, attn, proj;  // offsets of the shared scratch
+  size_t bytes;
+  gt::BwdWorkspace attn_ws;
+};
+
+StackLayout stack_layout(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  StackLayout s{};
+  const size_t hid = static_cast<size_t>(H) * D, n = static_cast<size_t>(N);
+  const size_t st = dtype == GT_BF16 ? 2 : 4;
+  size_t o = 0;
+  s.q = o;
+  o += up256(n * hid * st);
+  s.k = o;
+  o += up256(n * hid * st);
+  s.v = o;
+  o += up256(n * hid * st);
+  s.out = o;
+  o += up256(n * hid * 4);
+  s.lse = o;
+  o += up256(n * H * 4);
+  s.xn = o;
+  o += up256(n * hid * st);
+  s.layer = o;
+  o = s.layer * static_cast<size_t>(L);
+  s.g = o;
+  o += up256(n * hid * 4);
+  s.dob = o;
+  o += up256(n * hid * st);
+  s.dq = o;
+  o += up256(n * hid * 4);
+  s.dk = o;
+  o += up256(n * hid * 4);
+  s.dv = o;
+  o += up256(n * hid * 4);
+  s.attn_ws = gt::bwd_workspace(N, H, D, NB, dtype);
+  s.attn = o;
+  o += up256(s.attn_ws.bytes);
+  s.proj = o;
+  o += up256(gt::qkv_bwd_workspace(N, static_cast<int>(hid)));
+  s.bytes = o;
+  return s;
+}
+
+hipError_t attn_fwd(const gt::FwdArgs& a, hipStream_t s) {
+  return gt::mfma_supported(a.H, a.D, a.dtype) ? gt::launch_fwd_mfma(a, s) : gt::launch_fwd_valu(a, s);
+}
+
+hipError_t attn_bwd(const gt::BwdArgs& a, const gt::BwdWorkspace& w, hipStream_t s) {
+  return gt::mfma_supported(a.H, a.D, a.dtype) ? gt::launch_bwd_mfma(a, w, s) : gt::launch_bwd_valu(a, w, s);
+}
 
 }  // namespace
 
@@ -188,9 +265,7 @@ int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(out, "out"));
   GT_CHECK(check_ptr(lse, "lse"));
   gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype};
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = gt::mfma_supported(H, D, dtype) ? gt::launch_fwd_mfma(a, s) : gt::launch_fwd_valu(a, s);
-  return hip_status(e, "gt_attn_fwd launch");
+  return hip_status(attn_fwd(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd launch");
 }
 
 size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
@@ -220,16 +295,10 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(dk, "dk"));
   GT_CHECK(check_ptr(dv, "dv"));
   GT_CHECK(check_ptr(dtable, "dtable"));
-  if (workspace == nullptr) return fail(GT_EINVAL, "workspace is null");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(GT_EINVAL, "workspace is not 256-byte aligned");
   const gt::BwdWorkspace w = gt::bwd_workspace(N, H, D, NB, dtype);
-  if (workspace_bytes < w.bytes)
-    return fail(GT_EINVAL, "workspace_bytes=%zu < %zu required", workspace_bytes, w.bytes);
+  GT_CHECK(check_workspace(workspace, workspace_bytes, w.bytes));
   gt::BwdArgs a{q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, workspace, N, H, D, NB, dtype};
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = gt::mfma_supported(H, D, dtype) ? gt::launch_bwd_mfma(a, w, s) : gt::launch_bwd_valu(a, w, s);
-  return hip_status(e, "gt_attn_bwd launch");
+  return hip_status(attn_bwd(a, w, static_cast<hipStream_t>(stream)), "gt_attn_bwd launch");
 }
 
 int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C, uint8_t* spd,
@@ -239,6 +308,124 @@ int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32
   const std::string why = gt::spd_validate(indptr, indices, N, C);
   if (!why.empty()) return fail(GT_EINVAL, "gt_spd_build: %s", why.c_str());
   gt::spd_fill(indptr, indices, N, C, spd, nthreads);
+  return GT_OK;
+}
+
+int gt_qkv_fwd(const void* x, const void* w, void* q, void* k, void* v, int64_t N, int32_t hid, int32_t dtype,
+               void* stream) {
+  GT_CHECK(check_proj(N, hid, dtype));
+  GT_CHECK(check_ptr(x, "x"));
+  GT_CHECK(check_ptr(w, "w"));
+  GT_CHECK(check_ptr(q, "q"));
+  GT_CHECK(check_ptr(k, "k"));
+  GT_CHECK(check_ptr(v, "v"));
+  return hip_status(gt::launch_qkv_fwd(x, w, q, k, v, N, hid, dtype, static_cast<hipStream_t>(stream)),
+                    "gt_qkv_fwd launch");
+}
+
+size_t gt_qkv_bwd_workspace_bytes(int64_t N, int32_t hid) {
+  const std::string saved = g_error;
+  const int rc = check_proj(N, hid, GT_F32);
+  g_error = saved;
+  return rc != GT_OK ? 0 : up256(gt::qkv_bwd_workspace(N, hid));
+}
+
+int gt_qkv_bwd(const void* x, const void* w, const float* dq, const float* dk, const float* dv, float* dx, float* dw,
+               void* workspace, size_t workspace_bytes, int64_t N, int32_t hid, int32_t dtype, void* stream) {
+  GT_CHECK(check_proj(N, hid, dtype));
+  GT_CHECK(check_ptr(x, "x"));
+  GT_CHECK(check_ptr(w, "w"));
+  GT_CHECK(check_ptr(dq, "dq"));
+  GT_CHECK(check_ptr(dk, "dk"));
+  GT_CHECK(check_ptr(dv, "dv"));
+  GT_CHECK(check_ptr(dx, "dx"));
+  GT_CHECK(check_ptr(dw, "dw"));
+  GT_CHECK(check_workspace(workspace, workspace_bytes, gt::qkv_bwd_workspace(N, hid)));
+  return hip_status(
+      gt::launch_qkv_bwd(x, w, dq, dk, dv, dx, dw, workspace, N, hid, dtype, static_cast<hipStream_t>(stream)),
+      "gt_qkv_bwd launch");
+}
+
+int gt_store(const float* src, void* dst, int64_t n, int32_t dtype, void* stream) {
+  GT_CHECK(check_dtype(dtype));
+  if (n < 0) return fail(GT_EINVAL, "n=%lld must be >= 0", (long long)n);
+  if (n == 0) return GT_OK;
+  GT_CHECK(check_ptr(src, "src"));
+  GT_CHECK(check_ptr(dst, "dst"));
+  return hip_status(gt::launch_store(src, dst, n, dtype, static_cast<hipStream_t>(stream)), "gt_store launch");
+}
+
+size_t gt_stack_workspace_bytes(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  const std::string saved = g_error;
+  const int rc = check_shape(N, H, D, NB, dtype);
+  g_error = saved;
+  if (rc != GT_OK || L < 1 || L > 1024) return 0;
+  return stack_layout(N, L, H, D, NB, dtype).bytes;
+}
+
+int gt_stack_fwd_bwd(const void* x0, const void* w, const float* tables, const uint8_t* spd, const uint8_t* spd_t,
+                     const void* dout, void* x_last, float* dx0, float* dw, float* dtable, void* workspace,
+                     size_t workspace_bytes, int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB, int32_t dtype,
+                     void* stream) {
+  GT_CHECK(check_shape(N, H, D, NB, dtype));
+  if (L < 1 || L > 1024) return fail(GT_EINVAL, "L=%d must lie in [1, 1024]", L);
+  GT_CHECK(check_ptr(x0, "x0"));
+  GT_CHECK(check_ptr(w, "w"));
+  GT_CHECK(check_ptr(tables, "tables"));
+  GT_CHECK(check_ptr(spd, "spd"));
+  GT_CHECK(check_ptr(spd_t, "spd_t"));
+  GT_CHECK(check_ptr(dout, "dout"));
+  GT_CHECK(check_ptr(x_last, "x_last"));
+  GT_CHECK(check_ptr(dx0, "dx0"));
+  GT_CHECK(check_ptr(dw, "dw"));
+  GT_CHECK(check_ptr(dtable, "dtable"));
+  const StackLayout lay = stack_layout(N, L, H, D, NB, dtype);
+  GT_CHECK(check_workspace(workspace, workspace_bytes, lay.bytes));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int hid = H * D;
+  const size_t st = dtype == GT_BF16 ? 2 : 4;
+  const size_t wsz = static_cast<size_t>(3) * hid * hid;
+  char* base = static_cast<char*>(workspace);
+  auto layer = [&](int l, size_t off) { return base + static_cast<size_t>(l) * lay.layer + off; };
+  float* G = reinterpret_cast<float*>(base + lay.g);
+  void* dO = base + lay.dob;
+  float* dq = reinterpret_cast<float*>(base + lay.dq);
+  float* dk = reinterpret_cast<float*>(base + lay.dk);
+  float* dv = reinterpret_cast<float*>(base + lay.dv);
+  const int64_t nel = N * hid;
+  // forward: X_{l+1} = store(attention_l(X_l W_l)); the last layer writes x_last
+  const void* X = x0;
+  for (int l = 0; l < L; ++l) {
+    const void* wl = static_cast<const char*>(w) + l * wsz * st;
+    void *q = layer(l, lay.q), *k = layer(l, lay.k), *v = layer(l, lay.v);
+    float* out = reinterpret_cast<float*>(layer(l, lay.out));
+    float* lse = reinterpret_cast<float*>(layer(l, lay.lse));
+    void* xn = l == L - 1 ? x_last : layer(l, lay.xn);
+    GT_CHECK(hip_status(gt::launch_qkv_fwd(X, wl, q, k, v, N, hid, dtype, s), "gt_stack_fwd_bwd qkv"));
+    const gt::FwdArgs fa{q, k, v, spd, tables + static_cast<size_t>(l) * H * NB, out, lse, N, H, D, NB, dtype};
+    GT_CHECK(hip_status(attn_fwd(fa, s), "gt_stack_fwd_bwd attention forward"));
+    GT_CHECK(hip_status(gt::launch_store(out, xn, nel, dtype, s), "gt_stack_fwd_bwd store"));
+    X = xn;
+  }
+  // backward of sum(dout * X_L): layer l gets store(dX_{l+1}) as its attention dout
+  for (int l = L - 1; l >= 0; --l) {
+    const void* wl = static_cast<const char*>(w) + l * wsz * st;
+    const void* dol = dout;
+    if (l < L - 1) {
+      GT_CHECK(hip_status(gt::launch_store(G, dO, nel, dtype, s), "gt_stack_fwd_bwd store"));
+      dol = dO;
+    }
+    const gt::BwdArgs ba{layer(l, lay.q), layer(l, lay.k), layer(l, lay.v), spd, spd_t,
+                         tables + static_cast<size_t>(l) * H * NB, reinterpret_cast<float*>(layer(l, lay.out)),
+                         reinterpret_cast<float*>(layer(l, lay.lse)), dol, dq, dk, dv,
+                         dtable + static_cast<size_t>(l) * H * NB, base + lay.attn, N, H, D, NB, dtype};
+    GT_CHECK(hip_status(attn_bwd(ba, lay.attn_ws, s), "gt_stack_fwd_bwd attention backward"));
+    const void* Xl = l == 0 ? x0 : layer(l - 1, lay.xn);
+    float* dxl = l == 0 ? dx0 : G;
+    GT_CHECK(hip_status(gt::launch_qkv_bwd(Xl, wl, dq, dk, dv, dxl, dw + static_cast<size_t>(l) * wsz,
+                                           base + lay.proj, N, hid, dtype, s),
+                        "gt_stack_fwd_bwd qkv backward"));
+  }
   return GT_OK;
 }
 

@@ -46,6 +46,19 @@ struct BwdWorkspace {
   int64_t n_kv_blocks;
 };
 
+// Kernel timing ids (gt_trace_enable); the first five are the header's GT_KERNEL_* ids.
+enum {
+  kTraceFwd = 0,
+  kTraceBwdDelta = 1,
+  kTraceBwdKv = 2,
+  kTraceBwdQ = 3,
+  kTraceBwdDtable = 4,
+  kTraceQkvFwd = 5,
+  kTraceQkvDx = 6,
+  kTraceQkvDw = 7,
+  kTraceStore = 8,
+};
+
 // Kernel timing hook (gt_trace_enable): bracket one launch with events on its stream.
 void trace_begin(int kernel_id, hipStream_t s);
 void trace_end(int kernel_id, hipStream_t s);
@@ -63,5 +76,13 @@ hipError_t launch_dtable_reduce(const float* partial, float* dtable, int64_t nbl
 hipError_t launch_bwd_valu(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 int64_t valu_kv_block(int H);
 hipError_t launch_probe(int kind, int blocks, int iters, float* sink, hipStream_t s);
+
+// Q/K/V projections and storage rounding (proj.hip). dtype 1 = bfloat16 storage.
+size_t qkv_bwd_workspace(int64_t N, int hid);
+hipError_t launch_qkv_fwd(const void* x, const void* w, void* q, void* k, void* v, int64_t N, int hid, int dtype,
+                          hipStream_t s);
+hipError_t launch_qkv_bwd(const void* x, const void* w, const float* dq, const float* dk, const float* dv, float* dx,
+                          float* dw, void* workspace, int64_t N, int hid, int dtype, hipStream_t s);
+hipError_t launch_store(const float* src, void* dst, int64_t n, int dtype, hipStream_t s);
 
 }  // namespace gt

@@ -71,6 +71,9 @@ size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, 
 
 /* Backward of gt_attn_fwd for the loss sum(dout * out): recomputes the scores and the
  * softmax from q, k, spd, table and lse (the forward's outputs out and lse are inputs).
+ *   spd_t                  device [N,N] uint8, the transpose of spd (the key-outer pass
+ *                          walks code columns as rows). For an undirected graph spd is
+ *                          symmetric and the caller passes spd itself.
  *   out                    device [N,H,D] float32, as written by gt_attn_fwd
  *   dout                   device [N,H,D] dtype
  *   dq, dk, dv             device [N,H,D] float32 (overwritten)
@@ -97,6 +100,60 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
 int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C,
                  uint8_t* spd, int32_t nthreads);
 
+/* ---- Stacked layers (MegaGraph pages, Fig. 8 caption: the evaluated Graph
+ * Transformer has 16 layers, 8 heads and hidden size 64). Only the attention layers
+ * and their Q/K/V projections are modelled, with no residual, normalisation or
+ * feed-forward block. Per layer l, with hid = H*D and store() the rounding of a
+ * float32 value to the storage dtype (bfloat16: nearest even; float32: none):
+ *     [Q|K|V]_l = store(X_l W_{l,t}), t = q, k, v          (gt_qkv_fwd)
+ *     X_{l+1}   = store(attention_l(Q_l, K_l, V_l))         (gt_attn_fwd, own table)
+ * ------------------------------------------------------------------------------- */
+
+/* Q/K/V projection of one layer, float32 accumulation, result stored in dtype.
+ *   x        device [N, hid] dtype
+ *   w        device [3, hid, hid] dtype: w[t][a][b] multiplies x[:, a] into column b of q, k, v
+ *   q, k, v  device [N, hid] dtype (overwritten); as attention inputs they are [N, H, D]
+ * Sizes: 1 <= N < 2^31, hid a multiple of 8 in [8, 512]. Errors: GT_EINVAL.        */
+int gt_qkv_fwd(const void* x, const void* w, void* q, void* k, void* v, int64_t N, int32_t hid,
+               int32_t dtype, void* stream);
+
+/* Bytes of device workspace gt_qkv_bwd needs (0 on invalid sizes). */
+size_t gt_qkv_bwd_workspace_bytes(int64_t N, int32_t hid);
+
+/* Backward of gt_qkv_fwd for float32 output gradients dq, dk, dv:
+ *   dx = dq w_q^T + dk w_k^T + dv w_v^T     device [N, hid] float32 (overwritten)
+ *   dw[t] = x^T d_t                         device [3, hid, hid] float32 (overwritten)
+ * dw is summed over fixed 256-node chunks, then over the chunks in order, so it is
+ * bitwise reproducible. workspace: device, >= gt_qkv_bwd_workspace_bytes, 256-byte
+ * aligned, contents ignored on entry.                                              */
+int gt_qkv_bwd(const void* x, const void* w, const float* dq, const float* dk, const float* dv,
+               float* dx, float* dw, void* workspace, size_t workspace_bytes, int64_t N,
+               int32_t hid, int32_t dtype, void* stream);
+
+/* dst[i] = store(src[i]) for i < n: float32 -> dtype (bfloat16: round to nearest even,
+ * inputs finite; float32: a copy). src and dst device, 16-byte aligned; n = 0 is a no-op. */
+int gt_store(const float* src, void* dst, int64_t n, int32_t dtype, void* stream);
+
+/* Bytes of device workspace gt_stack_fwd_bwd needs (0 on invalid sizes). It holds
+ * every layer's Q, K, V, attention output and lse for the backward. */
+size_t gt_stack_workspace_bytes(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB,
+                                int32_t dtype);
+
+/* Forward and backward of L stacked layers for the loss sum(dout * X_L):
+ *   x0       device [N, hid] dtype                 w       device [L, 3, hid, hid] dtype
+ *   tables   device [L, H, NB] float32             spd, spd_t as in gt_attn_bwd
+ *   dout     device [N, hid] dtype (the gradient of X_L)
+ *   x_last   device [N, hid] dtype (overwritten with X_L)
+ *   dx0      device [N, hid] float32 (overwritten with the gradient of x0)
+ *   dw       device [L, 3, hid, hid] float32, dtable device [L, H, NB] float32 (overwritten)
+ * In the backward, layer l's attention takes store(dX_{l+1}) as its dout; dq, dk, dv,
+ * dX and dW stay float32. workspace: device, >= gt_stack_workspace_bytes, 256-byte
+ * aligned. Shapes as for gt_attn_fwd, 1 <= L <= 1024.                               */
+int gt_stack_fwd_bwd(const void* x0, const void* w, const float* tables, const uint8_t* spd,
+                     const uint8_t* spd_t, const void* dout, void* x_last, float* dx0, float* dw,
+                     float* dtable, void* workspace, size_t workspace_bytes, int64_t N, int32_t L,
+                     int32_t H, int32_t D, int32_t NB, int32_t dtype, void* stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* gt_last_error(void);
 
@@ -117,7 +174,11 @@ enum {
   GT_KERNEL_BWD_KV = 2,     /* backward: key-outer dK, dV and bucket partial sums  */
   GT_KERNEL_BWD_Q = 3,      /* backward: query-outer dQ                            */
   GT_KERNEL_BWD_DTABLE = 4, /* backward: reduction of bucket partials to dtable    */
-  GT_KERNEL_COUNT = 5
+  GT_KERNEL_QKV_FWD = 5,    /* gt_qkv_fwd                                          */
+  GT_KERNEL_QKV_BWD_DX = 6, /* gt_qkv_bwd: dX                                      */
+  GT_KERNEL_QKV_BWD_DW = 7, /* gt_qkv_bwd: dW partial sums and their reduction     */
+  GT_KERNEL_STORE = 8,      /* gt_store                                            */
+  GT_KERNEL_COUNT = 9
 };
 int gt_trace_enable(int32_t on);
 int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n);

@@ -1,0 +1,111 @@
+"""Write the stored expected values of the full-size workloads (calls only the oracle).
+
+    python tests/golden/make_golden.py ba32768-bf16 [--workers 8]
+
+For a single-layer workload the oracle runs breadth-first search from every
+source and one full row-blocked float64 forward+backward sweep, and the file
+keeps what a GPU test compares: the sampled query rows of out, lse and dq (and
+of dk and dv, which are sums over every query row), the whole dtable, the
+histogram of the codes and a SHA-256 digest of the full uint8 code matrix. For
+the stacked workload it runs the oracle's 16-layer stack and keeps the final
+features and dX0 on sampled rows, and every layer's dW and dtable, together with
+the spread of each of them over stack runs whose pre-rounding values carry a
+float32-sized relative error: how far the method itself fixes each output once
+activations are rounded to bfloat16 between layers.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import oracle  # noqa: E402
+from workloads import WORKLOADS, make_inputs  # noqa: E402
+
+
+def codes_of(inp, workers):
+    w = inp.workload
+    t0 = time.perf_counter()
+    codes = oracle.bfs_codes_parallel(inp.indptr, inp.indices, w.C, np.arange(w.N), workers=workers)
+    print(f"[golden] {w.name}: BFS codes in {time.perf_counter() - t0:.0f} s", flush=True)
+    return codes
+
+
+def single_layer(inp, workers, block):
+    w = inp.workload
+    codes = codes_of(inp, workers)
+    digest = hashlib.sha256(codes.tobytes()).hexdigest()
+    hist = np.bincount(codes.ravel(), minlength=256)[:w.NB + 1]
+    t0 = time.perf_counter()
+    out, lse, dq, dk, dv, dt = oracle.full_backward(inp.q.value, inp.k.value, inp.v.value, codes,
+                                                    inp.table.value, inp.dout.value, block=block,
+                                                    workers=workers)
+    print(f"[golden] {w.name}: full sweep in {time.perf_counter() - t0:.0f} s", flush=True)
+    r = inp.rows
+    return dict(rows=r, out=out[r], lse=lse[r], dq=dq[r], dk=dk[r], dv=dv[r], dtable=dt,
+                code_hist=hist, codes_sha256=np.array(digest))
+
+
+NOISE_EPS = 2.0 ** -21   # a few float32 units of relative error before a bf16 rounding
+NOISE_RUNS = 3
+
+
+def rel_err(a, b):
+    """max |a - b| / rms(b), the bfloat16 comparison measure."""
+    return float(np.max(np.abs(a - b)) / np.sqrt(np.mean(b ** 2)))
+
+
+def stacked(inp, workers, block):
+    w = inp.workload
+    codes = codes_of(inp, workers)
+    digest = hashlib.sha256(codes.tobytes()).hexdigest()
+    args = (inp.x0.value, inp.w_qkv.value, inp.table.value, codes, inp.dout.value)
+    t0 = time.perf_counter()
+    res = oracle.stack_forward_backward(*args, workers=workers, block=block)
+    print(f"[golden] {w.name}: stack in {time.perf_counter() - t0:.0f} s", flush=True)
+    rows = np.sort(np.random.default_rng(w.number).choice(w.N, 512, replace=False))
+    ref = dict(x_last=res["x"][-1][rows], dx0=res["dx0"][rows], dw=res["dw"], dtable=res["dtable"])
+    # The method's own spread at bf16 storage: the same stack with every pre-rounding
+    # value perturbed by a float32-sized relative error (seeded runs).
+    # spread of each whole output tensor (the comparison unit), and per layer for the record
+    L = w.layers
+    spread = dict(x_last=0.0, dx0=0.0, dw=0.0, dtable=0.0, dw_layer=np.zeros(L), dtable_layer=np.zeros(L))
+    for r in range(NOISE_RUNS):
+        pr = oracle.stack_forward_backward(*args, workers=workers, block=block,
+                                           pre_round_noise=(np.random.default_rng(1000 + r), NOISE_EPS))
+        got = dict(x_last=pr["x"][-1][rows], dx0=pr["dx0"][rows], dw=pr["dw"], dtable=pr["dtable"])
+        for k in ("x_last", "dx0", "dw", "dtable"):
+            spread[k] = max(spread[k], rel_err(got[k], ref[k]))
+        for l in range(L):
+            spread["dw_layer"][l] = max(spread["dw_layer"][l], rel_err(pr["dw"][l], ref["dw"][l]))
+            spread["dtable_layer"][l] = max(spread["dtable_layer"][l],
+                                            rel_err(pr["dtable"][l], ref["dtable"][l]))
+        print(f"[golden] {w.name}: perturbed run {r}: spread so far "
+              + ", ".join(f"{k} {spread[k]:.2e}" for k in ("x_last", "dx0", "dw", "dtable")), flush=True)
+    return dict(rows=rows, codes_sha256=np.array(digest), noise_eps=np.array(NOISE_EPS),
+                **ref, **{f"spread_{k}": np.asarray(v) for k, v in spread.items()})
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("workload")
+    ap.add_argument("--workers", type=int, default=8)
+    ap.add_argument("--block", type=int, default=256)
+    a = ap.parse_args()
+    w = {x.name: x for x in WORKLOADS.values()}[a.workload]
+    inp = make_inputs(w.number)
+    data = stacked(inp, a.workers, a.block) if w.layers > 1 else single_layer(inp, a.workers, a.block)
+    path = os.path.join(HERE, f"{w.name}.npz")
+    np.savez_compressed(path, workload=np.array(w.name), **data)
+    print(f"[golden] wrote {path} ({os.path.getsize(path) / 1e6:.2f} MB)", flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,24 +24,27 @@ def host64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def err(got, ref, dtype):
+def err(got, ref, dtype, bound=None):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     e = float(np.max(np.abs(got - ref))) if got.size else 0.0
     if dtype == "f32":
-        return e, e <= TOL_F32_ABS
+        return e, e <= (TOL_F32_ABS if bound is None else bound)
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     if rms == 0.0:
         return e, e == 0.0
-    return e / rms, e / rms <= TOL_BF16_REL
+    return e / rms, e / rms <= (TOL_BF16_REL if bound is None else bound)
 
 
-def check(name, got, ref, dtype, report=None):
-    e, ok = err(got, ref, dtype)
+def check(name, got, ref, dtype, report=None, bound=None):
+    """Compare at the stated tolerance, or at `bound` where a test derives a wider one
+    from the oracle's own spread (the stacked bfloat16 model)."""
+    e, ok = err(got, ref, dtype, bound)
     if report is not None:
         report[name] = e
-    bound = TOL_F32_ABS if dtype == "f32" else TOL_BF16_REL
+    if bound is None:
+        bound = TOL_F32_ABS if dtype == "f32" else TOL_BF16_REL
     kind = "max-abs" if dtype == "f32" else "max-abs/rms"
-    assert ok, f"{name}: {kind} error {e:.3e} exceeds {bound:.0e}"
+    assert ok, f"{name}: {kind} error {e:.3e} exceeds {bound:.1e}"
     return e

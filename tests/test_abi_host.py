@@ -173,3 +173,32 @@ def test_spd_build_rejects_malformed(bad):
     with pytest.raises(gta.GtError) as e:
         gta.spd_build(ip, ix, 10, C)
     assert e.value.code == gta.GT_EINVAL
+
+
+def test_projection_and_stack_argument_errors():
+    L = gta.lib()
+    assert L.gt_qkv_fwd(P, P, P, P, P, 100, 12, 1, None) == gta.GT_EINVAL and "hid=12" in gta.last_error()
+    assert L.gt_qkv_fwd(P, P, P, P, P, 100, 1024, 1, None) == gta.GT_EINVAL
+    assert L.gt_qkv_fwd(None, P, P, P, P, 100, 64, 1, None) == gta.GT_EINVAL and "x is null" in gta.last_error()
+    assert L.gt_qkv_fwd(P, P, P, P, P, 0, 64, 1, None) == gta.GT_EINVAL
+    assert L.gt_qkv_fwd(P, P, P, P, P, 100, 64, 5, None) == gta.GT_EINVAL
+    need = L.gt_qkv_bwd_workspace_bytes(6800, 64)
+    assert need >= 27 * 3 * 64 * 64 * 4 and L.gt_qkv_bwd_workspace_bytes(6800, 63) == 0
+    assert L.gt_qkv_bwd(P, P, P, P, P, P, P, P, need - 1, 6800, 64, 1, None) == gta.GT_EINVAL
+    assert "workspace_bytes" in gta.last_error()
+    assert L.gt_qkv_bwd(P, P, P, P, P, P, P, P + 16, need, 6800, 64, 1, None) == gta.GT_EINVAL
+    assert L.gt_store(P, P, -1, 1, None) == gta.GT_EINVAL
+    assert L.gt_store(None, None, 0, 1, None) == gta.GT_OK
+    assert L.gt_store(P, P + 2, 10, 1, None) == gta.GT_EINVAL and "aligned" in gta.last_error()
+    sw = L.gt_stack_workspace_bytes(6800, 16, 8, 8, 33, 1)
+    assert sw > 16 * 6800 * 64 * (3 * 2 + 4 + 2) and L.gt_stack_workspace_bytes(6800, 0, 8, 8, 33, 1) == 0
+
+    def stack(L_=16, ws=P, wsb=sw, **kw):
+        a = dict(x0=P, dout=P)
+        a.update(kw)
+        return L.gt_stack_fwd_bwd(a["x0"], P, P, P, P, a["dout"], P, P, P, P, ws, wsb, 6800, L_, 8, 8, 33, 1,
+                                  None)
+    assert stack(L_=0) == gta.GT_EINVAL and "L=0" in gta.last_error()
+    assert stack(wsb=sw - 1) == gta.GT_EINVAL
+    assert stack(x0=None) == gta.GT_EINVAL and "x0" in gta.last_error()
+    assert stack(dout=P + 8) == gta.GT_EINVAL
