@@ -15,136 +15,27 @@
 // starts from the tile's bias, table[h, code] read from LDS by the uint8 code, so
 // adding the bias costs no vector instruction.
 //
-// Work split: one 64-lane wave per workgroup owns 32 nodes of the outer loop and two
-// heads (blockIdx.y selects the head pair). Lane l holds column c = l % 32 of every
-// 32x32 tile and one half hp = l / 32 of its rows.
-//
-// Row order inside a 32-row tile: MFMA row r stands for node offset
-//     a(r) = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3),
-// so the 16 accumulator entries of lane half hp are exactly offsets 16*hp + 0..15.
-// The lane's codes are then one contiguous 16-byte load, and each 8-entry half of
-// its accumulator is directly a bf16 operand of the 32x32x16 MFMA that contracts
-// over those nodes, whose other operand is read as 8 consecutive nodes of a
-// transposed [d][node] tile in LDS.
+// Work split: workgroups of 4 waves; each wave owns 32 nodes of its outer loop and
+// two heads (the head pair follows from the workgroup order, xcd_map). Lane l holds
+// column c = l % 32 of every 32x32 tile and one half hp = l / 32 of its rows, in the
+// row order of node_of_row (mfma_common.h): the lane's 16 accumulator entries are 16
+// consecutive nodes, so its codes are one 16-byte load and each 8-entry half of its
+// accumulator is directly an operand of the 32x32x16 MFMA that contracts over those
+// nodes, whose other operand is read as 8 consecutive nodes of a transposed
+// [d][node] tile in LDS.
 //
 // Table in LDS: for each of the wave's two heads, 256 floats: entry b holds
 // table[h, min(b, NB-1)] * sqrt(D), so every byte value indexes it without a clamp.
-#include "gt_internal.h"
+#include "mfma_common.h"
 
 #include <algorithm>
 
 namespace gt {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kD = 8;
 constexpr int kH = 8;
 constexpr int kHD = kH * kD;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ int node_of_row(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
-
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued once before a
-// software-pipelined loop: with a load of the first tile still pending at loop entry,
-// the compiler's wait analysis would otherwise merge that state into the loop header
-// and wait for every outstanding load (the next tile's prefetch included) at the top
-// of each iteration.
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// 16 consecutive codes of one row starting at column col; zero past column `limit`.
-template <bool kAligned>
-__device__ __forceinline__ u32x4 load_codes16(const uint8_t* row, int64_t col, int64_t limit) {
-  if (kAligned && col + 16 <= limit) return *reinterpret_cast<const u32x4*>(row + col);
-  u32x4 r = {0u, 0u, 0u, 0u};
-  for (int b = 0; b < 16; ++b) {
-    const uint32_t x = (col + b < limit) ? row[col + b] : 0u;
-    r[b >> 2] |= x << (8 * (b & 3));
-  }
-  return r;
-}
-
-__device__ __forceinline__ uint32_t code_byte(const u32x4& cw, int v) { return (cw[v >> 2] >> (8 * (v & 3))) & 0xffu; }
-
-// Four bf16 of one (node, head) row at d = 4*hp .. 4*hp+3, or zeros past N.
-__device__ __forceinline__ s16x4 load_op4(const uint16_t* base, int64_t node, int64_t N, int h, int hp) {
-  if (node < N) return *reinterpret_cast<const s16x4*>(base + node * kHD + h * kD + 4 * hp);
-  return s16x4{0, 0, 0, 0};
-}
-
-__device__ __forceinline__ s16x8 pack_f16x8(const f32x16& a, int first) {
-  f16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = static_cast<_Float16>(a[first + e]);
-  return __builtin_bit_cast(s16x8, r);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-// Two bf16 in one dword -> two halves in one dword (same element order).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  f16x2 r = {static_cast<_Float16>(bf16_lo(w)), static_cast<_Float16>(bf16_hi(w))};
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ f32x16 mfma_x8(s16x4 a, s16x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma_h16(s16x8 a, s16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
-                                                 0, 0, 0);
-}
-
-// Stage the transposed half-precision tile T[hl][d][0..31] of nodes n0..n0+31 for the
-// wave's heads h0, h0+1 from a node-major [N][H][D] bf16 tensor: lane (hl, group g of 4
-// nodes, d-pair dp) loads 4 dwords, converts them and packs two 8-byte rows of the tile.
-__device__ __forceinline__ void stage_transposed(uint16_t* tile, const uint16_t* src, int64_t n0,
-                                                 int64_t N, int h0, int lane) {
-  const int hl = lane >> 5, g = (lane >> 2) & 7, dp = lane & 3;
-  uint32_t w[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t n = n0 + 4 * g + r;
-    w[r] = n < N ? bf16x2_to_f16x2(*reinterpret_cast<const uint32_t*>(src + n * kHD + (h0 + hl) * kD + 2 * dp))
-                 : 0u;
-  }
-  // low halves are d = 2dp, high halves d = 2dp+1
-  const u32x2 lo = {__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)};
-  const u32x2 hi = {__builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)};
-  *reinterpret_cast<u32x2*>(tile + (hl * kD + 2 * dp) * 32 + 4 * g) = lo;
-  *reinterpret_cast<u32x2*>(tile + (hl * kD + 2 * dp + 1) * 32 + 4 * g) = hi;
-}
-
-// A operand of a half-precision contraction over 8 nodes: rows m < 8 are
-// T[hl][m][first..first+7]; row 8 is all ones when `ones_row` (it yields the row sums);
-// other rows are zero.
-__device__ __forceinline__ s16x8 read_operand_t(const uint16_t* tile, int hl, int m, int first, bool ones_row) {
-  if (m < kD) return *reinterpret_cast<const s16x8*>(tile + (hl * kD + m) * 32 + first);
-  const short one = ones_row && m == kD ? static_cast<short>(0x3C00) : static_cast<short>(0);
-  return s16x8{one, one, one, one, one, one, one, one};
-}
-
-// Workgroup -> (node block, head pair) mapping. Workgroups are dispatched round-robin
-// over the 8 XCDs (each with its own L2). The 4 head pairs of one node block read
-// the same code rows, so they are placed on one XCD, in consecutive dispatch slots.
-constexpr int kXcds = 8;
-__device__ __forceinline__ void xcd_map(int wg, int nblocks, int& blk, int& hpair) {
-  const int xcd = wg % kXcds, slot = wg / kXcds;
-  hpair = slot & 3;
-  blk = (slot >> 2) * kXcds + xcd;
-  if (blk >= nblocks) blk = -1;  // padding workgroup (grid rounded up to whole groups)
-}
-__host__ __device__ constexpr int xcd_grid(int nblocks) {
-  return ((nblocks + kXcds - 1) / kXcds) * kXcds * 4;
-}
 
 // ---------------------------------------------------------------------------------
 // Forward. S^T = K Q^T per 32-key tile (rows = keys in the order above, columns =
@@ -160,7 +51,6 @@ __host__ __device__ constexpr int xcd_grid(int nblocks) {
 // The running max is updated lazily: a wave rescales its accumulators only when some
 // lane's tile max exceeds its current max by more than kLazy (in log2 units), so the
 // probabilities fed to the MFMA stay below 2^kLazy and rescales are rare.
-constexpr float kLazy = 8.0f;
 constexpr int kFwdWaves = 4;
 
 struct FwdTile {
@@ -430,14 +320,6 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
   }
 }
 
-__device__ __forceinline__ s16x8 load_h8(const uint16_t* p) { return *reinterpret_cast<const s16x8*>(p); }
-
-// A operand of a contraction over 8 nodes from a transposed [head][d][npad] half copy:
-// lane row m reads d = m & 7 (rows >= 8 only feed output rows that are never read).
-__device__ __forceinline__ s16x8 load_t8(const uint16_t* t, int64_t npad, int h, int m, int64_t first) {
-  return *reinterpret_cast<const s16x8*>(t + (static_cast<int64_t>(h) * kD + (m & 7)) * npad + first);
-}
-
 constexpr int kBwdWaves = 4;              // waves per backward workgroup: 4 x 32 nodes, one head pair
 constexpr int kBwdThreads = 64 * kBwdWaves;
 
@@ -462,11 +344,6 @@ struct StageSrc {
   const uint16_t* tr0;   // first transposed copy at head h0, d 0, node 0
   const uint16_t* tr1;   // second transposed copy (unused when only one is staged)
 };
-
-__host__ __device__ constexpr int slot_of_node(int n) {  // inverse of node_of_row
-  return (((n >> 2) & 3) << 3) | (((n >> 4) & 1) << 2) | (n & 3);
-}
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 32 + 8 * (chunk ^ ((row >> 1) & 3)); }
 
 // global chunk c of an augmented tile: node = c >> 2, chunk = c & 3 (head = bit 1, half = bit 0)
 __device__ __forceinline__ const uint16_t* aug_chunk(const uint16_t* base, int64_t n0, int c) {
@@ -522,13 +399,6 @@ __device__ __forceinline__ s16x8 staged_aug(const uint16_t* aug, int c, int hl, 
 // Staged transposed operand: head hl, d = m & 7, nodes 8g .. 8g+7.
 __device__ __forceinline__ s16x8 staged_tr(const uint16_t* tr, int hl, int m, int g) {
   return *reinterpret_cast<const s16x8*>(tr + swz(hl * kD + (m & 7), g));
-}
-
-// 16 codes of one row from column col (col is a multiple of 16); kGuard zero-fills past N.
-template <bool kGuard, bool kAligned>
-__device__ __forceinline__ u32x4 codes_at(const uint8_t* row, int64_t col, int64_t N) {
-  if (kGuard || !kAligned) return load_codes16<false>(row, col, N);
-  return *reinterpret_cast<const u32x4*>(row + col);
 }
 
 // Backward, step 2 (key-outer). A workgroup is 4 waves = 128 keys x one head pair;
@@ -771,13 +641,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
 }
 
 size_t kv_mfma_lds(int NB) { return 4ull * kBwdWaves * 2 * NB * 64 + 4ull * 128 + 2ull * 2 * kStageHalves; }
-
-template <typename K>
-hipError_t allow_lds_mfma(K kernel, size_t bytes) {
-  if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(bytes));
-}
 
 }  // namespace
 
