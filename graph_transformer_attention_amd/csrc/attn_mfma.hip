@@ -644,7 +644,7 @@ size_t kv_mfma_lds(int NB) { return 4ull * kBwdWaves * 2 * NB * 64 + 4ull * 128 
 
 }  // namespace
 
-bool mfma_supported(int H, int D, int dtype) { return H == kH && D == kD && dtype == 1; }
+bool mfma_supported(int H, int D, int dtype) { return H == kH && (D == 8 || D == 32) && dtype == 1; }
 
 int64_t mfma_npad(int64_t N) { return (N + 31) / 32 * 32; }
 

@@ -1,0 +1,778 @@
+// Biased attention on the gfx950 matrix cores (MFMA) for head dimension 32, 8 heads,
+// bfloat16 inputs, float32 accumulation and outputs.
+//
+// MegaGraph pages, abstract: the score matrix and the topology-aware bias matrix make
+// full-graph attention expensive; Fig. 4 caption: work proceeds over key blocks with
+// the bias columns sliced to each block. As at D = 8, neither matrix is stored: each
+// 32x32 score tile of a head starts its MFMA accumulator from table[h, code] read from
+// LDS, and the contractions over D (QK^T, dO V^T) and over nodes (PV, P^T dO, dS^T Q,
+// dS K) run on 32x32x16 MFMAs, all 32 accumulator rows carrying head dimensions.
+//
+// Precision as at D = 8: QK^T multiplies the bf16 inputs exactly (bf16 MFMA in the
+// forward, inputs converted exactly to half in the backward), P and dS enter the
+// contractions over nodes as IEEE half, lse*sqrt(D) and delta enter the backward's
+// score MFMAs split into two halves (an extra 16-deep contraction chunk).
+//
+// Work split: 4-wave workgroups over 128 nodes of one head pair (xcd_map); lane l
+// holds column l % 32 of every tile and half l / 32 of its rows in the order of
+// node_of_row.
+#include "mfma_common.h"
+
+namespace gt {
+namespace {
+
+constexpr int kD = 32;
+constexpr int kH = 8;
+constexpr int kHD = kH * kD;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+// ---------------------------------------------------------------------------------
+// Forward: per 32-key tile, S^T = K Q^T (two bf16 MFMAs over D), online softmax per
+// query column, O^T += V^T P^T (two half MFMAs over the tile's keys). The row sum l
+// is accumulated on the vector ALU (all 32 rows of V^T are head dimensions). V^T is
+// staged per tile in LDS as half, rows of 40 halves (80 bytes) so that the 16 lanes
+// of an LDS cycle reading rows d..d+15 hit distinct banks.
+constexpr int kVtRow = 40;
+constexpr int kVtHead = kD * kVtRow;  // halves per head in one buffer
+
+struct FwdTileD32 {
+  u32x4 cw;           // 16 codes: query row, keys 16*hp .. 16*hp+15 of the tile
+  s16x8 ka[2][2];     // K operand rows (head, d chunk) for MFMA row c
+  u32x2 va, vb;       // staging: 4 d values of keys 2kp and 2kp+1 (bf16)
+};
+
+template <bool kGuard, bool kAligned>
+__device__ __forceinline__ void fwd_load_d32(FwdTileD32& t, const uint8_t* srow, const uint16_t* k,
+                                             const uint16_t* v, int64_t j0, int64_t N, int h0, int hp, int kr,
+                                             int shl, int sdq, int skp) {
+  t.cw = codes_at<kGuard, kAligned>(srow, j0 + 16 * hp, N);
+  const int64_t kn = j0 + kr;
+#pragma unroll
+  for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      t.ka[hl][i] = (!kGuard || kn < N) ? load_h8(k + kn * kHD + (h0 + hl) * kD + 16 * i + 8 * hp)
+                                        : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  const int64_t v0 = j0 + 2 * skp, v1 = v0 + 1;
+  const uint16_t* vp = v + (h0 + shl) * kD + 4 * sdq;
+  t.va = (!kGuard || v0 < N) ? *reinterpret_cast<const u32x2*>(vp + v0 * kHD) : u32x2{0u, 0u};
+  t.vb = (!kGuard || v1 < N) ? *reinterpret_cast<const u32x2*>(vp + v1 * kHD) : u32x2{0u, 0u};
+}
+
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ k,
+                                                                const uint16_t* __restrict__ v,
+                                                                const uint8_t* __restrict__ spd,
+                                                                const float* __restrict__ table,
+                                                                float* __restrict__ out, float* __restrict__ lse,
+                                                                int64_t N, int NB) {
+  __shared__ float tb[2 * 256];
+  __shared__ __align__(16) uint16_t vt[2][2 * kVtHead];  // [buffer][head][d][key], rows of kVtRow
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int c = lane & 31, hp = lane >> 5;
+  const int nqb = static_cast<int>((N + 32 * kWaves - 1) / (32 * kWaves));
+  int qb, hpair;
+  xcd_map(blockIdx.x, nqb, qb, hpair);
+  if (qb < 0) return;
+  const int h0 = 2 * hpair;
+  const int64_t i = static_cast<int64_t>(qb) * (32 * kWaves) + 32 * w + c;
+  const bool qvalid = i < N;
+  const int64_t irow = qvalid ? i : N - 1;
+  const float sqd = sqrtf(static_cast<float>(kD));
+  const float sc2 = kLog2e / sqd;
+  const float lazy_raw = kLazy / sc2;
+
+  for (int x = tid; x < 512; x += kThreads) {
+    const int hl = x >> 8, b = x & 255;
+    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  }
+  s16x8 qop[2][2];
+#pragma unroll
+  for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci)
+      qop[hl][ci] = qvalid ? load_h8(q + i * kHD + (h0 + hl) * kD + 16 * ci + 8 * hp)
+                           : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  const uint8_t* srow = spd + irow * N;
+  const int kr = node_of_row(c);
+  // staging role: head shl, d quad sdq (d = 4*sdq .. +3), key pair skp (keys 2*skp, 2*skp+1)
+  const int shl = tid >> 7, sdq = (tid >> 4) & 7, skp = tid & 15;
+  auto stage = [&](int buf, const u32x2& va, const u32x2& vb) {
+    // halves of (key 2skp, key 2skp+1) for each of the four d values
+    const uint32_t a0 = bf16x2_to_f16x2(va[0]), a1 = bf16x2_to_f16x2(va[1]);
+    const uint32_t b0 = bf16x2_to_f16x2(vb[0]), b1 = bf16x2_to_f16x2(vb[1]);
+    uint32_t* base = reinterpret_cast<uint32_t*>(&vt[buf][shl * kVtHead + (4 * sdq) * kVtRow + 2 * skp]);
+    constexpr int kRowWords = kVtRow / 2;
+    base[0 * kRowWords] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+    base[1 * kRowWords] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+    base[2 * kRowWords] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+    base[3 * kRowWords] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+  };
+
+  const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
+  FwdTileD32 cur, nxt;
+  if (nfull > 0)
+    fwd_load_d32<false, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, shl, sdq, skp);
+  else
+    fwd_load_d32<true, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, shl, sdq, skp);
+  stage(0, cur.va, cur.vb);
+  wait_vm0();
+  __syncthreads();
+
+  f32x16 o0 = {}, o1 = {};
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t j0 = t * 32;
+    const int buf = static_cast<int>(t & 1);
+    if (t + 1 < nfull)
+      fwd_load_d32<false, kAligned>(nxt, srow, k, v, j0 + 32, N, h0, hp, kr, shl, sdq, skp);
+    else if (t + 1 < ntiles)
+      fwd_load_d32<true, kAligned>(nxt, srow, k, v, j0 + 32, N, h0, hp, kr, shl, sdq, skp);
+    f32x16 s0, s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t cb = code_byte(cur.cw, e);
+      s0[e] = tb[cb];
+      s1[e] = tb[256 + cb];
+    }
+    s0 = mfma_b16(cur.ka[0][0], qop[0][0], s0);
+    s1 = mfma_b16(cur.ka[1][0], qop[1][0], s1);
+    s0 = mfma_b16(cur.ka[0][1], qop[0][1], s0);
+    s1 = mfma_b16(cur.ka[1][1], qop[1][1], s1);
+    if (t >= nfull) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (j0 + 16 * hp + e >= N) {
+          s0[e] = -INFINITY;
+          s1[e] = -INFINITY;
+        }
+      }
+    }
+    float x0 = s0[0], x1 = s1[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) {
+      x0 = fmaxf(x0, s0[e]);
+      x1 = fmaxf(x1, s1[e]);
+    }
+    x0 = fmaxf(x0, __shfl_xor(x0, 32));
+    x1 = fmaxf(x1, __shfl_xor(x1, 32));
+    if (__any(x0 > m0 + lazy_raw || x1 > m1 + lazy_raw)) {
+      const float n0 = fmaxf(m0, x0), n1 = fmaxf(m1, x1);
+      const float a0 = __builtin_amdgcn_exp2f((m0 - n0) * sc2);
+      const float a1 = __builtin_amdgcn_exp2f((m1 - n1) * sc2);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        o0[e] *= a0;
+        o1[e] *= a1;
+      }
+      l0 *= a0;
+      l1 *= a1;
+      m0 = n0;
+      m1 = n1;
+    }
+    const float b0 = -m0 * sc2, b1 = -m1 * sc2;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, b0));
+      s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, b1));
+      l0 += s0[e];
+      l1 += s1[e];
+    }
+    const uint16_t* vb0 = &vt[buf][c * kVtRow + 16 * hp];
+#pragma unroll
+    for (int k1 = 0; k1 < 2; ++k1) {
+      o0 = mfma_h16(load_h8(vb0 + 8 * k1), pack_f16x8(s0, 8 * k1), o0);
+      o1 = mfma_h16(load_h8(vb0 + kVtHead + 8 * k1), pack_f16x8(s1, 8 * k1), o1);
+    }
+    if (t + 1 < ntiles) {
+      stage(buf ^ 1, nxt.va, nxt.vb);
+      cur = nxt;
+    }
+    __syncthreads();
+  }
+  // each lane half summed its 16 keys of every tile
+  l0 += __shfl_xor(l0, 32);
+  l1 += __shfl_xor(l1, 32);
+  if (qvalid) {
+    // O^T rows held by this lane: d = 8*j + 4*hp + (0..3), entries 4*j .. 4*j+3
+    const float r0 = 1.f / l0, r1 = 1.f / l1;
+    float* op0 = out + i * kHD + h0 * kD + 4 * hp;
+    float* op1 = op0 + kD;
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      *reinterpret_cast<float4*>(op0 + 8 * jq) =
+          make_float4(o0[4 * jq] * r0, o0[4 * jq + 1] * r0, o0[4 * jq + 2] * r0, o0[4 * jq + 3] * r0);
+      *reinterpret_cast<float4*>(op1 + 8 * jq) =
+          make_float4(o1[4 * jq] * r1, o1[4 * jq + 1] * r1, o1[4 * jq + 2] * r1, o1[4 * jq + 3] * r1);
+    }
+    if (hp == 0) {
+      lse[i * kH + h0] = (m0 * sc2 + log2f(l0)) * kLn2;
+      lse[i * kH + h0 + 1] = (m1 * sc2 + log2f(l1)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Backward operand copies, written once per call for all Npad = N rounded up to 32
+// nodes (rows past N padded):
+//   qd, kd, vd, od   [node][head][32] half      q, k, v, dout
+//   qt, kt, ot       [head][32][node] half      transposed q, k, dout
+//   lq, dl           [head][node] two halves    (-L_hi, -L_lo), L = lse*sqrt(D), and
+//                                               (-delta_hi, -delta_lo), delta = <dout, out>
+// The score MFMAs contract over 48: the 32 head dimensions, then a chunk holding
+// [-L_hi, -L_lo, 1, 0...] on the query side against [1, 1, pen, 0...] on the key
+// side (pen = -inf for padded keys), so S comes out as q.k - lse*sqrt(D); likewise
+// [-delta_hi, -delta_lo, 0...] against [1, 1, 0...] gives dout.v - delta. Padded
+// queries get -L_hi = -inf.
+struct OpsD32 {
+  uint16_t *qd, *kd, *vd, *od, *qt, *kt, *ot;
+  uint32_t *lq, *dl;
+  int64_t npad;
+};
+
+__device__ __forceinline__ uint16_t hbits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+
+__global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ k,
+                                                                const uint16_t* __restrict__ v,
+                                                                const float* __restrict__ out,
+                                                                const uint16_t* __restrict__ dout,
+                                                                const float* __restrict__ lse, OpsD32 ops,
+                                                                int64_t N) {
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t npad = ops.npad;
+  if (x >= npad * kH) return;
+  const int h = static_cast<int>(x / npad);
+  const int64_t n = x - h * npad;
+  const int64_t row = (n * kH + h) * kD;
+  const uint16_t* srcs[4] = {q, k, v, dout};
+  uint16_t* dsts[4] = {ops.qd, ops.kd, ops.vd, ops.od};
+  uint16_t* trs[4] = {ops.qt, ops.kt, nullptr, ops.ot};
+  const uint16_t ninf = hbits(-INFINITY);
+  if (n < N) {
+    float delta = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(srcs[s] + row + 8 * part);
+        u32x4 hv;
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi) hv[wi] = bf16x2_to_f16x2(wv[wi]);
+        *reinterpret_cast<u32x4*>(dsts[s] + row + 8 * part) = hv;
+        if (s == 3) {
+          const float4 oa = *reinterpret_cast<const float4*>(out + row + 8 * part);
+          const float4 ob = *reinterpret_cast<const float4*>(out + row + 8 * part + 4);
+          delta = fmaf(bf16_lo(wv[0]), oa.x, delta);
+          delta = fmaf(bf16_hi(wv[0]), oa.y, delta);
+          delta = fmaf(bf16_lo(wv[1]), oa.z, delta);
+          delta = fmaf(bf16_hi(wv[1]), oa.w, delta);
+          delta = fmaf(bf16_lo(wv[2]), ob.x, delta);
+          delta = fmaf(bf16_hi(wv[2]), ob.y, delta);
+          delta = fmaf(bf16_lo(wv[3]), ob.z, delta);
+          delta = fmaf(bf16_hi(wv[3]), ob.w, delta);
+        }
+        if (trs[s] != nullptr) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t word = hv[e >> 1];
+            trs[s][(static_cast<int64_t>(h) * kD + 8 * part + e) * npad + n] =
+                static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
+          }
+        }
+      }
+    }
+    const float L = lse[n * kH + h] * sqrtf(static_cast<float>(kD));
+    const _Float16 lh = static_cast<_Float16>(L);
+    ops.lq[static_cast<int64_t>(h) * npad + n] = pack2(hbits(-static_cast<float>(lh)), hbits(-(L - static_cast<float>(lh))));
+    const _Float16 dh = static_cast<_Float16>(delta);
+    ops.dl[static_cast<int64_t>(h) * npad + n] =
+        pack2(hbits(-static_cast<float>(dh)), hbits(-(delta - static_cast<float>(dh))));
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part)
+        *reinterpret_cast<u32x4*>(dsts[s] + row + 8 * part) = u32x4{0u, 0u, 0u, 0u};
+      if (trs[s] != nullptr)
+        for (int d = 0; d < kD; ++d) trs[s][(static_cast<int64_t>(h) * kD + d) * npad + n] = 0;
+    }
+    ops.lq[static_cast<int64_t>(h) * npad + n] = pack2(ninf, 0);
+    ops.dl[static_cast<int64_t>(h) * npad + n] = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Staged tiles of the backward: one 32-node tile of a head pair, 16-byte chunks.
+//   row tile      [slot][head][32] half, slot s holding node a(s): 32 rows of 128 bytes,
+//                 chunk k of row s stored at chunk position k ^ rswz(s)
+//   transposed    [head][d][32 nodes] half: 64 rows of 64 bytes, chunk g of row r at
+//                 g ^ tswz(r)
+// Both swizzles give the 8 (or 16) lanes of one LDS cycle distinct bank groups when
+// they read consecutive rows at one chunk index.
+constexpr int kRowTile = 32 * 2 * kD;  // halves
+constexpr int kTrTile = 2 * kD * 32;   // halves
+
+__device__ __forceinline__ int rswz(int s) { return (s >> 1) & 7; }
+__device__ __forceinline__ int tswz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int row_pos(int slot, int chunk) { return slot * 64 + 8 * (chunk ^ rswz(slot)); }
+__device__ __forceinline__ int tr_pos(int row, int g) { return row * 32 + 8 * (g ^ tswz(row)); }
+
+// global chunk x of a row tile: node = x >> 3, chunk = x & 7 (head = chunk >> 2, 8 halves of d)
+__device__ __forceinline__ const uint16_t* row_src(const uint16_t* base, int64_t n0, int h0, int x) {
+  return base + ((n0 + (x >> 3)) * kH + h0) * kD + 8 * (x & 7);
+}
+// global chunk x of a transposed tile: row = x >> 2 (head = row >> 5, d = row & 31), nodes 8*(x & 3)
+__device__ __forceinline__ const uint16_t* tr_src(const uint16_t* base, int64_t npad, int64_t n0, int h0, int x) {
+  return base + (static_cast<int64_t>(h0) * kD + (x >> 2)) * npad + n0 + 8 * (x & 3);
+}
+
+// A tile set: kRows row tiles followed by kTrs transposed tiles; 256 chunks each, so
+// thread tid (of kThreads = 256) moves chunk tid of every tile.
+template <int kRows, int kTrs>
+struct StageSetD32 {
+  static constexpr int kChunks = 256 * (kRows + kTrs);
+  static constexpr int kPer = kChunks / kThreads;
+  static constexpr int kHalves = kRows * kRowTile + kTrs * kTrTile;
+  const uint16_t* rows[kRows > 0 ? kRows : 1];
+  const uint16_t* trs[kTrs > 0 ? kTrs : 1];
+  int h0;
+  int64_t npad;
+
+  __device__ __forceinline__ void load(s16x8 (&r)[kPer], int64_t n0, int tid) const {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {  // thread tid moves chunk tid of tile u
+      r[u] = u < kRows ? load_h8(row_src(rows[u < kRows ? u : 0], n0, h0, tid))
+                       : load_h8(tr_src(trs[u < kRows ? 0 : u - kRows], npad, n0, h0, tid));
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* buf, const s16x8 (&r)[kPer], int tid) const {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pos = u < kRows ? u * kRowTile + row_pos(slot_of_node(tid >> 3), tid & 7)
+                                : kRows * kRowTile + (u - kRows) * kTrTile + tr_pos(tid >> 2, tid & 3);
+      *reinterpret_cast<s16x8*>(buf + pos) = r[u];
+    }
+  }
+};
+
+// Row tile operand of MFMA row c (node a(c)): head hl, d chunk ci (16 wide), half hp.
+__device__ __forceinline__ s16x8 row_op(const uint16_t* tile, int c, int hl, int ci, int hp) {
+  return load_h8(tile + row_pos(c, 4 * hl + 2 * ci + hp));
+}
+// Transposed operand: head hl, d = m (0..31), nodes 8g .. 8g+7.
+__device__ __forceinline__ s16x8 tr_op(const uint16_t* tile, int hl, int m, int g) {
+  return load_h8(tile + tr_pos(hl * kD + m, g));
+}
+
+// The third 16-deep contraction chunk of a lane: lanes of half 0 carry
+// [a, b, c, 0, 0, 0, 0, 0] (halves), lanes of half 1 carry zeros.
+__device__ __forceinline__ s16x8 aug_chunk(uint32_t ab, uint16_t cc, int hp) {
+  if (hp != 0) return s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  const u32x4 w = {ab, static_cast<uint32_t>(cc), 0u, 0u};
+  return __builtin_bit_cast(s16x8, w);
+}
+
+// ---------------------------------------------------------------------------------
+// Backward, key-outer: a wave owns 32 keys (lane c keeps key c) and a head pair; the
+// 4 waves share each staged query tile (q and dout rows, q^T and dout^T), staged
+// once per tile in LDS. S and dP - delta come from 3 MFMAs each (rows = queries,
+// columns = keys), P = exp2(S log2e / sqrt(D)), dS = P (dP - delta); dV^T += dO^T P
+// and dK^T += Q^T dS contract over the tile's queries. Bucket sums of dS go to LDS
+// bins [bucket][key][head] shared by the two lane halves of a wave, which update them
+// one half after the other (in program order) so no two lanes touch a bin at once.
+constexpr int kKvTbD32 = 2 * 64;
+
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t* __restrict__ spd_t,
+                                                                   const float* __restrict__ table, OpsD32 ops,
+                                                                   float* __restrict__ dk, float* __restrict__ dv,
+                                                                   float* __restrict__ partial, int64_t N, int NB) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 32);  // [NB][32 keys][2 heads] per wave
+  float* tb = reinterpret_cast<float*>(smem) + kWaves * 2 * NB * 32;  // [2][64] by clamped code
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTbD32);
+
+  const int npad32 = static_cast<int>(ops.npad / 32);
+  const int nkb = (npad32 + kWaves - 1) / kWaves;
+  int kb, hpair;
+  xcd_map(blockIdx.x, nkb, kb, hpair);
+  if (kb < 0) return;
+  const int c = lane & 31, hp = lane >> 5;
+  const int h0 = 2 * hpair;
+  const int64_t jw = static_cast<int64_t>(kb) * (32 * kWaves) + 32 * w;
+  const int64_t j = jw + c;
+  const bool wave_live = jw < ops.npad;
+  const int64_t jj = wave_live ? j : 0;
+  const int64_t npad = ops.npad;
+  const float sqd = sqrtf(static_cast<float>(kD));
+  const float sc2 = kLog2e / sqd;
+
+  for (int x = tid; x < 128; x += kThreads) {
+    const int hl = x >> 6, b = x & 63;
+    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  }
+  for (int x = lane; x < 2 * NB * 32; x += 64) bins[x] = 0.f;
+  s16x8 kop[2][2], vop[2][2];
+#pragma unroll
+  for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) {
+      kop[hl][ci] = load_h8(ops.kd + (jj * kH + h0 + hl) * kD + 16 * ci + 8 * hp);
+      vop[hl][ci] = load_h8(ops.vd + (jj * kH + h0 + hl) * kD + 16 * ci + 8 * hp);
+    }
+  const uint16_t one = 0x3C00u, ninf = 0xFC00u;
+  const s16x8 kaug = aug_chunk(pack2(one, one), j < N ? 0 : ninf, hp);
+  const s16x8 vaug = aug_chunk(pack2(one, one), 0, hp);
+  f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
+  const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
+  float2* mybins = reinterpret_cast<float2*>(bins) + c;
+  const uint8_t* crow = spd_t + (j < N ? j : N - 1) * N;
+  const int64_t cc = 16 * hp;
+  const int qr = node_of_row(c);
+
+  StageSetD32<2, 2> set;
+  set.rows[0] = ops.qd;
+  set.rows[1] = ops.od;
+  set.trs[0] = ops.qt;
+  set.trs[1] = ops.ot;
+  set.h0 = h0;
+  set.npad = npad;
+  const int64_t ntiles = npad / 32, nfull = N / 32;
+  s16x8 sr[StageSetD32<2, 2>::kPer];
+  set.load(sr, 0, tid);
+  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
+  uint32_t lw0 = ops.lq[static_cast<int64_t>(h0) * npad + qr], lw1 = ops.lq[static_cast<int64_t>(h0 + 1) * npad + qr];
+  uint32_t dw0 = ops.dl[static_cast<int64_t>(h0) * npad + qr], dw1 = ops.dl[static_cast<int64_t>(h0 + 1) * npad + qr];
+  wait_vm0();
+
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t i0 = t * 32;
+    set.store(stage, sr, tid);
+    __syncthreads();
+    u32x4 cwn = cw;
+    uint32_t lwn0 = lw0, lwn1 = lw1, dwn0 = dw0, dwn1 = dw1;
+    if (t + 1 < ntiles) {
+      set.load(sr, i0 + 32, tid);
+      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(crow, i0 + 32 + cc, N)
+                            : codes_at<true, kAligned>(crow, i0 + 32 + cc, N);
+      const int64_t qn = i0 + 32 + qr;
+      lwn0 = ops.lq[static_cast<int64_t>(h0) * npad + qn];
+      lwn1 = ops.lq[static_cast<int64_t>(h0 + 1) * npad + qn];
+      dwn0 = ops.dl[static_cast<int64_t>(h0) * npad + qn];
+      dwn1 = ops.dl[static_cast<int64_t>(h0 + 1) * npad + qn];
+    }
+    if (wave_live) {
+      const uint16_t* q_t = stage;
+      const uint16_t* o_t = stage + kRowTile;
+      const uint16_t* qt_t = stage + 2 * kRowTile;
+      const uint16_t* ot_t = qt_t + kTrTile;
+      f32x16 s0, s1;
+      uint32_t code[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        code[e] = min(code_byte(cw, e), nbm1);
+        s0[e] = tb[code[e]];
+        s1[e] = tb[64 + code[e]];
+      }
+      f32x16 p0 = {}, p1 = {};
+#pragma unroll
+      for (int ci = 0; ci < 2; ++ci) {
+        s0 = mfma_h16(row_op(q_t, c, 0, ci, hp), kop[0][ci], s0);
+        s1 = mfma_h16(row_op(q_t, c, 1, ci, hp), kop[1][ci], s1);
+        p0 = mfma_h16(row_op(o_t, c, 0, ci, hp), vop[0][ci], p0);
+        p1 = mfma_h16(row_op(o_t, c, 1, ci, hp), vop[1][ci], p1);
+      }
+      s0 = mfma_h16(aug_chunk(lw0, one, hp), kaug, s0);
+      s1 = mfma_h16(aug_chunk(lw1, one, hp), kaug, s1);
+      p0 = mfma_h16(aug_chunk(dw0, 0, hp), vaug, p0);
+      p1 = mfma_h16(aug_chunk(dw1, 0, hp), vaug, p1);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pa = __builtin_amdgcn_exp2f(s0[e] * sc2);
+        const float pb = __builtin_amdgcn_exp2f(s1[e] * sc2);
+        s0[e] = pa;
+        s1[e] = pb;
+        p0[e] *= pa;
+        p1[e] *= pb;
+      }
+      // lane half 0 first, then half 1: the two halves hold the same 32 keys
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (hp == half) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float2 bin = mybins[code[e] * 32];
+            bin.x += p0[e];
+            bin.y += p1[e];
+            mybins[code[e] * 32] = bin;
+          }
+        }
+      }
+#pragma unroll
+      for (int k1 = 0; k1 < 2; ++k1) {
+        const int g = 2 * hp + k1;
+        dv0 = mfma_h16(tr_op(ot_t, 0, c, g), pack_f16x8(s0, 8 * k1), dv0);
+        dv1 = mfma_h16(tr_op(ot_t, 1, c, g), pack_f16x8(s1, 8 * k1), dv1);
+        dk0 = mfma_h16(tr_op(qt_t, 0, c, g), pack_f16x8(p0, 8 * k1), dk0);
+        dk1 = mfma_h16(tr_op(qt_t, 1, c, g), pack_f16x8(p1, 8 * k1), dk1);
+      }
+    }
+    cw = cwn;
+    lw0 = lwn0;
+    lw1 = lwn1;
+    dw0 = dwn0;
+    dw1 = dwn1;
+    __syncthreads();
+  }
+  if (wave_live && j < N) {
+    const float rs = 1.f / sqd;
+    float* kp0 = dk + j * kHD + h0 * kD + 4 * hp;
+    float* vp0 = dv + j * kHD + h0 * kD + 4 * hp;
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      *reinterpret_cast<float4*>(kp0 + 8 * jq) =
+          make_float4(dk0[4 * jq] * rs, dk0[4 * jq + 1] * rs, dk0[4 * jq + 2] * rs, dk0[4 * jq + 3] * rs);
+      *reinterpret_cast<float4*>(kp0 + kD + 8 * jq) =
+          make_float4(dk1[4 * jq] * rs, dk1[4 * jq + 1] * rs, dk1[4 * jq + 2] * rs, dk1[4 * jq + 3] * rs);
+      *reinterpret_cast<float4*>(vp0 + 8 * jq) = make_float4(dv0[4 * jq], dv0[4 * jq + 1], dv0[4 * jq + 2], dv0[4 * jq + 3]);
+      *reinterpret_cast<float4*>(vp0 + kD + 8 * jq) =
+          make_float4(dv1[4 * jq], dv1[4 * jq + 1], dv1[4 * jq + 2], dv1[4 * jq + 3]);
+    }
+  }
+  // per-wave bins -> one partial row per 32-key block and head (a wave past the last key
+  // block writes its zero bins too, so every partial row is defined)
+  for (int x = lane; x < 2 * NB; x += 64) {
+    const int hl = x / NB, b = x - hl * NB;
+    const float* srcb = bins + b * 64 + hl;
+    float sum = 0.f;
+    for (int l = 0; l < 32; ++l) sum += srcb[2 * l];
+    partial[((jw / 32) * kH + h0 + hl) * NB + b] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Backward, query-outer: a wave owns 32 queries (lane c keeps query c) and a head
+// pair; the 4 waves share each staged key tile (k and v rows, k^T), double-buffered.
+// S^T and dP^T - delta come from 3 MFMAs each (rows = keys, columns = queries);
+// dQ^T += K^T dS^T per key tile.
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t* __restrict__ spd,
+                                                                  const float* __restrict__ table, OpsD32 ops,
+                                                                  float* __restrict__ dq, int64_t N, int NB) {
+  using Set = StageSetD32<2, 1>;
+  __shared__ float tb[2 * 256];
+  __shared__ __align__(16) uint16_t stage[2 * Set::kHalves];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int npad32 = static_cast<int>(ops.npad / 32);
+  const int nqb = (npad32 + kWaves - 1) / kWaves;
+  int qb, hpair;
+  xcd_map(blockIdx.x, nqb, qb, hpair);
+  if (qb < 0) return;
+  const int c = lane & 31, hp = lane >> 5;
+  const int h0 = 2 * hpair;
+  const int64_t iw = static_cast<int64_t>(qb) * (32 * kWaves) + 32 * w;
+  const int64_t i = iw + c;
+  const bool wave_live = iw < ops.npad;
+  const int64_t ii = wave_live ? i : 0;
+  const bool qvalid = i < N;
+  const int64_t npad = ops.npad;
+  const float sqd = sqrtf(static_cast<float>(kD));
+  const float sc2 = kLog2e / sqd;
+
+  for (int x = tid; x < 512; x += kThreads) {
+    const int hl = x >> 8, b = x & 255;
+    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  }
+  s16x8 qop[2][2], oop[2][2], qaug[2], oaug[2];
+  const uint16_t one = 0x3C00u, ninf = 0xFC00u;
+#pragma unroll
+  for (int hl = 0; hl < 2; ++hl) {
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) {
+      qop[hl][ci] = load_h8(ops.qd + (ii * kH + h0 + hl) * kD + 16 * ci + 8 * hp);
+      oop[hl][ci] = load_h8(ops.od + (ii * kH + h0 + hl) * kD + 16 * ci + 8 * hp);
+    }
+    qaug[hl] = aug_chunk(ops.lq[static_cast<int64_t>(h0 + hl) * npad + ii], one, hp);
+    oaug[hl] = aug_chunk(ops.dl[static_cast<int64_t>(h0 + hl) * npad + ii], 0, hp);
+  }
+  const s16x8 vaug = aug_chunk(pack2(one, one), 0, hp);
+  f32x16 dq0 = {}, dq1 = {};
+  const uint8_t* srow = spd + (qvalid ? i : N - 1) * N;
+  const int64_t cc = 16 * hp;
+  const int kr = node_of_row(c);
+
+  Set set;
+  set.rows[0] = ops.kd;
+  set.rows[1] = ops.vd;
+  set.trs[0] = ops.kt;
+  set.h0 = h0;
+  set.npad = npad;
+  const int64_t ntiles = npad / 32, nfull = N / 32;
+  s16x8 sr[Set::kPer];
+  set.load(sr, 0, tid);
+  set.store(stage, sr, tid);
+  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(srow, cc, N) : codes_at<true, kAligned>(srow, cc, N);
+  wait_vm0();
+  __syncthreads();
+
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t j0 = t * 32;
+    const uint16_t* cur = stage + (t & 1) * Set::kHalves;
+    u32x4 cwn = cw;
+    if (t + 1 < ntiles) {
+      set.load(sr, j0 + 32, tid);
+      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(srow, j0 + 32 + cc, N)
+                            : codes_at<true, kAligned>(srow, j0 + 32 + cc, N);
+    }
+    if (wave_live) {
+      const uint16_t* k_t = cur;
+      const uint16_t* v_t = cur + kRowTile;
+      const uint16_t* kt_t = cur + 2 * kRowTile;
+      f32x16 s0, s1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t cb = code_byte(cw, e);
+        s0[e] = tb[cb];
+        s1[e] = tb[256 + cb];
+      }
+      f32x16 p0 = {}, p1 = {};
+#pragma unroll
+      for (int ci = 0; ci < 2; ++ci) {
+        s0 = mfma_h16(row_op(k_t, c, 0, ci, hp), qop[0][ci], s0);
+        s1 = mfma_h16(row_op(k_t, c, 1, ci, hp), qop[1][ci], s1);
+        p0 = mfma_h16(row_op(v_t, c, 0, ci, hp), oop[0][ci], p0);
+        p1 = mfma_h16(row_op(v_t, c, 1, ci, hp), oop[1][ci], p1);
+      }
+      const s16x8 kaug = aug_chunk(pack2(one, one), j0 + kr < N ? 0 : ninf, hp);
+      s0 = mfma_h16(kaug, qaug[0], s0);
+      s1 = mfma_h16(kaug, qaug[1], s1);
+      p0 = mfma_h16(vaug, oaug[0], p0);
+      p1 = mfma_h16(vaug, oaug[1], p1);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p0[e] *= __builtin_amdgcn_exp2f(s0[e] * sc2);
+        p1[e] *= __builtin_amdgcn_exp2f(s1[e] * sc2);
+      }
+#pragma unroll
+      for (int k1 = 0; k1 < 2; ++k1) {
+        const int g = 2 * hp + k1;
+        dq0 = mfma_h16(tr_op(kt_t, 0, c, g), pack_f16x8(p0, 8 * k1), dq0);
+        dq1 = mfma_h16(tr_op(kt_t, 1, c, g), pack_f16x8(p1, 8 * k1), dq1);
+      }
+    }
+    if (t + 1 < ntiles) set.store(stage + ((t + 1) & 1) * Set::kHalves, sr, tid);
+    cw = cwn;
+    __syncthreads();
+  }
+  if (wave_live && qvalid) {
+    const float rs = 1.f / sqd;
+    float* qp0 = dq + i * kHD + h0 * kD + 4 * hp;
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      *reinterpret_cast<float4*>(qp0 + 8 * jq) =
+          make_float4(dq0[4 * jq] * rs, dq0[4 * jq + 1] * rs, dq0[4 * jq + 2] * rs, dq0[4 * jq + 3] * rs);
+      *reinterpret_cast<float4*>(qp0 + kD + 8 * jq) =
+          make_float4(dq1[4 * jq] * rs, dq1[4 * jq + 1] * rs, dq1[4 * jq + 2] * rs, dq1[4 * jq + 3] * rs);
+    }
+  }
+}
+
+OpsD32 carve_ops_d32(void* base, int64_t N) {
+  OpsD32 o{};
+  o.npad = (N + 31) / 32 * 32;
+  const size_t node = static_cast<size_t>(o.npad) * kH * kD;  // halves per node-major or transposed array
+  uint16_t* p = static_cast<uint16_t*>(base);
+  o.qd = p;
+  o.kd = p + node;
+  o.vd = p + 2 * node;
+  o.od = p + 3 * node;
+  o.qt = p + 4 * node;
+  o.kt = p + 5 * node;
+  o.ot = p + 6 * node;
+  o.lq = reinterpret_cast<uint32_t*>(p + 7 * node);
+  o.dl = o.lq + static_cast<size_t>(o.npad) * kH;
+  return o;
+}
+
+size_t kv_d32_lds(int NB) { return 4ull * kWaves * 2 * NB * 32 + 4ull * kKvTbD32 + 2ull * StageSetD32<2, 2>::kHalves; }
+
+}  // namespace
+
+size_t mfma_d32_ops_bytes(int64_t N) {
+  const size_t npad = static_cast<size_t>((N + 31) / 32 * 32);
+  return npad * kH * kD * 2 * 7 + npad * kH * 4 * 2;
+}
+
+int64_t mfma_d32_kv_blocks(int64_t N) {
+  const int64_t nblk = ((N + 31) / 32 + kWaves - 1) / kWaves;
+  return nblk * kWaves;
+}
+
+hipError_t launch_fwd_mfma_d32(const FwdArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(xcd_grid(static_cast<int>((a.N + 32 * kWaves - 1) / (32 * kWaves)))));
+  trace_begin(kTraceFwd, s);
+  if (a.N % 16 == 0)
+    hipLaunchKernelGGL(fwd_mfma_d32_kernel<true>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table, a.out,
+                       a.lse, a.N, a.NB);
+  else
+    hipLaunchKernelGGL(fwd_mfma_d32_kernel<false>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table, a.out,
+                       a.lse, a.N, a.NB);
+  const hipError_t e = hipGetLastError();
+  trace_end(kTraceFwd, s);
+  return e;
+}
+
+hipError_t launch_bwd_mfma_d32(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
+  char* base = static_cast<char*>(a.workspace);
+  const OpsD32 ops = carve_ops_d32(base + w.ops_off, a.N);
+  float* partial = reinterpret_cast<float*>(base + w.partial_off);
+  const bool aligned = a.N % 16 == 0;
+  const int64_t prep_threads = ops.npad * kH;
+  trace_begin(kTraceBwdDelta, s);
+  hipLaunchKernelGGL(bwd_prep_mfma_d32_kernel, dim3(static_cast<unsigned>((prep_threads + 255) / 256)), dim3(256), 0,
+                     s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.out, static_cast<const uint16_t*>(a.dout), a.lse, ops, a.N);
+  hipError_t e = hipGetLastError();
+  trace_end(kTraceBwdDelta, s);
+  if (e != hipSuccess) return e;
+
+  const int nblk = static_cast<int>((ops.npad / 32 + kWaves - 1) / kWaves);
+  const dim3 grid(static_cast<unsigned>(xcd_grid(nblk)));
+  const size_t lds = kv_d32_lds(a.NB);
+  e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<true>, lds);
+  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<false>, lds);
+  if (e != hipSuccess) return e;
+  trace_begin(kTraceBwdKv, s);
+  if (aligned)
+    hipLaunchKernelGGL(bwd_kv_mfma_d32_kernel<true>, grid, dim3(kThreads), lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
+                       partial, a.N, a.NB);
+  else
+    hipLaunchKernelGGL(bwd_kv_mfma_d32_kernel<false>, grid, dim3(kThreads), lds, s, a.spd_t, a.table, ops, a.dk,
+                       a.dv, partial, a.N, a.NB);
+  e = hipGetLastError();
+  trace_end(kTraceBwdKv, s);
+  if (e != hipSuccess) return e;
+
+  trace_begin(kTraceBwdQ, s);
+  if (aligned)
+    hipLaunchKernelGGL(bwd_q_mfma_d32_kernel<true>, grid, dim3(kThreads), 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
+  else
+    hipLaunchKernelGGL(bwd_q_mfma_d32_kernel<false>, grid, dim3(kThreads), 0, s, a.spd, a.table, ops, a.dq, a.N,
+                       a.NB);
+  e = hipGetLastError();
+  trace_end(kTraceBwdQ, s);
+  if (e != hipSuccess) return e;
+  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, s);
+}
+
+}  // namespace gt

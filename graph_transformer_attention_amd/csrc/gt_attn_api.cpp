@@ -162,11 +162,13 @@ StackLayout stack_layout(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB,
 }
 
 hipError_t attn_fwd(const gt::FwdArgs& a, hipStream_t s) {
-  return gt::mfma_supported(a.H, a.D, a.dtype) ? gt::launch_fwd_mfma(a, s) : gt::launch_fwd_valu(a, s);
+  if (!gt::mfma_supported(a.H, a.D, a.dtype)) return gt::launch_fwd_valu(a, s);
+  return a.D == 32 ? gt::launch_fwd_mfma_d32(a, s) : gt::launch_fwd_mfma(a, s);
 }
 
 hipError_t attn_bwd(const gt::BwdArgs& a, const gt::BwdWorkspace& w, hipStream_t s) {
-  return gt::mfma_supported(a.H, a.D, a.dtype) ? gt::launch_bwd_mfma(a, w, s) : gt::launch_bwd_valu(a, w, s);
+  if (!gt::mfma_supported(a.H, a.D, a.dtype)) return gt::launch_bwd_valu(a, w, s);
+  return a.D == 32 ? gt::launch_bwd_mfma_d32(a, w, s) : gt::launch_bwd_mfma(a, w, s);
 }
 
 }  // namespace
@@ -194,10 +196,10 @@ BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const bool mfma = mfma_supported(H, D, dtype);
   const int64_t kb = valu_kv_block(H);
-  w.n_kv_blocks = mfma ? mfma_kv_blocks(N) : (N + kb - 1) / kb;
+  w.n_kv_blocks = mfma ? (D == 32 ? mfma_d32_kv_blocks(N) : mfma_kv_blocks(N)) : (N + kb - 1) / kb;
   w.delta_off = 0;
   w.ops_off = up(static_cast<size_t>(N) * H * sizeof(float));
-  w.partial_off = w.ops_off + (mfma ? up(mfma_ops_bytes(N)) : 0);
+  w.partial_off = w.ops_off + (mfma ? up(D == 32 ? mfma_d32_ops_bytes(N) : mfma_ops_bytes(N)) : 0);
   w.bytes = w.partial_off + up(static_cast<size_t>(w.n_kv_blocks) * H * NB * sizeof(float));
   return w;
 }

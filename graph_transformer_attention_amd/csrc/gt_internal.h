@@ -66,12 +66,18 @@ void trace_end(int kernel_id, hipStream_t s);
 BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype);
 
 hipError_t launch_fwd_valu(const FwdArgs& a, hipStream_t s);
+// matrix-core kernels exist for bf16, H = 8, D in {8, 32}
 bool mfma_supported(int H, int D, int dtype);
 int64_t mfma_npad(int64_t N);
 int64_t mfma_kv_blocks(int64_t N);
 size_t mfma_ops_bytes(int64_t N);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
+// head dimension 32 (attn_mfma_d32.hip)
+size_t mfma_d32_ops_bytes(int64_t N);
+int64_t mfma_d32_kv_blocks(int64_t N);
+hipError_t launch_fwd_mfma_d32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_mfma_d32(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 hipError_t launch_dtable_reduce(const float* partial, float* dtable, int64_t nblocks, int HNB, hipStream_t s);
 hipError_t launch_bwd_valu(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 int64_t valu_kv_block(int H);

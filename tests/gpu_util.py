@@ -3,7 +3,8 @@ against the float64 oracle at the stated tolerances.
 
 Tolerances, per output tensor T in {out, lse, dq, dk, dv, dtable}:
   float32 inputs:  max |T_gpu - T_ref| <= 1e-4
-  bfloat16 inputs: max |T_gpu - T_ref| / rms(T_ref) <= 2e-2   (float32 accumulation)
+  bfloat16 inputs: max |T_gpu - T_ref| / rms(T_ref) <= 2e-2   (float32 accumulation);
+                   a reference that is exactly zero is held to max |T_gpu| <= 1e-4
 """
 import numpy as np
 import torch
@@ -33,7 +34,9 @@ def err(got, ref, dtype, bound=None):
         return e, e <= (TOL_F32_ABS if bound is None else bound)
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     if rms == 0.0:
-        return e, e == 0.0
+        # an exactly zero reference (N = 1: dq = dk = 0) has no RMS to scale by; the
+        # float32 rounding of the GPU's arithmetic is held to the float32 bound instead
+        return e, e <= TOL_F32_ABS
     return e / rms, e / rms <= (TOL_BF16_REL if bound is None else bound)
 
 

@@ -63,6 +63,12 @@ def test_er256_f32_full():
     (64, 1, 8, 3, "f32", "empty"),
     (200, 16, 32, 12, "f32", "er"),
     (65, 64, 8, 63, "bf16", "er"),
+    # the matrix-core path for head dimension 32 (bf16, H = 8): one node, ragged tiles,
+    # a long path (distances past the clip), the widest table
+    (1, 8, 32, 20, "bf16", "er"),
+    (17, 8, 32, 20, "bf16", "er"),
+    (129, 8, 32, 30, "bf16", "path"),
+    (161, 8, 32, 63, "bf16", "er"),
 ])
 def test_small_cases(N, H, D, C, dtype, family):
     inp = small_case(N, H, D, C, dtype, seed=11, family=family)
@@ -115,11 +121,11 @@ def test_bad_arguments_raise_without_launch():
         gta.fwd(q, q, q, spd[:, :8], table)
 
 
-@pytest.mark.parametrize("dtype,N", [("bf16", 200), ("f32", 200), ("bf16", 93)])
-def test_asymmetric_codes_with_transpose(dtype, N):
+@pytest.mark.parametrize("dtype,N,D", [("bf16", 200, 8), ("f32", 200, 8), ("bf16", 93, 8), ("bf16", 93, 32)])
+def test_asymmetric_codes_with_transpose(dtype, N, D):
     """Codes of a directed relation (spd != spd^T): the backward reads the key-outer
     codes from spd_t, which the caller passes as the transpose."""
-    inp = small_case(N, 8, 8, 10, dtype, seed=5)
+    inp = small_case(N, 8, D, 10, dtype, seed=5)
     rng = np.random.default_rng(9)
     codes = rng.integers(0, 11, size=(N, N)).astype(np.uint8)
     assert not np.array_equal(codes, codes.T)
