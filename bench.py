@@ -9,7 +9,8 @@ like loading the graph); every input is resident in device memory when the
 timed region starts.
 
 Prints ONE JSON line. Throughput is giga score-pairs per second,
-H*N^2 / (fwd+bwd seconds) / 1e9.
+L*H*N^2 / (fwd+bwd seconds) / 1e9 (L = 1 but for the stacked workload, whose step
+is the forward and backward of all its layers, projections included).
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload ba32768-bf16]
 """
@@ -74,20 +75,32 @@ def work_model(name: str, N: int, H: int, D: int, s_bytes: int):
         return E * (6 * D + 4), E, N * N + 4 * node + 2 * N * H * 4 + f32node
     if name == "bwd_delta":
         return N * H * 2 * D, 0, 4 * node + f32node + N * H * 4
+    hid = H * D
+    if name == "qkv_fwd":      # X [N,hid] times three [hid,hid] weights
+        return 2 * N * hid * 3 * hid, 0, node + 3 * hid * hid * s_bytes + 3 * node
+    if name in ("qkv_bwd_dx", "qkv_bwd_dw"):
+        return 2 * N * hid * 3 * hid, 0, 3 * f32node + 3 * hid * hid * s_bytes + f32node
+    if name == "store":        # float32 -> storage type
+        return 0, 0, f32node + node
     return 0, 0, 0
 
 
 def cpu_baseline(inp, n_rows: int, cores: int):
-    """Time the float64 oracle's forward+backward on a bounded row sample."""
+    """Time the float64 oracle's forward+backward on a bounded row sample (for a stacked
+    workload: the first layer's attention, its Q/K/V from the oracle's projection)."""
     import oracle
     w = inp.workload
     rows = np.sort(np.random.default_rng(12345).choice(w.N, size=min(n_rows, w.N), replace=False))
     t0 = time.perf_counter()
     codes = oracle.bfs_codes_parallel(inp.indptr, inp.indices, w.C, rows, workers=cores)
     t_bfs = time.perf_counter() - t0
+    if w.layers > 1:
+        q, k, v = (t.reshape(w.N, w.H, w.D) for t in oracle.qkv_projection(inp.x0.value, inp.w_qkv.value[0]))
+        table, dout = inp.table.value[0], inp.dout.value.reshape(w.N, w.H, w.D)
+    else:
+        q, k, v, table, dout = inp.q.value, inp.k.value, inp.v.value, inp.table.value, inp.dout.value
     t0 = time.perf_counter()
-    oracle.full_backward(inp.q.value[rows], inp.k.value, inp.v.value, codes, inp.table.value,
-                         inp.dout.value[rows], block=16, workers=cores)
+    oracle.full_backward(q[rows], k, v, codes, table, dout[rows], block=16, workers=cores)
     t_attn = time.perf_counter() - t0
     pairs = len(rows) * w.H * w.N
     return {
@@ -126,8 +139,6 @@ def main():
 
     byname = {w.name: w for w in WORKLOADS.values()}
     w = byname[args.workload]
-    if w.layers != 1:
-        raise SystemExit(f"{w.name} is a stacked workload; bench.py times single-layer workloads")
     print(f"[bench] {w.describe()}", file=sys.stderr, flush=True)
     inp = make_inputs(w.number)
     N, H, D, C, NB = w.N, w.H, w.D, w.C, w.NB
@@ -144,20 +155,37 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(st.raw)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    q, k, v, do, table = put(inp.q), put(inp.k), put(inp.v), put(inp.dout), put(inp.table)
     spd = torch.from_numpy(spd_host).to(dev)
     hist = np.bincount(spd_host.ravel(), minlength=NB)
     del spd_host
-    out = torch.empty((N, H, D), dtype=torch.float32, device=dev)
-    lse = torch.empty((N, H), dtype=torch.float32, device=dev)
-    dq, dk, dv = (torch.empty((N, H, D), dtype=torch.float32, device=dev) for _ in range(3))
-    dtab = torch.empty((H, NB), dtype=torch.float32, device=dev)
     dt = gta.GT_BF16 if w.dtype == "bf16" else gta.GT_F32
-    ws = torch.empty(gta.bwd_workspace_bytes(N, H, D, NB, dt), dtype=torch.uint8, device=dev)
+    L = w.layers
+    if L == 1:
+        q, k, v, do, table = put(inp.q), put(inp.k), put(inp.v), put(inp.dout), put(inp.table)
+        out = torch.empty((N, H, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((N, H), dtype=torch.float32, device=dev)
+        dq, dk, dv = (torch.empty((N, H, D), dtype=torch.float32, device=dev) for _ in range(3))
+        dtab = torch.empty((H, NB), dtype=torch.float32, device=dev)
+        ws = torch.empty(gta.bwd_workspace_bytes(N, H, D, NB, dt), dtype=torch.uint8, device=dev)
 
-    def step():
-        gta.fwd(q, k, v, spd, table, out=out, lse=lse)
-        gta.bwd(q, k, v, spd, table, out, lse, do, dq=dq, dk=dk, dv=dv, dtable=dtab, workspace=ws)
+        def step():
+            gta.fwd(q, k, v, spd, table, out=out, lse=lse)
+            gta.bwd(q, k, v, spd, table, out, lse, do, dq=dq, dk=dk, dv=dv, dtable=dtab, workspace=ws)
+
+        def outputs():
+            return [out, dq, dk, dv], dtab
+    else:
+        # the stacked model: L layers of projections + attention, forward and backward
+        x0, wq, tables, do = put(inp.x0), put(inp.w_qkv), put(inp.table), put(inp.dout)
+        ws = torch.empty(gta.stack_workspace_bytes(N, L, H, D, NB, dt), dtype=torch.uint8, device=dev)
+        res = {}
+
+        def step():
+            res["r"] = gta.stack_fwd_bwd(x0, wq, tables, spd, do, H, workspace=ws)
+
+        def outputs():
+            x_last, dx0, dw, dtl = res["r"]
+            return [x_last.float(), dx0, dw], dtl.reshape(L * H, NB)
 
     for _ in range(args.warmup):
         step()
@@ -189,11 +217,11 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     # Invariants that hold at any size (cheap checks that the timed outputs are sane).
-    dtab_h = dtab.double().cpu().numpy()
+    tensors, dtab_t = outputs()
+    dtab_h = dtab_t.double().cpu().numpy()
     absent = hist[:NB] == 0
     checks = {
-        "finite": bool(torch.isfinite(out.float()).all() and torch.isfinite(dq).all()
-                       and torch.isfinite(dk).all() and torch.isfinite(dv).all()),
+        "finite": bool(all(torch.isfinite(t).all() for t in tensors)),
         "dtable_row_sum_max_abs": float(np.abs(dtab_h.sum(axis=1)).max()),
         "dtable_absent_buckets_exact_zero": bool(np.all(dtab_h[:, absent] == 0.0)),
     }
@@ -219,7 +247,7 @@ def main():
                 "ops_per_launch": ex, "algorithmic_bytes_per_launch": by,
                 "avg_launch_ms": round(dom_s * 1e3, 4)}
 
-    pairs = H * N * N
+    pairs = L * H * N * N
     fwd_ms = kern.get("fwd", {}).get("avg_ms", 0.0)
     bwd_ms = sum(kern[n]["avg_ms"] for n in kern if n.startswith("bwd"))
     passes = 3  # the code matrix is read by the forward, key-outer and query-outer kernels
@@ -234,14 +262,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if (w.dtype == "bf16" and H == 8 and D == 8) else "f32",
+        "dtype": "bf16" if (w.dtype == "bf16" and H == 8 and D in (8, 32)) else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "graph": f"{w.family} {w.graph_args}", "N": N, "H": H,
-                   "D": D, "NB": NB, "storage": w.dtype, "layers": 1},
+                   "D": D, "NB": NB, "storage": w.dtype, "layers": L},
         "ms_fwd": fwd_ms,
         "ms_bwd": round(bwd_ms, 4),
-        "spd_stream_gbs": round(passes * N * N / (ms_step * 1e-3) / 1e9, 1),
-        "spd_stream_frac_of_hbm_peak": round(passes * N * N / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "spd_stream_gbs": round(L * passes * N * N / (ms_step * 1e-3) / 1e9, 1),
+        "spd_stream_frac_of_hbm_peak": round(L * passes * N * N / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "exp_per_s": round(3 * pairs / (ms_step * 1e-3), 1),
         "kernels": kern,
         "roofline": roofline,
