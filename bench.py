@@ -12,7 +12,14 @@ Prints ONE JSON line. Throughput is giga score-pairs per second,
 L*H*N^2 / (fwd+bwd seconds) / 1e9 (L = 1 but for the stacked workload, whose step
 is the forward and backward of all its layers, projections included).
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload ba32768-bf16]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload ba32768-bf16] [--cp P]
+
+With --cp P the step is the key-block schedule of graph-aware context parallelism
+(MegaGraph pages, Fig. 4) run on this one GPU: P virtual ranks each hold N/P query
+rows; every rank processes every one of the P key blocks (with its slice of code
+columns) in ring order, merging the partial forward results by log-sum-exp, then
+the backward of every (rank, block) pair against the merged statistics. The step
+covers all P*P block steps, i.e. the same N^2 pairs as the unsplit path.
 """
 from __future__ import annotations
 
@@ -82,6 +89,8 @@ def work_model(name: str, N: int, H: int, D: int, s_bytes: int):
         return 2 * N * hid * 3 * hid, 0, 3 * f32node + 3 * hid * hid * s_bytes + f32node
     if name == "store":        # float32 -> storage type
         return 0, 0, f32node + node
+    if name == "merge":        # two partial (out, lse) in, one out
+        return 3 * N * H * D, 2 * N * H, 3 * f32node + 3 * N * H * 4
     return 0, 0, 0
 
 
@@ -122,6 +131,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ba32768-bf16")
+    ap.add_argument("--cp", type=int, default=1,
+                    help="time the key-block (context-parallel) schedule with P virtual ranks")
     ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -160,7 +171,45 @@ def main():
     del spd_host
     dt = gta.GT_BF16 if w.dtype == "bf16" else gta.GT_F32
     L = w.layers
-    if L == 1:
+    P = args.cp
+    if P > 1 and (L != 1 or N % (32 * P) != 0):
+        print(f"bench.py: --cp {P} needs a single-layer workload with N a multiple of {32 * P}", file=sys.stderr)
+        sys.exit(2)
+    if P > 1:
+        q, k, v, do, table = put(inp.q), put(inp.k), put(inp.v), put(inp.dout), put(inp.table)
+        spd_t = spd  # undirected graphs: the code matrix is its own transpose
+        Nb = N // P
+        cuts = [(i * Nb, (i + 1) * Nb) for i in range(P)]
+        out = torch.empty((N, H, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((N, H), dtype=torch.float32, device=dev)
+        ob = torch.empty((Nb, H, D), dtype=torch.float32, device=dev)
+        lb = torch.empty((Nb, H), dtype=torch.float32, device=dev)
+        dq, dk, dv = (torch.empty((N, H, D), dtype=torch.float32, device=dev) for _ in range(3))
+        dtab = torch.empty((H, NB), dtype=torch.float32, device=dev)
+        ws = torch.empty(gta.bwd_block_workspace_bytes(Nb, Nb, H, D, NB, dt), dtype=torch.uint8, device=dev)
+
+        def step():
+            for r, (r0, r1) in enumerate(cuts):
+                for t in range(P):
+                    c0, c1 = cuts[(r - t) % P]
+                    if t == 0:
+                        gta.fwd_block(q[r0:r1], k[c0:c1], v[c0:c1], spd[r0:r1, c0:c1], table,
+                                      out=out[r0:r1], lse=lse[r0:r1])
+                    else:
+                        gta.fwd_block(q[r0:r1], k[c0:c1], v[c0:c1], spd[r0:r1, c0:c1], table, out=ob, lse=lb)
+                        gta.merge(out[r0:r1], lse[r0:r1], ob, lb, out[r0:r1], lse[r0:r1])
+            for r, (r0, r1) in enumerate(cuts):
+                for t in range(P):
+                    c0, c1 = cuts[(r - t) % P]
+                    acc = ((gta.ACC_DQ if t > 0 else 0) | (gta.ACC_DKV if r > 0 else 0)
+                           | (gta.ACC_DTABLE if (r, t) != (0, 0) else 0))
+                    gta.bwd_block(q[r0:r1], k[c0:c1], v[c0:c1], spd[r0:r1, c0:c1], spd_t[c0:c1, r0:r1], table,
+                                  out[r0:r1], lse[r0:r1], do[r0:r1], dq[r0:r1], dk[c0:c1], dv[c0:c1], dtab,
+                                  accumulate=acc, workspace=ws)
+
+        def outputs():
+            return [out, dq, dk, dv], dtab
+    elif L == 1:
         q, k, v, do, table = put(inp.q), put(inp.k), put(inp.v), put(inp.dout), put(inp.table)
         out = torch.empty((N, H, D), dtype=torch.float32, device=dev)
         lse = torch.empty((N, H), dtype=torch.float32, device=dev)
@@ -230,26 +279,27 @@ def main():
     kern = {}
     for name, (cnt, tot) in per_kernel.items():
         avg = tot / cnt
-        fl, ex, by = work_model(name, N, H, D, s_bytes)
+        fl, ex, by = work_model(name, N // P, H, D, s_bytes)
         kern[name] = {"launches": cnt, "avg_ms": round(avg, 4),
                       "tflops": round(fl / (avg * 1e-3) / 1e12, 2),
                       "gexp_per_s": round(ex / (avg * 1e-3) / 1e9, 1),
                       "gbs": round(by / (avg * 1e-3) / 1e9, 1)}
     dom = max(per_kernel, key=lambda n: per_kernel[n][1])
-    fl, ex, by = work_model(dom, N, H, D, s_bytes)
+    fl, ex, by = work_model(dom, N // P, H, D, s_bytes)
     dom_s = per_kernel[dom][1] / per_kernel[dom][0] * 1e-3
     achieved = ex / dom_s / 1e12
     roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved, 4),
                 "peak": round(exp_peak, 3), "unit": "TFLOP/s",
                 "frac": round(achieved / exp_peak, 4),
-                "traffic": recorded_traffic(dom, w.name),
+                "traffic": recorded_traffic(dom, w.name) if P == 1 else None,
                 "op": "exp2 (one per score entry and pass; peak = measured v_exp_f32 rate)",
                 "ops_per_launch": ex, "algorithmic_bytes_per_launch": by,
                 "avg_launch_ms": round(dom_s * 1e3, 4)}
 
     pairs = L * H * N * N
-    fwd_ms = kern.get("fwd", {}).get("avg_ms", 0.0)
-    bwd_ms = sum(kern[n]["avg_ms"] for n in kern if n.startswith("bwd"))
+    # per step: each kernel's average launch time times its launches per step
+    fwd_ms = sum(kern[n]["avg_ms"] * kern[n]["launches"] / args.steps for n in ("fwd", "merge") if n in kern)
+    bwd_ms = sum(kern[n]["avg_ms"] * kern[n]["launches"] / args.steps for n in kern if n.startswith("bwd"))
     passes = 3  # the code matrix is read by the forward, key-outer and query-outer kernels
     res = {
         "metric": METRIC,
@@ -265,8 +315,9 @@ def main():
         "dtype": "bf16" if (w.dtype == "bf16" and H == 8 and D in (8, 32)) else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "graph": f"{w.family} {w.graph_args}", "N": N, "H": H,
-                   "D": D, "NB": NB, "storage": w.dtype, "layers": L},
-        "ms_fwd": fwd_ms,
+                   "D": D, "NB": NB, "storage": w.dtype, "layers": L,
+                   **({"cp_ranks": P, "block": f"{N // P}x{N // P}"} if P > 1 else {})},
+        "ms_fwd": round(fwd_ms, 4),
         "ms_bwd": round(bwd_ms, 4),
         "spd_stream_gbs": round(L * passes * N * N / (ms_step * 1e-3) / 1e9, 1),
         "spd_stream_frac_of_hbm_peak": round(L * passes * N * N / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -11,6 +11,10 @@ raises.
     q, k, v = qkv_fwd(x, w)                         # one layer's projections
     dx, dw = qkv_bwd(x, w, dq, dk, dv)
     x_last, dx0, dw, dtable = stack_fwd_bwd(x0, w, tables, spd, dout, H)
+    out_b, lse_b = fwd_block(q_rows, k_blk, v_blk, spd[rows, cols], table)   # one key block
+    merge(out, lse, out_b, lse_b, out, lse)                                  # running merge
+    bwd_block(q_rows, k_blk, v_blk, spd[rows, cols], spd_t[cols, rows], table, out, lse,
+              dout_rows, dq, dk, dv, dtable, accumulate=True)
 """
 from __future__ import annotations
 
@@ -22,6 +26,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgt_attn.so")
 GT_F32, GT_BF16 = 0, 1
 GT_OK, GT_EINVAL, GT_EUNSUPPORTED, GT_EHIP = 0, -1, -2, -3
+ACC_DQ, ACC_DKV, ACC_DTABLE, ACC_ALL = 1, 2, 4, 7   # gt_attn_bwd_block accumulate bits
 
 _lib = None
 
@@ -72,6 +77,15 @@ def lib() -> ctypes.CDLL:
         L.gt_stack_workspace_bytes.argtypes = [I64, I32, I32, I32, I32, I32]
         L.gt_stack_workspace_bytes.restype = SZ
         L.gt_stack_fwd_bwd.argtypes = [P] * 11 + [SZ, I64, I32, I32, I32, I32, I32, P]
+        L.gt_attn_fwd_block.argtypes = [P, P, P, P, I64, P, P, P, I64, I64, I32, I32, I32, I32, P]
+        L.gt_attn_fwd_block.restype = ctypes.c_int
+        L.gt_attn_merge.argtypes = [P] * 6 + [I64, I32, I32, P]
+        L.gt_attn_merge.restype = ctypes.c_int
+        L.gt_attn_bwd_block_workspace_bytes.argtypes = [I64, I64, I32, I32, I32, I32]
+        L.gt_attn_bwd_block_workspace_bytes.restype = SZ
+        L.gt_attn_bwd_block.argtypes = [P, P, P, P, I64, P, I64] + [P] * 9 + [SZ, I64, I64, I32, I32, I32, I32,
+                                                                               I32, P]
+        L.gt_attn_bwd_block.restype = ctypes.c_int
         L.gt_stack_fwd_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -164,6 +178,104 @@ def bwd(q, k, v, spd, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=N
             _dev(workspace, "workspace")]
     _check("gt_attn_bwd", lib().gt_attn_bwd(*args, workspace.numel() * workspace.element_size(),
                                             N, H, D, NB, dt, _stream(stream)))
+    return dq, dk, dv, dtable
+
+
+def _codes(t, name, rows, cols):
+    """A 2-D uint8 GPU view [rows, cols] whose elements are contiguous along a row; its
+    rows may lie further apart (a column slice of a larger code matrix). Returns the
+    pointer and the row stride in elements."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be a uint8 GPU tensor")
+    if tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(rows, cols)}")
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be contiguous along its rows")
+    ld = t.stride(0) if rows > 1 else cols
+    if ld < cols:
+        raise ValueError(f"{name}: row stride {ld} < {cols}")
+    return ctypes.c_void_p(t.data_ptr()), ld
+
+
+def fwd_block(q, k, v, spd, table, out=None, lse=None, stream=None):
+    """Attention of Nq query rows restricted to one block of Nk keys.
+
+    q [Nq,H,D], k, v [Nk,H,D] (float32 or bfloat16); spd [Nq,Nk] uint8, usually a
+    slice spd_all[r0:r1, c0:c1] (rows may be strided); table [H,NB] float32.
+    Returns the block's (out [Nq,H,D], lse [Nq,H]) float32, to be merged with merge()."""
+    import torch
+    Nq, H, D = q.shape
+    Nk = k.shape[0]
+    NB = table.shape[1]
+    dt = _dtype_code(q)
+    f32 = torch.float32
+    out = torch.empty((Nq, H, D), dtype=f32, device=q.device) if out is None else out
+    lse = torch.empty((Nq, H), dtype=f32, device=q.device) if lse is None else lse
+    sp, ld = _codes(spd, "spd", Nq, Nk)
+    args = [_dev(q, "q", q.dtype, (Nq, H, D)), _dev(k, "k", q.dtype, (Nk, H, D)),
+            _dev(v, "v", q.dtype, (Nk, H, D)), sp, ld, _dev(table, "table", f32, (H, NB)),
+            _dev(out, "out", f32, (Nq, H, D)), _dev(lse, "lse", f32, (Nq, H))]
+    _check("gt_attn_fwd_block", lib().gt_attn_fwd_block(*args, Nq, Nk, H, D, NB, dt, _stream(stream)))
+    return out, lse
+
+
+def merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, stream=None):
+    """Merge two partial results over disjoint key sets by their lse. out/lse may be
+    out_a/lse_a (running merge). Returns (out, lse)."""
+    import torch
+    Nq, H, D = out_a.shape
+    f32 = torch.float32
+    out = torch.empty_like(out_a) if out is None else out
+    lse = torch.empty_like(lse_a) if lse is None else lse
+    args = [_dev(out_a, "out_a", f32, (Nq, H, D)), _dev(lse_a, "lse_a", f32, (Nq, H)),
+            _dev(out_b, "out_b", f32, (Nq, H, D)), _dev(lse_b, "lse_b", f32, (Nq, H)),
+            _dev(out, "out", f32, (Nq, H, D)), _dev(lse, "lse", f32, (Nq, H))]
+    _check("gt_attn_merge", lib().gt_attn_merge(*args, Nq, H, D, _stream(stream)))
+    return out, lse
+
+
+def bwd_block_workspace_bytes(Nq: int, Nk: int, H: int, D: int, NB: int, dtype: int) -> int:
+    return int(lib().gt_attn_bwd_block_workspace_bytes(Nq, Nk, H, D, NB, dtype))
+
+
+def bwd_block(q, k, v, spd, spd_t, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=None,
+              accumulate=False, workspace=None, stream=None):
+    """Backward of one key block given the MERGED out/lse over all keys.
+
+    spd [Nq,Nk] and spd_t [Nk,Nq] are the block's code slices (spd_t rows = keys).
+    Returns dq [Nq,H,D] (this block's share), dk, dv [Nk,H,D], dtable [H,NB].
+    accumulate: True adds all four into the given tensors, False overwrites them, or
+    an int of ACC_DQ | ACC_DKV | ACC_DTABLE bits picks per output."""
+    import torch
+    Nq, H, D = q.shape
+    Nk = k.shape[0]
+    NB = table.shape[1]
+    dt = _dtype_code(q)
+    f32 = torch.float32
+    acc = ACC_ALL if accumulate is True else (0 if accumulate is False else int(accumulate))
+    need = ((ACC_DQ, dq, "dq"), (ACC_DKV, dk, "dk"), (ACC_DKV, dv, "dv"), (ACC_DTABLE, dtable, "dtable"))
+    for bit, t, name in need:
+        if acc & bit and t is None:
+            raise ValueError(f"accumulating into {name} needs {name} to be given")
+    dq = torch.empty((Nq, H, D), dtype=f32, device=q.device) if dq is None else dq
+    dk = torch.empty((Nk, H, D), dtype=f32, device=q.device) if dk is None else dk
+    dv = torch.empty((Nk, H, D), dtype=f32, device=q.device) if dv is None else dv
+    dtable = torch.empty((H, NB), dtype=f32, device=q.device) if dtable is None else dtable
+    wsb = bwd_block_workspace_bytes(Nq, Nk, H, D, NB, dt)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=q.device)
+    sp, ld = _codes(spd, "spd", Nq, Nk)
+    spt, ldt = _codes(spd_t, "spd_t", Nk, Nq)
+    args = [_dev(q, "q", q.dtype, (Nq, H, D)), _dev(k, "k", q.dtype, (Nk, H, D)),
+            _dev(v, "v", q.dtype, (Nk, H, D)), sp, ld, spt, ldt,
+            _dev(table, "table", f32, (H, NB)), _dev(out, "out", f32, (Nq, H, D)),
+            _dev(lse, "lse", f32, (Nq, H)), _dev(dout, "dout", q.dtype, (Nq, H, D)),
+            _dev(dq, "dq", f32, (Nq, H, D)), _dev(dk, "dk", f32, (Nk, H, D)),
+            _dev(dv, "dv", f32, (Nk, H, D)), _dev(dtable, "dtable", f32, (H, NB)),
+            _dev(workspace, "workspace")]
+    _check("gt_attn_bwd_block", lib().gt_attn_bwd_block(*args, _nbytes(workspace), Nq, Nk, H, D, NB, dt,
+                                                        acc, _stream(stream)))
     return dq, dk, dv, dtable
 
 
@@ -266,7 +378,7 @@ def stack_fwd_bwd(x0, w, tables, spd, dout, H: int, spd_t=None, workspace=None, 
     return x_last, dx0, dw, dtable
 
 
-KERNEL_COUNT = 9
+KERNEL_COUNT = 10
 
 
 def kernel_names():

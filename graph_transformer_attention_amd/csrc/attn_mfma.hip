@@ -87,7 +87,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
                                                                     const uint8_t* __restrict__ spd,
                                                                     const float* __restrict__ table,
                                                                     float* __restrict__ out,
-                                                                    float* __restrict__ lse, int64_t N, int NB) {
+                                                                    float* __restrict__ lse, int64_t N, int64_t Nk,
+                                                                    int64_t ldc, int NB) {
   __shared__ float tb[2 * 256];
   __shared__ __align__(16) uint16_t vt[2][2][kD + 1][32];  // [buffer][head][d or ones][key]
   const int tid = threadIdx.x;
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
     qop0 = *reinterpret_cast<const s16x4*>(qp);
     qop1 = *reinterpret_cast<const s16x4*>(qp + kD);
   }
-  const uint8_t* srow = spd + irow * N;
+  const uint8_t* srow = spd + irow * ldc;
   const int kr = node_of_row(c);
   // staging role: key sk of the tile, head shl, d pair sdp (one dword per thread)
   const int sk = 8 * w + (lane >> 3), shl = (lane >> 2) & 1, sdp = lane & 3;
@@ -126,12 +127,12 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
     vt[buf][shl][2 * sdp + 1][sk] = static_cast<uint16_t>(hh >> 16);
   };
 
-  const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
+  const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
   FwdTile cur, nxt;
   if (nfull > 0)
-    fwd_load<false, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, sk, shl, sdp);
+    fwd_load<false, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, kr, sk, shl, sdp);
   else
-    fwd_load<true, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, sk, shl, sdp);
+    fwd_load<true, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, kr, sk, shl, sdp);
   stage(0, cur.vw);
   wait_vm0();
   __syncthreads();
@@ -142,9 +143,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
     const int64_t j0 = t * 32;
     const int buf = static_cast<int>(t & 1);
     if (t + 1 < nfull)
-      fwd_load<false, kAligned>(nxt, srow, k, v, j0 + 32, N, h0, hp, kr, sk, shl, sdp);
+      fwd_load<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, kr, sk, shl, sdp);
     else if (t + 1 < ntiles)
-      fwd_load<true, kAligned>(nxt, srow, k, v, j0 + 32, N, h0, hp, kr, sk, shl, sdp);
+      fwd_load<true, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, kr, sk, shl, sdp);
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
     if (t >= nfull) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        if (j0 + 16 * hp + e >= N) {
+        if (j0 + 16 * hp + e >= Nk) {
           s0[e] = -INFINITY;
           s1[e] = -INFINITY;
         }
@@ -219,20 +220,21 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
 }
 
 // ---------------------------------------------------------------------------------
-// Backward operand copies, written once per call into the workspace for all Npad =
-// N rounded up to 32 nodes (rows past N padded so the main loops need no bounds
-// checks). Augmented half-precision rows [node][head][16] fold the per-query terms of
+// Backward operand copies, written once per call into the workspace: query-side rows
+// for the N queries rounded up to 32 (npq), key-side rows for the Nk keys rounded up
+// to 32 (npk); padded rows let the main loops run without bounds checks. Augmented half-precision rows [node][head][16] fold the per-query terms of
 // the backward into the score MFMAs (contraction index 8.. holds the extra columns):
 //   qa  = [q(8), -L_hi, -L_lo, 1, 0..]    L = lse * sqrt(D), split into two halves
 //   ka  = [k(8),  1,     1,  pen, 0..]    pen = 0, or -inf for padded keys
 //   doa = [do(8), -dl_hi, -dl_lo, 0..]    dl = delta = <dout, out>
 //   va  = [v(8),  1,     1,   0, 0..]
-// so that qa.ka = q.k - lse*sqrt(D) (+ -inf past N) and doa.va = dout.v - delta. Padded
-// queries get -L_hi = -inf. Transposed half copies [head][d][node] of q, k and dout are
-// the A operands of the contractions over nodes.
+// so that qa.ka = q.k - lse*sqrt(D) (+ -inf past Nk) and doa.va = dout.v - delta. Padded
+// queries get -L_hi = -inf. Transposed half copies [head][d][node] of q, k and dout
+// (q and dout over npq nodes, k over npk) are the A operands of the contractions over
+// nodes.
 struct BwdOps {
   uint16_t *qa, *ka, *doa, *va, *qt, *kt, *ot;
-  int64_t npad;
+  int64_t npq, npk;
 };
 
 __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* __restrict__ q,
@@ -241,56 +243,14 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
                                                                const float* __restrict__ out,
                                                                const uint16_t* __restrict__ dout,
                                                                const float* __restrict__ lse, BwdOps ops,
-                                                               int64_t N) {
+                                                               int64_t N, int64_t Nk) {
   const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t npad = ops.npad;
-  if (x >= npad * kH) return;
-  const int h = static_cast<int>(x / npad);
-  const int64_t n = x - h * npad;
-  // Rows are assembled as raw half bit patterns (uint16) and stored as four dwordx4.
-  uint16_t qa[16] = {}, ka[16] = {}, da[16] = {}, va[16] = {};
+  const int64_t nmax = ops.npq > ops.npk ? ops.npq : ops.npk;
+  if (x >= nmax * kH) return;
+  const int h = static_cast<int>(x / nmax);
+  const int64_t n = x - h * nmax;
+  // Rows are assembled as raw half bit patterns (uint16) and stored as two dwordx4.
   auto hbits = [](float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); };
-  const uint16_t one = hbits(1.0f);
-  const uint16_t ninf = hbits(-INFINITY);
-  ka[8] = one;
-  ka[9] = one;
-  va[8] = one;
-  va[9] = one;
-  qa[10] = one;
-  if (n < N) {
-    const int64_t r = n * kH + h;
-    const u32x4 qw = *reinterpret_cast<const u32x4*>(q + r * kD);
-    const u32x4 kw = *reinterpret_cast<const u32x4*>(k + r * kD);
-    const u32x4 vw = *reinterpret_cast<const u32x4*>(v + r * kD);
-    const u32x4 dw = *reinterpret_cast<const u32x4*>(dout + r * kD);
-    const float4 o0 = *reinterpret_cast<const float4*>(out + r * kD);
-    const float4 o1 = *reinterpret_cast<const float4*>(out + r * kD + 4);
-    const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-    float delta = 0.f;
-#pragma unroll
-    for (int d = 0; d < kD; ++d) {
-      const int wi = d >> 1;
-      const float qf = (d & 1) ? bf16_hi(qw[wi]) : bf16_lo(qw[wi]);
-      const float kf = (d & 1) ? bf16_hi(kw[wi]) : bf16_lo(kw[wi]);
-      const float vf = (d & 1) ? bf16_hi(vw[wi]) : bf16_lo(vw[wi]);
-      const float df = (d & 1) ? bf16_hi(dw[wi]) : bf16_lo(dw[wi]);
-      delta = fmaf(df, ov[d], delta);
-      qa[d] = hbits(qf);
-      ka[d] = hbits(kf);
-      va[d] = hbits(vf);
-      da[d] = hbits(df);
-    }
-    const float L = lse[r] * sqrtf(static_cast<float>(kD));
-    const _Float16 lh = static_cast<_Float16>(L);
-    qa[8] = hbits(-static_cast<float>(lh));
-    qa[9] = hbits(-(L - static_cast<float>(lh)));
-    const _Float16 dh = static_cast<_Float16>(delta);
-    da[8] = hbits(-static_cast<float>(dh));
-    da[9] = hbits(-(delta - static_cast<float>(dh)));
-  } else {
-    qa[8] = ninf;
-    ka[10] = ninf;
-  }
   auto pack = [](const uint16_t* e, int first) {
     u32x4 w;
 #pragma unroll
@@ -298,25 +258,75 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
       w[t] = static_cast<uint32_t>(e[first + 2 * t]) | (static_cast<uint32_t>(e[first + 2 * t + 1]) << 16);
     return w;
   };
-  const int64_t row = (n * kH + h) * 16;
-  u32x4* qa_out = reinterpret_cast<u32x4*>(ops.qa + row);
-  u32x4* ka_out = reinterpret_cast<u32x4*>(ops.ka + row);
-  u32x4* da_out = reinterpret_cast<u32x4*>(ops.doa + row);
-  u32x4* va_out = reinterpret_cast<u32x4*>(ops.va + row);
-  qa_out[0] = pack(qa, 0);
-  qa_out[1] = pack(qa, 8);
-  ka_out[0] = pack(ka, 0);
-  ka_out[1] = pack(ka, 8);
-  da_out[0] = pack(da, 0);
-  da_out[1] = pack(da, 8);
-  va_out[0] = pack(va, 0);
-  va_out[1] = pack(va, 8);
+  auto put_row = [&](uint16_t* dst, const uint16_t* e) {
+    u32x4* o = reinterpret_cast<u32x4*>(dst + (n * kH + h) * 16);
+    o[0] = pack(e, 0);
+    o[1] = pack(e, 8);
+  };
+  const uint16_t one = hbits(1.0f);
+  const uint16_t ninf = hbits(-INFINITY);
+  if (n < ops.npq) {
+    uint16_t qa[16] = {}, da[16] = {};
+    qa[10] = one;
+    if (n < N) {
+      const int64_t r = n * kH + h;
+      const u32x4 qw = *reinterpret_cast<const u32x4*>(q + r * kD);
+      const u32x4 dw = *reinterpret_cast<const u32x4*>(dout + r * kD);
+      const float4 o0 = *reinterpret_cast<const float4*>(out + r * kD);
+      const float4 o1 = *reinterpret_cast<const float4*>(out + r * kD + 4);
+      const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+      float delta = 0.f;
 #pragma unroll
-  for (int d = 0; d < kD; ++d) {
-    const int64_t t = (static_cast<int64_t>(h) * kD + d) * npad + n;
-    ops.qt[t] = qa[d];
-    ops.kt[t] = ka[d];
-    ops.ot[t] = da[d];
+      for (int d = 0; d < kD; ++d) {
+        const int wi = d >> 1;
+        const float qf = (d & 1) ? bf16_hi(qw[wi]) : bf16_lo(qw[wi]);
+        const float df = (d & 1) ? bf16_hi(dw[wi]) : bf16_lo(dw[wi]);
+        delta = fmaf(df, ov[d], delta);
+        qa[d] = hbits(qf);
+        da[d] = hbits(df);
+      }
+      const float L = lse[r] * sqrtf(static_cast<float>(kD));
+      const _Float16 lh = static_cast<_Float16>(L);
+      qa[8] = hbits(-static_cast<float>(lh));
+      qa[9] = hbits(-(L - static_cast<float>(lh)));
+      const _Float16 dh = static_cast<_Float16>(delta);
+      da[8] = hbits(-static_cast<float>(dh));
+      da[9] = hbits(-(delta - static_cast<float>(dh)));
+    } else {
+      qa[8] = ninf;
+    }
+    put_row(ops.qa, qa);
+    put_row(ops.doa, da);
+#pragma unroll
+    for (int d = 0; d < kD; ++d) {
+      const int64_t t = (static_cast<int64_t>(h) * kD + d) * ops.npq + n;
+      ops.qt[t] = qa[d];
+      ops.ot[t] = da[d];
+    }
+  }
+  if (n < ops.npk) {
+    uint16_t ka[16] = {}, va[16] = {};
+    ka[8] = one;
+    ka[9] = one;
+    va[8] = one;
+    va[9] = one;
+    if (n < Nk) {
+      const int64_t r = n * kH + h;
+      const u32x4 kw = *reinterpret_cast<const u32x4*>(k + r * kD);
+      const u32x4 vw = *reinterpret_cast<const u32x4*>(v + r * kD);
+#pragma unroll
+      for (int d = 0; d < kD; ++d) {
+        const int wi = d >> 1;
+        ka[d] = hbits((d & 1) ? bf16_hi(kw[wi]) : bf16_lo(kw[wi]));
+        va[d] = hbits((d & 1) ? bf16_hi(vw[wi]) : bf16_lo(vw[wi]));
+      }
+    } else {
+      ka[10] = ninf;
+    }
+    put_row(ops.ka, ka);
+    put_row(ops.va, va);
+#pragma unroll
+    for (int d = 0; d < kD; ++d) ops.kt[(static_cast<int64_t>(h) * kD + d) * ops.npk + n] = ka[d];
   }
 }
 
@@ -415,14 +425,14 @@ __device__ __forceinline__ s16x8 staged_tr(const uint16_t* tr, int hl, int m, in
 template <bool kAligned>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
     const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ partial, int64_t N, int NB) {
+    float* __restrict__ dv, float* __restrict__ partial, int64_t N, int64_t Nk, int64_t ldt, int NB, int acc) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 64);      // [NB][64 lanes][2 heads] per wave
   float* tb = reinterpret_cast<float*>(smem) + kBwdWaves * 2 * NB * 64;  // [2][64] by clamped code
   uint16_t* stage = reinterpret_cast<uint16_t*>(tb + 128);               // [2][kStageHalves]
 
-  const int npad32 = static_cast<int>(ops.npad / 32);
+  const int npad32 = static_cast<int>(ops.npk / 32);
   const int nkb = (npad32 + kBwdWaves - 1) / kBwdWaves;
   int kb, hpair;
   xcd_map(blockIdx.x, nkb, kb, hpair);
@@ -431,9 +441,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   const int h0 = 2 * hpair;
   const int64_t jw = static_cast<int64_t>(kb) * (32 * kBwdWaves) + 32 * w;  // this wave's first key
   const int64_t j = jw + c;
-  const bool wave_live = jw < ops.npad;
+  const bool wave_live = jw < ops.npk;
   const int64_t jj = wave_live ? j : 0;
-  const int64_t npad = ops.npad;
+  const int64_t npad = ops.npq;  // staged tiles are query tiles
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
@@ -449,7 +459,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
   const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
   float2* mybins = reinterpret_cast<float2*>(bins) + lane;
-  const uint8_t* crow = spd_t + (j < N ? j : N - 1) * N;
+  const uint8_t* crow = spd_t + (j < Nk ? j : Nk - 1) * ldt;
   const int64_t cc = 16 * hp;  // this lane's first code column within a tile
 
   StageSrc src;
@@ -518,14 +528,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
     cw = cwn;
     __syncthreads();
   }
-  if (wave_live && j < N) {
+  if (wave_live && j < Nk) {
     const float rs = 1.f / sqd;
     float* kp = dk + j * kHD + h0 * kD + 4 * hp;
     float* vp = dv + j * kHD + h0 * kD + 4 * hp;
-    *reinterpret_cast<float4*>(kp) = make_float4(dk0[0] * rs, dk0[1] * rs, dk0[2] * rs, dk0[3] * rs);
-    *reinterpret_cast<float4*>(kp + kD) = make_float4(dk1[0] * rs, dk1[1] * rs, dk1[2] * rs, dk1[3] * rs);
-    *reinterpret_cast<float4*>(vp) = make_float4(dv0[0], dv0[1], dv0[2], dv0[3]);
-    *reinterpret_cast<float4*>(vp + kD) = make_float4(dv1[0], dv1[1], dv1[2], dv1[3]);
+    store4(kp, make_float4(dk0[0] * rs, dk0[1] * rs, dk0[2] * rs, dk0[3] * rs), acc);
+    store4(kp + kD, make_float4(dk1[0] * rs, dk1[1] * rs, dk1[2] * rs, dk1[3] * rs), acc);
+    store4(vp, make_float4(dv0[0], dv0[1], dv0[2], dv0[3]), acc);
+    store4(vp + kD, make_float4(dv1[0], dv1[1], dv1[2], dv1[3]), acc);
   }
   // per-wave bins -> one partial row per 32-key block and head; a wave past the last
   // key block writes its (zero) bins too, so every partial row is defined
@@ -546,11 +556,12 @@ template <bool kAligned>
 __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_t* __restrict__ spd,
                                                                       const float* __restrict__ table,
                                                                       BwdOps ops, float* __restrict__ dq,
-                                                                      int64_t N, int NB) {
+                                                                      int64_t N, int64_t Nk, int64_t ldc, int NB,
+                                                                      int acc) {
   __shared__ float tb[2 * 256];
   __shared__ __align__(16) uint16_t stage[2 * kStageHalves];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int npad32 = static_cast<int>(ops.npad / 32);
+  const int npad32 = static_cast<int>(ops.npq / 32);
   const int nqb = (npad32 + kBwdWaves - 1) / kBwdWaves;
   int qb, hpair;
   xcd_map(blockIdx.x, nqb, qb, hpair);
@@ -559,10 +570,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   const int h0 = 2 * hpair;
   const int64_t iw = static_cast<int64_t>(qb) * (32 * kBwdWaves) + 32 * w;
   const int64_t i = iw + c;
-  const bool wave_live = iw < ops.npad;
+  const bool wave_live = iw < ops.npq;
   const int64_t ii = wave_live ? i : 0;
   const bool qvalid = i < N;
-  const int64_t npad = ops.npad;
+  const int64_t npad = ops.npk;  // staged tiles are key tiles
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   const s16x8 ob0 = load_h8(ops.doa + (ii * kH + h0) * 16 + 8 * hp);
   const s16x8 ob1 = load_h8(ops.doa + (ii * kH + h0 + 1) * 16 + 8 * hp);
   f32x16 dq0 = {}, dq1 = {};
-  const uint8_t* srow = spd + (qvalid ? i : N - 1) * N;
+  const uint8_t* srow = spd + (qvalid ? i : N - 1) * ldc;
   const int64_t cc = 16 * hp;
 
   StageSrc src;
@@ -583,12 +594,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   src.row1 = ops.va + h0 * 16;
   src.tr0 = ops.kt + static_cast<int64_t>(h0) * kD * npad;
   src.tr1 = nullptr;
-  const int64_t ntiles = npad / 32, nfull = N / 32;
+  const int64_t ntiles = npad / 32, nfull = Nk / 32;
   constexpr int kCh = 320;  // ka, va, k^T
   s16x8 sr[stage_per_thread<kCh>()];
   stage_load<kCh>(sr, src, npad, 0, tid);
   stage_store<kCh>(stage, sr, tid);
-  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(srow, cc, N) : codes_at<true, kAligned>(srow, cc, N);
+  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(srow, cc, Nk) : codes_at<true, kAligned>(srow, cc, Nk);
   wait_vm0();
   __syncthreads();
 
@@ -598,8 +609,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
     u32x4 cwn = cw;
     if (t + 1 < ntiles) {
       stage_load<kCh>(sr, src, npad, j0 + 32, tid);
-      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(srow, j0 + 32 + cc, N)
-                            : codes_at<true, kAligned>(srow, j0 + 32 + cc, N);
+      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(srow, j0 + 32 + cc, Nk)
+                            : codes_at<true, kAligned>(srow, j0 + 32 + cc, Nk);
     }
     if (wave_live) {
       const uint16_t* ka_t = cur;
@@ -635,8 +646,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   if (wave_live && qvalid) {
     const float rs = 1.f / sqd;
     float* qp = dq + i * kHD + h0 * kD + 4 * hp;
-    *reinterpret_cast<float4*>(qp) = make_float4(dq0[0] * rs, dq0[1] * rs, dq0[2] * rs, dq0[3] * rs);
-    *reinterpret_cast<float4*>(qp + kD) = make_float4(dq1[0] * rs, dq1[1] * rs, dq1[2] * rs, dq1[3] * rs);
+    store4(qp, make_float4(dq0[0] * rs, dq0[1] * rs, dq0[2] * rs, dq0[3] * rs), acc);
+    store4(qp + kD, make_float4(dq1[0] * rs, dq1[1] * rs, dq1[2] * rs, dq1[3] * rs), acc);
   }
 }
 
@@ -649,29 +660,29 @@ bool mfma_supported(int H, int D, int dtype) { return H == kH && (D == 8 || D ==
 int64_t mfma_npad(int64_t N) { return (N + 31) / 32 * 32; }
 
 // dtable partial rows: one per 32-key block (padded to whole key workgroups)
-int64_t mfma_kv_blocks(int64_t N) {
-  const int64_t nblk = (mfma_npad(N) / 32 + kBwdWaves - 1) / kBwdWaves;
+int64_t mfma_kv_blocks(int64_t Nk) {
+  const int64_t nblk = (mfma_npad(Nk) / 32 + kBwdWaves - 1) / kBwdWaves;
   return nblk * kBwdWaves;
 }
 
-size_t mfma_ops_bytes(int64_t N) {
-  const size_t npad = static_cast<size_t>(mfma_npad(N));
-  return 4 * npad * kH * 16 * 2 + 3 * npad * kH * kD * 2;
+size_t mfma_ops_bytes(int64_t N, int64_t Nk) {
+  const size_t npq = static_cast<size_t>(mfma_npad(N)), npk = static_cast<size_t>(mfma_npad(Nk));
+  return 2 * (npq + npk) * kH * 16 * 2 + (2 * npq + npk) * kH * kD * 2;
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(xcd_grid(static_cast<int>((a.N + 32 * kFwdWaves - 1) / (32 * kFwdWaves)))));
-  trace_begin(0, s);
-  if (a.N % 16 == 0)
+  trace_begin(kTraceFwd, s);
+  if (codes_aligned(a.spd, a.ld))
     hipLaunchKernelGGL(fwd_mfma_d8_kernel<true>, grid, dim3(64 * kFwdWaves), 0, s, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table,
-                       a.out, a.lse, a.N, a.NB);
+                       a.out, a.lse, a.N, a.Nk, a.ld, a.NB);
   else
     hipLaunchKernelGGL(fwd_mfma_d8_kernel<false>, grid, dim3(64 * kFwdWaves), 0, s, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table,
-                       a.out, a.lse, a.N, a.NB);
+                       a.out, a.lse, a.N, a.Nk, a.ld, a.NB);
   const hipError_t e = hipGetLastError();
-  trace_end(0, s);
+  trace_end(kTraceFwd, s);
   return e;
 }
 
@@ -679,55 +690,57 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   char* ws = static_cast<char*>(a.workspace);
   float* partial = reinterpret_cast<float*>(ws + w.partial_off);
   BwdOps ops;
-  ops.npad = mfma_npad(a.N);
-  const size_t big = static_cast<size_t>(ops.npad) * kH * 16;  // halves per augmented copy
-  const size_t small = static_cast<size_t>(ops.npad) * kH * kD;
+  ops.npq = mfma_npad(a.N);
+  ops.npk = mfma_npad(a.Nk);
+  const size_t hq = static_cast<size_t>(ops.npq) * kH, hk = static_cast<size_t>(ops.npk) * kH;
   uint16_t* base = reinterpret_cast<uint16_t*>(ws + w.ops_off);
   ops.qa = base;
-  ops.ka = ops.qa + big;
-  ops.doa = ops.ka + big;
-  ops.va = ops.doa + big;
-  ops.qt = ops.va + big;
-  ops.kt = ops.qt + small;
-  ops.ot = ops.kt + small;
-  const bool aligned = a.N % 16 == 0;
+  ops.doa = ops.qa + hq * 16;
+  ops.ka = ops.doa + hq * 16;
+  ops.va = ops.ka + hk * 16;
+  ops.qt = ops.va + hk * 16;
+  ops.ot = ops.qt + hq * kD;
+  ops.kt = ops.ot + hq * kD;
 
-  trace_begin(1, s);
-  hipLaunchKernelGGL(bwd_prep_mfma_d8_kernel, dim3(static_cast<unsigned>((ops.npad * kH + 255) / 256)), dim3(256),
-                     0, s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+  trace_begin(kTraceBwdDelta, s);
+  const int64_t nmax = std::max(ops.npq, ops.npk);
+  hipLaunchKernelGGL(bwd_prep_mfma_d8_kernel, dim3(static_cast<unsigned>((nmax * kH + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.out, static_cast<const uint16_t*>(a.dout), a.lse, ops,
-                     a.N);
+                     a.N, a.Nk);
   hipError_t e = hipGetLastError();
-  trace_end(1, s);
+  trace_end(kTraceBwdDelta, s);
   if (e != hipSuccess) return e;
 
-  const int nblk = static_cast<int>((ops.npad / 32 + kBwdWaves - 1) / kBwdWaves);
-  const dim3 grid(static_cast<unsigned>(xcd_grid(nblk)));
   const dim3 block(kBwdThreads);
+  const int nkb = static_cast<int>((ops.npk / 32 + kBwdWaves - 1) / kBwdWaves);
   const size_t lds = kv_mfma_lds(a.NB);
   e = allow_lds_mfma(bwd_kv_mfma_d8_kernel<true>, lds);
   if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d8_kernel<false>, lds);
   if (e != hipSuccess) return e;
-  trace_begin(2, s);
-  if (aligned)
-    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<true>, grid, block, lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
-                       partial, a.N, a.NB);
+  trace_begin(kTraceBwdKv, s);
+  if (codes_aligned(a.spd_t, a.ld_t))
+    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<true>, dim3(static_cast<unsigned>(xcd_grid(nkb))), block, lds, s,
+                       a.spd_t, a.table, ops, a.dk, a.dv, partial, a.N, a.Nk, a.ld_t, a.NB, a.acc & kAccDkv);
   else
-    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<false>, grid, block, lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
-                       partial, a.N, a.NB);
+    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<false>, dim3(static_cast<unsigned>(xcd_grid(nkb))), block, lds, s,
+                       a.spd_t, a.table, ops, a.dk, a.dv, partial, a.N, a.Nk, a.ld_t, a.NB, a.acc & kAccDkv);
   e = hipGetLastError();
-  trace_end(2, s);
+  trace_end(kTraceBwdKv, s);
   if (e != hipSuccess) return e;
 
-  trace_begin(3, s);
-  if (aligned)
-    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<true>, grid, block, 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
+  const int nqb = static_cast<int>((ops.npq / 32 + kBwdWaves - 1) / kBwdWaves);
+  trace_begin(kTraceBwdQ, s);
+  if (codes_aligned(a.spd, a.ld))
+    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<true>, dim3(static_cast<unsigned>(xcd_grid(nqb))), block, 0, s, a.spd,
+                       a.table, ops, a.dq, a.N, a.Nk, a.ld, a.NB, a.acc & kAccDq);
   else
-    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<false>, grid, block, 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
+    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<false>, dim3(static_cast<unsigned>(xcd_grid(nqb))), block, 0, s, a.spd,
+                       a.table, ops, a.dq, a.N, a.Nk, a.ld, a.NB, a.acc & kAccDq);
   e = hipGetLastError();
-  trace_end(3, s);
+  trace_end(kTraceBwdQ, s);
   if (e != hipSuccess) return e;
-  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, s);
+  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, a.acc & kAccDtable, s);
 }
 
 }  // namespace gt

@@ -18,6 +18,8 @@
 // node_of_row.
 #include "mfma_common.h"
 
+#include <algorithm>
+
 namespace gt {
 namespace {
 
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
                                                                 const uint8_t* __restrict__ spd,
                                                                 const float* __restrict__ table,
                                                                 float* __restrict__ out, float* __restrict__ lse,
-                                                                int64_t N, int NB) {
+                                                                int64_t N, int64_t Nk, int64_t ldc, int NB) {
   __shared__ float tb[2 * 256];
   __shared__ __align__(16) uint16_t vt[2][2 * kVtHead];  // [buffer][head][d][key], rows of kVtRow
   const int tid = threadIdx.x;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     for (int ci = 0; ci < 2; ++ci)
       qop[hl][ci] = qvalid ? load_h8(q + i * kHD + (h0 + hl) * kD + 16 * ci + 8 * hp)
                            : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  const uint8_t* srow = spd + irow * N;
+  const uint8_t* srow = spd + irow * ldc;
   const int kr = node_of_row(c);
   // staging role: head shl, d quad sdq (d = 4*sdq .. +3), key pair skp (keys 2*skp, 2*skp+1)
   const int shl = tid >> 7, sdq = (tid >> 4) & 7, skp = tid & 15;
@@ -112,12 +114,12 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     base[3 * kRowWords] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
   };
 
-  const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
+  const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
   FwdTileD32 cur, nxt;
   if (nfull > 0)
-    fwd_load_d32<false, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, shl, sdq, skp);
+    fwd_load_d32<false, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, kr, shl, sdq, skp);
   else
-    fwd_load_d32<true, kAligned>(cur, srow, k, v, 0, N, h0, hp, kr, shl, sdq, skp);
+    fwd_load_d32<true, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, kr, shl, sdq, skp);
   stage(0, cur.va, cur.vb);
   wait_vm0();
   __syncthreads();
@@ -128,9 +130,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     const int64_t j0 = t * 32;
     const int buf = static_cast<int>(t & 1);
     if (t + 1 < nfull)
-      fwd_load_d32<false, kAligned>(nxt, srow, k, v, j0 + 32, N, h0, hp, kr, shl, sdq, skp);
+      fwd_load_d32<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, kr, shl, sdq, skp);
     else if (t + 1 < ntiles)
-      fwd_load_d32<true, kAligned>(nxt, srow, k, v, j0 + 32, N, h0, hp, kr, shl, sdq, skp);
+      fwd_load_d32<true, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, kr, shl, sdq, skp);
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     if (t >= nfull) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        if (j0 + 16 * hp + e >= N) {
+        if (j0 + 16 * hp + e >= Nk) {
           s0[e] = -INFINITY;
           s1[e] = -INFINITY;
         }
@@ -216,8 +218,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------------
-// Backward operand copies, written once per call for all Npad = N rounded up to 32
-// nodes (rows past N padded):
+// Backward operand copies, written once per call: query-side arrays (q, dout, lse,
+// delta) for the N queries rounded up to 32 (npq), key-side arrays (k, v) for the Nk
+// keys rounded up to 32 (npk); padded rows are zero:
 //   qd, kd, vd, od   [node][head][32] half      q, k, v, dout
 //   qt, kt, ot       [head][32][node] half      transposed q, k, dout
 //   lq, dl           [head][node] two halves    (-L_hi, -L_lo), L = lse*sqrt(D), and
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
 struct OpsD32 {
   uint16_t *qd, *kd, *vd, *od, *qt, *kt, *ot;
   uint32_t *lq, *dl;
-  int64_t npad;
+  int64_t npq, npk;
 };
 
 __device__ __forceinline__ uint16_t hbits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
@@ -244,67 +247,79 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* 
                                                                 const float* __restrict__ out,
                                                                 const uint16_t* __restrict__ dout,
                                                                 const float* __restrict__ lse, OpsD32 ops,
-                                                                int64_t N) {
+                                                                int64_t N, int64_t Nk) {
   const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t npad = ops.npad;
-  if (x >= npad * kH) return;
-  const int h = static_cast<int>(x / npad);
-  const int64_t n = x - h * npad;
+  const int64_t nmax = ops.npq > ops.npk ? ops.npq : ops.npk;
+  if (x >= nmax * kH) return;
+  const int h = static_cast<int>(x / nmax);
+  const int64_t n = x - h * nmax;
   const int64_t row = (n * kH + h) * kD;
-  const uint16_t* srcs[4] = {q, k, v, dout};
-  uint16_t* dsts[4] = {ops.qd, ops.kd, ops.vd, ops.od};
-  uint16_t* trs[4] = {ops.qt, ops.kt, nullptr, ops.ot};
   const uint16_t ninf = hbits(-INFINITY);
-  if (n < N) {
-    float delta = 0.f;
+  // One node's row of 32 bf16 values -> half row (and its transposed column when tr is
+  // given, over npad nodes); with o given, also returns <row, o's row>.
+  auto copy = [&](const uint16_t* src, uint16_t* dst, uint16_t* tr, int64_t npad, const float* o) {
+    float dot = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int part = 0; part < 4; ++part) {
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(src + row + 8 * part);
+      u32x4 hv;
 #pragma unroll
-      for (int part = 0; part < 4; ++part) {
-        const u32x4 wv = *reinterpret_cast<const u32x4*>(srcs[s] + row + 8 * part);
-        u32x4 hv;
+      for (int wi = 0; wi < 4; ++wi) hv[wi] = bf16x2_to_f16x2(wv[wi]);
+      *reinterpret_cast<u32x4*>(dst + row + 8 * part) = hv;
+      if (o != nullptr) {
+        const float4 oa = *reinterpret_cast<const float4*>(o + row + 8 * part);
+        const float4 ob = *reinterpret_cast<const float4*>(o + row + 8 * part + 4);
+        dot = fmaf(bf16_lo(wv[0]), oa.x, dot);
+        dot = fmaf(bf16_hi(wv[0]), oa.y, dot);
+        dot = fmaf(bf16_lo(wv[1]), oa.z, dot);
+        dot = fmaf(bf16_hi(wv[1]), oa.w, dot);
+        dot = fmaf(bf16_lo(wv[2]), ob.x, dot);
+        dot = fmaf(bf16_hi(wv[2]), ob.y, dot);
+        dot = fmaf(bf16_lo(wv[3]), ob.z, dot);
+        dot = fmaf(bf16_hi(wv[3]), ob.w, dot);
+      }
+      if (tr != nullptr) {
 #pragma unroll
-        for (int wi = 0; wi < 4; ++wi) hv[wi] = bf16x2_to_f16x2(wv[wi]);
-        *reinterpret_cast<u32x4*>(dsts[s] + row + 8 * part) = hv;
-        if (s == 3) {
-          const float4 oa = *reinterpret_cast<const float4*>(out + row + 8 * part);
-          const float4 ob = *reinterpret_cast<const float4*>(out + row + 8 * part + 4);
-          delta = fmaf(bf16_lo(wv[0]), oa.x, delta);
-          delta = fmaf(bf16_hi(wv[0]), oa.y, delta);
-          delta = fmaf(bf16_lo(wv[1]), oa.z, delta);
-          delta = fmaf(bf16_hi(wv[1]), oa.w, delta);
-          delta = fmaf(bf16_lo(wv[2]), ob.x, delta);
-          delta = fmaf(bf16_hi(wv[2]), ob.y, delta);
-          delta = fmaf(bf16_lo(wv[3]), ob.z, delta);
-          delta = fmaf(bf16_hi(wv[3]), ob.w, delta);
-        }
-        if (trs[s] != nullptr) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t word = hv[e >> 1];
-            trs[s][(static_cast<int64_t>(h) * kD + 8 * part + e) * npad + n] =
-                static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
-          }
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = hv[e >> 1];
+          tr[(static_cast<int64_t>(h) * kD + 8 * part + e) * npad + n] =
+              static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
         }
       }
     }
-    const float L = lse[n * kH + h] * sqrtf(static_cast<float>(kD));
-    const _Float16 lh = static_cast<_Float16>(L);
-    ops.lq[static_cast<int64_t>(h) * npad + n] = pack2(hbits(-static_cast<float>(lh)), hbits(-(L - static_cast<float>(lh))));
-    const _Float16 dh = static_cast<_Float16>(delta);
-    ops.dl[static_cast<int64_t>(h) * npad + n] =
-        pack2(hbits(-static_cast<float>(dh)), hbits(-(delta - static_cast<float>(dh))));
-  } else {
+    return dot;
+  };
+  auto zero = [&](uint16_t* dst, uint16_t* tr, int64_t npad) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int part = 0; part < 4; ++part)
-        *reinterpret_cast<u32x4*>(dsts[s] + row + 8 * part) = u32x4{0u, 0u, 0u, 0u};
-      if (trs[s] != nullptr)
-        for (int d = 0; d < kD; ++d) trs[s][(static_cast<int64_t>(h) * kD + d) * npad + n] = 0;
+    for (int part = 0; part < 4; ++part) *reinterpret_cast<u32x4*>(dst + row + 8 * part) = u32x4{0u, 0u, 0u, 0u};
+    if (tr != nullptr)
+      for (int d = 0; d < kD; ++d) tr[(static_cast<int64_t>(h) * kD + d) * npad + n] = 0;
+  };
+  if (n < ops.npq) {
+    const int64_t lrow = static_cast<int64_t>(h) * ops.npq + n;
+    if (n < N) {
+      copy(q, ops.qd, ops.qt, ops.npq, nullptr);
+      const float delta = copy(dout, ops.od, ops.ot, ops.npq, out);
+      const float L = lse[n * kH + h] * sqrtf(static_cast<float>(kD));
+      const _Float16 lh = static_cast<_Float16>(L);
+      ops.lq[lrow] = pack2(hbits(-static_cast<float>(lh)), hbits(-(L - static_cast<float>(lh))));
+      const _Float16 dh = static_cast<_Float16>(delta);
+      ops.dl[lrow] = pack2(hbits(-static_cast<float>(dh)), hbits(-(delta - static_cast<float>(dh))));
+    } else {
+      zero(ops.qd, ops.qt, ops.npq);
+      zero(ops.od, ops.ot, ops.npq);
+      ops.lq[lrow] = pack2(ninf, 0);
+      ops.dl[lrow] = 0u;
     }
-    ops.lq[static_cast<int64_t>(h) * npad + n] = pack2(ninf, 0);
-    ops.dl[static_cast<int64_t>(h) * npad + n] = 0u;
+  }
+  if (n < ops.npk) {
+    if (n < Nk) {
+      copy(k, ops.kd, ops.kt, ops.npk, nullptr);
+      copy(v, ops.vd, nullptr, ops.npk, nullptr);
+    } else {
+      zero(ops.kd, ops.kt, ops.npk);
+      zero(ops.vd, nullptr, ops.npk);
+    }
   }
 }
 
@@ -393,14 +408,15 @@ template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t* __restrict__ spd_t,
                                                                    const float* __restrict__ table, OpsD32 ops,
                                                                    float* __restrict__ dk, float* __restrict__ dv,
-                                                                   float* __restrict__ partial, int64_t N, int NB) {
+                                                                   float* __restrict__ partial, int64_t N, int64_t Nk,
+                                                                   int64_t ldt, int NB, int acc) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 32);  // [NB][32 keys][2 heads] per wave
   float* tb = reinterpret_cast<float*>(smem) + kWaves * 2 * NB * 32;  // [2][64] by clamped code
   uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTbD32);
 
-  const int npad32 = static_cast<int>(ops.npad / 32);
+  const int npad32 = static_cast<int>(ops.npk / 32);
   const int nkb = (npad32 + kWaves - 1) / kWaves;
   int kb, hpair;
   xcd_map(blockIdx.x, nkb, kb, hpair);
@@ -409,9 +425,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   const int h0 = 2 * hpair;
   const int64_t jw = static_cast<int64_t>(kb) * (32 * kWaves) + 32 * w;
   const int64_t j = jw + c;
-  const bool wave_live = jw < ops.npad;
+  const bool wave_live = jw < ops.npk;
   const int64_t jj = wave_live ? j : 0;
-  const int64_t npad = ops.npad;
+  const int64_t npad = ops.npq;  // staged tiles (and lse, delta) are over queries
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
@@ -429,12 +445,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
       vop[hl][ci] = load_h8(ops.vd + (jj * kH + h0 + hl) * kD + 16 * ci + 8 * hp);
     }
   const uint16_t one = 0x3C00u, ninf = 0xFC00u;
-  const s16x8 kaug = aug_chunk(pack2(one, one), j < N ? 0 : ninf, hp);
+  const s16x8 kaug = aug_chunk(pack2(one, one), j < Nk ? 0 : ninf, hp);
   const s16x8 vaug = aug_chunk(pack2(one, one), 0, hp);
   f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
   const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
   float2* mybins = reinterpret_cast<float2*>(bins) + c;
-  const uint8_t* crow = spd_t + (j < N ? j : N - 1) * N;
+  const uint8_t* crow = spd_t + (j < Nk ? j : Nk - 1) * ldt;
   const int64_t cc = 16 * hp;
   const int qr = node_of_row(c);
 
@@ -532,19 +548,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
     dw1 = dwn1;
     __syncthreads();
   }
-  if (wave_live && j < N) {
+  if (wave_live && j < Nk) {
     const float rs = 1.f / sqd;
     float* kp0 = dk + j * kHD + h0 * kD + 4 * hp;
     float* vp0 = dv + j * kHD + h0 * kD + 4 * hp;
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
-      *reinterpret_cast<float4*>(kp0 + 8 * jq) =
-          make_float4(dk0[4 * jq] * rs, dk0[4 * jq + 1] * rs, dk0[4 * jq + 2] * rs, dk0[4 * jq + 3] * rs);
-      *reinterpret_cast<float4*>(kp0 + kD + 8 * jq) =
-          make_float4(dk1[4 * jq] * rs, dk1[4 * jq + 1] * rs, dk1[4 * jq + 2] * rs, dk1[4 * jq + 3] * rs);
-      *reinterpret_cast<float4*>(vp0 + 8 * jq) = make_float4(dv0[4 * jq], dv0[4 * jq + 1], dv0[4 * jq + 2], dv0[4 * jq + 3]);
-      *reinterpret_cast<float4*>(vp0 + kD + 8 * jq) =
-          make_float4(dv1[4 * jq], dv1[4 * jq + 1], dv1[4 * jq + 2], dv1[4 * jq + 3]);
+      store4(kp0 + 8 * jq, make_float4(dk0[4 * jq] * rs, dk0[4 * jq + 1] * rs, dk0[4 * jq + 2] * rs, dk0[4 * jq + 3] * rs),
+             acc);
+      store4(kp0 + kD + 8 * jq,
+             make_float4(dk1[4 * jq] * rs, dk1[4 * jq + 1] * rs, dk1[4 * jq + 2] * rs, dk1[4 * jq + 3] * rs), acc);
+      store4(vp0 + 8 * jq, make_float4(dv0[4 * jq], dv0[4 * jq + 1], dv0[4 * jq + 2], dv0[4 * jq + 3]), acc);
+      store4(vp0 + kD + 8 * jq, make_float4(dv1[4 * jq], dv1[4 * jq + 1], dv1[4 * jq + 2], dv1[4 * jq + 3]), acc);
     }
   }
   // per-wave bins -> one partial row per 32-key block and head (a wave past the last key
@@ -566,12 +581,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t* __restrict__ spd,
                                                                   const float* __restrict__ table, OpsD32 ops,
-                                                                  float* __restrict__ dq, int64_t N, int NB) {
+                                                                  float* __restrict__ dq, int64_t N, int64_t Nk,
+                                                                  int64_t ldc, int NB, int acc) {
   using Set = StageSetD32<2, 1>;
   __shared__ float tb[2 * 256];
   __shared__ __align__(16) uint16_t stage[2 * Set::kHalves];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int npad32 = static_cast<int>(ops.npad / 32);
+  const int npad32 = static_cast<int>(ops.npq / 32);
   const int nqb = (npad32 + kWaves - 1) / kWaves;
   int qb, hpair;
   xcd_map(blockIdx.x, nqb, qb, hpair);
@@ -580,10 +596,10 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
   const int h0 = 2 * hpair;
   const int64_t iw = static_cast<int64_t>(qb) * (32 * kWaves) + 32 * w;
   const int64_t i = iw + c;
-  const bool wave_live = iw < ops.npad;
+  const bool wave_live = iw < ops.npq;
   const int64_t ii = wave_live ? i : 0;
   const bool qvalid = i < N;
-  const int64_t npad = ops.npad;
+  const int64_t npad = ops.npk;  // staged tiles are key tiles
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
@@ -600,12 +616,12 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
       qop[hl][ci] = load_h8(ops.qd + (ii * kH + h0 + hl) * kD + 16 * ci + 8 * hp);
       oop[hl][ci] = load_h8(ops.od + (ii * kH + h0 + hl) * kD + 16 * ci + 8 * hp);
     }
-    qaug[hl] = aug_chunk(ops.lq[static_cast<int64_t>(h0 + hl) * npad + ii], one, hp);
-    oaug[hl] = aug_chunk(ops.dl[static_cast<int64_t>(h0 + hl) * npad + ii], 0, hp);
+    qaug[hl] = aug_chunk(ops.lq[static_cast<int64_t>(h0 + hl) * ops.npq + ii], one, hp);
+    oaug[hl] = aug_chunk(ops.dl[static_cast<int64_t>(h0 + hl) * ops.npq + ii], 0, hp);
   }
   const s16x8 vaug = aug_chunk(pack2(one, one), 0, hp);
   f32x16 dq0 = {}, dq1 = {};
-  const uint8_t* srow = spd + (qvalid ? i : N - 1) * N;
+  const uint8_t* srow = spd + (qvalid ? i : N - 1) * ldc;
   const int64_t cc = 16 * hp;
   const int kr = node_of_row(c);
 
@@ -615,11 +631,11 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
   set.trs[0] = ops.kt;
   set.h0 = h0;
   set.npad = npad;
-  const int64_t ntiles = npad / 32, nfull = N / 32;
+  const int64_t ntiles = npad / 32, nfull = Nk / 32;
   s16x8 sr[Set::kPer];
   set.load(sr, 0, tid);
   set.store(stage, sr, tid);
-  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(srow, cc, N) : codes_at<true, kAligned>(srow, cc, N);
+  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(srow, cc, Nk) : codes_at<true, kAligned>(srow, cc, Nk);
   wait_vm0();
   __syncthreads();
 
@@ -629,8 +645,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
     u32x4 cwn = cw;
     if (t + 1 < ntiles) {
       set.load(sr, j0 + 32, tid);
-      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(srow, j0 + 32 + cc, N)
-                            : codes_at<true, kAligned>(srow, j0 + 32 + cc, N);
+      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(srow, j0 + 32 + cc, Nk)
+                            : codes_at<true, kAligned>(srow, j0 + 32 + cc, Nk);
     }
     if (wave_live) {
       const uint16_t* k_t = cur;
@@ -651,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
         p0 = mfma_h16(row_op(v_t, c, 0, ci, hp), oop[0][ci], p0);
         p1 = mfma_h16(row_op(v_t, c, 1, ci, hp), oop[1][ci], p1);
       }
-      const s16x8 kaug = aug_chunk(pack2(one, one), j0 + kr < N ? 0 : ninf, hp);
+      const s16x8 kaug = aug_chunk(pack2(one, one), j0 + kr < Nk ? 0 : ninf, hp);
       s0 = mfma_h16(kaug, qaug[0], s0);
       s1 = mfma_h16(kaug, qaug[1], s1);
       p0 = mfma_h16(vaug, oaug[0], p0);
@@ -677,28 +693,30 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
     float* qp0 = dq + i * kHD + h0 * kD + 4 * hp;
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
-      *reinterpret_cast<float4*>(qp0 + 8 * jq) =
-          make_float4(dq0[4 * jq] * rs, dq0[4 * jq + 1] * rs, dq0[4 * jq + 2] * rs, dq0[4 * jq + 3] * rs);
-      *reinterpret_cast<float4*>(qp0 + kD + 8 * jq) =
-          make_float4(dq1[4 * jq] * rs, dq1[4 * jq + 1] * rs, dq1[4 * jq + 2] * rs, dq1[4 * jq + 3] * rs);
+      store4(qp0 + 8 * jq, make_float4(dq0[4 * jq] * rs, dq0[4 * jq + 1] * rs, dq0[4 * jq + 2] * rs, dq0[4 * jq + 3] * rs),
+             acc);
+      store4(qp0 + kD + 8 * jq,
+             make_float4(dq1[4 * jq] * rs, dq1[4 * jq + 1] * rs, dq1[4 * jq + 2] * rs, dq1[4 * jq + 3] * rs), acc);
     }
   }
 }
 
-OpsD32 carve_ops_d32(void* base, int64_t N) {
+OpsD32 carve_ops_d32(void* base, int64_t N, int64_t Nk) {
   OpsD32 o{};
-  o.npad = (N + 31) / 32 * 32;
-  const size_t node = static_cast<size_t>(o.npad) * kH * kD;  // halves per node-major or transposed array
+  o.npq = (N + 31) / 32 * 32;
+  o.npk = (Nk + 31) / 32 * 32;
+  const size_t nq = static_cast<size_t>(o.npq) * kH * kD;  // halves per query-side array
+  const size_t nk = static_cast<size_t>(o.npk) * kH * kD;  // halves per key-side array
   uint16_t* p = static_cast<uint16_t*>(base);
   o.qd = p;
-  o.kd = p + node;
-  o.vd = p + 2 * node;
-  o.od = p + 3 * node;
-  o.qt = p + 4 * node;
-  o.kt = p + 5 * node;
-  o.ot = p + 6 * node;
-  o.lq = reinterpret_cast<uint32_t*>(p + 7 * node);
-  o.dl = o.lq + static_cast<size_t>(o.npad) * kH;
+  o.od = o.qd + nq;
+  o.qt = o.od + nq;
+  o.ot = o.qt + nq;
+  o.kd = o.ot + nq;
+  o.vd = o.kd + nk;
+  o.kt = o.vd + nk;
+  o.lq = reinterpret_cast<uint32_t*>(o.kt + nk);
+  o.dl = o.lq + static_cast<size_t>(o.npq) * kH;
   return o;
 }
 
@@ -706,27 +724,27 @@ size_t kv_d32_lds(int NB) { return 4ull * kWaves * 2 * NB * 32 + 4ull * kKvTbD32
 
 }  // namespace
 
-size_t mfma_d32_ops_bytes(int64_t N) {
-  const size_t npad = static_cast<size_t>((N + 31) / 32 * 32);
-  return npad * kH * kD * 2 * 7 + npad * kH * 4 * 2;
+size_t mfma_d32_ops_bytes(int64_t N, int64_t Nk) {
+  const size_t npq = static_cast<size_t>((N + 31) / 32 * 32), npk = static_cast<size_t>((Nk + 31) / 32 * 32);
+  return (4 * npq + 3 * npk) * kH * kD * 2 + npq * kH * 4 * 2;
 }
 
-int64_t mfma_d32_kv_blocks(int64_t N) {
-  const int64_t nblk = ((N + 31) / 32 + kWaves - 1) / kWaves;
+int64_t mfma_d32_kv_blocks(int64_t Nk) {
+  const int64_t nblk = ((Nk + 31) / 32 + kWaves - 1) / kWaves;
   return nblk * kWaves;
 }
 
 hipError_t launch_fwd_mfma_d32(const FwdArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(xcd_grid(static_cast<int>((a.N + 32 * kWaves - 1) / (32 * kWaves)))));
   trace_begin(kTraceFwd, s);
-  if (a.N % 16 == 0)
+  if (codes_aligned(a.spd, a.ld))
     hipLaunchKernelGGL(fwd_mfma_d32_kernel<true>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table, a.out,
-                       a.lse, a.N, a.NB);
+                       a.lse, a.N, a.Nk, a.ld, a.NB);
   else
     hipLaunchKernelGGL(fwd_mfma_d32_kernel<false>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table, a.out,
-                       a.lse, a.N, a.NB);
+                       a.lse, a.N, a.Nk, a.ld, a.NB);
   const hipError_t e = hipGetLastError();
   trace_end(kTraceFwd, s);
   return e;
@@ -734,45 +752,48 @@ hipError_t launch_fwd_mfma_d32(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_mfma_d32(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
   char* base = static_cast<char*>(a.workspace);
-  const OpsD32 ops = carve_ops_d32(base + w.ops_off, a.N);
+  const OpsD32 ops = carve_ops_d32(base + w.ops_off, a.N, a.Nk);
   float* partial = reinterpret_cast<float*>(base + w.partial_off);
-  const bool aligned = a.N % 16 == 0;
-  const int64_t prep_threads = ops.npad * kH;
+  const int64_t prep_threads = std::max(ops.npq, ops.npk) * kH;
   trace_begin(kTraceBwdDelta, s);
   hipLaunchKernelGGL(bwd_prep_mfma_d32_kernel, dim3(static_cast<unsigned>((prep_threads + 255) / 256)), dim3(256), 0,
                      s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.out, static_cast<const uint16_t*>(a.dout), a.lse, ops, a.N);
+                     static_cast<const uint16_t*>(a.v), a.out, static_cast<const uint16_t*>(a.dout), a.lse, ops, a.N,
+                     a.Nk);
   hipError_t e = hipGetLastError();
   trace_end(kTraceBwdDelta, s);
   if (e != hipSuccess) return e;
 
-  const int nblk = static_cast<int>((ops.npad / 32 + kWaves - 1) / kWaves);
-  const dim3 grid(static_cast<unsigned>(xcd_grid(nblk)));
+  const int nkb = static_cast<int>((ops.npk / 32 + kWaves - 1) / kWaves);
+  const dim3 kgrid(static_cast<unsigned>(xcd_grid(nkb)));
   const size_t lds = kv_d32_lds(a.NB);
   e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<true>, lds);
   if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<false>, lds);
   if (e != hipSuccess) return e;
   trace_begin(kTraceBwdKv, s);
-  if (aligned)
-    hipLaunchKernelGGL(bwd_kv_mfma_d32_kernel<true>, grid, dim3(kThreads), lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
-                       partial, a.N, a.NB);
+  if (codes_aligned(a.spd_t, a.ld_t))
+    hipLaunchKernelGGL(bwd_kv_mfma_d32_kernel<true>, kgrid, dim3(kThreads), lds, s, a.spd_t, a.table, ops, a.dk, a.dv,
+                       partial, a.N, a.Nk, a.ld_t, a.NB, a.acc & kAccDkv);
   else
-    hipLaunchKernelGGL(bwd_kv_mfma_d32_kernel<false>, grid, dim3(kThreads), lds, s, a.spd_t, a.table, ops, a.dk,
-                       a.dv, partial, a.N, a.NB);
+    hipLaunchKernelGGL(bwd_kv_mfma_d32_kernel<false>, kgrid, dim3(kThreads), lds, s, a.spd_t, a.table, ops, a.dk,
+                       a.dv, partial, a.N, a.Nk, a.ld_t, a.NB, a.acc & kAccDkv);
   e = hipGetLastError();
   trace_end(kTraceBwdKv, s);
   if (e != hipSuccess) return e;
 
+  const int nqb = static_cast<int>((ops.npq / 32 + kWaves - 1) / kWaves);
+  const dim3 qgrid(static_cast<unsigned>(xcd_grid(nqb)));
   trace_begin(kTraceBwdQ, s);
-  if (aligned)
-    hipLaunchKernelGGL(bwd_q_mfma_d32_kernel<true>, grid, dim3(kThreads), 0, s, a.spd, a.table, ops, a.dq, a.N, a.NB);
+  if (codes_aligned(a.spd, a.ld))
+    hipLaunchKernelGGL(bwd_q_mfma_d32_kernel<true>, qgrid, dim3(kThreads), 0, s, a.spd, a.table, ops, a.dq, a.N, a.Nk,
+                       a.ld, a.NB, a.acc & kAccDq);
   else
-    hipLaunchKernelGGL(bwd_q_mfma_d32_kernel<false>, grid, dim3(kThreads), 0, s, a.spd, a.table, ops, a.dq, a.N,
-                       a.NB);
+    hipLaunchKernelGGL(bwd_q_mfma_d32_kernel<false>, qgrid, dim3(kThreads), 0, s, a.spd, a.table, ops, a.dq, a.N,
+                       a.Nk, a.ld, a.NB, a.acc & kAccDq);
   e = hipGetLastError();
   trace_end(kTraceBwdQ, s);
   if (e != hipSuccess) return e;
-  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, s);
+  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, a.acc & kAccDtable, s);
 }
 
 }  // namespace gt

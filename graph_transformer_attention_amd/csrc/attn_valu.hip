@@ -32,7 +32,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const uint8_t* __restrict__ spd, const float* __restrict__ table, float* __restrict__ out,
-    float* __restrict__ lse, int64_t N, int H, int NB, int BN, float qscale) {
+    float* __restrict__ lse, int64_t N, int64_t Nk, int64_t ldc, int H, int NB, int BN, float qscale) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int HD = H * D;
   const int R = kThreads / H;
@@ -58,8 +58,8 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(
   float m = -INFINITY, l = 0.f;
   const float* tbh = tb + h * NB;
 
-  for (int64_t j0 = 0; j0 < N; j0 += BN) {
-    const int nk = static_cast<int>(std::min<int64_t>(BN, N - j0));
+  for (int64_t j0 = 0; j0 < Nk; j0 += BN) {
+    const int nk = static_cast<int>(std::min<int64_t>(BN, Nk - j0));
     __syncthreads();
     for (int x = t; x < BN * HD; x += kThreads) {
       const int jj = x / HD;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(
     for (int x = t; x < R * BN; x += kThreads) {
       const int rr = x / BN, jj = x - rr * BN;
       const int64_t ii = row0 + rr;
-      cs[x] = (ii < N && jj < nk) ? spd[ii * N + j0 + jj] : 0;
+      cs[x] = (ii < N && jj < nk) ? spd[ii * ldc + j0 + jj] : 0;
     }
     __syncthreads();
     if (!valid) continue;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_valu_kernel(
     const uint8_t* __restrict__ spd, const float* __restrict__ table,
     const float* __restrict__ lse, const float* __restrict__ delta, const T* __restrict__ dout,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ partial, int64_t N,
-    int H, int NB, int BM, float qscale, float scale) {
+    int64_t Nk, int64_t ldc, int H, int NB, int BM, float qscale, float scale, int acc) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int HD = H * D;
   const int CK = kThreads / H;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_valu_kernel(
   const int c = t / H, h = t - c * H;
   const int64_t col0 = static_cast<int64_t>(blockIdx.x) * CK;
   const int64_t j = col0 + c;
-  const bool valid = (c < CK) && (j < N);
+  const bool valid = (c < CK) && (j < Nk);
 
   for (int x = t; x < H * NB; x += kThreads) tb[x] = table[x] * kLog2e;
   for (int b = 0; b < NB; ++b) bins[b * kThreads + t] = 0.f;
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_valu_kernel(
     }
     for (int x = t; x < BM * CK; x += kThreads) {
       const int ii = x / CK, cc = x - ii * CK;
-      cs[x] = (ii < nq && col0 + cc < N) ? spd[(i0 + ii) * N + col0 + cc] : 0;
+      cs[x] = (ii < nq && col0 + cc < Nk) ? spd[(i0 + ii) * ldc + col0 + cc] : 0;
     }
     __syncthreads();
     if (!valid) continue;
@@ -230,8 +230,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_valu_kernel(
   if (valid) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      dk[(j * H + h) * D + d] = dka[d] * scale;
-      dv[(j * H + h) * D + d] = dva[d];
+      const int64_t o = (j * H + h) * D + d;
+      dk[o] = acc ? dk[o] + dka[d] * scale : dka[d] * scale;
+      dv[o] = acc ? dv[o] + dva[d] : dva[d];
     }
   }
   __syncthreads();
@@ -250,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const uint8_t* __restrict__ spd, const float* __restrict__ table,
     const float* __restrict__ lse, const float* __restrict__ delta, const T* __restrict__ dout,
-    float* __restrict__ dq, int64_t N, int H, int NB, int BN, float qscale, float scale) {
+    float* __restrict__ dq, int64_t N, int64_t Nk, int64_t ldc, int H, int NB, int BN, float qscale, float scale,
+    int acc) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int HD = H * D;
   const int R = kThreads / H;
@@ -277,8 +279,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
   const float dl = valid ? delta[i * H + h] : 0.f;
   const float* tbh = tb + h * NB;
 
-  for (int64_t j0 = 0; j0 < N; j0 += BN) {
-    const int nk = static_cast<int>(std::min<int64_t>(BN, N - j0));
+  for (int64_t j0 = 0; j0 < Nk; j0 += BN) {
+    const int nk = static_cast<int>(std::min<int64_t>(BN, Nk - j0));
     __syncthreads();
     for (int x = t; x < BN * HD; x += kThreads) {
       const int jj = x / HD;
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
     for (int x = t; x < R * BN; x += kThreads) {
       const int rr = x / BN, jj = x - rr * BN;
       const int64_t ii = row0 + rr;
-      cs[x] = (ii < N && jj < nk) ? spd[ii * N + j0 + jj] : 0;
+      cs[x] = (ii < N && jj < nk) ? spd[ii * ldc + j0 + jj] : 0;
     }
     __syncthreads();
     if (!valid) continue;
@@ -317,7 +319,10 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
   }
   if (valid) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) dq[(i * H + h) * D + d] = dqa[d] * scale;
+    for (int d = 0; d < D; ++d) {
+      const int64_t o = (i * H + h) * D + d;
+      dq[o] = acc ? dq[o] + dqa[d] * scale : dqa[d] * scale;
+    }
   }
 }
 
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
 // order within each thread and a fixed tree across the workgroup (deterministic).
 __global__ __launch_bounds__(kThreads) void dtable_reduce_kernel(const float* __restrict__ partial,
                                                                  float* __restrict__ dtable,
-                                                                 int64_t nblocks, int HNB) {
+                                                                 int64_t nblocks, int HNB, int acc) {
   __shared__ float red[kThreads];
   const int x = blockIdx.x;
   float s = 0.f;
@@ -336,7 +341,30 @@ __global__ __launch_bounds__(kThreads) void dtable_reduce_kernel(const float* __
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) dtable[x] = red[0];
+  if (threadIdx.x == 0) dtable[x] = acc ? dtable[x] + red[0] : red[0];
+}
+
+// out = (exp(lse_a - lse) out_a + exp(lse_b - lse) out_b), lse = log(exp(lse_a) + exp(lse_b)),
+// one thread per (node, head) row of D values; out and lse may alias either input.
+__global__ __launch_bounds__(kThreads) void merge_kernel(const float* out_a, const float* lse_a,
+                                                         const float* out_b, const float* lse_b, float* out,
+                                                         float* lse, int64_t rows, int D) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (r >= rows) return;
+  const float la = lse_a[r], lb = lse_b[r];
+  const float m = fmaxf(la, lb);
+  // a side with lse = -inf (no keys) gets weight 0; both -inf cannot be normalised
+  const float wa = la == -INFINITY ? 0.f : expf(la - m);
+  const float wb = lb == -INFINITY ? 0.f : expf(lb - m);
+  const float sum = wa + wb;
+  const float fa = wa / sum, fb = wb / sum;
+  for (int d = 0; d < D; d += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(out_a + r * D + d);
+    const float4 b = *reinterpret_cast<const float4*>(out_b + r * D + d);
+    *reinterpret_cast<float4*>(out + r * D + d) =
+        make_float4(fa * a.x + fb * b.x, fa * a.y + fb * b.y, fa * a.z + fb * b.z, fa * a.w + fb * b.w);
+  }
+  lse[r] = m + logf(sum);
 }
 
 int fwd_tile_keys(int H, int D, int NB) {
@@ -383,7 +411,7 @@ hipError_t fwd_typed(const FwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((fwd_valu_kernel<T, D>), dim3(grid), dim3(kThreads), lds, s,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), a.spd, a.table, a.out, a.lse,
-                     a.N, a.H, a.NB, BN, qscale);
+                     a.N, a.Nk, a.ld, a.H, a.NB, BN, qscale);
   const hipError_t e = hipGetLastError();
   trace_end(0, s);
   return e;
@@ -416,7 +444,7 @@ hipError_t bwd_typed(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
   trace_begin(2, s);
   hipLaunchKernelGGL((bwd_kv_valu_kernel<T, D>), dim3(static_cast<unsigned>(w.n_kv_blocks)),
                      dim3(kThreads), lds_kv, s, q, k, v, a.spd, a.table, a.lse, delta, dout, a.dk,
-                     a.dv, partial, a.N, a.H, a.NB, BM, qscale, scale);
+                     a.dv, partial, a.N, a.Nk, a.ld, a.H, a.NB, BM, qscale, scale, a.acc & kAccDkv);
   e = hipGetLastError();
   trace_end(2, s);
   if (e != hipSuccess) return e;
@@ -427,12 +455,12 @@ hipError_t bwd_typed(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
   trace_begin(3, s);
   hipLaunchKernelGGL((bwd_q_valu_kernel<T, D>), dim3(static_cast<unsigned>((a.N + R - 1) / R)),
                      dim3(kThreads), lds_q, s, q, k, v, a.spd, a.table, a.lse, delta, dout, a.dq,
-                     a.N, a.H, a.NB, BN, qscale, scale);
+                     a.N, a.Nk, a.ld, a.H, a.NB, BN, qscale, scale, a.acc & kAccDq);
   e = hipGetLastError();
   trace_end(3, s);
   if (e != hipSuccess) return e;
 
-  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, a.H * a.NB, s);
+  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, a.H * a.NB, a.acc & kAccDtable, s);
 }
 
 template <typename T>
@@ -459,12 +487,23 @@ hipError_t bwd_by_d(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
 
 int64_t valu_kv_block(int H) { return kThreads / H; }
 
-hipError_t launch_dtable_reduce(const float* partial, float* dtable, int64_t nblocks, int HNB, hipStream_t s) {
-  trace_begin(4, s);
+hipError_t launch_dtable_reduce(const float* partial, float* dtable, int64_t nblocks, int HNB, int acc,
+                                hipStream_t s) {
+  trace_begin(kTraceBwdDtable, s);
   hipLaunchKernelGGL(dtable_reduce_kernel, dim3(static_cast<unsigned>(HNB)), dim3(kThreads), 0, s, partial,
-                     dtable, nblocks, HNB);
+                     dtable, nblocks, HNB, acc);
   const hipError_t e = hipGetLastError();
-  trace_end(4, s);
+  trace_end(kTraceBwdDtable, s);
+  return e;
+}
+
+hipError_t launch_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b, float* out,
+                        float* lse, int64_t rows, int D, hipStream_t s) {
+  trace_begin(kTraceMerge, s);
+  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>((rows + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, out_a, lse_a, out_b, lse_b, out, lse, rows, D);
+  const hipError_t e = hipGetLastError();
+  trace_end(kTraceMerge, s);
   return e;
 }
 

@@ -91,7 +91,7 @@ hipEvent_t trace_event() {
 }
 
 const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd",     "bwd_delta",  "bwd_kv",     "bwd_q", "bwd_dtable",
-                                                   "qkv_fwd", "qkv_bwd_dx", "qkv_bwd_dw", "store"};
+                                                   "qkv_fwd", "qkv_bwd_dx", "qkv_bwd_dw", "store", "merge"};
 
 int check_dtype(int32_t dtype) {
   if (dtype != GT_F32 && dtype != GT_BF16) return fail(GT_EINVAL, "dtype=%d is not GT_F32 or GT_BF16", dtype);
@@ -112,6 +112,18 @@ int check_workspace(const void* ws, size_t have, size_t need) {
 }
 
 size_t up256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Shapes of a block step: Nq queries against Nk keys.
+int check_block(int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  if (Nq < 1 || Nq > 0x7FFFFFFFll) return fail(GT_EINVAL, "Nq=%lld must lie in [1, 2^31-1]", (long long)Nq);
+  if (Nk < 1 || Nk > 0x7FFFFFFFll) return fail(GT_EINVAL, "Nk=%lld must lie in [1, 2^31-1]", (long long)Nk);
+  return check_shape(Nq, H, D, NB, dtype);
+}
+
+int check_ld(int64_t ld, int64_t n, const char* name, const char* nname) {
+  if (ld < n) return fail(GT_EINVAL, "%s=%lld must be >= %s=%lld", name, (long long)ld, nname, (long long)n);
+  return GT_OK;
+}
 
 // Workspace of gt_stack_fwd_bwd: per layer the saved activations (Q, K, V and the
 // next layer's input in storage type, out and lse in float32), then the backward's
@@ -152,7 +164,7 @@ StackLayout stack_layout(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB,
   o += up256(n * hid * 4);
   s.dv = o;
   o += up256(n * hid * 4);
-  s.attn_ws = gt::bwd_workspace(N, H, D, NB, dtype);
+  s.attn_ws = gt::bwd_workspace(N, N, H, D, NB, dtype);
   s.attn = o;
   o += up256(s.attn_ws.bytes);
   s.proj = o;
@@ -191,15 +203,15 @@ void trace_end(int kernel_id, hipStream_t s) {
   g_trace_open = nullptr;
 }
 
-BwdWorkspace bwd_workspace(int64_t N, int H, int D, int NB, int dtype) {
+BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtype) {
   BwdWorkspace w{};
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const bool mfma = mfma_supported(H, D, dtype);
   const int64_t kb = valu_kv_block(H);
-  w.n_kv_blocks = mfma ? (D == 32 ? mfma_d32_kv_blocks(N) : mfma_kv_blocks(N)) : (N + kb - 1) / kb;
+  w.n_kv_blocks = mfma ? (D == 32 ? mfma_d32_kv_blocks(Nk) : mfma_kv_blocks(Nk)) : (Nk + kb - 1) / kb;
   w.delta_off = 0;
   w.ops_off = up(static_cast<size_t>(N) * H * sizeof(float));
-  w.partial_off = w.ops_off + (mfma ? up(D == 32 ? mfma_d32_ops_bytes(N) : mfma_ops_bytes(N)) : 0);
+  w.partial_off = w.ops_off + (mfma ? up(D == 32 ? mfma_d32_ops_bytes(N, Nk) : mfma_ops_bytes(N, Nk)) : 0);
   w.bytes = w.partial_off + up(static_cast<size_t>(w.n_kv_blocks) * H * NB * sizeof(float));
   return w;
 }
@@ -266,7 +278,7 @@ int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(table, "table"));
   GT_CHECK(check_ptr(out, "out"));
   GT_CHECK(check_ptr(lse, "lse"));
-  gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype};
+  gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype, N, N};
   return hip_status(attn_fwd(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd launch");
 }
 
@@ -275,7 +287,7 @@ size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, 
   const int rc = check_shape(N, H, D, NB, dtype);
   g_error = saved;
   if (rc != GT_OK) return 0;
-  return gt::bwd_workspace(N, H, D, NB, dtype).bytes;
+  return gt::bwd_workspace(N, N, H, D, NB, dtype).bytes;
 }
 
 int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd, const uint8_t* spd_t,
@@ -297,10 +309,81 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(dk, "dk"));
   GT_CHECK(check_ptr(dv, "dv"));
   GT_CHECK(check_ptr(dtable, "dtable"));
-  const gt::BwdWorkspace w = gt::bwd_workspace(N, H, D, NB, dtype);
+  const gt::BwdWorkspace w = gt::bwd_workspace(N, N, H, D, NB, dtype);
   GT_CHECK(check_workspace(workspace, workspace_bytes, w.bytes));
-  gt::BwdArgs a{q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, workspace, N, H, D, NB, dtype};
+  gt::BwdArgs a{q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, workspace, N, H, D, NB, dtype,
+                N, N, N, 0};
   return hip_status(attn_bwd(a, w, static_cast<hipStream_t>(stream)), "gt_attn_bwd launch");
+}
+
+int gt_attn_fwd_block(const void* q, const void* k, const void* v, const uint8_t* spd, int64_t ld,
+                      const float* table, float* out, float* lse, int64_t Nq, int64_t Nk, int32_t H, int32_t D,
+                      int32_t NB, int32_t dtype, void* stream) {
+  GT_CHECK(check_block(Nq, Nk, H, D, NB, dtype));
+  GT_CHECK(check_ld(ld, Nk, "ld", "Nk"));
+  GT_CHECK(check_ptr(q, "q"));
+  GT_CHECK(check_ptr(k, "k"));
+  GT_CHECK(check_ptr(v, "v"));
+  if (spd == nullptr) return fail(GT_EINVAL, "spd is null");
+  GT_CHECK(check_ptr(table, "table"));
+  GT_CHECK(check_ptr(out, "out"));
+  GT_CHECK(check_ptr(lse, "lse"));
+  gt::FwdArgs a{q, k, v, spd, table, out, lse, Nq, H, D, NB, dtype, Nk, ld};
+  return hip_status(attn_fwd(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd_block launch");
+}
+
+int gt_attn_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b, float* out,
+                  float* lse, int64_t Nq, int32_t H, int32_t D, void* stream) {
+  if (Nq < 1 || Nq > 0x7FFFFFFFll) return fail(GT_EINVAL, "Nq=%lld must lie in [1, 2^31-1]", (long long)Nq);
+  if (H < 1 || H > 64) return fail(GT_EINVAL, "H=%d must lie in [1, 64]", H);
+  if (D != 8 && D != 16 && D != 32 && D != 64)
+    return fail(GT_EUNSUPPORTED, "D=%d: supported head dimensions are 8, 16, 32, 64", D);
+  GT_CHECK(check_ptr(out_a, "out_a"));
+  GT_CHECK(check_ptr(lse_a, "lse_a"));
+  GT_CHECK(check_ptr(out_b, "out_b"));
+  GT_CHECK(check_ptr(lse_b, "lse_b"));
+  GT_CHECK(check_ptr(out, "out"));
+  GT_CHECK(check_ptr(lse, "lse"));
+  return hip_status(gt::launch_merge(out_a, lse_a, out_b, lse_b, out, lse, Nq * H, D, static_cast<hipStream_t>(stream)),
+                    "gt_attn_merge launch");
+}
+
+size_t gt_attn_bwd_block_workspace_bytes(int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  const std::string saved = g_error;
+  const int rc = check_block(Nq, Nk, H, D, NB, dtype);
+  g_error = saved;
+  if (rc != GT_OK) return 0;
+  return gt::bwd_workspace(Nq, Nk, H, D, NB, dtype).bytes;
+}
+
+int gt_attn_bwd_block(const void* q, const void* k, const void* v, const uint8_t* spd, int64_t ld,
+                      const uint8_t* spd_t, int64_t ld_t, const float* table, const float* out, const float* lse,
+                      const void* dout, float* dq, float* dk, float* dv, float* dtable, void* workspace,
+                      size_t workspace_bytes, int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB,
+                      int32_t dtype, int32_t accumulate, void* stream) {
+  GT_CHECK(check_block(Nq, Nk, H, D, NB, dtype));
+  GT_CHECK(check_ld(ld, Nk, "ld", "Nk"));
+  GT_CHECK(check_ld(ld_t, Nq, "ld_t", "Nq"));
+  if (accumulate < 0 || accumulate > GT_ACC_ALL)
+    return fail(GT_EINVAL, "accumulate=%d must be a combination of the GT_ACC_* bits", accumulate);
+  GT_CHECK(check_ptr(q, "q"));
+  GT_CHECK(check_ptr(k, "k"));
+  GT_CHECK(check_ptr(v, "v"));
+  if (spd == nullptr) return fail(GT_EINVAL, "spd is null");
+  if (spd_t == nullptr) return fail(GT_EINVAL, "spd_t is null");
+  GT_CHECK(check_ptr(table, "table"));
+  GT_CHECK(check_ptr(out, "out"));
+  GT_CHECK(check_ptr(lse, "lse"));
+  GT_CHECK(check_ptr(dout, "dout"));
+  GT_CHECK(check_ptr(dq, "dq"));
+  GT_CHECK(check_ptr(dk, "dk"));
+  GT_CHECK(check_ptr(dv, "dv"));
+  GT_CHECK(check_ptr(dtable, "dtable"));
+  const gt::BwdWorkspace w = gt::bwd_workspace(Nq, Nk, H, D, NB, dtype);
+  GT_CHECK(check_workspace(workspace, workspace_bytes, w.bytes));
+  gt::BwdArgs a{q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, workspace, Nq, H, D, NB, dtype,
+                Nk, ld, ld_t, accumulate};
+  return hip_status(attn_bwd(a, w, static_cast<hipStream_t>(stream)), "gt_attn_bwd_block launch");
 }
 
 int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C, uint8_t* spd,
@@ -404,7 +487,7 @@ int gt_stack_fwd_bwd(const void* x0, const void* w, const float* tables, const u
     float* lse = reinterpret_cast<float*>(layer(l, lay.lse));
     void* xn = l == L - 1 ? x_last : layer(l, lay.xn);
     GT_CHECK(hip_status(gt::launch_qkv_fwd(X, wl, q, k, v, N, hid, dtype, s), "gt_stack_fwd_bwd qkv"));
-    const gt::FwdArgs fa{q, k, v, spd, tables + static_cast<size_t>(l) * H * NB, out, lse, N, H, D, NB, dtype};
+    const gt::FwdArgs fa{q, k, v, spd, tables + static_cast<size_t>(l) * H * NB, out, lse, N, H, D, NB, dtype, N, N};
     GT_CHECK(hip_status(attn_fwd(fa, s), "gt_stack_fwd_bwd attention forward"));
     GT_CHECK(hip_status(gt::launch_store(out, xn, nel, dtype, s), "gt_stack_fwd_bwd store"));
     X = xn;
@@ -420,7 +503,8 @@ int gt_stack_fwd_bwd(const void* x0, const void* w, const float* tables, const u
     const gt::BwdArgs ba{layer(l, lay.q), layer(l, lay.k), layer(l, lay.v), spd, spd_t,
                          tables + static_cast<size_t>(l) * H * NB, reinterpret_cast<float*>(layer(l, lay.out)),
                          reinterpret_cast<float*>(layer(l, lay.lse)), dol, dq, dk, dv,
-                         dtable + static_cast<size_t>(l) * H * NB, base + lay.attn, N, H, D, NB, dtype};
+                         dtable + static_cast<size_t>(l) * H * NB, base + lay.attn, N, H, D, NB, dtype,
+                         N, N, N, 0};
     GT_CHECK(hip_status(attn_bwd(ba, lay.attn_ws, s), "gt_stack_fwd_bwd attention backward"));
     const void* Xl = l == 0 ? x0 : layer(l - 1, lay.xn);
     float* dxl = l == 0 ? dx0 : G;

@@ -97,6 +97,15 @@ __device__ __forceinline__ f32x16 mfma_b16(s16x8 a, s16x8 b, f32x16 c) {
 
 __device__ __forceinline__ s16x8 load_h8(const uint16_t* p) { return *reinterpret_cast<const s16x8*>(p); }
 
+// Epilogue store of four float results: overwrite, or add into what is there (acc).
+__device__ __forceinline__ void store4(float* p, float4 x, int acc) {
+  if (acc) {
+    const float4 o = *reinterpret_cast<const float4*>(p);
+    x = make_float4(o.x + x.x, o.y + x.y, o.z + x.z, o.w + x.w);
+  }
+  *reinterpret_cast<float4*>(p) = x;
+}
+
 // Workgroup -> (node block, head pair) mapping. Workgroups are dispatched round-robin
 // over the 8 XCDs (each with its own L2). The 4 head pairs of one node block read
 // the same code rows, so they are placed on one XCD, in consecutive dispatch slots.

@@ -89,6 +89,64 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
                 size_t workspace_bytes, int64_t N, int32_t H, int32_t D, int32_t NB,
                 int32_t dtype, void* stream);
 
+/* ---- Key-block steps (MegaGraph pages, Fig. 4 and its caption: under graph-aware
+ * context parallelism each device keeps its query rows while key/value blocks travel
+ * around a ring, and each arriving block is paired with the matching column slice of
+ * the bias). One call covers one device's work for one arriving block; running the
+ * blocks of a key partition in turn and merging reproduces gt_attn_fwd/gt_attn_bwd.
+ * For a key block [c0, c1) of a graph with N nodes and query rows [r0, r1):
+ *     q = q_all + r0*H*D, k = k_all + c0*H*D, v = v_all + c0*H*D,
+ *     spd = spd_all + r0*N + c0, ld = N          (column slice, rows stay N apart)
+ *     spd_t = spd_t_all + c0*N + r0, ld_t = N    (row slice of the transpose)
+ * Code pointers may have any alignment (16-byte aligned rows with ld a multiple of 16
+ * take whole-row vector loads). Other conventions as above, with Nq queries and Nk keys.
+ * ------------------------------------------------------------------------------- */
+
+/* Partial forward of Nq queries against Nk keys:
+ *   q        device [Nq,H,D] dtype          k, v   device [Nk,H,D] dtype
+ *   spd      device uint8, code of (query i, key j) at spd[i*ld + j], ld >= Nk
+ *   out      device [Nq,H,D] float32        lse    device [Nq,H] float32 (overwritten):
+ *            attention restricted to these keys, and its log-sum-exp.
+ * Sizes: 1 <= Nq, Nk < 2^31; H, D, NB, dtype as for gt_attn_fwd.                     */
+int gt_attn_fwd_block(const void* q, const void* k, const void* v, const uint8_t* spd, int64_t ld,
+                      const float* table, float* out, float* lse, int64_t Nq, int64_t Nk, int32_t H,
+                      int32_t D, int32_t NB, int32_t dtype, void* stream);
+
+/* Merge of two partial results over disjoint key sets (log-sum-exp rescaling):
+ *   lse = log(exp(lse_a) + exp(lse_b)),
+ *   out = exp(lse_a - lse) * out_a + exp(lse_b - lse) * out_b
+ * out_*: device [Nq,H,D] float32, lse_*: device [Nq,H] float32. out/lse may be the same
+ * buffers as out_a/lse_a (or out_b/lse_b), which makes it a running merge. A side with
+ * lse = -inf contributes nothing. D in {8,16,32,64}, 1 <= H <= 64.                   */
+int gt_attn_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b,
+                  float* out, float* lse, int64_t Nq, int32_t H, int32_t D, void* stream);
+
+/* Bytes of device workspace gt_attn_bwd_block needs (0 on invalid sizes). */
+size_t gt_attn_bwd_block_workspace_bytes(int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB,
+                                         int32_t dtype);
+
+/* Backward of one key block for the loss sum(dout * out), where out and lse are the
+ * MERGED results over all keys (so the block's probabilities are the full softmax's):
+ *   spd, ld        as in gt_attn_fwd_block; spd_t: code of (query i, key j) at
+ *                  spd_t[j*ld_t + i], ld_t >= Nq
+ *   out, lse       device [Nq,H,D], [Nq,H] float32: merged forward results
+ *   dout           device [Nq,H,D] dtype
+ *   dq             device [Nq,H,D] float32: this block's share of dQ
+ *   dk, dv         device [Nk,H,D] float32: the block's keys' gradients from these queries
+ *   dtable         device [H,NB] float32: this block's share of the bucket gradient
+ *   accumulate     GT_ACC_* bits: a set bit adds that output into what the buffer
+ *                  holds (summing blocks), a clear bit overwrites it. In a ring, dq
+ *                  stays with its rank (add from the second block on) while dk, dv
+ *                  travel with their block (add from the second rank on).
+ *   workspace      device, >= gt_attn_bwd_block_workspace_bytes(Nq, Nk, ...), as for
+ *                  gt_attn_bwd.                                                       */
+enum { GT_ACC_DQ = 1, GT_ACC_DKV = 2, GT_ACC_DTABLE = 4, GT_ACC_ALL = 7 };
+int gt_attn_bwd_block(const void* q, const void* k, const void* v, const uint8_t* spd, int64_t ld,
+                      const uint8_t* spd_t, int64_t ld_t, const float* table, const float* out,
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv, float* dtable,
+                      void* workspace, size_t workspace_bytes, int64_t Nq, int64_t Nk, int32_t H,
+                      int32_t D, int32_t NB, int32_t dtype, int32_t accumulate, void* stream);
+
 /* Clipped hop-distance codes on the host (the topology that "topology-aware" refers to).
  *   indptr   host int64 [N+1], indices host int32 [indptr[N]]: an undirected graph in
  *            CSR form (both directions stored; neighbour order is free).
@@ -178,7 +236,8 @@ enum {
   GT_KERNEL_QKV_BWD_DX = 6, /* gt_qkv_bwd: dX                                      */
   GT_KERNEL_QKV_BWD_DW = 7, /* gt_qkv_bwd: dW partial sums and their reduction     */
   GT_KERNEL_STORE = 8,      /* gt_store                                            */
-  GT_KERNEL_COUNT = 9
+  GT_KERNEL_MERGE = 9,      /* gt_attn_merge                                       */
+  GT_KERNEL_COUNT = 10
 };
 int gt_trace_enable(int32_t on);
 int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n);

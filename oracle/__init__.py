@@ -24,6 +24,6 @@ closed forms, permutation equivariance and finite differences. No function
 here is "parity unpinned".
 """
 from .spd import bfs_codes, bfs_codes_parallel, certify_codes, components  # noqa: F401
-from .attention import forward, backward, full_backward, sum_dtable_rows  # noqa: F401
+from .attention import forward, backward, backward_block, full_backward, merge, sum_dtable_rows  # noqa: F401
 from .bf16 import round_bf16  # noqa: F401
 from .stack import qkv_projection, qkv_projection_backward, stack_forward_backward  # noqa: F401

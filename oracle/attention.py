@@ -82,6 +82,64 @@ def backward(q, k, v, codes, table, dout):
     return out, lse, dq, dk, dv, dtable
 
 
+def merge(out_a, lse_a, out_b, lse_b):
+    """Attention over the union of two disjoint key sets from the results over each.
+
+    MegaGraph pages, Fig. 4 and its caption: under graph-aware context parallelism
+    each key/value block (with its slice of bias columns) yields a partial result,
+    and the partial results are combined through their softmax statistics. With
+    lse the log of a set's softmax denominator, the union's denominator is the sum
+    of the two, and each partial output enters with the share of the denominator
+    its keys hold. A side with lse = -inf (no keys) has share 0.
+    """
+    lse_a = np.asarray(lse_a, np.float64)
+    lse_b = np.asarray(lse_b, np.float64)
+    lse = np.logaddexp(lse_a, lse_b)
+    wa = np.exp(lse_a - lse)[..., None]
+    wb = np.exp(lse_b - lse)[..., None]
+    return wa * np.asarray(out_a, np.float64) + wb * np.asarray(out_b, np.float64), lse
+
+
+def backward_block(q, k, v, codes, table, out, lse, dout):
+    """Gradient contributions of one key block, given the forward over ALL keys.
+
+    q, dout: [R,H,D] query rows; k, v: [K,H,D] the block's keys; codes: [R,K] the
+    bias columns of the block; out, lse: [R,H,D], [R,H] the merged forward results
+    over every key. The block's probabilities are the full softmax's entries in
+    its columns, P = exp(S - lse), and with delta = rowsum(dout * out) the score
+    gradient is dS = P (dout v^T - delta). Returns dq [R,H,D] (this block's share:
+    summing over blocks gives the full dq), dk, dv [K,H,D] (the block's keys'
+    gradients from these rows) and dtable [H,NB] (this block's share).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    out = np.asarray(out, np.float64)
+    lse = np.asarray(lse, np.float64)
+    table = np.asarray(table, np.float64)
+    R, H, D = q.shape
+    K = k.shape[0]
+    NB = table.shape[1]
+    sc = 1.0 / np.sqrt(D)
+    cl = np.minimum(codes, NB - 1)
+    dq = np.empty((R, H, D))
+    dk = np.empty((K, H, D))
+    dv = np.empty((K, H, D))
+    dtable = np.empty((H, NB))
+    for h in range(H):
+        S = q[:, h, :] @ k[:, h, :].T * sc + table[h][cl]
+        P = np.exp(S - lse[:, h:h + 1])
+        dO = dout[:, h, :]
+        delta = (dO * out[:, h, :]).sum(axis=1, keepdims=True)
+        dS = P * (dO @ v[:, h, :].T - delta)
+        dq[:, h, :] = dS @ k[:, h, :] * sc
+        dk[:, h, :] = dS.T @ q[:, h, :] * sc
+        dv[:, h, :] = P.T @ dO
+        dtable[h] = np.bincount(cl.ravel(), weights=dS.ravel(), minlength=NB)
+    return dq, dk, dv, dtable
+
+
 def sum_dtable_rows(dtable_blocks):
     return np.sum(np.stack(dtable_blocks), axis=0)
 

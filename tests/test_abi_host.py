@@ -202,3 +202,42 @@ def test_projection_and_stack_argument_errors():
     assert stack(wsb=sw - 1) == gta.GT_EINVAL
     assert stack(x0=None) == gta.GT_EINVAL and "x0" in gta.last_error()
     assert stack(dout=P + 8) == gta.GT_EINVAL
+
+
+def test_block_argument_errors():
+    """Key-block steps: row strides, counts, the accumulate flag and the workspace are
+    checked before anything is enqueued; code pointers may have any alignment."""
+    L = gta.lib()
+    Nq, Nk, H, D, NB = 700, 300, 8, 8, 33
+
+    def fwd(ld=1000, Nq_=Nq, Nk_=Nk, spd=P + 3, q=P):
+        return L.gt_attn_fwd_block(q, P, P, spd, ld, P, P, P, Nq_, Nk_, H, D, NB, 1, None)
+    assert fwd(ld=Nk - 1) == gta.GT_EINVAL and "ld=299" in gta.last_error()
+    assert fwd(Nk_=0) == gta.GT_EINVAL and "Nk=0" in gta.last_error()
+    assert fwd(Nq_=0) == gta.GT_EINVAL and "Nq=0" in gta.last_error()
+    assert fwd(spd=None) == gta.GT_EINVAL and "spd is null" in gta.last_error()
+    assert fwd(q=P + 2) == gta.GT_EINVAL and "aligned" in gta.last_error()
+
+    need = L.gt_attn_bwd_block_workspace_bytes(Nq, Nk, H, D, NB, 1)
+    assert need >= Nq * H * 4
+    assert L.gt_attn_bwd_block_workspace_bytes(Nq, 0, H, D, NB, 1) == 0
+    # a square block needs exactly the whole-graph backward's workspace
+    assert L.gt_attn_bwd_block_workspace_bytes(Nq, Nq, H, D, NB, 1) == L.gt_attn_bwd_workspace_bytes(Nq, H, D, NB, 1)
+
+    def bwd(ld=1000, ldt=1000, acc=0, wsb=need, spdt=P + 5):
+        return L.gt_attn_bwd_block(P, P, P, P + 1, ld, spdt, ldt, P, P, P, P, P, P, P, P, P, wsb,
+                                   Nq, Nk, H, D, NB, 1, acc, None)
+    assert bwd(ldt=Nq - 1) == gta.GT_EINVAL and "ld_t=699" in gta.last_error()
+    assert bwd(ld=10) == gta.GT_EINVAL and "ld=10" in gta.last_error()
+    assert bwd(acc=8) == gta.GT_EINVAL and "accumulate" in gta.last_error()
+    assert bwd(acc=-1) == gta.GT_EINVAL
+    assert bwd(wsb=need - 1) == gta.GT_EINVAL and "workspace_bytes" in gta.last_error()
+    assert bwd(spdt=None) == gta.GT_EINVAL and "spd_t is null" in gta.last_error()
+
+    def merge(Nq_=Nq, H_=H, D_=D, out=P):
+        return L.gt_attn_merge(P, P, P, P, out, P, Nq_, H_, D_, None)
+    assert merge(Nq_=0) == gta.GT_EINVAL
+    assert merge(D_=12) == gta.GT_EUNSUPPORTED
+    assert merge(H_=0) == gta.GT_EINVAL
+    assert merge(out=None) == gta.GT_EINVAL and "out is null" in gta.last_error()
+    assert gta.kernel_names()[9] == "merge"

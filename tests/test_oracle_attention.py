@@ -232,6 +232,58 @@ def test_key_split_merge_by_lse():
     np.testing.assert_allclose(merged, out, rtol=1e-11, atol=1e-13)
 
 
+def test_merge_running_equals_unsplit():
+    """oracle.merge applied block after block (a running merge, as each key block
+    arrives) gives unsplit attention; the order of the blocks does not matter."""
+    q, k, v, codes, table, _ = _rand(31, 41, H=3, D=4, NB=6)
+    out, lse = oracle.forward(q, k, v, codes, table)
+    cuts = [0, 1, 16, 29, 41]
+    parts = [oracle.forward(q, k[a:b], v[a:b], codes[:, a:b], table) for a, b in zip(cuts, cuts[1:])]
+    for order in ([0, 1, 2, 3], [3, 1, 0, 2]):
+        o, l = parts[order[0]]
+        for i in order[1:]:
+            o, l = oracle.merge(o, l, *parts[i])
+        np.testing.assert_allclose(l, lse, rtol=1e-13)
+        np.testing.assert_allclose(o, out, rtol=1e-11, atol=1e-13)
+
+
+def test_merge_with_empty_side_is_identity():
+    rng = np.random.default_rng(32)
+    o = rng.standard_normal((5, 2, 8))
+    l = rng.standard_normal((5, 2))
+    empty_o = rng.standard_normal((5, 2, 8))
+    empty_l = np.full((5, 2), -np.inf)
+    for got in (oracle.merge(o, l, empty_o, empty_l), oracle.merge(empty_o, empty_l, o, l)):
+        np.testing.assert_array_equal(got[0], o)
+        np.testing.assert_array_equal(got[1], l)
+
+
+def test_backward_block_sums_to_full_backward():
+    """Key blocks x query blocks (virtual ranks holding query rows, key/value blocks
+    visiting each): dq summed over key blocks, dk/dv summed over query blocks and
+    dtable summed over both equal the unsplit backward."""
+    q, k, v, codes, table, do = _rand(33, 37, H=2, D=4, NB=5)
+    out, lse, dq, dk, dv, dtable = oracle.backward(q, k, v, codes, table, do)
+    kc = [0, 11, 12, 37]
+    qc = [0, 20, 37]
+    gdq = np.zeros_like(dq)
+    gdk = np.zeros_like(dk)
+    gdv = np.zeros_like(dv)
+    gdt = np.zeros_like(dtable)
+    for r0, r1 in zip(qc, qc[1:]):
+        for c0, c1 in zip(kc, kc[1:]):
+            a, b, c, d = oracle.backward_block(q[r0:r1], k[c0:c1], v[c0:c1], codes[r0:r1, c0:c1], table,
+                                               out[r0:r1], lse[r0:r1], do[r0:r1])
+            gdq[r0:r1] += a
+            gdk[c0:c1] += b
+            gdv[c0:c1] += c
+            gdt += d
+    np.testing.assert_allclose(gdq, dq, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(gdk, dk, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(gdv, dv, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(gdt, dtable, rtol=1e-10, atol=1e-13)
+
+
 def test_bf16_rounding_vs_torch():
     rng = np.random.default_rng(20)
     x = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.integers(-6, 6, 100000),
