@@ -46,7 +46,11 @@ def lib() -> ctypes.CDLL:
                                "`python -m graph_transformer_attention_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
-        L.gt_attn_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I32, I32, P]
+        L.gt_attn_fwd.argtypes = [P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, I32, P]
+        L.gt_attn_fwd_workspace_bytes.argtypes = [I64, I32, I32, I32, I32]
+        L.gt_attn_fwd_workspace_bytes.restype = SZ
+        L.gt_attn_fwd_block_workspace_bytes.argtypes = [I64, I64, I32, I32, I32, I32]
+        L.gt_attn_fwd_block_workspace_bytes.restype = SZ
         L.gt_attn_fwd.restype = ctypes.c_int
         L.gt_attn_bwd_workspace_bytes.argtypes = [I64, I32, I32, I32, I32]
         L.gt_attn_bwd_workspace_bytes.restype = SZ
@@ -77,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.gt_stack_workspace_bytes.argtypes = [I64, I32, I32, I32, I32, I32]
         L.gt_stack_workspace_bytes.restype = SZ
         L.gt_stack_fwd_bwd.argtypes = [P] * 11 + [SZ, I64, I32, I32, I32, I32, I32, P]
-        L.gt_attn_fwd_block.argtypes = [P, P, P, P, I64, P, P, P, I64, I64, I32, I32, I32, I32, P]
+        L.gt_attn_fwd_block.argtypes = [P, P, P, P, I64, P, P, P, P, SZ, I64, I64, I32, I32, I32, I32, I32, P]
         L.gt_attn_fwd_block.restype = ctypes.c_int
         L.gt_attn_merge.argtypes = [P] * 6 + [I64, I32, I32, P]
         L.gt_attn_merge.restype = ctypes.c_int
@@ -128,13 +132,28 @@ def _dev(t, name, dtype=None, shape=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def fwd(q, k, v, spd, table, out=None, lse=None, stream=None):
+def _workspace(nbytes, workspace, device, name="workspace"):
+    """(pointer, size) of a caller's workspace, or of a new one; none when nbytes is 0."""
+    import torch
+    if nbytes == 0 and workspace is None:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _dev(workspace, name), _nbytes(workspace)
+
+
+def fwd_workspace_bytes(N: int, H: int, D: int, NB: int, dtype: int) -> int:
+    return int(lib().gt_attn_fwd_workspace_bytes(N, H, D, NB, dtype))
+
+
+def fwd(q, k, v, spd, table, out=None, lse=None, workspace=None, stream=None):
     """Forward: q, k, v [N,H,D] (float32 or bfloat16), spd [N,N] uint8, table [H,NB] float32.
     Returns (out [N,H,D] float32, lse [N,H] float32)."""
     import torch
     N, H, D = q.shape
     NB = table.shape[1]
     dt = _dtype_code(q)
+    wp, wn = _workspace(fwd_workspace_bytes(N, H, D, NB, dt), workspace, q.device)
     if out is None:
         out = torch.empty((N, H, D), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -143,7 +162,7 @@ def fwd(q, k, v, spd, table, out=None, lse=None, stream=None):
             _dev(v, "v", q.dtype, (N, H, D)), _dev(spd, "spd", torch.uint8, (N, N)),
             _dev(table, "table", torch.float32, (H, NB)), _dev(out, "out", torch.float32, (N, H, D)),
             _dev(lse, "lse", torch.float32, (N, H))]
-    _check("gt_attn_fwd", lib().gt_attn_fwd(*args, N, H, D, NB, dt, _stream(stream)))
+    _check("gt_attn_fwd", lib().gt_attn_fwd(*args, wp, wn, N, H, D, NB, dt, _stream(stream)))
     return out, lse
 
 
@@ -198,25 +217,34 @@ def _codes(t, name, rows, cols):
     return ctypes.c_void_p(t.data_ptr()), ld
 
 
-def fwd_block(q, k, v, spd, table, out=None, lse=None, stream=None):
+def fwd_block_workspace_bytes(Nq: int, Nk: int, H: int, D: int, NB: int, dtype: int) -> int:
+    return int(lib().gt_attn_fwd_block_workspace_bytes(Nq, Nk, H, D, NB, dtype))
+
+
+def fwd_block(q, k, v, spd, table, out=None, lse=None, workspace=None, accumulate=False, stream=None):
     """Attention of Nq query rows restricted to one block of Nk keys.
 
     q [Nq,H,D], k, v [Nk,H,D] (float32 or bfloat16); spd [Nq,Nk] uint8, usually a
     slice spd_all[r0:r1, c0:c1] (rows may be strided); table [H,NB] float32.
-    Returns the block's (out [Nq,H,D], lse [Nq,H]) float32, to be merged with merge()."""
+    Returns the block's (out [Nq,H,D], lse [Nq,H]) float32. With accumulate=True, out
+    and lse hold a result over other keys on entry and the block is merged into them."""
     import torch
     Nq, H, D = q.shape
     Nk = k.shape[0]
     NB = table.shape[1]
     dt = _dtype_code(q)
     f32 = torch.float32
+    if accumulate and (out is None or lse is None):
+        raise ValueError("accumulate=True needs the running out and lse")
     out = torch.empty((Nq, H, D), dtype=f32, device=q.device) if out is None else out
     lse = torch.empty((Nq, H), dtype=f32, device=q.device) if lse is None else lse
     sp, ld = _codes(spd, "spd", Nq, Nk)
+    wp, wn = _workspace(fwd_block_workspace_bytes(Nq, Nk, H, D, NB, dt), workspace, q.device)
     args = [_dev(q, "q", q.dtype, (Nq, H, D)), _dev(k, "k", q.dtype, (Nk, H, D)),
             _dev(v, "v", q.dtype, (Nk, H, D)), sp, ld, _dev(table, "table", f32, (H, NB)),
-            _dev(out, "out", f32, (Nq, H, D)), _dev(lse, "lse", f32, (Nq, H))]
-    _check("gt_attn_fwd_block", lib().gt_attn_fwd_block(*args, Nq, Nk, H, D, NB, dt, _stream(stream)))
+            _dev(out, "out", f32, (Nq, H, D)), _dev(lse, "lse", f32, (Nq, H)), wp, wn]
+    _check("gt_attn_fwd_block", lib().gt_attn_fwd_block(*args, Nq, Nk, H, D, NB, dt, int(bool(accumulate)),
+                                                        _stream(stream)))
     return out, lse
 
 
@@ -378,7 +406,7 @@ def stack_fwd_bwd(x0, w, tables, spd, dout, H: int, spd_t=None, workspace=None, 
     return x_last, dx0, dw, dtable
 
 
-KERNEL_COUNT = 10
+KERNEL_COUNT = 12
 
 
 def kernel_names():

@@ -88,9 +88,21 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
                                                                     const float* __restrict__ table,
                                                                     float* __restrict__ out,
                                                                     float* __restrict__ lse, int64_t N, int64_t Nk,
-                                                                    int64_t ldc, int NB) {
+                                                                    int64_t ldc, int NB, int64_t kchunk,
+                                                                    int64_t ostride, int64_t lstride) {
   __shared__ float tb[2 * 256];
   __shared__ __align__(16) uint16_t vt[2][2][kD + 1][32];  // [buffer][head][d or ones][key]
+  // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial
+  // results at out + y*ostride, lse + y*lstride
+  {
+    const int64_t jb = static_cast<int64_t>(blockIdx.y) * kchunk;
+    k += jb * kHD;
+    v += jb * kHD;
+    spd += jb;
+    Nk = Nk - jb < kchunk ? Nk - jb : kchunk;
+    out += blockIdx.y * ostride;
+    lse += blockIdx.y * lstride;
+  }
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int c = lane & 31, hp = lane >> 5;
@@ -425,8 +437,20 @@ __device__ __forceinline__ s16x8 staged_tr(const uint16_t* tr, int hl, int m, in
 template <bool kAligned>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
     const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ partial, int64_t N, int64_t Nk, int64_t ldt, int NB, int acc) {
+    float* __restrict__ dv, float* __restrict__ partial, int64_t N, int64_t Nk, int64_t ldt, int NB, int acc,
+    int64_t qchunk, int64_t gstride, int64_t pstride) {
   extern __shared__ __align__(16) unsigned char smem[];
+  // workgroup row y of a split launch: queries [y*qchunk, min(N, (y+1)*qchunk)), partial
+  // dK, dV at + y*gstride and bucket partials at + y*pstride
+  const int64_t ib = static_cast<int64_t>(blockIdx.y) * qchunk;
+  N = N - ib < qchunk ? N - ib : qchunk;
+  ops.qa += ib * kH * 16;
+  ops.doa += ib * kH * 16;
+  ops.qt += ib;
+  ops.ot += ib;
+  dk += blockIdx.y * gstride;
+  dv += blockIdx.y * gstride;
+  partial += blockIdx.y * pstride;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 64);      // [NB][64 lanes][2 heads] per wave
   float* tb = reinterpret_cast<float*>(smem) + kBwdWaves * 2 * NB * 64;  // [2][64] by clamped code
@@ -459,7 +483,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
   const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
   float2* mybins = reinterpret_cast<float2*>(bins) + lane;
-  const uint8_t* crow = spd_t + (j < Nk ? j : Nk - 1) * ldt;
+  const uint8_t* crow = spd_t + (j < Nk ? j : Nk - 1) * ldt + ib;
   const int64_t cc = 16 * hp;  // this lane's first code column within a tile
 
   StageSrc src;
@@ -467,7 +491,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   src.row1 = ops.doa + h0 * 16;
   src.tr0 = ops.qt + static_cast<int64_t>(h0) * kD * npad;
   src.tr1 = ops.ot + static_cast<int64_t>(h0) * kD * npad;
-  const int64_t ntiles = npad / 32, nfull = N / 32;
+  const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
   constexpr int kCh = 384;  // qa, doa, q^T, dout^T
   s16x8 sr[stage_per_thread<kCh>()];
   stage_load<kCh>(sr, src, npad, 0, tid);
@@ -542,8 +566,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   for (int x = lane; x < 2 * NB; x += 64) {
     const int hl = x / NB, b = x - hl * NB;
     const float* srcb = bins + b * 128 + hl;
-    float sum = 0.f;
-    for (int l = 0; l < 64; ++l) sum += srcb[2 * l];
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains, fixed order
+#pragma unroll
+    for (int l = 0; l < 64; l += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s4[u] += srcb[2 * (l + u)];
+    }
+    const float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     partial[((jw / 32) * kH + h0 + hl) * NB + b] = sum;
   }
 }
@@ -557,9 +586,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
                                                                       const float* __restrict__ table,
                                                                       BwdOps ops, float* __restrict__ dq,
                                                                       int64_t N, int64_t Nk, int64_t ldc, int NB,
-                                                                      int acc) {
+                                                                      int acc, int64_t kchunk, int64_t gstride) {
   __shared__ float tb[2 * 256];
   __shared__ __align__(16) uint16_t stage[2 * kStageHalves];
+  // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial dQ
+  // at dq + y*gstride
+  const int64_t jb = static_cast<int64_t>(blockIdx.y) * kchunk;
+  Nk = Nk - jb < kchunk ? Nk - jb : kchunk;
+  ops.ka += jb * kH * 16;
+  ops.va += jb * kH * 16;
+  ops.kt += jb;
+  spd += jb;
+  dq += blockIdx.y * gstride;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int npad32 = static_cast<int>(ops.npq / 32);
   const int nqb = (npad32 + kBwdWaves - 1) / kBwdWaves;
@@ -594,7 +632,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   src.row1 = ops.va + h0 * 16;
   src.tr0 = ops.kt + static_cast<int64_t>(h0) * kD * npad;
   src.tr1 = nullptr;
-  const int64_t ntiles = npad / 32, nfull = Nk / 32;
+  const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
   constexpr int kCh = 320;  // ka, va, k^T
   s16x8 sr[stage_per_thread<kCh>()];
   stage_load<kCh>(sr, src, npad, 0, tid);
@@ -671,19 +709,30 @@ size_t mfma_ops_bytes(int64_t N, int64_t Nk) {
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(xcd_grid(static_cast<int>((a.N + 32 * kFwdWaves - 1) / (32 * kFwdWaves)))));
+  const Split sp = inner_split(a.N, a.Nk, kH, kD, a.dtype, kSplitFwd);
+  const int64_t rows = a.N * kH;
+  float* out = a.out;
+  float* lse = a.lse;
+  const bool part = sp.S > 1 || a.acc;
+  if (part) {  // partial results per key range, merged (into out/lse when acc) below
+    out = static_cast<float*>(a.workspace);
+    lse = out + static_cast<size_t>(sp.S) * rows * kD;
+  }
+  const dim3 grid(static_cast<unsigned>(xcd_grid(static_cast<int>((a.N + 32 * kFwdWaves - 1) / (32 * kFwdWaves)))),
+                  static_cast<unsigned>(sp.S));
   trace_begin(kTraceFwd, s);
   if (codes_aligned(a.spd, a.ld))
     hipLaunchKernelGGL(fwd_mfma_d8_kernel<true>, grid, dim3(64 * kFwdWaves), 0, s, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table,
-                       a.out, a.lse, a.N, a.Nk, a.ld, a.NB);
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table, out,
+                       lse, a.N, a.Nk, a.ld, a.NB, sp.chunk, rows * kD, rows);
   else
     hipLaunchKernelGGL(fwd_mfma_d8_kernel<false>, grid, dim3(64 * kFwdWaves), 0, s, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table,
-                       a.out, a.lse, a.N, a.Nk, a.ld, a.NB);
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.spd, a.table, out,
+                       lse, a.N, a.Nk, a.ld, a.NB, sp.chunk, rows * kD, rows);
   const hipError_t e = hipGetLastError();
   trace_end(kTraceFwd, s);
-  return e;
+  if (e != hipSuccess || !part) return e;
+  return launch_merge_splits(out, lse, sp.S, a.out, a.lse, rows, kD, a.acc, s);
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {
@@ -712,35 +761,55 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   trace_end(kTraceBwdDelta, s);
   if (e != hipSuccess) return e;
 
+  // key-outer: split over query ranges writes partial dK, dV ([2][S][Nk*H*D] in the
+  // workspace) that are summed afterwards; unsplit it writes (or adds) directly
   const dim3 block(kBwdThreads);
+  const int64_t nk_el = a.Nk * kHD, nq_el = a.N * kHD;
+  const bool kv_split = w.kv.S > 1;
+  float* dkp = kv_split ? reinterpret_cast<float*>(ws + w.dkv_off) : a.dk;
+  float* dvp = kv_split ? dkp + static_cast<size_t>(w.kv.S) * nk_el : a.dv;
+  const int kv_acc = kv_split ? 0 : (a.acc & kAccDkv);
+  const int64_t pstride = w.n_kv_blocks * kH * a.NB;
   const int nkb = static_cast<int>((ops.npk / 32 + kBwdWaves - 1) / kBwdWaves);
+  const dim3 kgrid(static_cast<unsigned>(xcd_grid(nkb)), static_cast<unsigned>(w.kv.S));
   const size_t lds = kv_mfma_lds(a.NB);
   e = allow_lds_mfma(bwd_kv_mfma_d8_kernel<true>, lds);
   if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d8_kernel<false>, lds);
   if (e != hipSuccess) return e;
   trace_begin(kTraceBwdKv, s);
   if (codes_aligned(a.spd_t, a.ld_t))
-    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<true>, dim3(static_cast<unsigned>(xcd_grid(nkb))), block, lds, s,
-                       a.spd_t, a.table, ops, a.dk, a.dv, partial, a.N, a.Nk, a.ld_t, a.NB, a.acc & kAccDkv);
+    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<true>, kgrid, block, lds, s, a.spd_t, a.table, ops, dkp, dvp, partial,
+                       a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride);
   else
-    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<false>, dim3(static_cast<unsigned>(xcd_grid(nkb))), block, lds, s,
-                       a.spd_t, a.table, ops, a.dk, a.dv, partial, a.N, a.Nk, a.ld_t, a.NB, a.acc & kAccDkv);
+    hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<false>, kgrid, block, lds, s, a.spd_t, a.table, ops, dkp, dvp, partial,
+                       a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride);
   e = hipGetLastError();
   trace_end(kTraceBwdKv, s);
   if (e != hipSuccess) return e;
 
+  const bool q_split = w.q.S > 1;
+  float* dqp = q_split ? reinterpret_cast<float*>(ws + w.dq_off) : a.dq;
+  const int q_acc = q_split ? 0 : (a.acc & kAccDq);
   const int nqb = static_cast<int>((ops.npq / 32 + kBwdWaves - 1) / kBwdWaves);
+  const dim3 qgrid(static_cast<unsigned>(xcd_grid(nqb)), static_cast<unsigned>(w.q.S));
   trace_begin(kTraceBwdQ, s);
   if (codes_aligned(a.spd, a.ld))
-    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<true>, dim3(static_cast<unsigned>(xcd_grid(nqb))), block, 0, s, a.spd,
-                       a.table, ops, a.dq, a.N, a.Nk, a.ld, a.NB, a.acc & kAccDq);
+    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<true>, qgrid, block, 0, s, a.spd, a.table, ops, dqp, a.N, a.Nk, a.ld,
+                       a.NB, q_acc, w.q.chunk, nq_el);
   else
-    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<false>, dim3(static_cast<unsigned>(xcd_grid(nqb))), block, 0, s, a.spd,
-                       a.table, ops, a.dq, a.N, a.Nk, a.ld, a.NB, a.acc & kAccDq);
+    hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<false>, qgrid, block, 0, s, a.spd, a.table, ops, dqp, a.N, a.Nk, a.ld,
+                       a.NB, q_acc, w.q.chunk, nq_el);
   e = hipGetLastError();
   trace_end(kTraceBwdQ, s);
   if (e != hipSuccess) return e;
-  return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, a.acc & kAccDtable, s);
+  if (!kv_split && !q_split)
+    return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, a.acc & kAccDtable, s);
+  const SumSplits none{nullptr, nullptr, 0, 0, 0};
+  const int dkv = a.acc & kAccDkv;
+  const SumSplits sk = kv_split ? SumSplits{dkp, a.dk, nk_el, w.kv.S, dkv} : none;
+  const SumSplits sv = kv_split ? SumSplits{dvp, a.dv, nk_el, w.kv.S, dkv} : none;
+  const SumSplits sq = q_split ? SumSplits{dqp, a.dq, nq_el, w.q.S, a.acc & kAccDq} : none;
+  return launch_bwd_finish(sk, sv, sq, partial, a.dtable, w.kv.S * w.n_kv_blocks, kH * a.NB, a.acc & kAccDtable, s);
 }
 
 }  // namespace gt

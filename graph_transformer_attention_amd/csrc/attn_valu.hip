@@ -367,6 +367,86 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* out_a, con
   lse[r] = m + logf(sum);
 }
 
+// out, lse from S partial results over disjoint key ranges (one thread per (node, head)
+// row): lse = log sum_s exp(lse_s), out = sum_s exp(lse_s - lse) out_s.
+// With acc, out/lse on entry are one more partial result (a running merge); a partial
+// with lse = -inf has weight 0.
+__global__ __launch_bounds__(kThreads) void merge_splits_kernel(const float* __restrict__ opart,
+                                                                const float* __restrict__ lpart, int S,
+                                                                float* __restrict__ out, float* __restrict__ lse,
+                                                                int64_t rows, int D, int acc) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (r >= rows) return;
+  const float l_old = acc ? lse[r] : -INFINITY;
+  float m = l_old;
+  for (int sp = 0; sp < S; ++sp) m = fmaxf(m, lpart[sp * rows + r]);
+  float sum = l_old == -INFINITY ? 0.f : expf(l_old - m);
+  for (int sp = 0; sp < S; ++sp) sum += expf(lpart[sp * rows + r] - m);
+  const float inv = 1.f / sum;
+  const float w_old = l_old == -INFINITY ? 0.f : expf(l_old - m) * inv;
+  for (int d = 0; d < D; d += 4) {
+    float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (w_old != 0.f) {
+      const float4 o = *reinterpret_cast<const float4*>(out + r * D + d);
+      o4 = make_float4(w_old * o.x, w_old * o.y, w_old * o.z, w_old * o.w);
+    }
+    for (int sp = 0; sp < S; ++sp) {
+      const float wgt = expf(lpart[sp * rows + r] - m) * inv;
+      const float4 o = *reinterpret_cast<const float4*>(opart + (sp * rows + r) * D + d);
+      o4.x = fmaf(wgt, o.x, o4.x);
+      o4.y = fmaf(wgt, o.y, o4.y);
+      o4.z = fmaf(wgt, o.z, o4.z);
+      o4.w = fmaf(wgt, o.w, o4.w);
+    }
+    *reinterpret_cast<float4*>(out + r * D + d) = o4;
+  }
+  lse[r] = m + logf(sum);
+}
+
+// The backward's finishing launch after split kernels. Workgroups [0, e0) sum the
+// partials of a, [e0, e1) those of b, [e1, e2) those of c (dst = sum over S partial
+// arrays of n floats, + dst when acc, four floats per thread, partials in order);
+// workgroup e2 + x reduces dtable entry x over the partial rows (as dtable_reduce_kernel).
+__global__ __launch_bounds__(kThreads) void bwd_finish_kernel(SumSplits a, SumSplits b, SumSplits c, int64_t e0,
+                                                              int64_t e1, int64_t e2, const float* __restrict__ partial,
+                                                              float* __restrict__ dtable, int64_t nblocks, int HNB,
+                                                              int dacc) {
+  const int64_t bid = blockIdx.x;
+  if (bid < e2) {
+    // select the descriptor by value (workgroup-uniform)
+    const bool in_a = bid < e0, in_b = !in_a && bid < e1;
+    const float* part = in_a ? a.part : (in_b ? b.part : c.part);
+    float* dst = in_a ? a.dst : (in_b ? b.dst : c.dst);
+    const int64_t n = in_a ? a.n : (in_b ? b.n : c.n);
+    const int S = in_a ? a.S : (in_b ? b.S : c.S);
+    const int acc = in_a ? a.acc : (in_b ? b.acc : c.acc);
+    const int64_t b0 = in_a ? 0 : (in_b ? e0 : e1);
+    const int64_t x = ((bid - b0) * kThreads + threadIdx.x) * 4;
+    if (x >= n) return;
+    float4 s = acc ? *reinterpret_cast<const float4*>(dst + x) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < S; ++sp) {
+      const float4 p = *reinterpret_cast<const float4*>(part + sp * n + x);
+      s.x += p.x;
+      s.y += p.y;
+      s.z += p.z;
+      s.w += p.w;
+    }
+    *reinterpret_cast<float4*>(dst + x) = s;
+    return;
+  }
+  __shared__ float red[kThreads];
+  const int x = static_cast<int>(bid - e2);
+  float s = 0.f;
+  for (int64_t r = threadIdx.x; r < nblocks; r += kThreads) s += partial[r * HNB + x];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dtable[x] = dacc ? dtable[x] + red[0] : red[0];
+}
+
 int fwd_tile_keys(int H, int D, int NB) {
   const int HD = H * D;
   int bn = std::max(8, std::min(64, 4096 / HD));
@@ -497,6 +577,28 @@ hipError_t launch_dtable_reduce(const float* partial, float* dtable, int64_t nbl
   return e;
 }
 
+hipError_t launch_merge_splits(const float* opart, const float* lpart, int S, float* out, float* lse, int64_t rows,
+                               int D, int acc, hipStream_t s) {
+  trace_begin(kTraceFwdSplits, s);
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(static_cast<unsigned>((rows + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, opart, lpart, S, out, lse, rows, D, acc);
+  const hipError_t e = hipGetLastError();
+  trace_end(kTraceFwdSplits, s);
+  return e;
+}
+
+hipError_t launch_bwd_finish(const SumSplits& a, const SumSplits& b, const SumSplits& c, const float* partial,
+                             float* dtable, int64_t nblocks, int HNB, int dacc, hipStream_t s) {
+  auto blocks = [](const SumSplits& g) { return g.S > 0 ? (g.n / 4 + kThreads - 1) / kThreads : 0; };
+  const int64_t e0 = blocks(a), e1 = e0 + blocks(b), e2 = e1 + blocks(c);
+  trace_begin(kTraceBwdSplits, s);
+  hipLaunchKernelGGL(bwd_finish_kernel, dim3(static_cast<unsigned>(e2 + HNB)), dim3(kThreads), 0, s, a, b, c, e0, e1,
+                     e2, partial, dtable, nblocks, HNB, dacc);
+  const hipError_t e = hipGetLastError();
+  trace_end(kTraceBwdSplits, s);
+  return e;
+}
+
 hipError_t launch_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b, float* out,
                         float* lse, int64_t rows, int D, hipStream_t s) {
   trace_begin(kTraceMerge, s);
@@ -507,8 +609,15 @@ hipError_t launch_merge(const float* out_a, const float* lse_a, const float* out
   return e;
 }
 
-hipError_t launch_fwd_valu(const FwdArgs& a, hipStream_t s) {
-  return a.dtype == 0 ? fwd_by_d<float>(a, s) : fwd_by_d<uint16_t>(a, s);
+hipError_t launch_fwd_valu(const FwdArgs& a0, hipStream_t s) {
+  FwdArgs a = a0;
+  if (a0.acc) {  // partial result into the workspace, then merged into out/lse
+    a.out = static_cast<float*>(a0.workspace);
+    a.lse = a.out + a0.N * a0.H * a0.D;
+  }
+  const hipError_t e = a.dtype == 0 ? fwd_by_d<float>(a, s) : fwd_by_d<uint16_t>(a, s);
+  if (e != hipSuccess || !a0.acc) return e;
+  return launch_merge_splits(a.out, a.lse, 1, a0.out, a0.lse, a0.N * a0.H, a0.D, 1, s);
 }
 
 hipError_t launch_bwd_valu(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s) {

@@ -3,6 +3,7 @@
 // enqueued, so every argument error is reported without touching the GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -90,8 +91,9 @@ hipEvent_t trace_event() {
   return e;
 }
 
-const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd",     "bwd_delta",  "bwd_kv",     "bwd_q", "bwd_dtable",
-                                                   "qkv_fwd", "qkv_bwd_dx", "qkv_bwd_dw", "store", "merge"};
+const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd",        "bwd_delta",  "bwd_kv",     "bwd_q",
+                                                   "bwd_dtable", "qkv_fwd",    "qkv_bwd_dx", "qkv_bwd_dw",
+                                                   "store",      "merge",      "fwd_merge",  "bwd_finish"};
 
 int check_dtype(int32_t dtype) {
   if (dtype != GT_F32 && dtype != GT_BF16) return fail(GT_EINVAL, "dtype=%d is not GT_F32 or GT_BF16", dtype);
@@ -105,6 +107,7 @@ int check_proj(int64_t N, int32_t hid, int32_t dtype) {
 }
 
 int check_workspace(const void* ws, size_t have, size_t need) {
+  if (need == 0) return GT_OK;  // a call that needs no workspace accepts a null one
   if (ws == nullptr) return fail(GT_EINVAL, "workspace is null");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(GT_EINVAL, "workspace is not 256-byte aligned");
   if (have < need) return fail(GT_EINVAL, "workspace_bytes=%zu < %zu required", have, need);
@@ -130,7 +133,7 @@ int check_ld(int64_t ld, int64_t n, const char* name, const char* nname) {
 // scratch shared by all layers.
 struct StackLayout {
   size_t q, k, v, out, lse, xn, layer;    // offsets within one layer's block, block size
-  size_t g, dob, dq, dk, dv, attn, proj;  // offsets of the shared scratch
+  size_t g, dob, dq, dk, dv, attn, proj, fwd;  // offsets of the shared scratch
   size_t bytes;
   gt::BwdWorkspace attn_ws;
 };
@@ -169,6 +172,8 @@ StackLayout stack_layout(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB,
   o += up256(s.attn_ws.bytes);
   s.proj = o;
   o += up256(gt::qkv_bwd_workspace(N, static_cast<int>(hid)));
+  s.fwd = o;
+  o += up256(gt::fwd_workspace_bytes(N, N, H, D, dtype, false));
   s.bytes = o;
   return s;
 }
@@ -203,16 +208,57 @@ void trace_end(int kernel_id, hipStream_t s) {
   g_trace_open = nullptr;
 }
 
+// A matrix-core launch whose outer dimension gives fewer workgroups than fit on the GPU
+// at once (target_wgs) is split along its inner loop, each split keeping at least 256
+// nodes of it. Measured per-workgroup cost is a fixed ~10-20 us plus ~1.7-1.8 us per
+// 32-node tile, so one full round of longer workgroups beats two rounds of short ones.
+constexpr int64_t kSplitMinInner = 256;
+
+// 4-wave workgroups resident per CU, from each kernel's VGPR use (512 per SIMD lane):
+// D = 8: forward 128 -> 4, key-outer 212 -> 2, query-outer 160 -> 3; D = 32: 177, 252
+// and 200 -> 2 each.
+int64_t resident_wgs(int kind, int D) {
+  const int per_cu = D == 32 ? 2 : (kind == kSplitFwd ? 4 : kind == kSplitKv ? 2 : 3);
+  return 256 * per_cu;
+}
+
+Split inner_split(int64_t outer, int64_t inner, int H, int D, int dtype, int kind) {
+  Split sp{1, inner};
+  if (!mfma_supported(H, D, dtype)) return sp;
+  const int64_t target_wgs = resident_wgs(kind, D);
+  const int64_t wgs = (outer + 127) / 128 * (H / 2);  // 128 nodes x one head pair per workgroup
+  const int64_t want = (target_wgs + wgs - 1) / wgs;
+  const int64_t S = std::min(want, inner / kSplitMinInner);
+  if (S <= 1) return sp;
+  const int64_t chunk = ((inner + S - 1) / S + 31) / 32 * 32;
+  sp.S = static_cast<int>((inner + chunk - 1) / chunk);
+  sp.chunk = chunk;
+  return sp;
+}
+
+size_t fwd_workspace_bytes(int64_t N, int64_t Nk, int H, int D, int dtype, bool block) {
+  const Split sp = inner_split(N, Nk, H, D, dtype, kSplitFwd);
+  if (sp.S == 1 && !block) return 0;
+  const size_t rows = static_cast<size_t>(N) * H;
+  return up256(static_cast<size_t>(sp.S) * rows * D * sizeof(float)) + up256(static_cast<size_t>(sp.S) * rows * sizeof(float));
+}
+
 BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtype) {
   BwdWorkspace w{};
-  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const bool mfma = mfma_supported(H, D, dtype);
   const int64_t kb = valu_kv_block(H);
   w.n_kv_blocks = mfma ? (D == 32 ? mfma_d32_kv_blocks(Nk) : mfma_kv_blocks(Nk)) : (Nk + kb - 1) / kb;
+  w.kv = inner_split(Nk, N, H, D, dtype, kSplitKv);
+  w.q = inner_split(N, Nk, H, D, dtype, kSplitQ);
+  const size_t f = sizeof(float);
   w.delta_off = 0;
-  w.ops_off = up(static_cast<size_t>(N) * H * sizeof(float));
-  w.partial_off = w.ops_off + (mfma ? up(D == 32 ? mfma_d32_ops_bytes(N, Nk) : mfma_ops_bytes(N, Nk)) : 0);
-  w.bytes = w.partial_off + up(static_cast<size_t>(w.n_kv_blocks) * H * NB * sizeof(float));
+  w.ops_off = up256(static_cast<size_t>(N) * H * f);
+  w.partial_off = w.ops_off + (mfma ? up256(D == 32 ? mfma_d32_ops_bytes(N, Nk) : mfma_ops_bytes(N, Nk)) : 0);
+  w.dkv_off = w.partial_off + up256(static_cast<size_t>(w.kv.S) * w.n_kv_blocks * H * NB * f);
+  const size_t dkv = w.kv.S > 1 ? up256(2 * static_cast<size_t>(w.kv.S) * Nk * H * D * f) : 0;
+  w.dq_off = w.dkv_off + dkv;
+  const size_t dq = w.q.S > 1 ? up256(static_cast<size_t>(w.q.S) * N * H * D * f) : 0;
+  w.bytes = w.dq_off + dq;
   return w;
 }
 
@@ -267,9 +313,16 @@ const char* gt_kernel_name(int32_t id) {
   return (id >= 0 && id < GT_KERNEL_COUNT) ? kKernelNames[id] : "";
 }
 
+size_t gt_attn_fwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  const std::string saved = g_error;
+  const int rc = check_shape(N, H, D, NB, dtype);
+  g_error = saved;
+  return rc != GT_OK ? 0 : gt::fwd_workspace_bytes(N, N, H, D, dtype, false);
+}
+
 int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd, const float* table,
-                float* out, float* lse, int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype,
-                void* stream) {
+                float* out, float* lse, void* workspace, size_t workspace_bytes, int64_t N, int32_t H,
+                int32_t D, int32_t NB, int32_t dtype, void* stream) {
   GT_CHECK(check_shape(N, H, D, NB, dtype));
   GT_CHECK(check_ptr(q, "q"));
   GT_CHECK(check_ptr(k, "k"));
@@ -278,7 +331,8 @@ int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(table, "table"));
   GT_CHECK(check_ptr(out, "out"));
   GT_CHECK(check_ptr(lse, "lse"));
-  gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype, N, N};
+  GT_CHECK(check_workspace(workspace, workspace_bytes, gt::fwd_workspace_bytes(N, N, H, D, dtype, false)));
+  gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype, N, N, workspace, 0};
   return hip_status(attn_fwd(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd launch");
 }
 
@@ -316,9 +370,17 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   return hip_status(attn_bwd(a, w, static_cast<hipStream_t>(stream)), "gt_attn_bwd launch");
 }
 
+size_t gt_attn_fwd_block_workspace_bytes(int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  const std::string saved = g_error;
+  const int rc = check_block(Nq, Nk, H, D, NB, dtype);
+  g_error = saved;
+  return rc != GT_OK ? 0 : gt::fwd_workspace_bytes(Nq, Nk, H, D, dtype, true);
+}
+
 int gt_attn_fwd_block(const void* q, const void* k, const void* v, const uint8_t* spd, int64_t ld,
-                      const float* table, float* out, float* lse, int64_t Nq, int64_t Nk, int32_t H, int32_t D,
-                      int32_t NB, int32_t dtype, void* stream) {
+                      const float* table, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                      int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB, int32_t dtype, int32_t accumulate,
+                      void* stream) {
   GT_CHECK(check_block(Nq, Nk, H, D, NB, dtype));
   GT_CHECK(check_ld(ld, Nk, "ld", "Nk"));
   GT_CHECK(check_ptr(q, "q"));
@@ -328,7 +390,9 @@ int gt_attn_fwd_block(const void* q, const void* k, const void* v, const uint8_t
   GT_CHECK(check_ptr(table, "table"));
   GT_CHECK(check_ptr(out, "out"));
   GT_CHECK(check_ptr(lse, "lse"));
-  gt::FwdArgs a{q, k, v, spd, table, out, lse, Nq, H, D, NB, dtype, Nk, ld};
+  if (accumulate != 0 && accumulate != 1) return fail(GT_EINVAL, "accumulate=%d must be 0 or 1", accumulate);
+  GT_CHECK(check_workspace(workspace, workspace_bytes, gt::fwd_workspace_bytes(Nq, Nk, H, D, dtype, true)));
+  gt::FwdArgs a{q, k, v, spd, table, out, lse, Nq, H, D, NB, dtype, Nk, ld, workspace, accumulate};
   return hip_status(attn_fwd(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd_block launch");
 }
 
@@ -487,7 +551,8 @@ int gt_stack_fwd_bwd(const void* x0, const void* w, const float* tables, const u
     float* lse = reinterpret_cast<float*>(layer(l, lay.lse));
     void* xn = l == L - 1 ? x_last : layer(l, lay.xn);
     GT_CHECK(hip_status(gt::launch_qkv_fwd(X, wl, q, k, v, N, hid, dtype, s), "gt_stack_fwd_bwd qkv"));
-    const gt::FwdArgs fa{q, k, v, spd, tables + static_cast<size_t>(l) * H * NB, out, lse, N, H, D, NB, dtype, N, N};
+    const gt::FwdArgs fa{q, k, v, spd, tables + static_cast<size_t>(l) * H * NB, out, lse, N, H, D, NB, dtype, N, N,
+                         base + lay.fwd, 0};
     GT_CHECK(hip_status(attn_fwd(fa, s), "gt_stack_fwd_bwd attention forward"));
     GT_CHECK(hip_status(gt::launch_store(out, xn, nel, dtype, s), "gt_stack_fwd_bwd store"));
     X = xn;

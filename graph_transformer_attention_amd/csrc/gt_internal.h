@@ -21,7 +21,23 @@ struct FwdArgs {
   int64_t N;
   int H, D, NB, dtype;
   int64_t Nk, ld;
+  void* workspace;  // fwd_workspace_bytes(N, Nk, ...) bytes (may be null when that is 0)
+  int acc;          // nonzero: merge the result into out/lse (a running result over other keys)
 };
+
+// Split of a kernel's inner loop (keys of the forward and query-outer pass, queries of
+// the key-outer pass) over S workgroup rows of `chunk` nodes (a multiple of 32) each,
+// used when the outer dimension alone gives too few workgroups to fill the GPU. The
+// partial results go to the workspace and a reduction kernel combines them.
+struct Split {
+  int S;
+  int64_t chunk;
+};
+// kind: which matrix-core kernel (its occupancy sets how many workgroups fit at once).
+enum SplitKind { kSplitFwd = 0, kSplitKv = 1, kSplitQ = 2 };
+Split inner_split(int64_t outer, int64_t inner, int H, int D, int dtype, int kind);
+// block: room for at least one partial result (a block step may merge into out/lse)
+size_t fwd_workspace_bytes(int64_t N, int64_t Nk, int H, int D, int dtype, bool block);
 
 struct BwdArgs {
   const void* q;
@@ -48,11 +64,14 @@ struct BwdArgs {
 enum { kAccDq = 1, kAccDkv = 2, kAccDtable = 4 };
 
 // Workspace layout of the backward (each region 256-byte aligned): delta [N*H] float
-// (vector-ALU kernels), operand copies of the MFMA kernels (mfma_ops_bytes), then
-// per-key-block bucket partial sums [n_kv_blocks * H * NB] float.
+// (vector-ALU kernels), operand copies of the MFMA kernels (mfma_ops_bytes), per-key-
+// block bucket partial sums [kv.S * n_kv_blocks * H * NB] float, then when split the
+// key-outer pass's dK, dV partials [kv.S][2][Nk*H*D] and the query-outer pass's dQ
+// partials [q.S][N*H*D] float.
 struct BwdWorkspace {
-  size_t delta_off, ops_off, partial_off, bytes;
-  int64_t n_kv_blocks;
+  size_t delta_off, ops_off, partial_off, dkv_off, dq_off, bytes;
+  int64_t n_kv_blocks;  // partial rows of one split
+  Split kv, q;
 };
 
 // Kernel timing ids (gt_trace_enable); the first five are the header's GT_KERNEL_* ids.
@@ -67,6 +86,8 @@ enum {
   kTraceQkvDw = 7,
   kTraceStore = 8,
   kTraceMerge = 9,
+  kTraceFwdSplits = 10,
+  kTraceBwdSplits = 11,
 };
 
 // Kernel timing hook (gt_trace_enable): bracket one launch with events on its stream.
@@ -95,6 +116,21 @@ hipError_t launch_fwd_mfma_d32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma_d32(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 hipError_t launch_dtable_reduce(const float* partial, float* dtable, int64_t nblocks, int HNB, int acc,
                                 hipStream_t s);
+// out, lse from S partial results over disjoint key ranges: opart [S][rows*D], lpart [S][rows];
+// with acc, out/lse on entry are one more partial result
+hipError_t launch_merge_splits(const float* opart, const float* lpart, int S, float* out, float* lse, int64_t rows,
+                               int D, int acc, hipStream_t s);
+// dst[x] = sum_s part[s*n + x] (+ dst[x] when acc), n a multiple of 4
+struct SumSplits {
+  const float* part;
+  float* dst;
+  int64_t n;
+  int S, acc;
+};
+// The backward's last step after a split launch: up to three partial sums (S = 0 marks
+// an unused one) and the dtable reduction over `nblocks` partial rows, in one launch.
+hipError_t launch_bwd_finish(const SumSplits& a, const SumSplits& b, const SumSplits& c, const float* partial,
+                             float* dtable, int64_t nblocks, int HNB, int dacc, hipStream_t s);
 // out = merge of two partial attention results over disjoint key sets by their lse
 hipError_t launch_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b, float* out,
                         float* lse, int64_t rows, int D, hipStream_t s);

@@ -58,15 +58,26 @@ typedef enum {
   GT_EHIP = -3           /* the HIP runtime refused a launch */
 } gt_status;
 
-/* Forward of one biased attention layer (abstract and Fig. 4 of the MegaGraph pages).
- *   q, k, v  device [N,H,D] dtype        spd    device [N,N] uint8
- *   table    device [H,NB] float32       out    device [N,H,D] float32 (overwritten)
- *   lse      device [N,H] float32 (overwritten; the backward needs it)            */
-int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
-                const float* table, float* out, float* lse, int64_t N, int32_t H,
-                int32_t D, int32_t NB, int32_t dtype, void* stream);
+/* Bytes of device workspace gt_attn_fwd needs for these sizes (0 on invalid sizes, and
+ * 0 when the call needs none: then workspace may be NULL). Graphs too small to fill
+ * the GPU by query rows alone are split along the keys; the workspace holds the
+ * partial results, which a second kernel merges by their log-sum-exp.             */
+size_t gt_attn_fwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype);
 
-/* Bytes of device workspace gt_attn_bwd needs for these sizes (0 on invalid sizes). */
+/* Forward of one biased attention layer (abstract and Fig. 4 of the MegaGraph pages).
+ *   q, k, v    device [N,H,D] dtype        spd    device [N,N] uint8
+ *   table      device [H,NB] float32       out    device [N,H,D] float32 (overwritten)
+ *   lse        device [N,H] float32 (overwritten; the backward needs it)
+ *   workspace  device, >= gt_attn_fwd_workspace_bytes(...) bytes, 256-byte aligned,
+ *              contents ignored on entry (NULL allowed when that size is 0); calls
+ *              that share one workspace must be ordered on one stream.             */
+int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
+                const float* table, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype, void* stream);
+
+/* Bytes of device workspace gt_attn_bwd needs for these sizes (0 on invalid sizes). For
+ * graphs too small to fill the GPU by nodes alone it includes room for partial
+ * gradients of a backward split along its inner loop, summed in a fixed order.      */
 size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype);
 
 /* Backward of gt_attn_fwd for the loss sum(dout * out): recomputes the scores and the
@@ -102,15 +113,24 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
  * take whole-row vector loads). Other conventions as above, with Nq queries and Nk keys.
  * ------------------------------------------------------------------------------- */
 
+/* Bytes of device workspace gt_attn_fwd_block needs (0 on invalid sizes). */
+size_t gt_attn_fwd_block_workspace_bytes(int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB,
+                                         int32_t dtype);
+
 /* Partial forward of Nq queries against Nk keys:
- *   q        device [Nq,H,D] dtype          k, v   device [Nk,H,D] dtype
- *   spd      device uint8, code of (query i, key j) at spd[i*ld + j], ld >= Nk
- *   out      device [Nq,H,D] float32        lse    device [Nq,H] float32 (overwritten):
- *            attention restricted to these keys, and its log-sum-exp.
+ *   q          device [Nq,H,D] dtype          k, v   device [Nk,H,D] dtype
+ *   spd        device uint8, code of (query i, key j) at spd[i*ld + j], ld >= Nk
+ *   out        device [Nq,H,D] float32        lse    device [Nq,H] float32:
+ *              accumulate = 0: overwritten with attention restricted to these keys and
+ *              its log-sum-exp; accumulate = 1: on entry the result over other keys,
+ *              merged with this block's (as gt_attn_merge does, without a separate call).
+ *   workspace  device, >= gt_attn_fwd_block_workspace_bytes(...) bytes, 256-byte
+ *              aligned, contents ignored on entry.
  * Sizes: 1 <= Nq, Nk < 2^31; H, D, NB, dtype as for gt_attn_fwd.                     */
 int gt_attn_fwd_block(const void* q, const void* k, const void* v, const uint8_t* spd, int64_t ld,
-                      const float* table, float* out, float* lse, int64_t Nq, int64_t Nk, int32_t H,
-                      int32_t D, int32_t NB, int32_t dtype, void* stream);
+                      const float* table, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                      int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB, int32_t dtype,
+                      int32_t accumulate, void* stream);
 
 /* Merge of two partial results over disjoint key sets (log-sum-exp rescaling):
  *   lse = log(exp(lse_a) + exp(lse_b)),
@@ -237,7 +257,9 @@ enum {
   GT_KERNEL_QKV_BWD_DW = 7, /* gt_qkv_bwd: dW partial sums and their reduction     */
   GT_KERNEL_STORE = 8,      /* gt_store                                            */
   GT_KERNEL_MERGE = 9,      /* gt_attn_merge                                       */
-  GT_KERNEL_COUNT = 10
+  GT_KERNEL_FWD_MERGE = 10,  /* forward: merge of split or running partial results */
+  GT_KERNEL_BWD_FINISH = 11, /* backward after a split: partial sums and dtable     */
+  GT_KERNEL_COUNT = 12
 };
 int gt_trace_enable(int32_t on);
 int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n);

@@ -36,10 +36,10 @@ P = 0x10000  # a 16-byte-aligned stand-in address; these calls never reach the G
 
 
 def _fwd(**kw):
-    a = dict(q=P, k=P, v=P, spd=P, table=P, out=P, lse=P, N=100, H=8, D=8, NB=33, dt=1)
+    a = dict(q=P, k=P, v=P, spd=P, table=P, out=P, lse=P, ws=None, wsb=0, N=100, H=8, D=8, NB=33, dt=1)
     a.update(kw)
-    return gta.lib().gt_attn_fwd(a["q"], a["k"], a["v"], a["spd"], a["table"], a["out"], a["lse"],
-                                 a["N"], a["H"], a["D"], a["NB"], a["dt"], None)
+    return gta.lib().gt_attn_fwd(a["q"], a["k"], a["v"], a["spd"], a["table"], a["out"], a["lse"], a["ws"],
+                                 a["wsb"], a["N"], a["H"], a["D"], a["NB"], a["dt"], None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -79,6 +79,26 @@ def test_bwd_argument_errors():
     assert call(dout=None) == gta.GT_EINVAL and "dout" in gta.last_error()
     assert call(dtable=P + 8) == gta.GT_EINVAL
     assert call(N=-5) == gta.GT_EINVAL
+
+
+def test_split_workspaces():
+    """Graphs too small to fill the GPU by rows split the inner loop: the forward then
+    needs a workspace for its partial results, and the backward's grows; at full size
+    (32768 nodes) neither is split."""
+    L = gta.lib()
+    assert L.gt_attn_fwd_workspace_bytes(32768, 8, 8, 33, 1) == 0
+    assert L.gt_attn_fwd_workspace_bytes(100000, 8, 8, 33, 1) == 0
+    assert L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 0) == 0         # vector-ALU path: no split
+    need = L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 1)
+    assert need >= 2 * 6800 * 8 * 8 * 4
+    assert _fwd(N=6800) == gta.GT_EINVAL and "workspace is null" in gta.last_error()
+    assert _fwd(N=6800, ws=P, wsb=need - 1) == gta.GT_EINVAL and "workspace_bytes" in gta.last_error()
+    assert L.gt_attn_fwd_block_workspace_bytes(4096, 4096, 8, 32, 49, 1) >= 2 * 4096 * 8 * 32 * 4
+    # too few keys to split: one partial result's room (a block step may merge into out/lse)
+    assert L.gt_attn_fwd_block_workspace_bytes(4096, 200, 8, 8, 33, 1) == 4096 * 8 * 8 * 4 + 4096 * 8 * 4
+    # the small graph's backward holds split partial gradients on top of the unsplit needs
+    small, big = L.gt_attn_bwd_workspace_bytes(6800, 8, 8, 33, 1), L.gt_attn_bwd_workspace_bytes(32768, 8, 8, 33, 1)
+    assert small > 3 * 6800 * 8 * 8 * 4 and big < 40 * 32768 * 8 * 8 * 4
 
 
 def test_workspace_query_keeps_last_error():
@@ -210,13 +230,16 @@ def test_block_argument_errors():
     L = gta.lib()
     Nq, Nk, H, D, NB = 700, 300, 8, 8, 33
 
-    def fwd(ld=1000, Nq_=Nq, Nk_=Nk, spd=P + 3, q=P):
-        return L.gt_attn_fwd_block(q, P, P, spd, ld, P, P, P, Nq_, Nk_, H, D, NB, 1, None)
+    fwb = L.gt_attn_fwd_block_workspace_bytes(Nq, Nk, H, D, NB, 1)
+
+    def fwd(ld=1000, Nq_=Nq, Nk_=Nk, spd=P + 3, q=P, acc=0):
+        return L.gt_attn_fwd_block(q, P, P, spd, ld, P, P, P, P, fwb, Nq_, Nk_, H, D, NB, 1, acc, None)
     assert fwd(ld=Nk - 1) == gta.GT_EINVAL and "ld=299" in gta.last_error()
     assert fwd(Nk_=0) == gta.GT_EINVAL and "Nk=0" in gta.last_error()
     assert fwd(Nq_=0) == gta.GT_EINVAL and "Nq=0" in gta.last_error()
     assert fwd(spd=None) == gta.GT_EINVAL and "spd is null" in gta.last_error()
     assert fwd(q=P + 2) == gta.GT_EINVAL and "aligned" in gta.last_error()
+    assert fwd(acc=2) == gta.GT_EINVAL and "accumulate" in gta.last_error()
 
     need = L.gt_attn_bwd_block_workspace_bytes(Nq, Nk, H, D, NB, 1)
     assert need >= Nq * H * 4

@@ -50,12 +50,14 @@ def _ring(inp, codes, qcuts, kcuts):
     for r, (r0, r1) in enumerate(ranks):
         for t in range(P):
             c0, c1 = blocks[(r - t) % P]
-            ob, lb = gta.fwd_block(q[r0:r1], k[c0:c1], v[c0:c1], spd[r0:r1, c0:c1], table)
+            blk = (q[r0:r1], k[c0:c1], v[c0:c1], spd[r0:r1, c0:c1], table)
             if t == 0:
-                out[r0:r1].copy_(ob)
-                lse[r0:r1].copy_(lb)
-            else:
+                gta.fwd_block(*blk, out=out[r0:r1], lse=lse[r0:r1])
+            elif t % 2 == 1:   # separate merge call
+                ob, lb = gta.fwd_block(*blk)
                 gta.merge(out[r0:r1], lse[r0:r1], ob, lb, out[r0:r1], lse[r0:r1])
+            else:              # merged by the block step itself
+                gta.fwd_block(*blk, out=out[r0:r1], lse=lse[r0:r1], accumulate=True)
     # outputs start as NaN: each is overwritten on its first visit and added into after
     # (dq stays with its rank, dk/dv travel with their block, dtable is global)
     dq = torch.full((N, H, D), float("nan"), dtype=torch.float32, device="cuda")
@@ -85,6 +87,9 @@ def _ring(inp, codes, qcuts, kcuts):
     (257, 4, 16, 12, "f32", True, [0, 100, 257], [0, 1, 130, 257]),
     (200, 8, 8, 20, "f32", False, [0, 200], [0, 64, 133, 200]),
     (90, 2, 64, 5, "bf16", True, [0, 46, 90], [0, 33, 90]),
+    # blocks large enough that each block step splits its inner loop (2-3 splits)
+    (1290, 8, 8, 20, "bf16", True, [0, 600, 1290], [0, 577, 1290]),
+    (1200, 8, 32, 30, "bf16", False, [0, 1200], [0, 640, 1200]),
 ])
 def test_ring_blocks_equal_oracle(N, H, D, C, dtype, asym, qcuts, kcuts):
     print(f"ring N={N} H={H} D={D} {dtype} asym={asym} qcuts={qcuts} kcuts={kcuts}", flush=True)
