@@ -169,6 +169,22 @@ def main():
     spd = torch.from_numpy(spd_host).to(dev)
     hist = np.bincount(spd_host.ravel(), minlength=NB)
     del spd_host
+    # the same codes built on the GPU (graph preparation, outside the timed step): one
+    # untimed run, then one timed with events; it must equal the host build byte for byte
+    spd_dev = torch.empty_like(spd)
+    spd_ws = torch.empty(max(int(gta.lib().gt_spd_build_device_workspace_bytes(N, int(inp.indptr[-1]), C)), 256),
+                         dtype=torch.uint8, device=dev)
+    gta.spd_build_device(inp.indptr, inp.indices, N, C, out=spd_dev, workspace=spd_ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gta.spd_build_device(inp.indptr, inp.indices, N, C, out=spd_dev, workspace=spd_ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t_spd_dev = e0.elapsed_time(e1) * 1e-3
+    spd_dev_equal = bool(torch.equal(spd_dev, spd))
+    print(f"[bench] distance codes built on the GPU in {t_spd_dev * 1e3:.1f} ms (equal to host: {spd_dev_equal})",
+          file=sys.stderr, flush=True)
+    del spd_dev, spd_ws
     dt = gta.GT_BF16 if w.dtype == "bf16" else gta.GT_F32
     L = w.layers
     P = args.cp
@@ -324,6 +340,8 @@ def main():
         "kernels": kern,
         "roofline": roofline,
         "spd_build_host_s": round(t_spd, 2),
+        "spd_build_device_ms": round(t_spd_dev * 1e3, 2),
+        "spd_build_device_equals_host": spd_dev_equal,
         "exp_peak_tops": round(exp_peak, 3),
         "exp_frac_of_step": round(3 * pairs / (ms_step * 1e-3) / (exp_peak * 1e12), 4),
         "kernel_source_hash": kernel_source_hash(),

@@ -8,6 +8,7 @@ raises.
     out, lse = fwd(q, k, v, spd, table)
     dq, dk, dv, dtable = bwd(q, k, v, spd, table, out, lse, dout)
     spd = spd_build(indptr, indices, N, C)          # host numpy, uint8 [N, N]
+    spd = spd_build_device(indptr, indices, N, C)   # the same codes built on the GPU
     q, k, v = qkv_fwd(x, w)                         # one layer's projections
     dx, dw = qkv_bwd(x, w, dq, dk, dv)
     x_last, dx0, dw, dtable = stack_fwd_bwd(x0, w, tables, spd, dout, H)
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.gt_attn_bwd.argtypes = [P] * 14 + [SZ, I64, I32, I32, I32, I32, P]
         L.gt_attn_bwd.restype = ctypes.c_int
         L.gt_spd_build.argtypes = [P, P, I64, I32, P, I32]
+        L.gt_spd_build_device_workspace_bytes.argtypes = [I64, I64, I32]
+        L.gt_spd_build_device_workspace_bytes.restype = SZ
+        L.gt_spd_build_device.argtypes = [P, P, I64, I32, P, P, SZ, P]
+        L.gt_spd_build_device.restype = ctypes.c_int
         L.gt_spd_build.restype = ctypes.c_int
         L.gt_last_error.argtypes = []
         L.gt_last_error.restype = ctypes.c_char_p
@@ -322,6 +327,25 @@ def spd_build(indptr, indices, N: int, C: int, nthreads: int = 0, out=None) -> n
     return out
 
 
+def spd_build_device(indptr, indices, N: int, C: int, out=None, workspace=None, stream=None):
+    """The codes of spd_build computed on the GPU: uint8 [N, N] on the current device."""
+    import torch
+    indptr = np.ascontiguousarray(indptr, dtype=np.int64)
+    indices = np.ascontiguousarray(indices, dtype=np.int32)
+    if indptr.shape != (N + 1,):
+        raise ValueError("indptr must have N+1 entries")
+    if out is None:
+        out = torch.empty((N, N), dtype=torch.uint8, device="cuda")
+    nbytes = int(lib().gt_spd_build_device_workspace_bytes(N, int(indptr[-1]), C))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=out.device)
+    ip = indices.ctypes.data if indices.size else None
+    _check("gt_spd_build_device", lib().gt_spd_build_device(
+        indptr.ctypes.data, ip, N, C, _dev(out, "spd", torch.uint8, (N, N)), _dev(workspace, "workspace"),
+        _nbytes(workspace), _stream(stream)))
+    return out
+
+
 def version() -> str:
     return lib().gt_version().decode()
 
@@ -406,7 +430,7 @@ def stack_fwd_bwd(x0, w, tables, spd, dout, H: int, spd_t=None, workspace=None, 
     return x_last, dx0, dw, dtable
 
 
-KERNEL_COUNT = 12
+KERNEL_COUNT = 13
 
 
 def kernel_names():

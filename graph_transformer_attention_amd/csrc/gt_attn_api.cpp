@@ -16,6 +16,7 @@ namespace gt {
 std::string spd_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C);
 void spd_fill(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C, uint8_t* spd,
               int nthreads);
+std::vector<int64_t> components(const int64_t* indptr, const int32_t* indices, int64_t N);
 }  // namespace gt
 
 namespace {
@@ -93,7 +94,8 @@ hipEvent_t trace_event() {
 
 const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd",        "bwd_delta",  "bwd_kv",     "bwd_q",
                                                    "bwd_dtable", "qkv_fwd",    "qkv_bwd_dx", "qkv_bwd_dw",
-                                                   "store",      "merge",      "fwd_merge",  "bwd_finish"};
+                                                   "store",      "merge",      "fwd_merge",  "bwd_finish",
+                                                   "spd_device"};
 
 int check_dtype(int32_t dtype) {
   if (dtype != GT_F32 && dtype != GT_BF16) return fail(GT_EINVAL, "dtype=%d is not GT_F32 or GT_BF16", dtype);
@@ -458,6 +460,38 @@ int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32
   if (!why.empty()) return fail(GT_EINVAL, "gt_spd_build: %s", why.c_str());
   gt::spd_fill(indptr, indices, N, C, spd, nthreads);
   return GT_OK;
+}
+
+size_t gt_spd_build_device_workspace_bytes(int64_t N, int64_t nnz, int32_t C) {
+  if (N < 1 || N > 0x7FFFFFFFll || nnz < 0 || C < 1 || C > 254) return 0;
+  return gt::spd_device_layout(N, nnz).bytes;
+}
+
+int gt_spd_build_device(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C, uint8_t* spd,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (indptr == nullptr) return fail(GT_EINVAL, "indptr is null");
+  if (spd == nullptr) return fail(GT_EINVAL, "spd is null");
+  if (N < 1 || N > 0x7FFFFFFFll) return fail(GT_EINVAL, "N=%lld must lie in [1, 2^31-1]", (long long)N);
+  const std::string why = gt::spd_validate(indptr, indices, N, C);
+  if (!why.empty()) return fail(GT_EINVAL, "gt_spd_build_device: %s", why.c_str());
+  const int64_t nnz = indptr[N];
+  const gt::SpdDeviceLayout lay = gt::spd_device_layout(N, nnz);
+  GT_CHECK(check_workspace(workspace, workspace_bytes, lay.bytes));
+  const std::vector<int64_t> comp64 = gt::components(indptr, indices, N);
+  const std::vector<int32_t> comp(comp64.begin(), comp64.end());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  // the graph goes to the workspace first; the host arrays (and the labels above) are
+  // no longer needed once the copies are complete
+  GT_CHECK(hip_status(hipMemcpyAsync(base + lay.indptr_off, indptr, static_cast<size_t>(N + 1) * 8,
+                                     hipMemcpyHostToDevice, s), "gt_spd_build_device copy"));
+  if (nnz > 0)
+    GT_CHECK(hip_status(hipMemcpyAsync(base + lay.indices_off, indices, static_cast<size_t>(nnz) * 4,
+                                       hipMemcpyHostToDevice, s), "gt_spd_build_device copy"));
+  GT_CHECK(hip_status(hipMemcpyAsync(base + lay.comp_off, comp.data(), static_cast<size_t>(N) * 4,
+                                     hipMemcpyHostToDevice, s), "gt_spd_build_device copy"));
+  GT_CHECK(hip_status(hipStreamSynchronize(s), "gt_spd_build_device copy"));
+  return hip_status(gt::launch_spd_device(workspace, lay, N, C, spd, s), "gt_spd_build_device launch");
 }
 
 int gt_qkv_fwd(const void* x, const void* w, void* q, void* k, void* v, int64_t N, int32_t hid, int32_t dtype,

@@ -88,6 +88,7 @@ enum {
   kTraceMerge = 9,
   kTraceFwdSplits = 10,
   kTraceBwdSplits = 11,
+  kTraceSpd = 12,
 };
 
 // Kernel timing hook (gt_trace_enable): bracket one launch with events on its stream.
@@ -137,6 +138,18 @@ hipError_t launch_merge(const float* out_a, const float* lse_a, const float* out
 hipError_t launch_bwd_valu(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
 int64_t valu_kv_block(int H);
 hipError_t launch_probe(int kind, int blocks, int iters, float* sink, hipStream_t s);
+
+// GPU builder of the distance codes (spd_device.hip). Workspace regions (256-byte
+// aligned): the CSR graph and component labels copied from the host, per-level flags,
+// then three [N][G] masks (visited, frontier, fresh) for groups of G 64-source batches.
+constexpr size_t kSpdMaskBudget = size_t(1) << 30;  // bytes of masks per group
+struct SpdDeviceLayout {
+  size_t indptr_off, indices_off, comp_off, flags_off, masks_off, bytes;
+  int G;
+};
+SpdDeviceLayout spd_device_layout(int64_t N, int64_t nnz);
+hipError_t launch_spd_device(void* workspace, const SpdDeviceLayout& l, int64_t N, int32_t C, uint8_t* spd,
+                             hipStream_t s);
 
 // Q/K/V projections and storage rounding (proj.hip). dtype 1 = bfloat16 storage.
 size_t qkv_bwd_workspace(int64_t N, int hid);

@@ -20,9 +20,10 @@ namespace gt {
 std::string spd_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C);
 void spd_fill(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C, uint8_t* spd,
               int nthreads);
+std::vector<int64_t> components(const int64_t* indptr, const int32_t* indices, int64_t N);
 
-namespace {
-
+// Connected-component label of every node (the smallest node index in its component),
+// by union-find over the edges.
 std::vector<int64_t> components(const int64_t* indptr, const int32_t* indices, int64_t N) {
   std::vector<int64_t> parent(N);
   for (int64_t x = 0; x < N; ++x) parent[x] = x;
@@ -41,8 +42,6 @@ std::vector<int64_t> components(const int64_t* indptr, const int32_t* indices, i
   for (int64_t x = 0; x < N; ++x) parent[x] = find(x);
   return parent;
 }
-
-}  // namespace
 
 std::string spd_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C) {
   if (C < 1 || C > 254) return "C must lie in [1, 254] (codes 0..C fit in uint8)";

@@ -178,6 +178,25 @@ int gt_attn_bwd_block(const void* q, const void* k, const void* v, const uint8_t
 int gt_spd_build(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C,
                  uint8_t* spd, int32_t nthreads);
 
+/* Bytes of device workspace gt_spd_build_device needs for a graph of N nodes and nnz
+ * stored adjacency entries (0 on invalid sizes). */
+size_t gt_spd_build_device_workspace_bytes(int64_t N, int64_t nnz, int32_t C);
+
+/* The codes of gt_spd_build, computed on the GPU (same values, byte for byte).
+ *   indptr, indices  host CSR as for gt_spd_build (validated on the host, then copied
+ *                    into the workspace; the call waits for those copies, so the host
+ *                    arrays may be reused on return)
+ *   spd              device uint8 [N,N] (overwritten; any alignment)
+ *   workspace        device, >= gt_spd_build_device_workspace_bytes(N, indptr[N], C)
+ *                    bytes, 256-byte aligned, contents ignored on entry.
+ * Breadth-first search from all sources at once, 64 per bitmask, one launch per level
+ * (MegaGraph pages, Fig. 4 caption: the topology-aware bias comes from the graph's
+ * structure; the distance reading is stated with gt_spd_build). Component labels for
+ * the codes C-1 / C come from a union-find on the host. The search kernels are
+ * enqueued on `stream` and run asynchronously. Errors: as gt_spd_build, plus GT_EHIP. */
+int gt_spd_build_device(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C,
+                        uint8_t* spd, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Stacked layers (MegaGraph pages, Fig. 8 caption: the evaluated Graph
  * Transformer has 16 layers, 8 heads and hidden size 64). Only the attention layers
  * and their Q/K/V projections are modelled, with no residual, normalisation or
@@ -259,7 +278,8 @@ enum {
   GT_KERNEL_MERGE = 9,      /* gt_attn_merge                                       */
   GT_KERNEL_FWD_MERGE = 10,  /* forward: merge of split or running partial results */
   GT_KERNEL_BWD_FINISH = 11, /* backward after a split: partial sums and dtable     */
-  GT_KERNEL_COUNT = 12
+  GT_KERNEL_SPD = 12,        /* gt_spd_build_device: all of its kernels together    */
+  GT_KERNEL_COUNT = 13
 };
 int gt_trace_enable(int32_t on);
 int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n);
