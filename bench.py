@@ -89,6 +89,10 @@ def work_model(name: str, N: int, H: int, D: int, s_bytes: int):
         return 2 * N * hid * 3 * hid, 0, 3 * f32node + 3 * hid * hid * s_bytes + f32node
     if name == "store":        # float32 -> storage type
         return 0, 0, f32node + node
+    if name in ("layer_fwd", "layer_bwd"):   # one side of a full layer: three 64x64 products per node
+        return 3 * 2 * N * hid * hid, 0, 6 * f32node
+    if name == "layer_wgrad":                # eight sums over nodes of 64x64 outer products
+        return 8 * 2 * N * hid * hid, 0, 16 * f32node
     if name == "merge":        # two partial (out, lse) in, one out
         return 3 * N * H * D, 2 * N * H, 3 * f32node + 3 * N * H * 4
     return 0, 0, 0
@@ -103,7 +107,13 @@ def cpu_baseline(inp, n_rows: int, cores: int):
     t0 = time.perf_counter()
     codes = oracle.bfs_codes_parallel(inp.indptr, inp.indices, w.C, rows, workers=cores)
     t_bfs = time.perf_counter() - t0
-    if w.layers > 1:
+    if w.model == "gt":
+        from oracle import gt_layer as gl
+        g = {k: v.value[0] for k, v in inp.gt_params.items()}
+        a = gl.layer_norm(inp.x0.value, g["g1"], g["b1"])[0]
+        q, k, v = (oracle.round_bf16(a @ g[t]).reshape(w.N, w.H, w.D) for t in ("wq", "wk", "wv"))
+        table, dout = inp.table.value[0], oracle.round_bf16(inp.dout.value).reshape(w.N, w.H, w.D)
+    elif w.layers > 1:
         q, k, v = (t.reshape(w.N, w.H, w.D) for t in oracle.qkv_projection(inp.x0.value, inp.w_qkv.value[0]))
         table, dout = inp.table.value[0], inp.dout.value.reshape(w.N, w.H, w.D)
     else:
@@ -222,6 +232,21 @@ def main():
 
         def outputs():
             return [out, dq, dk, dv], dtab
+    elif w.model == "gt":
+        # the full model: L pre-norm layers (attention with the bias, output projection,
+        # residuals, norms, GELU feed-forward), forward and backward
+        x0, do, tables = put(inp.x0), put(inp.dout), put(inp.table)
+        params = torch.from_numpy(gta.model_pack({k: v.raw for k, v in inp.gt_params.items()}, w.hidden)).to(dev)
+        ws = torch.empty(int(gta.lib().gt_model_workspace_bytes(N, L, H, D, NB, dt)), dtype=torch.uint8, device=dev)
+        res = {}
+
+        def step():
+            res["r"] = gta.model_fwd_bwd(x0, params, tables, spd, do, H,
+                                         dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32, workspace=ws)
+
+        def outputs():
+            x_last, dx0, dpar, dtl = res["r"]
+            return [x_last, dx0, dpar], dtl.reshape(L * H, NB)
     elif L == 1:
         q, k, v, do, table = put(inp.q), put(inp.k), put(inp.v), put(inp.dout), put(inp.table)
         out = torch.empty((N, H, D), dtype=torch.float32, device=dev)

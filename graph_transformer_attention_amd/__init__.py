@@ -86,6 +86,12 @@ def lib() -> ctypes.CDLL:
         L.gt_stack_workspace_bytes.argtypes = [I64, I32, I32, I32, I32, I32]
         L.gt_stack_workspace_bytes.restype = SZ
         L.gt_stack_fwd_bwd.argtypes = [P] * 11 + [SZ, I64, I32, I32, I32, I32, I32, P]
+        L.gt_model_param_count.argtypes = [I32, I32]
+        L.gt_model_param_count.restype = I32
+        L.gt_model_workspace_bytes.argtypes = [I64, I32, I32, I32, I32, I32]
+        L.gt_model_workspace_bytes.restype = SZ
+        L.gt_model_fwd_bwd.argtypes = [P] * 11 + [SZ, I64, I32, I32, I32, I32, I32, P]
+        L.gt_model_fwd_bwd.restype = ctypes.c_int
         L.gt_attn_fwd_block.argtypes = [P, P, P, P, I64, P, P, P, P, SZ, I64, I64, I32, I32, I32, I32, I32, P]
         L.gt_attn_fwd_block.restype = ctypes.c_int
         L.gt_attn_merge.argtypes = [P] * 6 + [I64, I32, I32, P]
@@ -346,6 +352,52 @@ def spd_build_device(indptr, indices, N: int, C: int, out=None, workspace=None, 
     return out
 
 
+# One layer's parameter vector of the full model, in order (hid = ffn = 64).
+MODEL_PARAM_ORDER = (("g1", 1), ("b1", 1), ("wq", 2), ("wk", 2), ("wv", 2), ("wo", 2), ("g2", 1), ("b2", 1),
+                     ("w1", 2), ("c1", 1), ("w2", 2), ("c2", 1))
+
+
+def model_pack(named, hid: int = 64):
+    """float32 [L, P] parameter vectors from named per-layer arrays ([L, hid] or
+    [L, hid, hid], names as in MODEL_PARAM_ORDER)."""
+    parts = []
+    for name, rank in MODEL_PARAM_ORDER:
+        a = np.asarray(named[name], dtype=np.float32)
+        L = a.shape[0]
+        parts.append(a.reshape(L, hid ** rank))
+    out = np.ascontiguousarray(np.concatenate(parts, axis=1))
+    assert out.shape[1] == int(lib().gt_model_param_count(hid, hid))
+    return out
+
+
+def model_fwd_bwd(x0, params, tables, spd, dout, H: int, dtype=None, spd_t=None, workspace=None, stream=None):
+    """The full-layer model: x0, dout [N, 64] float32; params [L, P] float32 (model_pack);
+    tables [L, H, NB] float32; spd [N, N] uint8. dtype: storage type of Q/K/V and the
+    attention's output gradient (torch.bfloat16 or torch.float32).
+    Returns (x_last [N,64], dx0 [N,64], dparams [L,P], dtables [L,H,NB])."""
+    import torch
+    N, hid = x0.shape
+    L, P = params.shape
+    NB = tables.shape[2]
+    D = hid // H
+    dt = GT_BF16 if dtype in (None, torch.bfloat16) else GT_F32
+    f32 = torch.float32
+    x_last = torch.empty((N, hid), dtype=f32, device=x0.device)
+    dx0 = torch.empty((N, hid), dtype=f32, device=x0.device)
+    dparams = torch.empty((L, P), dtype=f32, device=x0.device)
+    dtables = torch.empty((L, H, NB), dtype=f32, device=x0.device)
+    nbytes = int(lib().gt_model_workspace_bytes(N, L, H, D, NB, dt))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x0.device)
+    args = [_dev(x0, "x0", f32, (N, hid)), _dev(params, "params", f32, (L, P)),
+            _dev(tables, "tables", f32, (L, H, NB)), _dev(spd, "spd", torch.uint8, (N, N)),
+            _dev(spd if spd_t is None else spd_t, "spd_t", torch.uint8, (N, N)), _dev(dout, "dout", f32, (N, hid)),
+            _dev(x_last, "x_last"), _dev(dx0, "dx0"), _dev(dparams, "dparams"), _dev(dtables, "dtables"),
+            _dev(workspace, "workspace")]
+    _check("gt_model_fwd_bwd", lib().gt_model_fwd_bwd(*args, _nbytes(workspace), N, L, H, D, NB, dt, _stream(stream)))
+    return x_last, dx0, dparams, dtables
+
+
 def version() -> str:
     return lib().gt_version().decode()
 
@@ -430,7 +482,7 @@ def stack_fwd_bwd(x0, w, tables, spd, dout, H: int, spd_t=None, workspace=None, 
     return x_last, dx0, dw, dtable
 
 
-KERNEL_COUNT = 13
+KERNEL_COUNT = 16
 
 
 def kernel_names():

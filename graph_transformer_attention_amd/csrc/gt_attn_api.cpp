@@ -95,7 +95,7 @@ hipEvent_t trace_event() {
 const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd",        "bwd_delta",  "bwd_kv",     "bwd_q",
                                                    "bwd_dtable", "qkv_fwd",    "qkv_bwd_dx", "qkv_bwd_dw",
                                                    "store",      "merge",      "fwd_merge",  "bwd_finish",
-                                                   "spd_device"};
+                                                   "spd_device", "layer_fwd",  "layer_bwd",  "layer_wgrad"};
 
 int check_dtype(int32_t dtype) {
   if (dtype != GT_F32 && dtype != GT_BF16) return fail(GT_EINVAL, "dtype=%d is not GT_F32 or GT_BF16", dtype);
@@ -178,6 +178,62 @@ StackLayout stack_layout(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB,
   o += up256(gt::fwd_workspace_bytes(N, N, H, D, dtype, false));
   s.bytes = o;
   return s;
+}
+
+// Workspace of gt_model_fwd_bwd: per layer the saved values of the forward (LN
+// statistics, Q, K, V in storage type, attention out and lse, X1, Hd and the layer's
+// output), then the backward's scratch shared by all layers.
+struct ModelLayout {
+  size_t st1, q, k, v, o, lse, x1, st2, hd, xout, layer;  // offsets within one layer's block
+  size_t dxa, dxb, dx1, dob, dq, dk, dv, fac, attn, fwd, part, bytes;
+  gt::BwdWorkspace attn_ws;
+};
+
+ModelLayout model_layout(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  ModelLayout m{};
+  const size_t n = static_cast<size_t>(N), hid = static_cast<size_t>(H) * D;
+  const size_t st = dtype == GT_BF16 ? 2 : 4, row = n * hid * 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up256(bytes);
+    return at;
+  };
+  m.st1 = take(n * 8);
+  m.q = take(n * hid * st);
+  m.k = take(n * hid * st);
+  m.v = take(n * hid * st);
+  m.o = take(row);
+  m.lse = take(n * H * 4);
+  m.x1 = take(row);
+  m.st2 = take(n * 8);
+  m.hd = take(row);
+  m.xout = take(row);
+  m.layer = o;
+  o = m.layer * static_cast<size_t>(L);
+  m.dxa = take(row);
+  m.dxb = take(row);
+  m.dx1 = take(row);
+  m.dob = take(n * hid * st);
+  m.dq = take(row);
+  m.dk = take(row);
+  m.dv = take(row);
+  m.fac = take(8 * row);  // g, b, dh, bhat, db, a, ahat, da
+  m.attn_ws = gt::bwd_workspace(N, N, H, D, NB, dtype);
+  m.attn = take(m.attn_ws.bytes);
+  m.fwd = take(gt::fwd_workspace_bytes(N, N, H, D, dtype, false));
+  m.part = take(static_cast<size_t>(gt::model_wgrad_chunks(N)) * gt::model_params(static_cast<int>(hid),
+                                                                                    static_cast<int>(hid)) * 4);
+  m.bytes = o;
+  return m;
+}
+
+int check_model(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  GT_CHECK(check_shape(N, H, D, NB, dtype));
+  if (L < 1 || L > 1024) return fail(GT_EINVAL, "L=%d must lie in [1, 1024]", L);
+  if (gt::model_params(H * D, H * D) == 0)
+    return fail(GT_EUNSUPPORTED, "H*D=%d: the full layer is built for hidden = feed-forward = 64", H * D);
+  return GT_OK;
 }
 
 hipError_t attn_fwd(const gt::FwdArgs& a, hipStream_t s) {
@@ -536,6 +592,84 @@ int gt_store(const float* src, void* dst, int64_t n, int32_t dtype, void* stream
   GT_CHECK(check_ptr(src, "src"));
   GT_CHECK(check_ptr(dst, "dst"));
   return hip_status(gt::launch_store(src, dst, n, dtype, static_cast<hipStream_t>(stream)), "gt_store launch");
+}
+
+int32_t gt_model_param_count(int32_t hid, int32_t ffn) { return gt::model_params(hid, ffn); }
+
+size_t gt_model_workspace_bytes(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
+  const std::string saved = g_error;
+  const int rc = check_model(N, L, H, D, NB, dtype);
+  g_error = saved;
+  return rc != GT_OK ? 0 : model_layout(N, L, H, D, NB, dtype).bytes;
+}
+
+int gt_model_fwd_bwd(const float* x0, const float* params, const float* tables, const uint8_t* spd,
+                     const uint8_t* spd_t, const float* dout, float* x_last, float* dx0, float* dparams,
+                     float* dtables, void* workspace, size_t workspace_bytes, int64_t N, int32_t L, int32_t H,
+                     int32_t D, int32_t NB, int32_t dtype, void* stream) {
+  GT_CHECK(check_model(N, L, H, D, NB, dtype));
+  GT_CHECK(check_ptr(x0, "x0"));
+  GT_CHECK(check_ptr(params, "params"));
+  GT_CHECK(check_ptr(tables, "tables"));
+  GT_CHECK(check_ptr(spd, "spd"));
+  GT_CHECK(check_ptr(spd_t, "spd_t"));
+  GT_CHECK(check_ptr(dout, "dout"));
+  GT_CHECK(check_ptr(x_last, "x_last"));
+  GT_CHECK(check_ptr(dx0, "dx0"));
+  GT_CHECK(check_ptr(dparams, "dparams"));
+  GT_CHECK(check_ptr(dtables, "dtables"));
+  const ModelLayout m = model_layout(N, L, H, D, NB, dtype);
+  GT_CHECK(check_workspace(workspace, workspace_bytes, m.bytes));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int P = gt::model_params(H * D, H * D);
+  char* base = static_cast<char*>(workspace);
+  auto at = [&](int l, size_t off) { return base + static_cast<size_t>(l) * m.layer + off; };
+  auto f32 = [](char* p) { return reinterpret_cast<float*>(p); };
+  const size_t row = static_cast<size_t>(N) * H * D;
+  // forward: X_{l+1} = layer_l(X_l); the last layer writes x_last
+  const float* X = x0;
+  for (int l = 0; l < L; ++l) {
+    const float* p = params + static_cast<size_t>(l) * P;
+    float* Xn = l == L - 1 ? x_last : f32(at(l, m.xout));
+    GT_CHECK(hip_status(gt::launch_layer_pre_fwd(X, p, at(l, m.q), at(l, m.k), at(l, m.v), f32(at(l, m.st1)), N,
+                                                 dtype, s),
+                        "gt_model_fwd_bwd layer forward"));
+    const gt::FwdArgs fa{at(l, m.q), at(l, m.k), at(l, m.v), spd, tables + static_cast<size_t>(l) * H * NB,
+                         f32(at(l, m.o)), f32(at(l, m.lse)), N, H, D, NB, dtype, N, N, base + m.fwd, 0};
+    GT_CHECK(hip_status(attn_fwd(fa, s), "gt_model_fwd_bwd attention forward"));
+    GT_CHECK(hip_status(gt::launch_layer_post_fwd(X, f32(at(l, m.o)), p, f32(at(l, m.x1)), f32(at(l, m.st2)),
+                                                  f32(at(l, m.hd)), Xn, N, s),
+                        "gt_model_fwd_bwd layer forward"));
+    X = Xn;
+  }
+  // backward of sum(dout * X_L)
+  float* fac = f32(base + m.fac);
+  float* const post_bufs[5] = {fac, fac + row, fac + 2 * row, fac + 3 * row, fac + 4 * row};  // g, b, dh, bhat, db
+  float* const pre_bufs[3] = {fac + 5 * row, fac + 6 * row, fac + 7 * row};                   // a, ahat, da
+  float* dxbuf[2] = {f32(base + m.dxa), f32(base + m.dxb)};
+  float* dx1 = f32(base + m.dx1);
+  float *dq = f32(base + m.dq), *dk = f32(base + m.dk), *dv = f32(base + m.dv);
+  const float* G = dout;
+  for (int l = L - 1; l >= 0; --l) {
+    const float* p = params + static_cast<size_t>(l) * P;
+    const float* Xl = l == 0 ? x0 : f32(at(l - 1, m.xout));
+    float* dXl = l == 0 ? dx0 : dxbuf[l & 1];
+    GT_CHECK(hip_status(gt::launch_layer_post_bwd(G, f32(at(l, m.x1)), f32(at(l, m.st2)), f32(at(l, m.hd)), p, dx1,
+                                                  base + m.dob, post_bufs, N, dtype, s),
+                        "gt_model_fwd_bwd layer backward"));
+    const gt::BwdArgs ba{at(l, m.q), at(l, m.k), at(l, m.v), spd, spd_t, tables + static_cast<size_t>(l) * H * NB,
+                         f32(at(l, m.o)), f32(at(l, m.lse)), base + m.dob, dq, dk, dv,
+                         dtables + static_cast<size_t>(l) * H * NB, base + m.attn, N, H, D, NB, dtype, N, N, N, 0};
+    GT_CHECK(hip_status(attn_bwd(ba, m.attn_ws, s), "gt_model_fwd_bwd attention backward"));
+    GT_CHECK(hip_status(gt::launch_layer_pre_bwd(dq, dk, dv, Xl, f32(at(l, m.st1)), p, dx1, dXl, pre_bufs, N, s),
+                        "gt_model_fwd_bwd layer backward"));
+    const gt::LayerGradFactors fg{pre_bufs[1], pre_bufs[2], pre_bufs[0], dq, dk, dv, f32(at(l, m.o)), dx1,
+                                  post_bufs[3], post_bufs[4], post_bufs[1], post_bufs[2], post_bufs[0], G};
+    GT_CHECK(hip_status(gt::launch_layer_wgrad(fg, f32(base + m.part), dparams + static_cast<size_t>(l) * P, N, s),
+                        "gt_model_fwd_bwd weight gradients"));
+    G = dXl;
+  }
+  return GT_OK;
 }
 
 size_t gt_stack_workspace_bytes(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB, int32_t dtype) {

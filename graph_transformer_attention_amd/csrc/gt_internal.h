@@ -89,6 +89,9 @@ enum {
   kTraceFwdSplits = 10,
   kTraceBwdSplits = 11,
   kTraceSpd = 12,
+  kTraceLayerFwd = 13,
+  kTraceLayerBwd = 14,
+  kTraceLayerWgrad = 15,
 };
 
 // Kernel timing hook (gt_trace_enable): bracket one launch with events on its stream.
@@ -158,5 +161,41 @@ hipError_t launch_qkv_fwd(const void* x, const void* w, void* q, void* k, void* 
 hipError_t launch_qkv_bwd(const void* x, const void* w, const float* dq, const float* dk, const float* dv, float* dx,
                           float* dw, void* workspace, int64_t N, int hid, int dtype, hipStream_t s);
 hipError_t launch_store(const float* src, void* dst, int64_t n, int dtype, hipStream_t s);
+
+// Dense parts of the full Graph-Transformer layer (gt_layer.hip); hidden = feed-forward
+// = 64. model_params: floats per layer's parameter vector (0 for other sizes).
+int model_params(int hid, int ffn);
+int64_t model_wgrad_chunks(int64_t N);
+struct WgradJob {
+  const float* a;  // [N][64] input factor
+  const float* d;  // [N][64] gradient factor
+  int diag;        // 0: 64 x 64 outer-product sum, 1: 64 column-wise products
+  int w_off;       // offset of the result in the layer's parameter gradient
+  int c_off;       // offset of the column sums of d, or -1
+};
+struct WgradJobs {
+  WgradJob j[8];
+  int n;       // jobs used
+  int stride;  // floats per partial row (the parameter count)
+};
+hipError_t launch_layer_pre_fwd(const float* x, const float* p, void* q, void* k, void* v, float* stats, int64_t N,
+                                int dtype, hipStream_t s);
+hipError_t launch_layer_post_fwd(const float* x, const float* o, const float* p, float* x1, float* stats, float* hd,
+                                 float* x2, int64_t N, hipStream_t s);
+hipError_t launch_layer_post_bwd(const float* dx2, const float* x1, const float* stats, const float* hd,
+                                 const float* p, float* dx1, void* dout_attn, float* const bufs[5], int64_t N,
+                                 int dtype, hipStream_t s);
+hipError_t launch_layer_pre_bwd(const float* dq, const float* dk, const float* dv, const float* x, const float* stats,
+                                const float* p, const float* dx1, float* dx, float* const bufs[3], int64_t N,
+                                hipStream_t s);
+hipError_t launch_wgrad_jobs(const WgradJobs& jobs, float* partial, float* grad, int64_t N, hipStream_t s);
+// The factors of one layer's parameter gradients, each [N][64] float32: LN1 (ahat, da),
+// the Q/K/V projections (a with dq, dk, dv), Wo (o, dx1), LN2 (bhat, db), W1 and c1
+// (b, dh), W2 and c2 (g, dx2). grad: the layer's parameter gradient (overwritten);
+// partial: model_wgrad_chunks(N) x model_params floats of scratch.
+struct LayerGradFactors {
+  const float *ahat, *da, *a, *dq, *dk, *dv, *o, *dx1, *bhat, *db, *b, *dh, *g, *dx2;
+};
+hipError_t launch_layer_wgrad(const LayerGradFactors& f, float* partial, float* grad, int64_t N, hipStream_t s);
 
 }  // namespace gt

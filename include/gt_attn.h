@@ -251,6 +251,48 @@ int gt_stack_fwd_bwd(const void* x0, const void* w, const float* tables, const u
                      float* dtable, void* workspace, size_t workspace_bytes, int64_t N, int32_t L,
                      int32_t H, int32_t D, int32_t NB, int32_t dtype, void* stream);
 
+/* ---- The full Graph-Transformer model (MegaGraph pages, Fig. 8 caption: 16 layers,
+ * 8 heads, hidden and feed-forward dimension 64; abstract: attention with a
+ * topology-aware bias plus a feed-forward block per layer). The pages do not give the
+ * layer's wiring; it is read as the pre-norm Transformer layer:
+ *     A  = LN(X; g1, b1)                 Q, K, V = store(A Wq), store(A Wk), store(A Wv)
+ *     O  = attention(Q, K, V)            (gt_attn_fwd, the layer's own bias table)
+ *     X1 = X + O Wo                      B = LN(X1; g2, b2)
+ *     X2 = X1 + gelu(B W1 + c1) W2 + c2
+ * LN over the hidden dimension (biased variance, eps 1e-5), gelu(x) = x Phi(x). The
+ * residual stream X, the attention output and all parameters are float32; store() is
+ * the attention's input type (dtype), which also carries the attention's output
+ * gradient in the backward.
+ * One layer's parameters are one float32 vector: g1[64], b1[64], Wq, Wk, Wv, Wo
+ * [64][64], g2[64], b2[64], W1 [64][64], c1[64], W2 [64][64], c2[64], where W[a][b]
+ * multiplies input column a into output column b.
+ * ------------------------------------------------------------------------------- */
+
+/* Floats in one layer's parameter vector for hidden size hid and feed-forward size ffn
+ * (24960 for 64 and 64; 0 for sizes without kernels). */
+int32_t gt_model_param_count(int32_t hid, int32_t ffn);
+
+/* Bytes of device workspace gt_model_fwd_bwd needs (0 on invalid sizes). */
+size_t gt_model_workspace_bytes(int64_t N, int32_t L, int32_t H, int32_t D, int32_t NB, int32_t dtype);
+
+/* Forward of L layers and the backward of the loss sum(dout * X_L):
+ *   x0       device [N, 64] float32          params  device [L, P] float32 (P above)
+ *   tables   device [L, H, NB] float32       spd, spd_t as in gt_attn_bwd
+ *   dout     device [N, 64] float32 (the gradient of X_L)
+ *   x_last   device [N, 64] float32 (overwritten with X_L)
+ *   dx0      device [N, 64] float32 (overwritten with the gradient of x0)
+ *   dparams  device [L, P] float32, dtables device [L, H, NB] float32 (overwritten)
+ *   workspace device, >= gt_model_workspace_bytes, 256-byte aligned; it holds each
+ *            layer's saved forward values.
+ * Shapes: H*D = 64 (8 heads of 8, or any H, D with H*D = 64), NB, N and dtype as for
+ * gt_attn_fwd; 1 <= L <= 1024. Errors: GT_EINVAL, GT_EUNSUPPORTED (H*D != 64).
+ * Weight gradients are summed over fixed 256-node chunks, then over the chunks in
+ * order, so results are reproducible run to run.                                   */
+int gt_model_fwd_bwd(const float* x0, const float* params, const float* tables, const uint8_t* spd,
+                     const uint8_t* spd_t, const float* dout, float* x_last, float* dx0, float* dparams,
+                     float* dtables, void* workspace, size_t workspace_bytes, int64_t N, int32_t L,
+                     int32_t H, int32_t D, int32_t NB, int32_t dtype, void* stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* gt_last_error(void);
 
@@ -279,7 +321,10 @@ enum {
   GT_KERNEL_FWD_MERGE = 10,  /* forward: merge of split or running partial results */
   GT_KERNEL_BWD_FINISH = 11, /* backward after a split: partial sums and dtable     */
   GT_KERNEL_SPD = 12,        /* gt_spd_build_device: all of its kernels together    */
-  GT_KERNEL_COUNT = 13
+  GT_KERNEL_LAYER_FWD = 13,  /* gt_model_fwd_bwd: norm, projections, FFN forward    */
+  GT_KERNEL_LAYER_BWD = 14,  /* gt_model_fwd_bwd: their backward (node gradients)   */
+  GT_KERNEL_LAYER_WGRAD = 15,/* gt_model_fwd_bwd: parameter gradients              */
+  GT_KERNEL_COUNT = 16
 };
 int gt_trace_enable(int32_t on);
 int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n);

@@ -11,7 +11,11 @@ the stacked workload it runs the oracle's 16-layer stack and keeps the final
 features and dX0 on sampled rows, and every layer's dW and dtable, together with
 the spread of each of them over stack runs whose pre-rounding values carry a
 float32-sized relative error: how far the method itself fixes each output once
-activations are rounded to bfloat16 between layers.
+activations are rounded to bfloat16 between layers. For the full-layer model it runs
+the oracle's 16 full layers and keeps the final features and dX0 on sampled rows,
+every layer's parameter and table gradients, and their spread under the same
+perturbation of the values rounded to bfloat16 (Q, K, V and the attention's output
+gradient).
 """
 from __future__ import annotations
 
@@ -93,6 +97,34 @@ def stacked(inp, workers, block):
                 **ref, **{f"spread_{k}": np.asarray(v) for k, v in spread.items()})
 
 
+def full_model(inp, workers, block):
+    from oracle import gt_layer as gl
+    w = inp.workload
+    codes = codes_of(inp, workers)
+    digest = hashlib.sha256(codes.tobytes()).hexdigest()
+    hid = w.hidden
+    params = np.stack([gl.pack({k: v.value[l] for k, v in inp.gt_params.items()}, hid, hid)
+                       for l in range(w.layers)])
+    args = (inp.x0.value, params, inp.table.value, codes, inp.dout.value)
+    t0 = time.perf_counter()
+    res = gl.model_forward_backward(*args, H=w.H, workers=workers, block=block)
+    print(f"[golden] {w.name}: model in {time.perf_counter() - t0:.0f} s", flush=True)
+    rows = np.sort(np.random.default_rng(w.number).choice(w.N, 512, replace=False))
+    ref = dict(x_last=res["x"][-1][rows], dx0=res["dx0"][rows], dparams=res["dparams"], dtables=res["dtables"])
+    spread = {k: 0.0 for k in ref}
+    for r in range(2):
+        pr = gl.model_forward_backward(*args, H=w.H, workers=workers, block=block,
+                                       pre_round_noise=(np.random.default_rng(2000 + r), NOISE_EPS))
+        got = dict(x_last=pr["x"][-1][rows], dx0=pr["dx0"][rows], dparams=pr["dparams"], dtables=pr["dtables"])
+        for k in ref:
+            spread[k] = max(spread[k], rel_err(got[k], ref[k]))
+        print(f"[golden] {w.name}: perturbed run {r}: spread so far "
+              + ", ".join(f"{k} {v:.2e}" for k, v in spread.items()), flush=True)
+    return dict(rows=rows, codes_sha256=np.array(digest), noise_eps=np.array(NOISE_EPS),
+                **{k: v.astype(np.float32) for k, v in ref.items()},
+                **{f"spread_{k}": np.asarray(v) for k, v in spread.items()})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("workload")
@@ -101,7 +133,12 @@ def main():
     a = ap.parse_args()
     w = {x.name: x for x in WORKLOADS.values()}[a.workload]
     inp = make_inputs(w.number)
-    data = stacked(inp, a.workers, a.block) if w.layers > 1 else single_layer(inp, a.workers, a.block)
+    if w.model == "gt":
+        data = full_model(inp, a.workers, a.block)
+    elif w.layers > 1:
+        data = stacked(inp, a.workers, a.block)
+    else:
+        data = single_layer(inp, a.workers, a.block)
     path = os.path.join(HERE, f"{w.name}.npz")
     np.savez_compressed(path, workload=np.array(w.name), **data)
     print(f"[golden] wrote {path} ({os.path.getsize(path) / 1e6:.2f} MB)", flush=True)

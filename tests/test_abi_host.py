@@ -264,3 +264,20 @@ def test_block_argument_errors():
     assert merge(H_=0) == gta.GT_EINVAL
     assert merge(out=None) == gta.GT_EINVAL and "out is null" in gta.last_error()
     assert gta.kernel_names()[9] == "merge"
+
+
+def test_model_argument_errors():
+    L = gta.lib()
+    assert L.gt_model_param_count(64, 64) == 24960
+    assert L.gt_model_param_count(32, 32) == 0
+    need = L.gt_model_workspace_bytes(6800, 16, 8, 8, 33, 1)
+    assert need > 16 * 6800 * 64 * 4 * 5
+    assert L.gt_model_workspace_bytes(6800, 16, 8, 16, 33, 1) == 0   # hidden 128: no kernels
+    assert L.gt_model_workspace_bytes(6800, 0, 8, 8, 33, 1) == 0
+
+    def call(L_=16, H=8, D=8, wsb=need, x0=P):
+        return L.gt_model_fwd_bwd(x0, P, P, P, P, P, P, P, P, P, P, wsb, 6800, L_, H, D, 33, 1, None)
+    assert call(H=8, D=16) == gta.GT_EUNSUPPORTED and "64" in gta.last_error()
+    assert call(L_=0) == gta.GT_EINVAL and "L=0" in gta.last_error()
+    assert call(wsb=need - 1) == gta.GT_EINVAL and "workspace_bytes" in gta.last_error()
+    assert call(x0=None) == gta.GT_EINVAL and "x0" in gta.last_error()

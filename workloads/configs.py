@@ -1,4 +1,4 @@
-"""The five synthetic workloads of biased full-graph attention and their seeded inputs.
+"""The synthetic workloads of biased full-graph attention and their seeded inputs.
 
 Each workload fixes a graph family, the SPD clip C (codes 0..C-1 for reachable
 pairs, C for unreachable ones, so the bias table has NB = C + 1 columns), the
@@ -29,6 +29,7 @@ class Workload:
     layers: int = 1        # >1: stacked layers with Q/K/V projections
     sample_rows: int = 0   # 0: compare every row against the oracle
     graph_args: dict = field(default_factory=dict)
+    model: str = "attn"    # "attn": attention (+ projections when stacked); "gt": full layers
 
     @property
     def NB(self) -> int:
@@ -53,6 +54,8 @@ WORKLOADS = {
                 graph_args=dict(m=4)),
     5: Workload(5, "sbm65536-d32-bf16", "sbm", 65536, 48, 8, 32, "bf16", sample_rows=256,
                 graph_args=dict(n_blocks=64, block_size=1024, p_in=0.01, p_out=2e-5)),
+    6: Workload(6, "gt16-ba6800-bf16", "ba", 6800, 32, 8, 8, "bf16", layers=16, graph_args=dict(m=4),
+                model="gt"),
 }
 
 _STREAMS = ("graph", "q", "k", "v", "dout", "table", "weights", "samples")
@@ -88,6 +91,7 @@ class Inputs:
     table: Stored = None          # [H, NB] float32  (single layer) or [L, H, NB]
     x0: Stored = None             # stacked workload: node features [N, hidden]
     w_qkv: Stored = None          # stacked workload: [L, 3, hidden, hidden]
+    gt_params: dict = None        # full layers: name -> Stored [L, ...] float32 (see gt_params)
     rows: np.ndarray = None       # sampled query rows (sorted, unique)
 
 
@@ -98,7 +102,13 @@ def make_inputs(w: Workload | int) -> Inputs:
     indptr, indices = make_graph(w, rs["graph"])
     inp = Inputs(w, indptr, indices)
     N, H, D, NB = w.N, w.H, w.D, w.NB
-    if w.layers == 1:
+    if w.model == "gt":
+        L, hid = w.layers, w.hidden
+        inp.x0 = store(normal(rs["q"], (N, hid)), "f32")
+        inp.dout = store(normal(rs["dout"], (N, hid)), "f32")
+        inp.table = store(normal(rs["table"], (L, H, NB), 0.5), "f32")
+        inp.gt_params = gt_params(rs["weights"], L, hid)
+    elif w.layers == 1:
         inp.q = store(normal(rs["q"], (N, H, D)), w.dtype)
         inp.k = store(normal(rs["k"], (N, H, D)), w.dtype)
         inp.v = store(normal(rs["v"], (N, H, D)), w.dtype)
@@ -112,6 +122,26 @@ def make_inputs(w: Workload | int) -> Inputs:
         inp.w_qkv = store(normal(rs["weights"], (L, 3, hid, hid), 1.0 / hid), w.dtype)
     inp.rows = sample_rows(w, indptr, rs["samples"])
     return inp
+
+
+def gt_params(rng: np.random.Generator, L: int, hid: int, ffn: int | None = None) -> dict:
+    """Named float32 parameters of L full layers: norm gains near 1, norm shifts and
+    biases near 0 (variance 0.01), weight matrices with variance 1/fan-in. Matrices are
+    [L, fan_in, fan_out]."""
+    ffn = hid if ffn is None else ffn
+    shapes = (("g1", (hid,)), ("b1", (hid,)), ("wq", (hid, hid)), ("wk", (hid, hid)), ("wv", (hid, hid)),
+              ("wo", (hid, hid)), ("g2", (hid,)), ("b2", (hid,)), ("w1", (hid, ffn)), ("c1", (ffn,)),
+              ("w2", (ffn, hid)), ("c2", (hid,)))
+    out = {}
+    for name, shape in shapes:
+        if len(shape) == 2:
+            x = normal(rng, (L,) + shape, 1.0 / shape[0])
+        elif name in ("g1", "g2"):
+            x = 1.0 + normal(rng, (L,) + shape, 0.01)
+        else:
+            x = normal(rng, (L,) + shape, 0.01)
+        out[name] = store(x, "f32")
+    return out
 
 
 def sample_rows(w: Workload, indptr: np.ndarray, rng: np.random.Generator) -> np.ndarray:
