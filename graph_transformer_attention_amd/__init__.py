@@ -47,7 +47,9 @@ def lib() -> ctypes.CDLL:
                                "`python -m graph_transformer_attention_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
-        L.gt_attn_fwd.argtypes = [P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, I32, P]
+        L.gt_attn_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I32, I32, P]
+        L.gt_attn_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, I32, P]
+        L.gt_attn_fwd_ws.restype = ctypes.c_int
         L.gt_attn_fwd_workspace_bytes.argtypes = [I64, I32, I32, I32, I32]
         L.gt_attn_fwd_workspace_bytes.restype = SZ
         L.gt_attn_fwd_block_workspace_bytes.argtypes = [I64, I64, I32, I32, I32, I32]
@@ -164,7 +166,7 @@ def fwd(q, k, v, spd, table, out=None, lse=None, workspace=None, stream=None):
     N, H, D = q.shape
     NB = table.shape[1]
     dt = _dtype_code(q)
-    wp, wn = _workspace(fwd_workspace_bytes(N, H, D, NB, dt), workspace, q.device)
+    need = fwd_workspace_bytes(N, H, D, NB, dt)
     if out is None:
         out = torch.empty((N, H, D), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -173,7 +175,11 @@ def fwd(q, k, v, spd, table, out=None, lse=None, workspace=None, stream=None):
             _dev(v, "v", q.dtype, (N, H, D)), _dev(spd, "spd", torch.uint8, (N, N)),
             _dev(table, "table", torch.float32, (H, NB)), _dev(out, "out", torch.float32, (N, H, D)),
             _dev(lse, "lse", torch.float32, (N, H))]
-    _check("gt_attn_fwd", lib().gt_attn_fwd(*args, wp, wn, N, H, D, NB, dt, _stream(stream)))
+    if need == 0:
+        _check("gt_attn_fwd", lib().gt_attn_fwd(*args, N, H, D, NB, dt, _stream(stream)))
+    else:  # a graph small enough that the key loop is split
+        wp, wn = _workspace(need, workspace, q.device)
+        _check("gt_attn_fwd_ws", lib().gt_attn_fwd_ws(*args, wp, wn, N, H, D, NB, dt, _stream(stream)))
     return out, lse
 
 

@@ -709,7 +709,8 @@ size_t mfma_ops_bytes(int64_t N, int64_t Nk) {
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
-  const Split sp = inner_split(a.N, a.Nk, kH, kD, a.dtype, kSplitFwd);
+  // no workspace (gt_attn_fwd): never split
+  const Split sp = a.workspace != nullptr ? inner_split(a.N, a.Nk, kH, kD, a.dtype, kSplitFwd) : Split{1, a.Nk};
   const int64_t rows = a.N * kH;
   float* out = a.out;
   float* lse = a.lse;

@@ -776,7 +776,8 @@ int64_t mfma_d32_kv_blocks(int64_t Nk) {
 }
 
 hipError_t launch_fwd_mfma_d32(const FwdArgs& a, hipStream_t s) {
-  const Split sp = inner_split(a.N, a.Nk, kH, kD, a.dtype, kSplitFwd);
+  // no workspace (gt_attn_fwd): never split
+  const Split sp = a.workspace != nullptr ? inner_split(a.N, a.Nk, kH, kD, a.dtype, kSplitFwd) : Split{1, a.Nk};
   const int64_t rows = a.N * kH;
   float* out = a.out;
   float* lse = a.lse;

@@ -379,8 +379,8 @@ size_t gt_attn_fwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, 
 }
 
 int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd, const float* table,
-                float* out, float* lse, void* workspace, size_t workspace_bytes, int64_t N, int32_t H,
-                int32_t D, int32_t NB, int32_t dtype, void* stream) {
+                float* out, float* lse, int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype,
+                void* stream) {
   GT_CHECK(check_shape(N, H, D, NB, dtype));
   GT_CHECK(check_ptr(q, "q"));
   GT_CHECK(check_ptr(k, "k"));
@@ -389,9 +389,25 @@ int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(table, "table"));
   GT_CHECK(check_ptr(out, "out"));
   GT_CHECK(check_ptr(lse, "lse"));
-  GT_CHECK(check_workspace(workspace, workspace_bytes, gt::fwd_workspace_bytes(N, N, H, D, dtype, false)));
-  gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype, N, N, workspace, 0};
+  gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype, N, N, nullptr, 0};
   return hip_status(attn_fwd(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd launch");
+}
+
+int gt_attn_fwd_ws(const void* q, const void* k, const void* v, const uint8_t* spd, const float* table,
+                   float* out, float* lse, void* workspace, size_t workspace_bytes, int64_t N, int32_t H,
+                   int32_t D, int32_t NB, int32_t dtype, void* stream) {
+  GT_CHECK(check_shape(N, H, D, NB, dtype));
+  GT_CHECK(check_ptr(q, "q"));
+  GT_CHECK(check_ptr(k, "k"));
+  GT_CHECK(check_ptr(v, "v"));
+  GT_CHECK(check_ptr(spd, "spd"));
+  GT_CHECK(check_ptr(table, "table"));
+  GT_CHECK(check_ptr(out, "out"));
+  GT_CHECK(check_ptr(lse, "lse"));
+  const size_t need = gt::fwd_workspace_bytes(N, N, H, D, dtype, false);
+  GT_CHECK(check_workspace(workspace, workspace_bytes, need));
+  gt::FwdArgs a{q, k, v, spd, table, out, lse, N, H, D, NB, dtype, N, N, need > 0 ? workspace : nullptr, 0};
+  return hip_status(attn_fwd(a, static_cast<hipStream_t>(stream)), "gt_attn_fwd_ws launch");
 }
 
 size_t gt_attn_bwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype) {

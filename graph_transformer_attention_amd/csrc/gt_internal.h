@@ -21,7 +21,7 @@ struct FwdArgs {
   int64_t N;
   int H, D, NB, dtype;
   int64_t Nk, ld;
-  void* workspace;  // fwd_workspace_bytes(N, Nk, ...) bytes (may be null when that is 0)
+  void* workspace;  // fwd_workspace_bytes(N, Nk, ...) bytes, or null: then the launch is never split
   int acc;          // nonzero: merge the result into out/lse (a running result over other keys)
 };
 

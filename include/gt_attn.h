@@ -58,22 +58,27 @@ typedef enum {
   GT_EHIP = -3           /* the HIP runtime refused a launch */
 } gt_status;
 
-/* Bytes of device workspace gt_attn_fwd needs for these sizes (0 on invalid sizes, and
- * 0 when the call needs none: then workspace may be NULL). Graphs too small to fill
- * the GPU by query rows alone are split along the keys; the workspace holds the
- * partial results, which a second kernel merges by their log-sum-exp.             */
+/* Forward of one biased attention layer (abstract and Fig. 4 of the MegaGraph pages).
+ *   q, k, v  device [N,H,D] dtype        spd    device [N,N] uint8
+ *   table    device [H,NB] float32       out    device [N,H,D] float32 (overwritten)
+ *   lse      device [N,H] float32 (overwritten; the backward needs it)            */
+int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
+                const float* table, float* out, float* lse, int64_t N, int32_t H,
+                int32_t D, int32_t NB, int32_t dtype, void* stream);
+
+/* Bytes of device workspace gt_attn_fwd_ws needs for these sizes (0 on invalid sizes, and
+ * 0 when the call needs none). Graphs too small to fill the GPU by query rows alone
+ * are split along the keys; the workspace holds the partial results, which a second
+ * kernel merges by their log-sum-exp.                                              */
 size_t gt_attn_fwd_workspace_bytes(int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype);
 
-/* Forward of one biased attention layer (abstract and Fig. 4 of the MegaGraph pages).
- *   q, k, v    device [N,H,D] dtype        spd    device [N,N] uint8
- *   table      device [H,NB] float32       out    device [N,H,D] float32 (overwritten)
- *   lse        device [N,H] float32 (overwritten; the backward needs it)
- *   workspace  device, >= gt_attn_fwd_workspace_bytes(...) bytes, 256-byte aligned,
- *              contents ignored on entry (NULL allowed when that size is 0); calls
- *              that share one workspace must be ordered on one stream.             */
-int gt_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* spd,
-                const float* table, float* out, float* lse, void* workspace, size_t workspace_bytes,
-                int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype, void* stream);
+/* gt_attn_fwd with a workspace, which lets small graphs split the key loop (same
+ * results up to float32 rounding order). workspace: device, >= gt_attn_fwd_workspace_bytes
+ * bytes, 256-byte aligned, contents ignored on entry (NULL allowed when that size is
+ * 0); calls that share one workspace must be ordered on one stream.                */
+int gt_attn_fwd_ws(const void* q, const void* k, const void* v, const uint8_t* spd,
+                   const float* table, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                   int64_t N, int32_t H, int32_t D, int32_t NB, int32_t dtype, void* stream);
 
 /* Bytes of device workspace gt_attn_bwd needs for these sizes (0 on invalid sizes). For
  * graphs too small to fill the GPU by nodes alone it includes room for partial

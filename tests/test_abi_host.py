@@ -36,10 +36,13 @@ P = 0x10000  # a 16-byte-aligned stand-in address; these calls never reach the G
 
 
 def _fwd(**kw):
-    a = dict(q=P, k=P, v=P, spd=P, table=P, out=P, lse=P, ws=None, wsb=0, N=100, H=8, D=8, NB=33, dt=1)
+    a = dict(q=P, k=P, v=P, spd=P, table=P, out=P, lse=P, N=100, H=8, D=8, NB=33, dt=1)
     a.update(kw)
-    return gta.lib().gt_attn_fwd(a["q"], a["k"], a["v"], a["spd"], a["table"], a["out"], a["lse"], a["ws"],
-                                 a["wsb"], a["N"], a["H"], a["D"], a["NB"], a["dt"], None)
+    if "ws" in a:  # the workspace variant
+        return gta.lib().gt_attn_fwd_ws(a["q"], a["k"], a["v"], a["spd"], a["table"], a["out"], a["lse"], a["ws"],
+                                        a["wsb"], a["N"], a["H"], a["D"], a["NB"], a["dt"], None)
+    return gta.lib().gt_attn_fwd(a["q"], a["k"], a["v"], a["spd"], a["table"], a["out"], a["lse"],
+                                 a["N"], a["H"], a["D"], a["NB"], a["dt"], None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -91,7 +94,7 @@ def test_split_workspaces():
     assert L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 0) == 0         # vector-ALU path: no split
     need = L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 1)
     assert need >= 2 * 6800 * 8 * 8 * 4
-    assert _fwd(N=6800) == gta.GT_EINVAL and "workspace is null" in gta.last_error()
+    assert _fwd(N=6800, ws=None, wsb=0) == gta.GT_EINVAL and "workspace is null" in gta.last_error()
     assert _fwd(N=6800, ws=P, wsb=need - 1) == gta.GT_EINVAL and "workspace_bytes" in gta.last_error()
     assert L.gt_attn_fwd_block_workspace_bytes(4096, 4096, 8, 32, 49, 1) >= 2 * 4096 * 8 * 32 * 4
     # too few keys to split: one partial result's room (a block step may merge into out/lse)
