@@ -24,8 +24,8 @@
 // nodes, whose other operand is read as 8 consecutive nodes of a transposed
 // [d][node] tile in LDS.
 //
-// Table in LDS: for each of the wave's two heads, 256 floats: entry b holds
-// table[h, min(b, NB-1)] * sqrt(D), so every byte value indexes it without a clamp.
+// Table in LDS: for each byte value b, both heads' table[h, min(b, NB-1)] * sqrt(D) as one
+// float2 (one 8-byte read per entry), so every byte value indexes it without a clamp.
 #include "mfma_common.h"
 
 #include <algorithm>
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
                                                                     float* __restrict__ lse, int64_t N, int64_t Nk,
                                                                     int64_t ldc, int NB, int64_t kchunk,
                                                                     int64_t ostride, int64_t lstride) {
-  __shared__ float tb[2 * 256];
+  __shared__ float2 tb[256];  // both heads' bias for each byte value
   __shared__ __align__(16) uint16_t vt[2][2][kD + 1][32];  // [buffer][head][d or ones][key]
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial
   // results at out + y*ostride, lse + y*lstride
@@ -118,9 +118,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
   const float sc2 = kLog2e / sqd;
   const float lazy_raw = kLazy / sc2;
 
-  for (int x = tid; x < 512; x += 64 * kFwdWaves) {
-    const int hl = x >> 8, b = x & 255;
-    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  for (int b = tid; b < 256; b += 64 * kFwdWaves) {
+    const int c = min(b, NB - 1);
+    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
   }
   for (int x = tid; x < 2 * 2 * 32; x += 64 * kFwdWaves) vt[x >> 6][(x >> 5) & 1][kD][x & 31] = 0x3C00;  // 1.0
   s16x4 qop0 = s16x4{0, 0, 0, 0}, qop1 = s16x4{0, 0, 0, 0};
@@ -161,9 +161,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const uint32_t cb = code_byte(cur.cw, e);
-      s0[e] = tb[cb];
-      s1[e] = tb[256 + cb];
+      const float2 t = tb[code_byte(cur.cw, e)];
+      s0[e] = t.x;
+      s1[e] = t.y;
     }
     s0 = mfma_x8(cur.ka, qop0, s0);
     s1 = mfma_x8(cur.kb, qop1, s1);
@@ -240,7 +240,10 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
 //   ka  = [k(8),  1,     1,  pen, 0..]    pen = 0, or -inf for padded keys
 //   doa = [do(8), -dl_hi, -dl_lo, 0..]    dl = delta = <dout, out>
 //   va  = [v(8),  1,     1,   0, 0..]
-// so that qa.ka = q.k - lse*sqrt(D) (+ -inf past Nk) and doa.va = dout.v - delta. Padded
+// so that qa.ka = q.k - lse*sqrt(D) (+ -inf past Nk) and doa.va = dout.v - delta. The bf16
+// inputs are exact in half precision, so the score products carry no rounding; the scale
+// log2(e)/sqrt(D) is applied in float32 before the exp2 (folding it into q would round
+// q to half precision and cost about 1e-3 of P). Padded
 // queries get -L_hi = -inf. Transposed half copies [head][d][node] of q, k and dout
 // (q and dout over npq nodes, k over npk) are the A operands of the contractions over
 // nodes.
@@ -343,6 +346,7 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
 }
 
 constexpr int kBwdWaves = 4;              // waves per backward workgroup: 4 x 32 nodes, one head pair
+constexpr int kKvTable = 64;              // key-outer table entries (codes clamped to NB-1 <= 63)
 constexpr int kBwdThreads = 64 * kBwdWaves;
 
 // One 32-node tile of backward operands of a head pair, staged into LDS: two
@@ -453,8 +457,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   partial += blockIdx.y * pstride;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 64);      // [NB][64 lanes][2 heads] per wave
-  float* tb = reinterpret_cast<float*>(smem) + kBwdWaves * 2 * NB * 64;  // [2][64] by clamped code
-  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + 128);               // [2][kStageHalves]
+  float2* tb = reinterpret_cast<float2*>(reinterpret_cast<float*>(smem) + kBwdWaves * 2 * NB * 64);  // [64] by code
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);           // [2][kStageHalves]
 
   const int npad32 = static_cast<int>(ops.npk / 32);
   const int nkb = (npad32 + kBwdWaves - 1) / kBwdWaves;
@@ -471,9 +475,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
-  for (int x = tid; x < 128; x += kBwdThreads) {
-    const int hl = x >> 6, b = x & 63;
-    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  for (int b = tid; b < kKvTable; b += kBwdThreads) {
+    const int c = min(b, NB - 1);
+    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
   }
   for (int x = lane; x < 2 * NB * 64; x += 64) bins[x] = 0.f;
   const s16x8 kb0 = load_h8(ops.ka + (jj * kH + h0) * 16 + 8 * hp);
@@ -519,8 +523,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         code[e] = min(code_byte(cw, e), nbm1);
-        s0[e] = tb[code[e]];
-        s1[e] = tb[64 + code[e]];
+        const float2 t = tb[code[e]];
+        s0[e] = t.x;
+        s1[e] = t.y;
       }
       s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), kb0, s0);
       s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), kb1, s1);
@@ -587,7 +592,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
                                                                       BwdOps ops, float* __restrict__ dq,
                                                                       int64_t N, int64_t Nk, int64_t ldc, int NB,
                                                                       int acc, int64_t kchunk, int64_t gstride) {
-  __shared__ float tb[2 * 256];
+  __shared__ float2 tb[256];  // both heads' bias for each byte value
   __shared__ __align__(16) uint16_t stage[2 * kStageHalves];
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial dQ
   // at dq + y*gstride
@@ -615,9 +620,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
-  for (int x = tid; x < 512; x += kBwdThreads) {
-    const int hl = x >> 8, b = x & 255;
-    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  for (int b = tid; b < 256; b += kBwdThreads) {
+    const int c = min(b, NB - 1);
+    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
   }
   const s16x8 qb0 = load_h8(ops.qa + (ii * kH + h0) * 16 + 8 * hp);
   const s16x8 qb1 = load_h8(ops.qa + (ii * kH + h0 + 1) * 16 + 8 * hp);
@@ -657,9 +662,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
       f32x16 s0, s1;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const uint32_t cb = code_byte(cw, e);
-        s0[e] = tb[cb];
-        s1[e] = tb[256 + cb];
+        const float2 t = tb[code_byte(cw, e)];
+        s0[e] = t.x;
+        s1[e] = t.y;
       }
       s0 = mfma_h16(staged_aug(ka_t, c, 0, hp), qb0, s0);
       s1 = mfma_h16(staged_aug(ka_t, c, 1, hp), qb1, s1);
@@ -689,7 +694,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   }
 }
 
-size_t kv_mfma_lds(int NB) { return 4ull * kBwdWaves * 2 * NB * 64 + 4ull * 128 + 2ull * 2 * kStageHalves; }
+size_t kv_mfma_lds(int NB) {
+  return 4ull * kBwdWaves * 2 * NB * 64 + sizeof(float2) * kKvTable + 2ull * 2 * kStageHalves;
+}
 
 }  // namespace
 
