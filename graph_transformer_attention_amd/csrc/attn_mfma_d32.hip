@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
                                                                 float* __restrict__ out, float* __restrict__ lse,
                                                                 int64_t N, int64_t Nk, int64_t ldc, int NB,
                                                                 int64_t kchunk, int64_t ostride, int64_t lstride) {
-  __shared__ float tb[2 * 256];
+  __shared__ float2 tb[256];  // both heads' bias * sqrt(D) for each byte value
   __shared__ __align__(16) uint16_t vt[2][2 * kVtHead];  // [buffer][head][d][key], rows of kVtRow
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial
   // results at out + y*ostride, lse + y*lstride
@@ -99,9 +99,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
   const float sc2 = kLog2e / sqd;
   const float lazy_raw = kLazy / sc2;
 
-  for (int x = tid; x < 512; x += kThreads) {
-    const int hl = x >> 8, b = x & 255;
-    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  for (int b = tid; b < 256; b += kThreads) {
+    const int c = min(b, NB - 1);
+    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
   }
   s16x8 qop[2][2];
 #pragma unroll
@@ -148,9 +148,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const uint32_t cb = code_byte(cur.cw, e);
-      s0[e] = tb[cb];
-      s1[e] = tb[256 + cb];
+      const float2 t = tb[code_byte(cur.cw, e)];
+      s0[e] = t.x;
+      s1[e] = t.y;
     }
     s0 = mfma_b16(cur.ka[0][0], qop[0][0], s0);
     s1 = mfma_b16(cur.ka[1][0], qop[1][0], s1);
@@ -414,7 +414,7 @@ __device__ __forceinline__ s16x8 aug_chunk(uint32_t ab, uint16_t cc, int hp) {
 // and dK^T += Q^T dS contract over the tile's queries. Bucket sums of dS go to LDS
 // bins [bucket][key][head] shared by the two lane halves of a wave, which update them
 // one half after the other (in program order) so no two lanes touch a bin at once.
-constexpr int kKvTbD32 = 2 * 64;
+constexpr int kKvTbD32 = 64;  // key-outer table entries (float2: both heads), codes clamped to NB-1 <= 63
 
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t* __restrict__ spd_t,
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   partial += blockIdx.y * pstride;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 32);  // [NB][32 keys][2 heads] per wave
-  float* tb = reinterpret_cast<float*>(smem) + kWaves * 2 * NB * 32;  // [2][64] by clamped code
+  float2* tb = reinterpret_cast<float2*>(reinterpret_cast<float*>(smem) + kWaves * 2 * NB * 32);  // by code
   uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTbD32);
 
   const int npad32 = static_cast<int>(ops.npk / 32);
@@ -457,9 +457,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
-  for (int x = tid; x < 128; x += kThreads) {
-    const int hl = x >> 6, b = x & 63;
-    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  for (int b = tid; b < kKvTbD32; b += kThreads) {
+    const int c = min(b, NB - 1);
+    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
   }
   for (int x = lane; x < 2 * NB * 32; x += 64) bins[x] = 0.f;
   s16x8 kop[2][2], vop[2][2];
@@ -521,8 +521,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         code[e] = min(code_byte(cw, e), nbm1);
-        s0[e] = tb[code[e]];
-        s1[e] = tb[64 + code[e]];
+        const float2 t = tb[code[e]];
+        s0[e] = t.x;
+        s1[e] = t.y;
       }
       f32x16 p0 = {}, p1 = {};
 #pragma unroll
@@ -616,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
                                                                   int64_t ldc, int NB, int acc, int64_t kchunk,
                                                                   int64_t gstride) {
   using Set = StageSetD32<2, 1>;
-  __shared__ float tb[2 * 256];
+  __shared__ float2 tb[256];  // both heads' bias * sqrt(D) for each byte value
   __shared__ __align__(16) uint16_t stage[2 * Set::kHalves];
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial dQ
   // at dq + y*gstride
@@ -644,9 +645,9 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
-  for (int x = tid; x < 512; x += kThreads) {
-    const int hl = x >> 8, b = x & 255;
-    tb[x] = table[(h0 + hl) * NB + min(b, NB - 1)] * sqd;
+  for (int b = tid; b < 256; b += kThreads) {
+    const int c = min(b, NB - 1);
+    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
   }
   s16x8 qop[2][2], oop[2][2], qaug[2], oaug[2];
   const uint16_t one = 0x3C00u, ninf = 0xFC00u;
@@ -696,9 +697,9 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
       f32x16 s0, s1;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const uint32_t cb = code_byte(cw, e);
-        s0[e] = tb[cb];
-        s1[e] = tb[256 + cb];
+        const float2 t = tb[code_byte(cw, e)];
+        s0[e] = t.x;
+        s1[e] = t.y;
       }
       f32x16 p0 = {}, p1 = {};
 #pragma unroll
@@ -761,7 +762,9 @@ OpsD32 carve_ops_d32(void* base, int64_t N, int64_t Nk) {
   return o;
 }
 
-size_t kv_d32_lds(int NB) { return 4ull * kWaves * 2 * NB * 32 + 4ull * kKvTbD32 + 2ull * StageSetD32<2, 2>::kHalves; }
+size_t kv_d32_lds(int NB) {
+  return 4ull * kWaves * 2 * NB * 32 + sizeof(float2) * kKvTbD32 + 2ull * StageSetD32<2, 2>::kHalves;
+}
 
 }  // namespace
 
