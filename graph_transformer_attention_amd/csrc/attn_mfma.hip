@@ -29,6 +29,7 @@
 #include "mfma_common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace gt {
 namespace {
@@ -81,7 +82,7 @@ __device__ __forceinline__ void fwd_load(FwdTile& t, const uint8_t* srow, const 
 }
 
 template <bool kAligned>
-__global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const uint16_t* __restrict__ q,
                                                                     const uint16_t* __restrict__ k,
                                                                     const uint16_t* __restrict__ v,
                                                                     const uint8_t* __restrict__ spd,
@@ -151,7 +152,11 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
 
   f32x16 o0 = {}, o1 = {};
   float m0 = -INFINITY, m1 = -INFINITY;
-  for (int64_t t = 0; t < ntiles; ++t) {
+  // One key tile; kMask (the partial last tile only) sets the scores of keys past Nk to
+  // -inf. The full tiles run without that code: kept in the loop, the compiler turns the
+  // tile-uniform test into per-entry selects executed on every tile.
+  auto tile = [&](int64_t t, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
     const int64_t j0 = t * 32;
     const int buf = static_cast<int>(t & 1);
     if (t + 1 < nfull)
@@ -161,16 +166,17 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float2 t = tb[code_byte(cur.cw, e)];
-      s0[e] = t.x;
-      s1[e] = t.y;
+      const float2 tv = tb[code_byte(cur.cw, e)];
+      s0[e] = tv.x;
+      s1[e] = tv.y;
     }
     s0 = mfma_x8(cur.ka, qop0, s0);
     s1 = mfma_x8(cur.kb, qop1, s1);
-    if (t >= nfull) {
+    if constexpr (kMask) {
+      const int64_t lim = Nk - (j0 + 16 * hp);  // entries e >= lim are past the last key
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        if (j0 + 16 * hp + e >= Nk) {
+        if (e >= lim) {
           s0[e] = -INFINITY;
           s1[e] = -INFINITY;
         }
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
     }
     x0 = fmaxf(x0, __shfl_xor(x0, 32));
     x1 = fmaxf(x1, __shfl_xor(x1, 32));
-    if (__any(x0 > m0 + lazy_raw || x1 > m1 + lazy_raw)) {
+    if (__builtin_expect(__any(x0 > m0 + lazy_raw || x1 > m1 + lazy_raw), 0)) {  // rare: keep it a branch
       const float n0 = fmaxf(m0, x0), n1 = fmaxf(m1, x1);
       const float a0 = __builtin_amdgcn_exp2f((m0 - n0) * sc2);
       const float a1 = __builtin_amdgcn_exp2f((m1 - n1) * sc2);
@@ -216,7 +222,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_mfma_d8_kernel(const uint1
       cur = nxt;
     }
     __syncthreads();
-  }
+  };
+  for (int64_t t = 0; t < nfull; ++t) tile(t, std::false_type{});
+  if (nfull < ntiles) tile(nfull, std::true_type{});
   // O^T rows: d = 4hp + e in entries e = 0..3; row 8 (lane half 0, entry 4) is l.
   const float l0 = __shfl(o0[4], c), l1 = __shfl(o1[4], c);
   if (qvalid) {
