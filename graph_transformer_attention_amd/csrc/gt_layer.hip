@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kLThreads) void pre_bwd_kernel(const float* __restr
 // written to partial[chunk][...]; grid (chunks, jobs).
 constexpr int kChunkRows = 256;
 constexpr int kSub = 64;        // nodes staged in LDS at a time
-constexpr int kWThreads = 256;  // thread t owns outer-product entries [t/4][16*(t%4) .. +15]
+constexpr int kWThreads = 256;  // thread t owns the 4 x 4 outer-product block at [4*(t/16)][4*(t%16)]
 
 __global__ __launch_bounds__(kWThreads) void wgrad_partial_kernel(WgradJobs jobs, float* __restrict__ partial,
                                                                   int64_t N) {
@@ -387,8 +387,8 @@ __global__ __launch_bounds__(kWThreads) void wgrad_partial_kernel(WgradJobs jobs
   const int diag = job.diag;
   const int tid = threadIdx.x;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kChunkRows;
-  const int ai = tid >> 2, b0 = 16 * (tid & 3);  // outer: entries [ai][b0 .. b0+15]
-  float acc[16] = {};
+  const int a0 = 4 * (tid >> 4), b0 = 4 * (tid & 15);  // outer: entries [a0 .. a0+3][b0 .. b0+3]
+  float acc[4][4] = {};
   float cs = 0.f, dg = 0.f;
   for (int s = 0; s < kChunkRows; s += kSub) {
     for (int e = tid; e < kSub * kHid / 4; e += kWThreads) {
@@ -404,10 +404,15 @@ __global__ __launch_bounds__(kWThreads) void wgrad_partial_kernel(WgradJobs jobs
     }
     __syncthreads();
     if (!diag) {
+#pragma unroll 4
       for (int r = 0; r < kSub; ++r) {
-        const float av = As[r][ai];
+        const float4 av = *reinterpret_cast<const float4*>(&As[r][a0]);
+        const float4 dv = *reinterpret_cast<const float4*>(&Ds[r][b0]);
+        const float ar[4] = {av.x, av.y, av.z, av.w}, dr[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = fmaf(av, Ds[r][b0 + i], acc[i]);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], dr[j], acc[i][j]);
       }
     }
     if (tid < kHid) {
@@ -421,7 +426,9 @@ __global__ __launch_bounds__(kWThreads) void wgrad_partial_kernel(WgradJobs jobs
   float* out = partial + static_cast<int64_t>(blockIdx.x) * jobs.stride;
   if (!diag) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) out[job.w_off + ai * kHid + b0 + i] = acc[i];
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(out + job.w_off + (a0 + i) * kHid + b0) =
+          make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
   } else if (tid < kHid) {
     out[job.w_off + tid] = dg;
   }
