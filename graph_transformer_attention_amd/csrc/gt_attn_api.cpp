@@ -266,10 +266,11 @@ void trace_end(int kernel_id, hipStream_t s) {
   g_trace_open = nullptr;
 }
 
-// A matrix-core launch whose outer dimension gives fewer workgroups than fit on the GPU
-// at once (target_wgs) is split along its inner loop, each split keeping at least 256
-// nodes of it. Measured per-workgroup cost is a fixed ~10-20 us plus ~1.7-1.8 us per
-// 32-node tile, so one full round of longer workgroups beats two rounds of short ones.
+// A matrix-core launch whose outer dimension gives at most half the workgroups that fit
+// on the GPU at once (target_wgs) is split along its inner loop into as many parts as
+// still fit in one round, each keeping at least 256 nodes of it. Measured per-workgroup
+// cost is a fixed ~10-20 us plus ~1.7-1.8 us per 32-node tile, so one round of longer
+// workgroups beats two rounds of short ones.
 constexpr int64_t kSplitMinInner = 256;
 
 // 4-wave workgroups resident per CU, from each kernel's VGPR use (512 per SIMD lane):
@@ -285,7 +286,9 @@ Split inner_split(int64_t outer, int64_t inner, int H, int D, int dtype, int kin
   if (!mfma_supported(H, D, dtype)) return sp;
   const int64_t target_wgs = resident_wgs(kind, D);
   const int64_t wgs = (outer + 127) / 128 * (H / 2);  // 128 nodes x one head pair per workgroup
-  const int64_t want = (target_wgs + wgs - 1) / wgs;
+  // as many splits as fit in one round of resident workgroups: a partly filled second
+  // round costs a whole workgroup's time for a fraction of the work
+  const int64_t want = target_wgs / wgs;
   const int64_t S = std::min(want, inner / kSplitMinInner);
   if (S <= 1) return sp;
   const int64_t chunk = ((inner + S - 1) / S + 31) / 32 * 32;
