@@ -266,12 +266,16 @@ void trace_end(int kernel_id, hipStream_t s) {
   g_trace_open = nullptr;
 }
 
-// A matrix-core launch whose outer dimension gives at most half the workgroups that fit
-// on the GPU at once (target_wgs) is split along its inner loop into as many parts as
-// still fit in one round, each keeping at least 256 nodes of it. Measured per-workgroup
-// cost is a fixed ~10-20 us plus ~1.7-1.8 us per 32-node tile, so one round of longer
-// workgroups beats two rounds of short ones.
+// A matrix-core launch may be split along its inner loop into S grid rows (each keeping at
+// least 256 inner nodes). S minimises a time model of the launch in units of one 32-node
+// tile: ceil(W*S / R) rounds of workgroups, each costing a fixed overhead plus its
+// inner tiles, with W workgroups per row (128 outer nodes x one head pair) and R
+// workgroups resident at once (the kernel's occupancy). Measured per-workgroup costs
+// are a fixed ~10-20 us plus ~1.7-1.8 us per tile, so the fixed part is about 12 tiles.
+// This both fills the GPU when the outer dimension is short and evens out the last
+// round when W is not a multiple of R.
 constexpr int64_t kSplitMinInner = 256;
+constexpr int64_t kSplitFixedTiles = 12;
 
 // 4-wave workgroups resident per CU, from each kernel's VGPR use (512 per SIMD lane):
 // D = 8: forward 128 -> 4, key-outer 212 -> 2, query-outer 160 -> 3; D = 32: 177, 252
@@ -284,16 +288,21 @@ int64_t resident_wgs(int kind, int D) {
 Split inner_split(int64_t outer, int64_t inner, int H, int D, int dtype, int kind) {
   Split sp{1, inner};
   if (!mfma_supported(H, D, dtype)) return sp;
-  const int64_t target_wgs = resident_wgs(kind, D);
-  const int64_t wgs = (outer + 127) / 128 * (H / 2);  // 128 nodes x one head pair per workgroup
-  // as many splits as fit in one round of resident workgroups: a partly filled second
-  // round costs a whole workgroup's time for a fraction of the work
-  const int64_t want = target_wgs / wgs;
-  const int64_t S = std::min(want, inner / kSplitMinInner);
-  if (S <= 1) return sp;
-  const int64_t chunk = ((inner + S - 1) / S + 31) / 32 * 32;
-  sp.S = static_cast<int>((inner + chunk - 1) / chunk);
-  sp.chunk = chunk;
+  const int64_t R = resident_wgs(kind, D);
+  const int64_t W = (outer + 127) / 128 * (H / 2);
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, inner / kSplitMinInner));
+  int64_t best_t = -1;
+  for (int64_t S = 1; S <= smax; ++S) {
+    const int64_t chunk = S == 1 ? inner : ((inner + S - 1) / S + 31) / 32 * 32;
+    const int64_t parts = (inner + chunk - 1) / chunk;
+    const int64_t rounds = (W * parts + R - 1) / R;
+    const int64_t t = rounds * (kSplitFixedTiles + (chunk + 31) / 32);
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      sp.S = static_cast<int>(parts);
+      sp.chunk = chunk;
+    }
+  }
   return sp;
 }
 

@@ -85,12 +85,14 @@ def test_bwd_argument_errors():
 
 
 def test_split_workspaces():
-    """Graphs too small to fill the GPU by rows split the inner loop: the forward then
-    needs a workspace for its partial results, and the backward's grows; at full size
-    (32768 nodes) neither is split."""
+    """Launches whose workgroups would not fill whole rounds split the inner loop: the
+    forward then needs a workspace for its partial results, and the backward's grows;
+    at 32768 nodes the forward and key-outer passes fill whole rounds and do not split."""
     L = gta.lib()
-    assert L.gt_attn_fwd_workspace_bytes(32768, 8, 8, 33, 1) == 0
-    assert L.gt_attn_fwd_workspace_bytes(100000, 8, 8, 33, 1) == 0
+    assert L.gt_attn_fwd_workspace_bytes(32768, 8, 8, 33, 1) == 0    # 1024 workgroups: one full round
+    assert L.gt_attn_fwd_workspace_bytes(65536, 8, 32, 49, 1) == 0   # 2048: four full rounds
+    # 100000 nodes: 3128 workgroups would leave a last round 5% full; two splits do better
+    assert L.gt_attn_fwd_workspace_bytes(100000, 8, 8, 33, 1) > 0
     assert L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 0) == 0         # vector-ALU path: no split
     need = L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 1)
     assert need >= 2 * 6800 * 8 * 8 * 4
