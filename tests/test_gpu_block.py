@@ -106,13 +106,16 @@ def test_ring_blocks_equal_oracle(N, H, D, C, dtype, asym, qcuts, kcuts):
     (300, 8, "bf16", 50, 290, 77, 200),
     (300, 32, "bf16", 0, 300, 0, 33),
     (300, 16, "f32", 10, 11, 3, 300),
+    # one query row against one key, on each matrix-core path
+    (300, 8, "bf16", 299, 300, 150, 151),
+    (300, 32, "bf16", 0, 1, 299, 300),
 ])
 def test_single_block_overwrite_equals_oracle_block(N, D, dtype, r0, r1, c0, c1):
     """One block without accumulation: out/lse of the block alone, and the block's
     backward shares against the merged (whole-graph) statistics."""
     print(f"block N={N} D={D} {dtype} rows=[{r0},{r1}) cols=[{c0},{c1})", flush=True)
     H = 8
-    inp, codes = _inputs(N, H, D, 20, dtype, True, seed=9)
+    inp, codes = _inputs(N, H, D, 63, dtype, True, seed=9)   # the widest table, NB = 64
     Q, K, V, DO, T = (x.value for x in (inp.q, inp.k, inp.v, inp.dout, inp.table))
     out_all, lse_all = oracle.forward(Q[r0:r1], K, V, codes[r0:r1], T)
     ob_ref, lb_ref = oracle.forward(Q[r0:r1], K[c0:c1], V[c0:c1], codes[r0:r1, c0:c1], T)
