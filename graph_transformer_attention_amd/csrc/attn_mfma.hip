@@ -188,9 +188,11 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
       x0 = fmaxf(x0, s0[e]);
       x1 = fmaxf(x1, s1[e]);
     }
-    x0 = fmaxf(x0, __shfl_xor(x0, 32));
-    x1 = fmaxf(x1, __shfl_xor(x1, 32));
+    // Each lane tests its own 16 keys; the two lane halves of a query column are combined
+    // only on the rare rescale path, so the common path has no cross-lane step.
     if (__builtin_expect(__any(x0 > m0 + lazy_raw || x1 > m1 + lazy_raw), 0)) {  // rare: keep it a branch
+      x0 = fmaxf(x0, __shfl_xor(x0, 32));
+      x1 = fmaxf(x1, __shfl_xor(x1, 32));
       const float n0 = fmaxf(m0, x0), n1 = fmaxf(m1, x1);
       const float a0 = __builtin_amdgcn_exp2f((m0 - n0) * sc2);
       const float a1 = __builtin_amdgcn_exp2f((m1 - n1) * sc2);
