@@ -145,6 +145,9 @@ def main():
                     help="time the key-block (context-parallel) schedule with P virtual ranks")
     ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays; per-kernel averages then come "
+                         "from the same number of eager steps run after the timed replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (the reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -290,14 +293,41 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    gta.trace(True)
+    graph = None
+    if args.graph:
+        # the library allocates nothing, never synchronises and records no memset, so a
+        # whole step (every launch of every layer) can be captured and replayed
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print("[bench] one step captured in a HIP graph", file=sys.stderr, flush=True)
+
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph is None:
+        gta.trace(True)
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        step()
+        if graph is None:
+            step()
+        else:
+            graph.replay()
     stop.record()
     torch.cuda.synchronize()
+    if graph is not None:  # per-kernel averages from eager steps (the trace events are not captured)
+        gta.trace(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
     gta.trace(False)
     per_kernel = gta.trace_collect()
     ms_total = start.elapsed_time(stop)
@@ -354,6 +384,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if (w.dtype == "bf16" and H == 8 and D in (8, 32)) else "f32",
         "data": "synthetic",
+        "launch": "hip_graph" if graph is not None else "eager",
         "config": {"workload": w.name, "graph": f"{w.family} {w.graph_args}", "N": N, "H": H,
                    "D": D, "NB": NB, "storage": w.dtype, "layers": L,
                    **({"cp_ranks": P, "block": f"{N // P}x{N // P}"} if P > 1 else {})},

@@ -24,8 +24,13 @@
  *     every output (out, lse, dq, dk, dv, dtable) is float32, so a bfloat16
  *     caller loses nothing to output rounding; table is float32.
  *   - Pointers marked "device" are device memory owned by the caller; the
- *     library never allocates, frees or synchronises device memory, and keeps
- *     no state between calls. Every base pointer must be 16-byte aligned.
+ *     library never allocates or frees device memory, and keeps no state
+ *     between calls. Every base pointer must be 16-byte aligned.
+ *   - Graph capture: every device entry point except gt_spd_build_device only
+ *     enqueues kernels on `stream` (no allocation, memset, copy or
+ *     synchronisation), so calls may be captured into a HIP graph and replayed;
+ *     every kernel is deterministic, so a replay reproduces the eager call bit
+ *     for bit. gt_spd_build_device copies host arrays and waits for the copies.
  *   - A code >= NB in spd is a caller error; kernels clamp it to NB-1.
  *   - Device calls are asynchronous on `stream` (a hipStream_t; NULL = the
  *     null stream) and return once the kernels are enqueued. Device faults
