@@ -73,6 +73,14 @@ def test_er256_f32_full():
     # loop (3 splits here, the last one ragged) and partial results are combined
     (777, 8, 8, 20, "bf16", "er"),
     (1000, 8, 32, 30, "bf16", "er"),
+    # the table extremes on the matrix-core paths: NB = 64 (the key-outer kernel's bins
+    # then need more than 64 KB of LDS per workgroup) and NB = 2 (every reachable pair in
+    # bucket 0, unreachable pairs in bucket 1). Both NB = 2 graphs have pairs in both
+    # buckets: with a single bucket dtable is zero in exact arithmetic (rows of P sum to
+    # one) and a ratio to its RMS would compare rounding noise.
+    (300, 8, 8, 63, "bf16", "path"),
+    (100, 8, 8, 1, "bf16", "er"),
+    (100, 8, 32, 1, "bf16", "empty"),
 ])
 def test_small_cases(N, H, D, C, dtype, family):
     inp = small_case(N, H, D, C, dtype, seed=11, family=family)
