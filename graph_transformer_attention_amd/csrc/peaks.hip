@@ -2,7 +2,9 @@
 // (v_exp_f32, a transcendental), fp32 fused multiply-add on the vector ALU, and the
 // bf16 matrix cores (32x32x8 and 32x32x16 shapes). Each probe runs independent
 // dependency chains in every lane of a full grid so the measured rate is the unit's
-// issue rate; the result is written to `sink` so the compiler keeps the work.
+// issue rate; the result is written to `sink` so the compiler keeps the work. The exp
+// chains step x -> exp2(-|x|), which stays in [0.5, 1] and costs one v_exp_f32 with
+// source modifiers (negate, absolute value) and no other instruction.
 #include "gt_internal.h"
 
 namespace gt {
@@ -21,7 +23,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_exp(float* sink, int iter
   for (int c = 0; c < kChains; ++c) x[c] = -1.0f - 1e-3f * (threadIdx.x + c);
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int c = 0; c < kChains; ++c) x[c] = __builtin_amdgcn_exp2f(x[c]) - 2.0f;  // stays in [-2,-1]
+    for (int c = 0; c < kChains; ++c) x[c] = __builtin_amdgcn_exp2f(-__builtin_fabsf(x[c]));
   }
   float s = 0.f;
 #pragma unroll
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_exp_fma(float* sink, int 
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int c = 0; c < kChains; ++c) {
-      x[c] = __builtin_amdgcn_exp2f(x[c]) - 2.0f;
+      x[c] = __builtin_amdgcn_exp2f(-__builtin_fabsf(x[c]));
       y[c] = fmaf(fmaf(fmaf(fmaf(y[c], a, b), a, b), a, b), a, b);
     }
   }
