@@ -156,7 +156,7 @@ def main():
                     help="also run one plain 256 MiB device copy (the reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported; the benchmark measures one GPU "
               "(the path shards by query rows across GPUs, but no multi-GPU run is made).",
               file=sys.stderr)
         sys.exit(2)

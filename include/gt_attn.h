@@ -59,7 +59,7 @@ typedef enum { GT_F32 = 0, GT_BF16 = 1 } gt_dtype;
 typedef enum {
   GT_OK = 0,
   GT_EINVAL = -1,        /* null or misaligned pointer, size out of range, workspace too small */
-  GT_EUNSUPPORTED = -2,  /* valid arguments this build has no kernel for (D, H*D, dtype) */
+  GT_EUNSUPPORTED = -2,  /* valid arguments the library has no kernel for (D, H*D, dtype) */
   GT_EHIP = -3           /* the HIP runtime refused a launch */
 } gt_status;
 

@@ -91,7 +91,7 @@ def test_split_workspaces():
     L = gta.lib()
     assert L.gt_attn_fwd_workspace_bytes(32768, 8, 8, 33, 1) == 0    # 1024 workgroups: one full round
     assert L.gt_attn_fwd_workspace_bytes(65536, 8, 32, 49, 1) == 0   # 2048: four full rounds
-    # 100000 nodes: 3128 workgroups would leave a last round 5% full; two splits do better
+    # 100000 nodes: 3128 workgroups would leave the last wave of resident workgroups 5% full; two splits do better
     assert L.gt_attn_fwd_workspace_bytes(100000, 8, 8, 33, 1) > 0
     assert L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 0) == 0         # vector-ALU path: no split
     need = L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 1)
