@@ -286,3 +286,33 @@ def test_model_argument_errors():
     assert call(L_=0) == gta.GT_EINVAL and "L=0" in gta.last_error()
     assert call(wsb=need - 1) == gta.GT_EINVAL and "workspace_bytes" in gta.last_error()
     assert call(x0=None) == gta.GT_EINVAL and "x0" in gta.last_error()
+
+
+def test_last_error_is_per_thread_and_calls_are_reentrant():
+    """gt_last_error() reports the calling thread's own last failure, and the host entry
+    points run concurrently from several threads with the results of a serial run."""
+    import threading
+    inp = small_case(300, 1, 8, 6, "f32", seed=4, avg_degree=3.0)
+    ref = gta.spd_build(inp.indptr, inp.indices, 300, 6, nthreads=1)
+    barrier = threading.Barrier(4)
+    results = {}
+
+    def worker(k):
+        barrier.wait()
+        if k % 2 == 0:
+            rc = _fwd(N=0) if k == 0 else _fwd(D=12)
+            msg = gta.last_error()
+        else:
+            rc, msg = 0, None
+        got = gta.spd_build(inp.indptr, inp.indices, 300, 6, nthreads=2)
+        # a successful call leaves this thread's message as it was
+        results[k] = (rc, msg, gta.last_error() if k % 2 == 0 else None, np.array_equal(got, ref))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert results[0][0] == gta.GT_EINVAL and "N=" in results[0][1] and results[0][2] == results[0][1]
+    assert results[2][0] == gta.GT_EUNSUPPORTED and "D=12" in results[2][1] and results[2][2] == results[2][1]
+    assert all(r[3] for r in results.values())
