@@ -408,15 +408,33 @@ __device__ __forceinline__ int stage_pos(int x) {
 template <int kChunks>
 constexpr int stage_per_thread() { return (kChunks + kBwdThreads - 1) / kBwdThreads; }
 
+// Per-thread global sources of the staged chunks, one tile after another: the mapping
+// from chunk to address (which depends on the chunk's kind) is worked out once, and each
+// tile's loads then only advance a pointer (32 nodes: 32*H*16 halves along augmented
+// rows, 32 halves along transposed rows).
 template <int kChunks>
-__device__ __forceinline__ void stage_load(s16x8 (&r)[stage_per_thread<kChunks>()], const StageSrc& s,
-                                           int64_t npad, int64_t n0, int tid) {
+struct StageCursor {
+  const uint16_t* p[stage_per_thread<kChunks>()];
+  int64_t step[stage_per_thread<kChunks>()];
+  __device__ __forceinline__ void init(const StageSrc& s, int64_t npad, int tid) {
 #pragma unroll
-  for (int u = 0; u < stage_per_thread<kChunks>(); ++u) {
-    const int x = tid + u * kBwdThreads;
-    if (x < kChunks) r[u] = load_h8(stage_chunk(s, npad, n0, x));
+    for (int u = 0; u < stage_per_thread<kChunks>(); ++u) {
+      const int x = tid + u * kBwdThreads;
+      p[u] = x < kChunks ? stage_chunk(s, npad, 0, x) : nullptr;
+      step[u] = x < 256 ? 32 * kH * 16 : 32;
+    }
   }
-}
+  // the next tile's chunks into r
+  __device__ __forceinline__ void load_next(s16x8 (&r)[stage_per_thread<kChunks>()], int tid) {
+#pragma unroll
+    for (int u = 0; u < stage_per_thread<kChunks>(); ++u) {
+      if (tid + u * kBwdThreads < kChunks) {
+        r[u] = load_h8(p[u]);
+        p[u] += step[u];
+      }
+    }
+  }
+};
 
 template <int kChunks>
 __device__ __forceinline__ void stage_store(uint16_t* buf, const s16x8 (&r)[stage_per_thread<kChunks>()],
@@ -508,7 +526,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
   constexpr int kCh = 384;  // qa, doa, q^T, dout^T
   s16x8 sr[stage_per_thread<kCh>()];
-  stage_load<kCh>(sr, src, npad, 0, tid);
+  StageCursor<kCh> cursor;
+  cursor.init(src, npad, tid);
+  cursor.load_next(sr, tid);
   stage_store<kCh>(stage, sr, tid);
   u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
   wait_vm0();
@@ -519,7 +539,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
     const uint16_t* cur = stage + (t & 1) * kStageHalves;
     u32x4 cwn = cw;
     if (t + 1 < ntiles) {
-      stage_load<kCh>(sr, src, npad, i0 + 32, tid);
+      cursor.load_next(sr, tid);
       cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(crow, i0 + 32 + cc, N)
                             : codes_at<true, kAligned>(crow, i0 + 32 + cc, N);
     }
@@ -650,7 +670,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
   constexpr int kCh = 320;  // ka, va, k^T
   s16x8 sr[stage_per_thread<kCh>()];
-  stage_load<kCh>(sr, src, npad, 0, tid);
+  StageCursor<kCh> cursor;
+  cursor.init(src, npad, tid);
+  cursor.load_next(sr, tid);
   stage_store<kCh>(stage, sr, tid);
   u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(srow, cc, Nk) : codes_at<true, kAligned>(srow, cc, Nk);
   wait_vm0();
@@ -661,7 +683,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
     const uint16_t* cur = stage + (t & 1) * kStageHalves;
     u32x4 cwn = cw;
     if (t + 1 < ntiles) {
-      stage_load<kCh>(sr, src, npad, j0 + 32, tid);
+      cursor.load_next(sr, tid);
       cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(srow, j0 + 32 + cc, Nk)
                             : codes_at<true, kAligned>(srow, j0 + 32 + cc, Nk);
     }
