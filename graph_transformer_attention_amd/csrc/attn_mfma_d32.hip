@@ -30,32 +30,54 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
 // ---------------------------------------------------------------------------------
+// Staged tiles: one 32-node tile of a head pair, 16-byte chunks (the forward stages
+// k as a row tile, the backward its operand copies).
+//   row tile      [slot][head][32] half, slot s holding node a(s): 32 rows of 128 bytes,
+//                 chunk k of row s stored at chunk position k ^ rswz(s)
+//   transposed    [head][d][32 nodes] half: 64 rows of 64 bytes, chunk g of row r at
+//                 g ^ tswz(r)
+// Both swizzles give the 8 (or 16) lanes of one LDS cycle distinct bank groups when
+// they read consecutive rows at one chunk index.
+constexpr int kRowTile = 32 * 2 * kD;  // halves
+constexpr int kTrTile = 2 * kD * 32;   // halves
+
+__device__ __forceinline__ int rswz(int s) { return (s >> 1) & 7; }
+__device__ __forceinline__ int tswz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int row_pos(int slot, int chunk) { return slot * 64 + 8 * (chunk ^ rswz(slot)); }
+__device__ __forceinline__ int tr_pos(int row, int g) { return row * 32 + 8 * (g ^ tswz(row)); }
+
+// global chunk x of a row tile: node = x >> 3, chunk = x & 7 (head = chunk >> 2, 8 halves of d)
+__device__ __forceinline__ const uint16_t* row_src(const uint16_t* base, int64_t n0, int h0, int x) {
+  return base + ((n0 + (x >> 3)) * kH + h0) * kD + 8 * (x & 7);
+}
+// Row tile operand of MFMA row c (node a(c)): head hl, d chunk ci (16 wide), half hp.
+__device__ __forceinline__ s16x8 row_op(const uint16_t* tile, int c, int hl, int ci, int hp) {
+  return load_h8(tile + row_pos(c, 4 * hl + 2 * ci + hp));
+}
+
+// ---------------------------------------------------------------------------------
 // Forward: per 32-key tile, S^T = K Q^T (two bf16 MFMAs over D), online softmax per
 // query column, O^T += V^T P^T (two half MFMAs over the tile's keys). The row sum l
-// is accumulated on the vector ALU (all 32 rows of V^T are head dimensions). V^T is
-// staged per tile in LDS as half, rows of 40 halves (80 bytes) so that the 16 lanes
-// of an LDS cycle reading rows d..d+15 hit distinct banks.
+// is accumulated on the vector ALU (all 32 rows of V^T are head dimensions). The 4 waves
+// of a workgroup share each key tile: its k rows are staged in LDS as a row tile (one
+// 16-byte chunk per thread, read back as the MFMA operands of every wave), and V^T as
+// half, rows of 40 halves (80 bytes) so that the 16 lanes of an LDS cycle reading rows
+// d..d+15 hit distinct banks.
 constexpr int kVtRow = 40;
 constexpr int kVtHead = kD * kVtRow;  // halves per head in one buffer
 
 struct FwdTileD32 {
   u32x4 cw;           // 16 codes: query row, keys 16*hp .. 16*hp+15 of the tile
-  s16x8 ka[2][2];     // K operand rows (head, d chunk) for MFMA row c
+  s16x8 ks;           // staging: chunk tid of the tile's k row tile
   u32x2 va, vb;       // staging: 4 d values of keys 2kp and 2kp+1 (bf16)
 };
 
 template <bool kGuard, bool kAligned>
 __device__ __forceinline__ void fwd_load_d32(FwdTileD32& t, const uint8_t* srow, const uint16_t* k,
-                                             const uint16_t* v, int64_t j0, int64_t N, int h0, int hp, int kr,
+                                             const uint16_t* v, int64_t j0, int64_t N, int h0, int hp, int tid,
                                              int shl, int sdq, int skp) {
   t.cw = codes_at<kGuard, kAligned>(srow, j0 + 16 * hp, N);
-  const int64_t kn = j0 + kr;
-#pragma unroll
-  for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      t.ka[hl][i] = (!kGuard || kn < N) ? load_h8(k + kn * kHD + (h0 + hl) * kD + 16 * i + 8 * hp)
-                                        : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  t.ks = (!kGuard || j0 + (tid >> 3) < N) ? load_h8(row_src(k, j0, h0, tid)) : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
   const int64_t v0 = j0 + 2 * skp, v1 = v0 + 1;
   const uint16_t* vp = v + (h0 + shl) * kD + 4 * sdq;
   t.va = (!kGuard || v0 < N) ? *reinterpret_cast<const u32x2*>(vp + v0 * kHD) : u32x2{0u, 0u};
@@ -73,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
                                                                 int64_t kchunk, int64_t ostride, int64_t lstride) {
   __shared__ float2 tb[256];  // both heads' bias * sqrt(D) for each byte value
   __shared__ __align__(16) uint16_t vt[2][2 * kVtHead];  // [buffer][head][d][key], rows of kVtRow
+  __shared__ __align__(16) uint16_t kt[2][kRowTile];     // [buffer] k row tile
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial
   // results at out + y*ostride, lse + y*lstride
   {
@@ -111,7 +134,6 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
       qop[hl][ci] = qvalid ? load_h8(q + i * kHD + (h0 + hl) * kD + 16 * ci + 8 * hp)
                            : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
   const uint8_t* srow = spd + irow * ldc;
-  const int kr = node_of_row(c);
   // staging role: head shl, d quad sdq (d = 4*sdq .. +3), key pair skp (keys 2*skp, 2*skp+1)
   const int shl = tid >> 7, sdq = (tid >> 4) & 7, skp = tid & 15;
   auto stage = [&](int buf, const u32x2& va, const u32x2& vb) {
@@ -125,14 +147,18 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     base[2 * kRowWords] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
     base[3 * kRowWords] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
   };
+  // k row tile: thread tid moves chunk tid (node tid >> 3, chunk tid & 7) to its row slot
+  const int kpos = row_pos(slot_of_node(tid >> 3), tid & 7);
+  auto stage_k = [&](int buf, const s16x8& ks) { *reinterpret_cast<s16x8*>(&kt[buf][kpos]) = ks; };
 
   const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
   FwdTileD32 cur, nxt;
   if (nfull > 0)
-    fwd_load_d32<false, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, kr, shl, sdq, skp);
+    fwd_load_d32<false, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, tid, shl, sdq, skp);
   else
-    fwd_load_d32<true, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, kr, shl, sdq, skp);
+    fwd_load_d32<true, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, tid, shl, sdq, skp);
   stage(0, cur.va, cur.vb);
+  stage_k(0, cur.ks);
   wait_vm0();
   __syncthreads();
 
@@ -142,9 +168,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     const int64_t j0 = t * 32;
     const int buf = static_cast<int>(t & 1);
     if (t + 1 < nfull)
-      fwd_load_d32<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, kr, shl, sdq, skp);
+      fwd_load_d32<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, tid, shl, sdq, skp);
     else if (t + 1 < ntiles)
-      fwd_load_d32<true, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, kr, shl, sdq, skp);
+      fwd_load_d32<true, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, tid, shl, sdq, skp);
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -152,10 +178,10 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
       s0[e] = t.x;
       s1[e] = t.y;
     }
-    s0 = mfma_b16(cur.ka[0][0], qop[0][0], s0);
-    s1 = mfma_b16(cur.ka[1][0], qop[1][0], s1);
-    s0 = mfma_b16(cur.ka[0][1], qop[0][1], s0);
-    s1 = mfma_b16(cur.ka[1][1], qop[1][1], s1);
+    s0 = mfma_b16(row_op(kt[buf], c, 0, 0, hp), qop[0][0], s0);
+    s1 = mfma_b16(row_op(kt[buf], c, 1, 0, hp), qop[1][0], s1);
+    s0 = mfma_b16(row_op(kt[buf], c, 0, 1, hp), qop[0][1], s0);
+    s1 = mfma_b16(row_op(kt[buf], c, 1, 1, hp), qop[1][1], s1);
     if (t >= nfull) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -203,6 +229,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     }
     if (t + 1 < ntiles) {
       stage(buf ^ 1, nxt.va, nxt.vb);
+      stage_k(buf ^ 1, nxt.ks);
       cur = nxt;
     }
     __syncthreads();
@@ -335,26 +362,6 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* 
   }
 }
 
-// ---------------------------------------------------------------------------------
-// Staged tiles of the backward: one 32-node tile of a head pair, 16-byte chunks.
-//   row tile      [slot][head][32] half, slot s holding node a(s): 32 rows of 128 bytes,
-//                 chunk k of row s stored at chunk position k ^ rswz(s)
-//   transposed    [head][d][32 nodes] half: 64 rows of 64 bytes, chunk g of row r at
-//                 g ^ tswz(r)
-// Both swizzles give the 8 (or 16) lanes of one LDS cycle distinct bank groups when
-// they read consecutive rows at one chunk index.
-constexpr int kRowTile = 32 * 2 * kD;  // halves
-constexpr int kTrTile = 2 * kD * 32;   // halves
-
-__device__ __forceinline__ int rswz(int s) { return (s >> 1) & 7; }
-__device__ __forceinline__ int tswz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int row_pos(int slot, int chunk) { return slot * 64 + 8 * (chunk ^ rswz(slot)); }
-__device__ __forceinline__ int tr_pos(int row, int g) { return row * 32 + 8 * (g ^ tswz(row)); }
-
-// global chunk x of a row tile: node = x >> 3, chunk = x & 7 (head = chunk >> 2, 8 halves of d)
-__device__ __forceinline__ const uint16_t* row_src(const uint16_t* base, int64_t n0, int h0, int x) {
-  return base + ((n0 + (x >> 3)) * kH + h0) * kD + 8 * (x & 7);
-}
 // global chunk x of a transposed tile: row = x >> 2 (head = row >> 5, d = row & 31), nodes 8*(x & 3)
 __device__ __forceinline__ const uint16_t* tr_src(const uint16_t* base, int64_t npad, int64_t n0, int h0, int x) {
   return base + (static_cast<int64_t>(h0) * kD + (x >> 2)) * npad + n0 + 8 * (x & 3);
@@ -389,10 +396,6 @@ struct StageSetD32 {
   }
 };
 
-// Row tile operand of MFMA row c (node a(c)): head hl, d chunk ci (16 wide), half hp.
-__device__ __forceinline__ s16x8 row_op(const uint16_t* tile, int c, int hl, int ci, int hp) {
-  return load_h8(tile + row_pos(c, 4 * hl + 2 * ci + hp));
-}
 // Transposed operand: head hl, d = m (0..31), nodes 8g .. 8g+7.
 __device__ __forceinline__ s16x8 tr_op(const uint16_t* tile, int hl, int m, int g) {
   return load_h8(tile + tr_pos(hl * kD + m, g));

@@ -278,10 +278,10 @@ constexpr int64_t kSplitMinInner = 256;
 constexpr int64_t kSplitFixedTiles = 12;
 
 // 4-wave workgroups resident per CU, from each kernel's VGPR use (512 per SIMD lane):
-// D = 8: forward 128 -> 4, key-outer 212 -> 2, query-outer 160 -> 3; D = 32: 177, 252
-// and 200 -> 2 each.
+// D = 8: forward 128 -> 4, key-outer 203 -> 2, query-outer 140 -> 3; D = 32: forward 156
+// -> 3, key-outer 252 and query-outer 200 -> 2.
 int64_t resident_wgs(int kind, int D) {
-  const int per_cu = D == 32 ? 2 : (kind == kSplitFwd ? 4 : kind == kSplitKv ? 2 : 3);
+  const int per_cu = D == 32 ? (kind == kSplitFwd ? 3 : 2) : (kind == kSplitFwd ? 4 : kind == kSplitKv ? 2 : 3);
   return 256 * per_cu;
 }
 
