@@ -56,29 +56,31 @@ constexpr int kFwdWaves = 4;
 
 struct FwdTile {
   u32x4 cw;       // 16 codes: query row, keys 16*hp .. 16*hp+15 of the tile
-  s16x4 ka, kb;   // K operand rows (both heads) for MFMA row c
-  uint32_t vw;    // one dword of V (two d values of one key and head) to stage
+  uint32_t kw;    // one dword of K (two d values of one key and head) to stage
+  uint32_t vw;    // the same dword of V
 };
+
+// Staged K tile of a head pair: [slot][8 dwords] (slot s = node a(s), 32 bytes: head 0
+// d 0-3, head 0 d 4-7, head 1 d 0-3, head 1 d 4-7), the four 8-byte chunks of row s
+// stored at chunk position chunk ^ ((s >> 3) & 3), so the 32 lanes reading rows 0..31 at
+// one chunk index cover all banks once.
+__device__ __forceinline__ int kt_pos(int slot, int dword) {
+  return slot * 8 + 2 * ((dword >> 1) ^ ((slot >> 3) & 3)) + (dword & 1);
+}
 
 template <bool kGuard, bool kAligned>
 __device__ __forceinline__ void fwd_load(FwdTile& t, const uint8_t* srow, const uint16_t* k,
                                          const uint16_t* v, int64_t j0, int64_t N, int h0, int hp,
-                                         int kr, int sk, int shl, int sdp) {
+                                         int sk, int shl, int sdp) {
   if (kGuard || !kAligned) {
     t.cw = load_codes16<false>(srow, j0 + 16 * hp, N);
   } else {
     t.cw = *reinterpret_cast<const u32x4*>(srow + j0 + 16 * hp);
   }
-  const int64_t kn = j0 + kr, vn = j0 + sk;
-  if (!kGuard || kn < N) {
-    const uint16_t* kp = k + kn * kHD + h0 * kD + 4 * hp;
-    t.ka = *reinterpret_cast<const s16x4*>(kp);
-    t.kb = *reinterpret_cast<const s16x4*>(kp + kD);
-  } else {
-    t.ka = s16x4{0, 0, 0, 0};
-    t.kb = s16x4{0, 0, 0, 0};
-  }
-  t.vw = (!kGuard || vn < N) ? *reinterpret_cast<const uint32_t*>(v + vn * kHD + (h0 + shl) * kD + 2 * sdp) : 0u;
+  const int64_t vn = j0 + sk;
+  const int64_t off = vn * kHD + (h0 + shl) * kD + 2 * sdp;
+  t.kw = (!kGuard || vn < N) ? *reinterpret_cast<const uint32_t*>(k + off) : 0u;
+  t.vw = (!kGuard || vn < N) ? *reinterpret_cast<const uint32_t*>(v + off) : 0u;
 }
 
 template <bool kAligned>
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
                                                                     int64_t ostride, int64_t lstride) {
   __shared__ float2 tb[256];  // both heads' bias for each byte value
   __shared__ __align__(16) uint16_t vt[2][2][kD + 1][32];  // [buffer][head][d or ones][key]
+  __shared__ __align__(16) uint32_t kt[2][32 * 8];         // [buffer] staged K tile (kt_pos)
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial
   // results at out + y*ostride, lse + y*lstride
   {
@@ -131,22 +134,27 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
     qop1 = *reinterpret_cast<const s16x4*>(qp + kD);
   }
   const uint8_t* srow = spd + irow * ldc;
-  const int kr = node_of_row(c);
   // staging role: key sk of the tile, head shl, d pair sdp (one dword per thread)
   const int sk = 8 * w + (lane >> 3), shl = (lane >> 2) & 1, sdp = lane & 3;
-  auto stage = [&](int buf, uint32_t vw) {
+  const int kslot = slot_of_node(sk), kdw = 4 * shl + sdp;  // this thread's K dword: row a^-1(sk)
+  auto stage = [&](int buf, uint32_t kw, uint32_t vw) {
+    kt[buf][kt_pos(kslot, kdw)] = kw;
     const uint32_t hh = bf16x2_to_f16x2(vw);
     vt[buf][shl][2 * sdp][sk] = static_cast<uint16_t>(hh & 0xffffu);
     vt[buf][shl][2 * sdp + 1][sk] = static_cast<uint16_t>(hh >> 16);
+  };
+  // K operand of MFMA row c, head hl: d 4hp .. 4hp+3 (8-byte chunk 2*hl + hp of row c)
+  auto kop = [&](int buf, int hl) {
+    return *reinterpret_cast<const s16x4*>(&kt[buf][kt_pos(c, 2 * (2 * hl + hp))]);
   };
 
   const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
   FwdTile cur, nxt;
   if (nfull > 0)
-    fwd_load<false, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, kr, sk, shl, sdp);
+    fwd_load<false, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, sk, shl, sdp);
   else
-    fwd_load<true, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, kr, sk, shl, sdp);
-  stage(0, cur.vw);
+    fwd_load<true, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, sk, shl, sdp);
+  stage(0, cur.kw, cur.vw);
   wait_vm0();
   __syncthreads();
 
@@ -160,9 +168,9 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
     const int64_t j0 = t * 32;
     const int buf = static_cast<int>(t & 1);
     if (t + 1 < nfull)
-      fwd_load<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, kr, sk, shl, sdp);
+      fwd_load<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, sk, shl, sdp);
     else if (t + 1 < ntiles)
-      fwd_load<true, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, kr, sk, shl, sdp);
+      fwd_load<true, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, sk, shl, sdp);
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -170,8 +178,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
       s0[e] = tv.x;
       s1[e] = tv.y;
     }
-    s0 = mfma_x8(cur.ka, qop0, s0);
-    s1 = mfma_x8(cur.kb, qop1, s1);
+    s0 = mfma_x8(kop(buf, 0), qop0, s0);
+    s1 = mfma_x8(kop(buf, 1), qop1, s1);
     if constexpr (kMask) {
       const int64_t lim = Nk - (j0 + 16 * hp);  // entries e >= lim are past the last key
 #pragma unroll
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
       o1 = mfma_h16(vb, pack_f16x8(s1, 8 * k1), o1);
     }
     if (t + 1 < ntiles) {
-      stage(buf ^ 1, nxt.vw);
+      stage(buf ^ 1, nxt.kw, nxt.vw);
       cur = nxt;
     }
     __syncthreads();
