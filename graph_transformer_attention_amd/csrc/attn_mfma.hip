@@ -44,10 +44,11 @@ constexpr int kHD = kH * kD;
 // the MFMA also accumulates the row sum l.
 //
 // A workgroup is 4 waves = 128 queries x 2 heads (ordered as in xcd_map); the waves
-// share one transposed half-precision V tile in LDS (double-buffered, one barrier per key tile; each wave
-// converts a quarter of it), and each wave prefetches the next tile's codes and K
-// operands into registers while it computes the current one. Only the last key tile
-// can be partial, so only it takes the guarded loads and the -inf mask.
+// share each key tile's K rows and transposed half-precision V in LDS (double-buffered,
+// one barrier per key tile; every thread stages one dword of each, V converted to half),
+// and each wave prefetches the next tile's codes and its staging share into registers
+// while it computes the current one. Only the last key tile can be partial, so only it
+// takes the guarded loads and the -inf mask.
 //
 // The running max is updated lazily: a wave rescales its accumulators only when some
 // lane's tile max exceeds its current max by more than kLazy (in log2 units), so the
