@@ -87,10 +87,13 @@ def test_bwd_argument_errors():
 def test_split_workspaces():
     """Launches whose workgroups would not fill whole rounds split the inner loop: the
     forward then needs a workspace for its partial results, and the backward's grows;
-    at 32768 nodes the forward and key-outer passes fill whole rounds and do not split."""
+    at 32768 nodes (D = 8) the forward and key-outer passes fill whole rounds and do not split."""
     L = gta.lib()
     assert L.gt_attn_fwd_workspace_bytes(32768, 8, 8, 33, 1) == 0    # 1024 workgroups: one full round
-    assert L.gt_attn_fwd_workspace_bytes(65536, 8, 32, 49, 1) == 0   # 2048: four full rounds
+    # D = 32, 65536 nodes: 2048 workgroups at 3 per CU would leave the third round two thirds
+    # full; three key splits (8 rounds of 683 tiles) cost less than 3 rounds of 2048 tiles
+    rows = 65536 * 8
+    assert L.gt_attn_fwd_workspace_bytes(65536, 8, 32, 49, 1) == 3 * (rows * 32 * 4 + rows * 4)
     # 100000 nodes: 3128 workgroups would leave the last wave of resident workgroups 5% full; two splits do better
     assert L.gt_attn_fwd_workspace_bytes(100000, 8, 8, 33, 1) > 0
     assert L.gt_attn_fwd_workspace_bytes(6800, 8, 8, 33, 0) == 0         # vector-ALU path: no split
