@@ -61,12 +61,17 @@ struct FwdTile {
   uint32_t vw;    // the same dword of V
 };
 
-// Staged K tile of a head pair: [slot][8 dwords] (slot s = node a(s), 32 bytes: head 0
-// d 0-3, head 0 d 4-7, head 1 d 0-3, head 1 d 4-7), the four 8-byte chunks of row s
-// stored at chunk position chunk ^ ((s >> 3) & 3), so the 32 lanes reading rows 0..31 at
-// one chunk index cover all banks once.
-__device__ __forceinline__ int kt_pos(int slot, int dword) {
-  return slot * 8 + 2 * ((dword >> 1) ^ ((slot >> 3) & 3)) + (dword & 1);
+// Staged K tile of a head pair: [key][8 dwords], 32 bytes per key: head h's 8 d values
+// (16 bytes) at half h ^ ((key >> 4) & 1), so the 16 lanes of one score MFMA that read
+// 16-byte halves of keys {8g..8g+7} and {16+8g..16+8g+7} cover all banks once.
+__device__ __forceinline__ int kt_pos(int key, int head) { return key * 8 + 4 * (head ^ ((key >> 4) & 1)); }
+
+// 8 of 16 accumulator entries (first, first+2, ..., first+14) as an f16 MFMA operand
+__device__ __forceinline__ s16x8 pack_f16x8_odd_even(const f32x16& a, int first) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<_Float16>(a[first + 2 * e]);
+  return __builtin_bit_cast(s16x8, r);
 }
 
 template <bool kGuard, bool kAligned>
@@ -97,6 +102,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
   __shared__ float2 tb[256];  // both heads' bias for each byte value
   __shared__ __align__(16) uint16_t vt[2][2][kD + 1][32];  // [buffer][head][d or ones][key]
   __shared__ __align__(16) uint32_t kt[2][32 * 8];         // [buffer] staged K tile (kt_pos)
+  __shared__ __align__(16) uint32_t kzero[4];              // the zero half of a score operand
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial
   // results at out + y*ostride, lse + y*lstride
   {
@@ -128,25 +134,29 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
     tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
   }
   for (int x = tid; x < 2 * 2 * 32; x += 64 * kFwdWaves) vt[x >> 6][(x >> 5) & 1][kD][x & 31] = 0x3C00;  // 1.0
-  s16x4 qop0 = s16x4{0, 0, 0, 0}, qop1 = s16x4{0, 0, 0, 0};
-  if (qvalid) {
-    const uint16_t* qp = q + i * kHD + h0 * kD + 4 * hp;
-    qop0 = *reinterpret_cast<const s16x4*>(qp);
-    qop1 = *reinterpret_cast<const s16x4*>(qp + kD);
-  }
+  if (tid < 4) kzero[tid] = 0u;
+  // query operand of the score MFMAs: the 8 d values of head h0 + hp (k-group hp)
+  const s16x8 qop = qvalid ? load_h8(q + i * kHD + (h0 + hp) * kD) : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
   const uint8_t* srow = spd + irow * ldc;
   // staging role: key sk of the tile, head shl, d pair sdp (one dword per thread)
   const int sk = 8 * w + (lane >> 3), shl = (lane >> 2) & 1, sdp = lane & 3;
-  const int kslot = slot_of_node(sk), kdw = 4 * shl + sdp;  // this thread's K dword: row a^-1(sk)
+  const int kdw = kt_pos(sk, shl) + sdp;  // this thread's K dword
   auto stage = [&](int buf, uint32_t kw, uint32_t vw) {
-    kt[buf][kt_pos(kslot, kdw)] = kw;
+    kt[buf][kdw] = kw;
     const uint32_t hh = bf16x2_to_f16x2(vw);
     vt[buf][shl][2 * sdp][sk] = static_cast<uint16_t>(hh & 0xffffu);
     vt[buf][shl][2 * sdp + 1][sk] = static_cast<uint16_t>(hh >> 16);
   };
-  // K operand of MFMA row c, head hl: d 4hp .. 4hp+3 (8-byte chunk 2*hl + hp of row c)
-  auto kop = [&](int buf, int hl) {
-    return *reinterpret_cast<const s16x4*>(&kt[buf][kt_pos(c, 2 * (2 * hl + hp))]);
+  // Score MFMA g (g = 0, 1) of a tile covers 16 keys of both heads: accumulator row r
+  // stands for key 16*((r >> 2) & 1) + 8g + 2*(r >> 3) + ((r & 3) >> 1) and head r & 1, so a
+  // lane's entries 2m and 2m+1 are key 16*hp + 8g + m of heads 0 and 1: one 8-byte table
+  // read fills both. The contraction runs over the 16 d values of both heads (k-group =
+  // head): row c's operand is its key's k for its head, zero for the other head.
+  const bool kown = (c & 1) == hp;
+  const int krow0 = 16 * ((c >> 2) & 1) + 2 * (c >> 3) + ((c & 3) >> 1);  // key of row c at g = 0
+  auto kop = [&](int buf, int g) {
+    const uint32_t* p = kown ? &kt[buf][kt_pos(krow0 + 8 * g, hp)] : kzero;
+    return *reinterpret_cast<const s16x8*>(p);
   };
 
   const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
@@ -172,30 +182,31 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
       fwd_load<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, sk, shl, sdp);
     else if (t + 1 < ntiles)
       fwd_load<true, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, sk, shl, sdp);
-    f32x16 s0, s1;
+    // sg[g]: entries 2m, 2m+1 = key 16*hp + 8g + m, heads 0 and 1
+    f32x16 sg[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float2 tv = tb[code_byte(cur.cw, e)];
-      s0[e] = tv.x;
-      s1[e] = tv.y;
-    }
-    s0 = mfma_x8(kop(buf, 0), qop0, s0);
-    s1 = mfma_x8(kop(buf, 1), qop1, s1);
-    if constexpr (kMask) {
-      const int64_t lim = Nk - (j0 + 16 * hp);  // entries e >= lim are past the last key
+    for (int g = 0; g < 2; ++g) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        if (e >= lim) {
-          s0[e] = -INFINITY;
-          s1[e] = -INFINITY;
-        }
+      for (int m = 0; m < 8; ++m) {
+        const float2 tv = tb[code_byte(cur.cw, 8 * g + m)];
+        sg[g][2 * m] = tv.x;
+        sg[g][2 * m + 1] = tv.y;
       }
+      sg[g] = mfma_b16(kop(buf, g), qop, sg[g]);
     }
-    float x0 = s0[0], x1 = s1[0];
+    if constexpr (kMask) {
+      const int64_t lim = Nk - (j0 + 16 * hp);  // lane keys 8g + m >= lim are past the last key
 #pragma unroll
-    for (int e = 1; e < 16; ++e) {
-      x0 = fmaxf(x0, s0[e]);
-      x1 = fmaxf(x1, s1[e]);
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (8 * g + (e >> 1) >= lim) sg[g][e] = -INFINITY;
+    }
+    float x0 = sg[0][0], x1 = sg[0][1];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) {
+      x0 = fmaxf(x0, sg[j >> 3][2 * (j & 7)]);
+      x1 = fmaxf(x1, sg[j >> 3][2 * (j & 7) + 1]);
     }
     // Each lane tests its own 16 keys; the two lane halves of a query column are combined
     // only on the rare rescale path, so the common path has no cross-lane step.
@@ -215,18 +226,21 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
     }
     const float b0 = -m0 * sc2, b1 = -m1 * sc2;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, b0));
-      s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, b1));
-    }
-    // rows >= 9 of the V^T operand only feed output rows that are never read
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        sg[g][e] = __builtin_amdgcn_exp2f(fmaf(sg[g][e], sc2, b0));
+        sg[g][e + 1] = __builtin_amdgcn_exp2f(fmaf(sg[g][e + 1], sc2, b1));
+      }
+    // rows >= 9 of the V^T operand only feed output rows that are never read; PV MFMA g
+    // contracts over keys 16*hp + 8g .. +7 (k-group hp), the lane's keys of score MFMA g
     const int vr = min(c, kD);
 #pragma unroll
-    for (int k1 = 0; k1 < 2; ++k1) {
-      const s16x8 va = *reinterpret_cast<const s16x8*>(&vt[buf][0][vr][16 * hp + 8 * k1]);
-      const s16x8 vb = *reinterpret_cast<const s16x8*>(&vt[buf][1][vr][16 * hp + 8 * k1]);
-      o0 = mfma_h16(va, pack_f16x8(s0, 8 * k1), o0);
-      o1 = mfma_h16(vb, pack_f16x8(s1, 8 * k1), o1);
+    for (int g = 0; g < 2; ++g) {
+      const s16x8 va = *reinterpret_cast<const s16x8*>(&vt[buf][0][vr][16 * hp + 8 * g]);
+      const s16x8 vb = *reinterpret_cast<const s16x8*>(&vt[buf][1][vr][16 * hp + 8 * g]);
+      o0 = mfma_h16(va, pack_f16x8_odd_even(sg[g], 0), o0);
+      o1 = mfma_h16(vb, pack_f16x8_odd_even(sg[g], 1), o1);
     }
     if (t + 1 < ntiles) {
       stage(buf ^ 1, nxt.kw, nxt.vw);
