@@ -11,18 +11,18 @@
 // MegaGraph pages, abstract: the score matrix and the topology-aware bias matrix are
 // what make full-graph attention expensive; Fig. 4 caption: work proceeds over key
 // blocks with the bias columns sliced to each block. Neither matrix exists here
-// outside registers: each 32x32 score tile of a head is one MFMA whose accumulator
-// starts from the tile's bias, table[h, code] read from LDS by the uint8 code, so
-// adding the bias costs no vector instruction.
+// outside registers: each score MFMA's accumulator starts from the tile's bias,
+// table[h, code] read from LDS by the uint8 code, so adding the bias costs no vector
+// instruction.
 //
 // Work split: workgroups of 4 waves; each wave owns 32 nodes of its outer loop and
 // two heads (the head pair follows from the workgroup order, xcd_map). Lane l holds
-// column c = l % 32 of every 32x32 tile and one half hp = l / 32 of its rows, in the
-// row order of node_of_row (mfma_common.h): the lane's 16 accumulator entries are 16
-// consecutive nodes, so its codes are one 16-byte load and each 8-entry half of its
-// accumulator is directly an operand of the 32x32x16 MFMA that contracts over those
-// nodes, whose other operand is read as 8 consecutive nodes of a transposed
-// [d][node] tile in LDS.
+// column c = l % 32 of every 32x32 tile and one half hp = l / 32 of its rows. In the
+// backward, rows follow node_of_row (mfma_common.h): the lane's 16 accumulator entries
+// are 16 consecutive nodes, so its codes are one 16-byte load and each 8-entry half of
+// its accumulator is directly an operand of the 32x32x16 MFMA that contracts over those
+// nodes, whose other operand is read as 8 consecutive nodes of a transposed [d][node]
+// tile in LDS. The forward interleaves the two heads in its score tiles (below).
 //
 // Table in LDS: for each byte value b, both heads' table[h, min(b, NB-1)] * sqrt(D) as one
 // float2 (one 8-byte read per entry), so every byte value indexes it without a clamp.
@@ -39,9 +39,10 @@ constexpr int kH = 8;
 constexpr int kHD = kH * kD;
 
 // ---------------------------------------------------------------------------------
-// Forward. S^T = K Q^T per 32-key tile (rows = keys in the order above, columns =
-// queries); running max per query column; O^T += V^T P^T with a ones row in V^T so
-// the MFMA also accumulates the row sum l.
+// Forward. Per 32-key tile, S^T = K Q^T for both heads as two MFMAs over 16 keys each
+// (rows = key and head pairs, columns = queries; see kop below); running max per query
+// column and head; O^T += V^T P^T with a ones row in V^T so the MFMA also accumulates
+// the row sum l.
 //
 // A workgroup is 4 waves = 128 queries x 2 heads (ordered as in xcd_map); the waves
 // share each key tile's K rows and transposed half-precision V in LDS (double-buffered,
