@@ -14,7 +14,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Running-max slack of the forward's lazy rescale, in log2 units.
 constexpr float kLazy = 8.0f;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -82,9 +81,6 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ f32x16 mfma_x8(s16x4 a, s16x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x16 mfma_h16(s16x8 a, s16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                  0, 0, 0);
