@@ -19,6 +19,7 @@
 #include "mfma_common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace gt {
 namespace {
@@ -286,8 +287,9 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* 
                                                                 const float* __restrict__ out,
                                                                 const uint16_t* __restrict__ dout,
                                                                 const float* __restrict__ lse, OpsD32 ops,
-                                                                int64_t N, int64_t Nk) {
+                                                                int64_t N, int64_t Nk, uint32_t* __restrict__ flag) {
   const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (x == 0) *flag = 0u;  // the key-outer pass's code-range flag starts clear
   const int64_t nmax = ops.npq > ops.npk ? ops.npq : ops.npk;
   if (x >= nmax * kH) return;
   const int h = static_cast<int>(x / nmax);
@@ -414,19 +416,29 @@ __device__ __forceinline__ s16x8 aug_chunk(uint32_t ab, uint16_t cc, int hp) {
 // 4 waves share each staged query tile (q and dout rows, q^T and dout^T), staged
 // once per tile in LDS. S and dP - delta come from 3 MFMAs each (rows = queries,
 // columns = keys), P = exp2(S log2e / sqrt(D)), dS = P (dP - delta); dV^T += dO^T P
-// and dK^T += Q^T dS contract over the tile's queries. Bucket sums of dS go to LDS
-// bins [bucket][key][head] shared by the two lane halves of a wave, which update them
-// one half after the other (in program order) so no two lanes touch a bin at once.
+// and dK^T += Q^T dS contract over the tile's queries. Bucket sums of dS go to LDS bins
+// in one of two layouts:
+//  * kPrivate: [bucket][64 lanes][2 heads], one bin row per lane, so every lane updates
+//    its own bins in the same instruction. Only buckets below kPrivBins fit in LDS at this
+//    occupancy; a lane that meets a larger code raises *flag, and the launch is then
+//    redone by the shared layout, which overwrites every output of this one.
+//  * shared: [bucket][32 keys][2 heads], the two lane halves of a wave (which hold the
+//    same 32 keys) updating it one half after the other, so no two lanes touch a bin at
+//    once. Any NB. As the rerun of a private launch (flag given) it returns at once unless
+//    *flag was raised.
 constexpr int kKvTbD32 = 64;  // key-outer table entries (float2: both heads), codes clamped to NB-1 <= 63
+constexpr int kPrivBins = 16;  // buckets of the private layout
 
-template <bool kAligned>
+template <bool kAligned, bool kPrivate>
 __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t* __restrict__ spd_t,
                                                                    const float* __restrict__ table, OpsD32 ops,
                                                                    float* __restrict__ dk, float* __restrict__ dv,
                                                                    float* __restrict__ partial, int64_t N, int64_t Nk,
                                                                    int64_t ldt, int NB, int acc, int64_t qchunk,
-                                                                   int64_t gstride, int64_t pstride) {
+                                                                   int64_t gstride, int64_t pstride,
+                                                                   uint32_t* __restrict__ flag) {
   extern __shared__ __align__(16) unsigned char smem[];
+  if (!kPrivate && flag != nullptr && *flag == 0u) return;  // the private launch was exact
   // workgroup row y of a split launch: queries [y*qchunk, min(N, (y+1)*qchunk)), partial
   // dK, dV at + y*gstride and bucket partials at + y*pstride
   const int64_t ib = static_cast<int64_t>(blockIdx.y) * qchunk;
@@ -441,8 +453,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   dv += blockIdx.y * gstride;
   partial += blockIdx.y * pstride;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 32);  // [NB][32 keys][2 heads] per wave
-  float2* tb = reinterpret_cast<float2*>(reinterpret_cast<float*>(smem) + kWaves * 2 * NB * 32);  // by code
+  constexpr int kBinLanes = kPrivate ? 64 : 32;                          // bin rows per bucket
+  const int nbins = kPrivate ? kPrivBins : NB;
+  float* bins = reinterpret_cast<float*>(smem) + w * (2 * nbins * kBinLanes);  // [nbins][rows][2 heads] per wave
+  float2* tb = reinterpret_cast<float2*>(reinterpret_cast<float*>(smem) + kWaves * 2 * nbins * kBinLanes);
   uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTbD32);
 
   const int npad32 = static_cast<int>(ops.npk / 32);
@@ -464,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
     const int c = min(b, NB - 1);
     tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
   }
-  for (int x = lane; x < 2 * NB * 32; x += 64) bins[x] = 0.f;
+  for (int x = lane; x < 2 * nbins * kBinLanes; x += 64) bins[x] = 0.f;
   s16x8 kop[2][2], vop[2][2];
 #pragma unroll
   for (int hl = 0; hl < 2; ++hl)
@@ -478,7 +492,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   const s16x8 vaug = aug_chunk(pack2(one, one), 0, hp);
   f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
   const uint32_t nbm1 = static_cast<uint32_t>(NB - 1);
-  float2* mybins = reinterpret_cast<float2*>(bins) + c;
+  float2* mybins = reinterpret_cast<float2*>(bins) + (kPrivate ? lane : c);
+  // private layout: bytes >= kPrivBins seen by this lane (a clamped code >= kPrivBins needs
+  // a raw byte >= kPrivBins; with NB <= kPrivBins every clamped code fits)
+  const bool check_range = kPrivate && NB > kPrivBins;
+  uint32_t over = 0u;
   const uint8_t* crow = spd_t + (j < Nk ? j : Nk - 1) * ldt + ib;
   const int64_t cc = 16 * hp;
   const int qr = node_of_row(c);
@@ -528,6 +546,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
         s0[e] = t.x;
         s1[e] = t.y;
       }
+      if (check_range) over |= (cw[0] | cw[1] | cw[2] | cw[3]) & 0xF0F0F0F0u;
       f32x16 p0 = {}, p1 = {};
 #pragma unroll
       for (int ci = 0; ci < 2; ++ci) {
@@ -549,16 +568,27 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
         p0[e] *= pa;
         p1[e] *= pb;
       }
-      // lane half 0 first, then half 1: the two halves hold the same 32 keys
+      if constexpr (kPrivate) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (hp == half) {
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t b = min(code[e], static_cast<uint32_t>(kPrivBins - 1));  // in range even when flagged
+          float2 bin = mybins[b * 64];
+          bin.x += p0[e];
+          bin.y += p1[e];
+          mybins[b * 64] = bin;
+        }
+      } else {
+        // lane half 0 first, then half 1: the two halves hold the same 32 keys
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float2 bin = mybins[code[e] * 32];
-            bin.x += p0[e];
-            bin.y += p1[e];
-            mybins[code[e] * 32] = bin;
+        for (int half = 0; half < 2; ++half) {
+          if (hp == half) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              float2 bin = mybins[code[e] * 32];
+              bin.x += p0[e];
+              bin.y += p1[e];
+              mybins[code[e] * 32] = bin;
+            }
           }
         }
       }
@@ -592,18 +622,23 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
       store4(vp0 + kD + 8 * jq, make_float4(dv1[4 * jq], dv1[4 * jq + 1], dv1[4 * jq + 2], dv1[4 * jq + 3]), acc);
     }
   }
+  if (kPrivate && over != 0u) *flag = 1u;  // every writer stores the same value
   // per-wave bins -> one partial row per 32-key block and head (a wave past the last key
-  // block writes its zero bins too, so every partial row is defined)
+  // block writes its zero bins too, so every partial row is defined); buckets past the
+  // private layout's bins had no entries unless the flag was raised
   for (int x = lane; x < 2 * NB; x += 64) {
     const int hl = x / NB, b = x - hl * NB;
-    const float* srcb = bins + b * 64 + hl;
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains, fixed order
+    float sum = 0.f;
+    if (b < nbins) {
+      const float* srcb = bins + b * (2 * kBinLanes) + hl;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains, fixed order
 #pragma unroll
-    for (int l = 0; l < 32; l += 4) {
+      for (int l = 0; l < kBinLanes; l += 4) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) s4[u] += srcb[2 * (l + u)];
+        for (int u = 0; u < 4; ++u) s4[u] += srcb[2 * (l + u)];
+      }
+      sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
-    const float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     partial[((jw / 32) * kH + h0 + hl) * NB + b] = sum;
   }
 }
@@ -765,8 +800,9 @@ OpsD32 carve_ops_d32(void* base, int64_t N, int64_t Nk) {
   return o;
 }
 
-size_t kv_d32_lds(int NB) {
-  return 4ull * kWaves * 2 * NB * 32 + sizeof(float2) * kKvTbD32 + 2ull * StageSetD32<2, 2>::kHalves;
+size_t kv_d32_lds(int NB, bool priv) {
+  const size_t bins = priv ? 4ull * kWaves * 2 * kPrivBins * 64 : 4ull * kWaves * 2 * NB * 32;
+  return bins + sizeof(float2) * kKvTbD32 + 2ull * StageSetD32<2, 2>::kHalves;
 }
 
 }  // namespace
@@ -813,12 +849,13 @@ hipError_t launch_bwd_mfma_d32(const BwdArgs& a, const BwdWorkspace& w, hipStrea
   char* base = static_cast<char*>(a.workspace);
   const OpsD32 ops = carve_ops_d32(base + w.ops_off, a.N, a.Nk);
   float* partial = reinterpret_cast<float*>(base + w.partial_off);
+  uint32_t* flag = reinterpret_cast<uint32_t*>(base + w.flag_off);
   const int64_t prep_threads = std::max(ops.npq, ops.npk) * kH;
   trace_begin(kTraceBwdDelta, s);
   hipLaunchKernelGGL(bwd_prep_mfma_d32_kernel, dim3(static_cast<unsigned>((prep_threads + 255) / 256)), dim3(256), 0,
                      s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.out, static_cast<const uint16_t*>(a.dout), a.lse, ops, a.N,
-                     a.Nk);
+                     a.Nk, flag);
   hipError_t e = hipGetLastError();
   trace_end(kTraceBwdDelta, s);
   if (e != hipSuccess) return e;
@@ -833,18 +870,39 @@ hipError_t launch_bwd_mfma_d32(const BwdArgs& a, const BwdWorkspace& w, hipStrea
   const int64_t pstride = w.n_kv_blocks * kH * a.NB;
   const int nkb = static_cast<int>((ops.npk / 32 + kWaves - 1) / kWaves);
   const dim3 kgrid(static_cast<unsigned>(xcd_grid(nkb)), static_cast<unsigned>(w.kv.S));
-  const size_t lds = kv_d32_lds(a.NB);
-  e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<true>, lds);
-  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<false>, lds);
+  // Private bins first when its outputs may be overwritten by a rerun (no accumulation
+  // into dK, dV); the shared-bin launch after it runs only if a code fell outside the
+  // private bins (never when NB <= kPrivBins, so it is then not launched).
+  const bool priv = kv_acc == 0;
+  const bool aligned = codes_aligned(a.spd_t, a.ld_t);
+  const size_t lds_priv = kv_d32_lds(a.NB, true), lds_shared = kv_d32_lds(a.NB, false);
+  e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<true, false>, lds_shared);
+  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<false, false>, lds_shared);
+  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<true, true>, lds_priv);
+  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<false, true>, lds_priv);
   if (e != hipSuccess) return e;
+  auto kv_launch = [&](auto private_tag, uint32_t* f) {
+    constexpr bool kP = decltype(private_tag)::value;
+    const size_t lds = kP ? lds_priv : lds_shared;
+    if (aligned)
+      hipLaunchKernelGGL((bwd_kv_mfma_d32_kernel<true, kP>), kgrid, dim3(kThreads), lds, s, a.spd_t, a.table, ops,
+                         dkp, dvp, partial, a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride, f);
+    else
+      hipLaunchKernelGGL((bwd_kv_mfma_d32_kernel<false, kP>), kgrid, dim3(kThreads), lds, s, a.spd_t, a.table, ops,
+                         dkp, dvp, partial, a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride, f);
+  };
   trace_begin(kTraceBwdKv, s);
-  if (codes_aligned(a.spd_t, a.ld_t))
-    hipLaunchKernelGGL(bwd_kv_mfma_d32_kernel<true>, kgrid, dim3(kThreads), lds, s, a.spd_t, a.table, ops, dkp, dvp,
-                       partial, a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride);
-  else
-    hipLaunchKernelGGL(bwd_kv_mfma_d32_kernel<false>, kgrid, dim3(kThreads), lds, s, a.spd_t, a.table, ops, dkp, dvp,
-                       partial, a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride);
-  e = hipGetLastError();
+  if (priv) {
+    kv_launch(std::true_type{}, flag);
+    e = hipGetLastError();
+    if (e == hipSuccess && a.NB > kPrivBins) {
+      kv_launch(std::false_type{}, flag);
+      e = hipGetLastError();
+    }
+  } else {
+    kv_launch(std::false_type{}, nullptr);
+    e = hipGetLastError();
+  }
   trace_end(kTraceBwdKv, s);
   if (e != hipSuccess) return e;
 

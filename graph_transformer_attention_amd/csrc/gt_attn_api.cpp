@@ -328,7 +328,8 @@ BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtyp
   const size_t dkv = w.kv.S > 1 ? up256(2 * static_cast<size_t>(w.kv.S) * Nk * H * D * f) : 0;
   w.dq_off = w.dkv_off + dkv;
   const size_t dq = w.q.S > 1 ? up256(static_cast<size_t>(w.q.S) * N * H * D * f) : 0;
-  w.bytes = w.dq_off + dq;
+  w.flag_off = w.dq_off + dq;  // one device word the kernels of a call share (D = 32 key-outer)
+  w.bytes = w.flag_off + 256;
   return w;
 }
 

@@ -69,7 +69,7 @@ enum { kAccDq = 1, kAccDkv = 2, kAccDtable = 4 };
 // key-outer pass's dK, dV partials [kv.S][2][Nk*H*D] and the query-outer pass's dQ
 // partials [q.S][N*H*D] float.
 struct BwdWorkspace {
-  size_t delta_off, ops_off, partial_off, dkv_off, dq_off, bytes;
+  size_t delta_off, ops_off, partial_off, dkv_off, dq_off, flag_off, bytes;
   int64_t n_kv_blocks;  // partial rows of one split
   Split kv, q;
 };

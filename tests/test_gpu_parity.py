@@ -69,6 +69,12 @@ def test_er256_f32_full():
     (17, 8, 32, 20, "bf16", "er"),
     (129, 8, 32, 30, "bf16", "path"),
     (161, 8, 32, 63, "bf16", "er"),
+    # the D = 32 key-outer pass keeps private bins for codes 0..15 and reruns with shared
+    # bins when a larger code occurs: a 16-node path tops out at code 15 (private bins
+    # only), a 17-node path reaches code 16 (rerun); the 1000-node path reruns a split launch
+    (16, 8, 32, 20, "bf16", "path"),
+    (17, 8, 32, 20, "bf16", "path"),
+    (1000, 8, 32, 30, "bf16", "path"),
     # graphs too small to fill the GPU by rows: every matrix-core kernel splits its inner
     # loop (3 splits here, the last one ragged) and partial results are combined
     (777, 8, 8, 20, "bf16", "er"),
