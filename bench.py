@@ -44,20 +44,23 @@ MFMA_PEAK_TFLOPS = 2500.0
 CONTRACTIONS = {"fwd": 2, "bwd_kv": 4, "bwd_q": 3}
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # sources of the kernels the default workload runs (bf16, H = 8, D = 8: the MFMA path)
-KERNEL_SOURCES = ["graph_transformer_attention_amd/csrc/attn_mfma.hip",
-                  "graph_transformer_attention_amd/csrc/mfma_common.h"]
+# matrix-core kernel sources by head dimension (what a recorded traffic figure was taken on)
+KERNEL_SOURCES = {8: ["graph_transformer_attention_amd/csrc/attn_mfma.hip",
+                      "graph_transformer_attention_amd/csrc/mfma_common.h"],
+                  32: ["graph_transformer_attention_amd/csrc/attn_mfma_d32.hip",
+                       "graph_transformer_attention_amd/csrc/mfma_common.h"]}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(D: int = 8) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES.get(D, KERNEL_SOURCES[8]):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel: str, workload: str):
+def recorded_traffic(kernel: str, workload: str, D: int = 8):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
     or None when there is none or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
@@ -65,7 +68,7 @@ def recorded_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(D):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -385,7 +388,7 @@ def main():
                     "op": "exp2 (one per score entry and pass; peak from unit counts: 1024 SIMDs x 8 lanes/clock x "
                           "2.4 GHz; peak_measured = this run's v_exp_f32 probe)",
                     "ops_per_launch": ex}
-    roofline.update({"traffic": recorded_traffic(dom, w.name) if P == 1 else None,
+    roofline.update({"traffic": recorded_traffic(dom, w.name, w.D) if P == 1 else None,
                      "algorithmic_bytes_per_launch": by, "avg_launch_ms": round(dom_s * 1e3, 4)})
 
     pairs = L * H * N * N
@@ -424,7 +427,7 @@ def main():
         "exp_peak_tops": round(exp_peak, 3),
         "exp_peak_measured_tops": round(exp_measured, 3),
         "exp_frac_of_step": round(3 * pairs / (ms_step * 1e-3) / (exp_peak * 1e12), 4),
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(w.D),
         "checks": checks,
     }
     if not args.no_cpu_baseline:

@@ -65,12 +65,20 @@ def test_traffic_record_is_tied_to_the_kernel_sources(bench, tmp_path, monkeypat
     if rec["source_hash"] == bench.kernel_source_hash():
         assert bench.recorded_traffic("bwd_kv", "ba32768-bf16") == rec["kernels"]["bwd_kv"]["hbm_bytes_per_launch"]
     assert bench.recorded_traffic("bwd_kv", "no-such-workload") is None
+    # the head-dimension-32 record is checked against that path's sources
+    with open(os.path.join(ROOT, "profiles", "traffic_sbm65536-d32-bf16.json")) as f:
+        rec32 = json.load(f)
+    assert bench.kernel_source_hash(32) != bench.kernel_source_hash(8)
+    if rec32["source_hash"] == bench.kernel_source_hash(32):
+        assert (bench.recorded_traffic("bwd_kv", "sbm65536-d32-bf16", 32)
+                == rec32["kernels"]["bwd_kv"]["hbm_bytes_per_launch"])
+    assert bench.recorded_traffic("bwd_kv", "sbm65536-d32-bf16", 8) is None
     # a record taken from other sources is not used
     (tmp_path / "profiles").mkdir()
     rec["source_hash"] = "0" * 16
     (tmp_path / "profiles" / "traffic_ba32768-bf16.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "f" * 16)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda D=8: "f" * 16)
     assert bench.recorded_traffic("bwd_kv", "ba32768-bf16") is None
 
 
