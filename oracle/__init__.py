@@ -20,10 +20,13 @@ not an online update.
 
 Pins (tests marked "not gpu") tie every function to something other than
 itself: brute force on tiny inputs, scipy/torch library special cases,
-closed forms, permutation equivariance and finite differences. No function
-here is "parity unpinned".
+closed forms, permutation equivariance and finite differences. The bf16
+storage points of the multi-layer models (stack and full layer) are pinned
+against torch autograd with torch's own bf16 conversion, and each point is
+shown to change the result when left out. No function here is "parity
+unpinned".
 """
 from .spd import bfs_codes, bfs_codes_parallel, certify_codes, components  # noqa: F401
-from .attention import forward, backward, backward_block, full_backward, merge, sum_dtable_rows  # noqa: F401
+from .attention import forward, backward, backward_block, full_backward, merge  # noqa: F401
 from .bf16 import round_bf16  # noqa: F401
 from .stack import qkv_projection, qkv_projection_backward, stack_forward_backward  # noqa: F401

@@ -140,10 +140,6 @@ def backward_block(q, k, v, codes, table, out, lse, dout):
     return dq, dk, dv, dtable
 
 
-def sum_dtable_rows(dtable_blocks):
-    return np.sum(np.stack(dtable_blocks), axis=0)
-
-
 _G = {}
 
 
