@@ -132,6 +132,26 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a binding call with `stream` (when given) as torch's current stream, so that the
+    outputs and temporary workspaces it allocates belong to the stream its kernels run on:
+    the caching allocator then hands a dropped temporary to later work on that stream only,
+    which the stream orders after the kernels that used it."""
+    import functools
+    import inspect
+    pos = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = kwargs.get("stream", args[pos] if len(args) > pos else None)
+        if stream is None:
+            return fn(*args, **kwargs)
+        import torch
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _dev(t, name, dtype=None, shape=None):
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -159,6 +179,7 @@ def fwd_workspace_bytes(N: int, H: int, D: int, NB: int, dtype: int) -> int:
     return int(lib().gt_attn_fwd_workspace_bytes(N, H, D, NB, dtype))
 
 
+@_on_stream
 def fwd(q, k, v, spd, table, out=None, lse=None, workspace=None, stream=None):
     """Forward: q, k, v [N,H,D] (float32 or bfloat16), spd [N,N] uint8, table [H,NB] float32.
     Returns (out [N,H,D] float32, lse [N,H] float32)."""
@@ -187,6 +208,7 @@ def bwd_workspace_bytes(N: int, H: int, D: int, NB: int, dtype: int) -> int:
     return int(lib().gt_attn_bwd_workspace_bytes(N, H, D, NB, dtype))
 
 
+@_on_stream
 def bwd(q, k, v, spd, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=None,
         workspace=None, stream=None, spd_t=None):
     """Backward of fwd for loss sum(dout*out). Returns (dq, dk, dv [N,H,D] float32, dtable [H,NB]).
@@ -238,6 +260,7 @@ def fwd_block_workspace_bytes(Nq: int, Nk: int, H: int, D: int, NB: int, dtype: 
     return int(lib().gt_attn_fwd_block_workspace_bytes(Nq, Nk, H, D, NB, dtype))
 
 
+@_on_stream
 def fwd_block(q, k, v, spd, table, out=None, lse=None, workspace=None, accumulate=False, stream=None):
     """Attention of Nq query rows restricted to one block of Nk keys.
 
@@ -265,6 +288,7 @@ def fwd_block(q, k, v, spd, table, out=None, lse=None, workspace=None, accumulat
     return out, lse
 
 
+@_on_stream
 def merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, stream=None):
     """Merge two partial results over disjoint key sets by their lse. out/lse may be
     out_a/lse_a (running merge). Returns (out, lse)."""
@@ -284,6 +308,7 @@ def bwd_block_workspace_bytes(Nq: int, Nk: int, H: int, D: int, NB: int, dtype: 
     return int(lib().gt_attn_bwd_block_workspace_bytes(Nq, Nk, H, D, NB, dtype))
 
 
+@_on_stream
 def bwd_block(q, k, v, spd, spd_t, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=None,
               accumulate=False, workspace=None, stream=None):
     """Backward of one key block given the MERGED out/lse over all keys.
@@ -339,6 +364,7 @@ def spd_build(indptr, indices, N: int, C: int, nthreads: int = 0, out=None) -> n
     return out
 
 
+@_on_stream
 def spd_build_device(indptr, indices, N: int, C: int, out=None, workspace=None, stream=None):
     """The codes of spd_build computed on the GPU: uint8 [N, N] on the current device."""
     import torch
@@ -376,6 +402,7 @@ def model_pack(named, hid: int = 64):
     return out
 
 
+@_on_stream
 def model_fwd_bwd(x0, params, tables, spd, dout, H: int, dtype=None, spd_t=None, workspace=None, stream=None):
     """The full-layer model: x0, dout [N, 64] float32; params [L, P] float32 (model_pack);
     tables [L, H, NB] float32; spd [N, N] uint8. dtype: storage type of Q/K/V and the
@@ -417,6 +444,7 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
+@_on_stream
 def qkv_fwd(x, w, q=None, k=None, v=None, stream=None):
     """One layer's projections: x [N, hid], w [3, hid, hid] (float32 or bfloat16).
     Returns q, k, v [N, hid] in x's dtype (float32 accumulation, then rounded)."""
@@ -429,6 +457,7 @@ def qkv_fwd(x, w, q=None, k=None, v=None, stream=None):
     return q, k, v
 
 
+@_on_stream
 def qkv_bwd(x, w, dq, dk, dv, dx=None, dw=None, workspace=None, stream=None):
     """Backward of qkv_fwd for float32 dq, dk, dv [N, hid]: returns dx [N, hid], dw [3, hid, hid]."""
     import torch
@@ -447,6 +476,7 @@ def qkv_bwd(x, w, dq, dk, dv, dx=None, dw=None, workspace=None, stream=None):
     return dx, dw
 
 
+@_on_stream
 def store(src, dtype, dst=None, stream=None):
     """float32 tensor -> dtype (torch.bfloat16: round to nearest even; torch.float32: copy)."""
     import torch
@@ -461,6 +491,7 @@ def stack_workspace_bytes(N: int, L: int, H: int, D: int, NB: int, dtype: int) -
     return int(lib().gt_stack_workspace_bytes(N, L, H, D, NB, dtype))
 
 
+@_on_stream
 def stack_fwd_bwd(x0, w, tables, spd, dout, H: int, spd_t=None, workspace=None, stream=None):
     """Forward and backward of L stacked layers (see gt_stack_fwd_bwd) for loss sum(dout * X_L).
     x0, dout [N, hid]; w [L, 3, hid, hid]; tables [L, H, NB] float32; spd [N, N] uint8.

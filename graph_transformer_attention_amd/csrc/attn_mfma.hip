@@ -298,8 +298,9 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
   if (x >= nmax * kH) return;
   const int h = static_cast<int>(x / nmax);
   const int64_t n = x - h * nmax;
-  // Rows are assembled as raw half bit patterns (uint16) and stored as two dwordx4.
-  auto hbits = [](float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); };
+  // Rows are assembled as raw half bit patterns (uint16) and stored as two dwordx4;
+  // values beyond half's range become NaN (half_bits_or_nan), constants are exact.
+  auto hbits = [](float x) { return half_bits_or_nan(x); };
   auto pack = [](const uint16_t* e, int first) {
     u32x4 w;
 #pragma unroll
@@ -312,8 +313,8 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
     o[0] = pack(e, 0);
     o[1] = pack(e, 8);
   };
-  const uint16_t one = hbits(1.0f);
-  const uint16_t ninf = hbits(-INFINITY);
+  const uint16_t one = 0x3C00u;   // half 1.0
+  const uint16_t ninf = 0xFC00u;  // half -inf (padding)
   if (n < ops.npq) {
     uint16_t qa[16] = {}, da[16] = {};
     qa[10] = one;
@@ -335,10 +336,10 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
         da[d] = hbits(df);
       }
       const float L = lse[r] * sqrtf(static_cast<float>(kD));
-      const _Float16 lh = static_cast<_Float16>(L);
+      const _Float16 lh = to_half_or_nan(L);
       qa[8] = hbits(-static_cast<float>(lh));
       qa[9] = hbits(-(L - static_cast<float>(lh)));
-      const _Float16 dh = static_cast<_Float16>(delta);
+      const _Float16 dh = to_half_or_nan(delta);
       da[8] = hbits(-static_cast<float>(dh));
       da[9] = hbits(-(delta - static_cast<float>(dh)));
     } else {
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 
   for (int b = tid; b < kKvTable; b += kBwdThreads) {
     const int c = min(b, NB - 1);
-    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
+    tb[b] = make_float2(table[h0 * NB + c] * kLog2e, table[(h0 + 1) * NB + c] * kLog2e);
   }
   for (int x = lane; x < 2 * NB * 64; x += 64) bins[x] = 0.f;
   const s16x8 kb0 = load_h8(ops.ka + (jj * kH + h0) * 16 + 8 * hp);
@@ -572,23 +573,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
       const uint16_t* doa_t = cur + kAugHalves;
       const uint16_t* qt_t = cur + 2 * kAugHalves;
       const uint16_t* ot_t = qt_t + kTrHalves;
-      f32x16 s0, s1;
       uint32_t code[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        code[e] = min(code_byte(cw, e), nbm1);
-        const float2 t = tb[code[e]];
-        s0[e] = t.x;
-        s1[e] = t.y;
-      }
-      s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), kb0, s0);
-      s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), kb1, s1);
+      for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), nbm1);
+      f32x16 s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), kb0, f32x16{});
+      f32x16 s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), kb1, f32x16{});
       f32x16 p0 = mfma_h16(staged_aug(doa_t, c, 0, hp), vb0, f32x16{});
       f32x16 p1 = mfma_h16(staged_aug(doa_t, c, 1, hp), vb1, f32x16{});
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pa = __builtin_amdgcn_exp2f(s0[e] * sc2);
-        const float pb = __builtin_amdgcn_exp2f(s1[e] * sc2);
+        // both heads' log2e-scaled bias in one 8-byte read, used as the FMA addends
+        const float2 t = tb[code[e]];
+        const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, t.x));
+        const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, t.y));
         s0[e] = pa;
         s1[e] = pb;
         p0[e] *= pa;
@@ -676,7 +673,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
 
   for (int b = tid; b < 256; b += kBwdThreads) {
     const int c = min(b, NB - 1);
-    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
+    tb[b] = make_float2(table[h0 * NB + c] * kLog2e, table[(h0 + 1) * NB + c] * kLog2e);
   }
   const s16x8 qb0 = load_h8(ops.qa + (ii * kH + h0) * 16 + 8 * hp);
   const s16x8 qb1 = load_h8(ops.qa + (ii * kH + h0 + 1) * 16 + 8 * hp);
@@ -715,21 +712,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
       const uint16_t* ka_t = cur;
       const uint16_t* va_t = cur + kAugHalves;
       const uint16_t* kt_t = cur + 2 * kAugHalves;
-      f32x16 s0, s1;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float2 t = tb[code_byte(cw, e)];
-        s0[e] = t.x;
-        s1[e] = t.y;
-      }
-      s0 = mfma_h16(staged_aug(ka_t, c, 0, hp), qb0, s0);
-      s1 = mfma_h16(staged_aug(ka_t, c, 1, hp), qb1, s1);
+      f32x16 s0 = mfma_h16(staged_aug(ka_t, c, 0, hp), qb0, f32x16{});
+      f32x16 s1 = mfma_h16(staged_aug(ka_t, c, 1, hp), qb1, f32x16{});
       f32x16 p0 = mfma_h16(staged_aug(va_t, c, 0, hp), ob0, f32x16{});
       f32x16 p1 = mfma_h16(staged_aug(va_t, c, 1, hp), ob1, f32x16{});
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p0[e] *= __builtin_amdgcn_exp2f(s0[e] * sc2);
-        p1[e] *= __builtin_amdgcn_exp2f(s1[e] * sc2);
+        const float2 t = tb[code_byte(cw, e)];  // both heads' log2e-scaled bias: the FMA addends
+        p0[e] *= __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, t.x));
+        p1[e] *= __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, t.y));
       }
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {

@@ -276,6 +276,7 @@ struct OpsD32 {
   int64_t npq, npk;
 };
 
+// half bits of a constant (exact: 1, -inf); data go through half_bits_or_nan
 __device__ __forceinline__ uint16_t hbits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
   return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* 
       const u32x4 wv = *reinterpret_cast<const u32x4*>(src + row + 8 * part);
       u32x4 hv;
 #pragma unroll
-      for (int wi = 0; wi < 4; ++wi) hv[wi] = bf16x2_to_f16x2(wv[wi]);
+      for (int wi = 0; wi < 4; ++wi) hv[wi] = bf16x2_to_f16x2_or_nan(wv[wi]);
       *reinterpret_cast<u32x4*>(dst + row + 8 * part) = hv;
       if (o != nullptr) {
         const float4 oa = *reinterpret_cast<const float4*>(o + row + 8 * part);
@@ -342,10 +343,10 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* 
       copy(q, ops.qd, ops.qt, ops.npq, nullptr);
       const float delta = copy(dout, ops.od, ops.ot, ops.npq, out);
       const float L = lse[n * kH + h] * sqrtf(static_cast<float>(kD));
-      const _Float16 lh = static_cast<_Float16>(L);
-      ops.lq[lrow] = pack2(hbits(-static_cast<float>(lh)), hbits(-(L - static_cast<float>(lh))));
-      const _Float16 dh = static_cast<_Float16>(delta);
-      ops.dl[lrow] = pack2(hbits(-static_cast<float>(dh)), hbits(-(delta - static_cast<float>(dh))));
+      const _Float16 lh = to_half_or_nan(L);
+      ops.lq[lrow] = pack2(hbits(-static_cast<float>(lh)), half_bits_or_nan(-(L - static_cast<float>(lh))));
+      const _Float16 dh = to_half_or_nan(delta);
+      ops.dl[lrow] = pack2(hbits(-static_cast<float>(dh)), half_bits_or_nan(-(delta - static_cast<float>(dh))));
     } else {
       zero(ops.qd, ops.qt, ops.npq);
       zero(ops.od, ops.ot, ops.npq);

@@ -81,6 +81,21 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Half precision for the backward's operand copies, with overflow turned into NaN: a
+// value at or beyond half's range (|x| >= 65520 rounds to infinity) would otherwise
+// become an infinity that can vanish from a product (exp2(-inf) = 0 makes a whole row's
+// probabilities 0) and leave finite, wrong gradients. NaN reaches every output it
+// touches instead.
+__device__ __forceinline__ _Float16 to_half_or_nan(float x) {
+  return fabsf(x) < 65520.0f ? static_cast<_Float16>(x) : static_cast<_Float16>(__builtin_nanf(""));
+}
+__device__ __forceinline__ uint16_t half_bits_or_nan(float x) { return __builtin_bit_cast(uint16_t, to_half_or_nan(x)); }
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_or_nan(uint32_t w) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 r = {to_half_or_nan(bf16_lo(w)), to_half_or_nan(bf16_hi(w))};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ __forceinline__ f32x16 mfma_h16(s16x8 a, s16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                  0, 0, 0);

@@ -20,9 +20,25 @@
  *       spd                              [N, N]      uint8, row = query node i, column = key node j
  *       table, dtable                    [H, NB]     float32
  *   - dtype selects the storage type of the inputs q, k, v and dout: GT_F32
- *     (float) or GT_BF16 (bfloat16 bits). Arithmetic is float32 throughout and
- *     every output (out, lse, dq, dk, dv, dtable) is float32, so a bfloat16
- *     caller loses nothing to output rounding; table is float32.
+ *     (float) or GT_BF16 (bfloat16 bits). Every output (out, lse, dq, dk, dv,
+ *     dtable) is float32, so a bfloat16 caller loses nothing to output
+ *     rounding; table is float32. Accumulation is float32 everywhere.
+ *   - Operand precision. GT_F32 inputs, and shapes without a matrix-core
+ *     kernel, compute every product in float32. The matrix-core paths (GT_BF16
+ *     with H = 8 and D in {8, 32}) differ in two ways:
+ *       * q, k, v and dout are converted to IEEE half precision for the
+ *         backward's score products and for P.V (exact for bfloat16 values
+ *         with 2^-14 <= |x| < 65504; smaller values become half subnormals,
+ *         absolute error <= 2^-25, and 0 below 2^-25);
+ *       * the softmax probabilities P and the score gradients
+ *         dS = P * (dO.V - delta) enter the contractions over nodes (P.V,
+ *         P^T dO, dS^T Q, dS K) as half (relative error 2^-11).
+ *     Input range on those paths: |q|, |k|, |v|, |dout| < 65504, and
+ *     |dS| < 65504, which |dout| * |v| * 2 * D < 65504 guarantees (|P| <= 1,
+ *     |delta| <= max_j |dout_i . v_j|). Outside it the half values overflow
+ *     to infinity and the affected outputs are not finite (never silently
+ *     finite and wrong). A caller whose data may exceed these limits passes
+ *     float32 inputs, which take the float32 kernels.
  *   - Pointers marked "device" are device memory owned by the caller; the
  *     library never allocates or frees device memory, and keeps no state
  *     between calls. Every base pointer must be 16-byte aligned.
@@ -200,8 +216,8 @@ size_t gt_spd_build_device_workspace_bytes(int64_t N, int64_t nnz, int32_t C);
  *   workspace        device, >= gt_spd_build_device_workspace_bytes(N, indptr[N], C)
  *                    bytes, 256-byte aligned, contents ignored on entry.
  * Breadth-first search from all sources at once, 64 per bitmask, one launch per level
- * (MegaGraph pages, Fig. 4 caption: the topology-aware bias comes from the graph's
- * structure; the distance reading is stated with gt_spd_build). Component labels for
+ * (MegaGraph pages, abstract: the bias matrix is topology-aware, i.e. it comes from the
+ * graph's structure; the distance reading is stated with gt_spd_build). Component labels for
  * the codes C-1 / C come from a union-find on the host. The search kernels are
  * enqueued on `stream` and run asynchronously. Errors: as gt_spd_build, plus GT_EHIP. */
 int gt_spd_build_device(const int64_t* indptr, const int32_t* indices, int64_t N, int32_t C,

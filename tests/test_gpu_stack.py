@@ -12,7 +12,7 @@ import graph_transformer_attention_amd as gta
 from workloads import graphs, make_inputs
 from workloads.tensors import normal, store
 
-from gpu_util import TOL_BF16_REL, check, dev, host64
+from gpu_util import TOL_BF16_REL, TOL_F32_ABS, check, dev, err, host64
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,9 @@ def _run_stack(indptr, indices, x0, w, tables, dout, N, H, C):
 # bfloat16 tolerance, or at three times that spread where the spread is larger.
 NOISE_EPS = 2.0 ** -21
 NOISE_RUNS = 3
+# a layer whose oracle gradient RMS is this far below the largest layer's is zero in
+# exact arithmetic (rounding noise of the oracle's float64 sums)
+ZERO_LAYER_RMS = 1e-9
 
 
 def _rel(a, b):
@@ -94,13 +97,41 @@ def _stack_outputs(r, rows=None):
     return dict(x_last=sel(r["x"][-1]), dx0=sel(r["dx0"]), dw=r["dw"], dtable=r["dtable"])
 
 
-def _compare_stack(got, ref, spread, dtype):
+def _compare_stack(got, ref, spread, dtype, layer_spread=None):
     rep = {}
     for name in ("x_last", "dx0", "dw", "dtable"):
         bound = None if dtype == "f32" else max(TOL_BF16_REL, 3.0 * float(spread[name]))
         check(name, got[name], ref[name], dtype, rep, bound)
     print("errors:", {k: f"{v:.2e}" for k, v in rep.items()},
           "spread:", {k: f"{float(v):.2e}" for k, v in spread.items()}, flush=True)
+    if layer_spread is None:
+        return
+    # Layer by layer: each layer's dW and dtable against its own RMS, at the stated 2e-2
+    # wherever the oracle's spread for that layer allows it (3 x spread <= 2e-2), and at
+    # 3 x spread only past that point. A whole-tensor bound set by the deep layers would
+    # otherwise let the well-determined early layers drift unnoticed.
+    # Without a residual path the layers average every row of X into the same vector (by
+    # layer 6 of ba6800); from there on every dS, so dtable, is exactly zero in real
+    # arithmetic and the oracle's values are float64 rounding noise (RMS ~1e-17, eleven
+    # orders below the last nonzero layer). A ratio to that RMS compares noise with noise,
+    # so such a layer is held like an exactly zero reference: max |GPU| <= 1e-4.
+    bad = []
+    for name in ("dw", "dtable"):
+        rms = np.sqrt(np.mean(ref[name].reshape(ref[name].shape[0], -1) ** 2, axis=1))
+        line = []
+        for l in range(ref[name].shape[0]):
+            if rms[l] < ZERO_LAYER_RMS * rms.max():
+                e = float(np.abs(got[name][l]).max())
+                bound, ok = TOL_F32_ABS, e <= TOL_F32_ABS
+                line.append(f"{l}:|{e:.1e}|/{bound:.0e}")
+            else:
+                bound = max(TOL_BF16_REL, 3.0 * float(layer_spread[name][l]))
+                e, ok = err(got[name][l], ref[name][l], dtype, bound)
+                line.append(f"{l}:{e:.1e}/{bound:.1e}")
+            if not ok:
+                bad.append((name, l, e, bound))
+        print(f"{name} per layer (error/bound; |max| for a zero layer):", " ".join(line), flush=True)
+    assert not bad, f"per-layer errors above bound: {bad}"
 
 
 @pytest.mark.parametrize("N,L,H,D,C,dtype", [(200, 3, 8, 8, 20, "bf16"), (131, 2, 8, 8, 12, "f32"),
@@ -136,5 +167,11 @@ def test_stack_ba6800_16_layers_full_size():
     got = dict(x_last=got["x_last"][rows], dx0=got["dx0"][rows], dw=got["dw"], dtable=got["dtable"])
     ref = {k: g[k] for k in ("x_last", "dx0", "dw", "dtable")}
     spread = {k: g[f"spread_{k}"] for k in ref}
-    _compare_stack(got, ref, spread, "bf16")
+    layer_spread = {"dw": g["spread_dw_layer"], "dtable": g["spread_dtable_layer"]}
+    # the stated 2e-2 holds, by the stored spreads, for dW of layers 0-3 and dtable of layers
+    # 0-1; dtable of layers 6-15 is zero in exact arithmetic
+    assert np.all(3 * layer_spread["dw"][:4] <= TOL_BF16_REL) and np.all(3 * layer_spread["dtable"][:2] <= TOL_BF16_REL)
+    dt_rms = np.sqrt(np.mean(ref["dtable"].reshape(16, -1) ** 2, axis=1))
+    assert np.all(dt_rms[6:] < ZERO_LAYER_RMS * dt_rms.max()) and np.all(dt_rms[:6] > 1e-6 * dt_rms.max())
+    _compare_stack(got, ref, spread, "bf16", layer_spread)
     assert absent.any() and np.all(got["dtable"][:, :, absent] == 0.0)
