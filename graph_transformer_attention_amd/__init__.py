@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.gt_attn_bwd_workspace_bytes.restype = SZ
         L.gt_attn_bwd.argtypes = [P] * 14 + [SZ, I64, I32, I32, I32, I32, P]
         L.gt_attn_bwd.restype = ctypes.c_int
+        L.gt_attn_bwd_static.argtypes = [P] * 13 + [I64, I32, I32, I32, I32, P]
+        L.gt_attn_bwd_static.restype = ctypes.c_int
         L.gt_spd_build.argtypes = [P, P, I64, I32, P, I32]
         L.gt_spd_build_device_workspace_bytes.argtypes = [I64, I64, I32]
         L.gt_spd_build_device_workspace_bytes.restype = SZ
@@ -236,6 +238,29 @@ def bwd(q, k, v, spd, table, out, lse, dout, dq=None, dk=None, dv=None, dtable=N
             _dev(workspace, "workspace")]
     _check("gt_attn_bwd", lib().gt_attn_bwd(*args, workspace.numel() * workspace.element_size(),
                                             N, H, D, NB, dt, _stream(stream)))
+    return dq, dk, dv, dtable
+
+
+BWD_STATIC_SCRATCH_BYTES = 128 << 20   # GT_BWD_STATIC_SCRATCH_BYTES
+
+
+@_on_stream
+def bwd_static(q, k, v, spd, table, out, lse, dout, dq, dk, dv, dtable, stream=None, spd_t=None):
+    """bwd through gt_attn_bwd_static: the library's fixed per-GPU scratch array instead of a
+    workspace. The caller passes every output (nothing is allocated here or in the call)."""
+    import torch
+    N, H, D = q.shape
+    NB = table.shape[1]
+    dt = _dtype_code(q)
+    f32 = torch.float32
+    args = [_dev(q, "q", q.dtype, (N, H, D)), _dev(k, "k", q.dtype, (N, H, D)),
+            _dev(v, "v", q.dtype, (N, H, D)), _dev(spd, "spd", torch.uint8, (N, N)),
+            _dev(spd if spd_t is None else spd_t, "spd_t", torch.uint8, (N, N)),
+            _dev(table, "table", f32, (H, NB)), _dev(out, "out", f32, (N, H, D)),
+            _dev(lse, "lse", f32, (N, H)), _dev(dout, "dout", q.dtype, (N, H, D)),
+            _dev(dq, "dq", f32, (N, H, D)), _dev(dk, "dk", f32, (N, H, D)),
+            _dev(dv, "dv", f32, (N, H, D)), _dev(dtable, "dtable", f32, (H, NB))]
+    _check("gt_attn_bwd_static", lib().gt_attn_bwd_static(*args, N, H, D, NB, dt, _stream(stream)))
     return dq, dk, dv, dtable
 
 

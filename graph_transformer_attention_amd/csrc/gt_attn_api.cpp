@@ -335,6 +335,10 @@ BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtyp
 
 }  // namespace gt
 
+namespace gt {
+void set_last_error(const char* msg) { g_error = msg; }
+}  // namespace gt
+
 extern "C" {
 
 const char* gt_last_error(void) { return g_error.c_str(); }

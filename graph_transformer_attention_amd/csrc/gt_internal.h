@@ -198,4 +198,7 @@ struct LayerGradFactors {
 };
 hipError_t launch_layer_wgrad(const LayerGradFactors& f, float* partial, float* grad, int64_t N, hipStream_t s);
 
+// Message for gt_last_error() on the calling thread (entry points outside gt_attn_api.cpp).
+void set_last_error(const char* msg);
+
 }  // namespace gt

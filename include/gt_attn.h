@@ -126,6 +126,26 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
                 size_t workspace_bytes, int64_t N, int32_t H, int32_t D, int32_t NB,
                 int32_t dtype, void* stream);
 
+/* gt_attn_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels and results as gt_attn_bwd, bit for bit; the
+ * scratch memory is a fixed array of GT_BWD_STATIC_SCRATCH_BYTES in the library's
+ * device image, one per GPU, held from the first call on that GPU until the process
+ * ends. The call itself allocates nothing. The first call on each device looks up the
+ * array's address (make it outside graph capture); later calls reuse it.
+ *   Errors: as gt_attn_bwd; GT_EINVAL when the sizes need more scratch than the array
+ *   holds (gt_attn_bwd_workspace_bytes > GT_BWD_STATIC_SCRATCH_BYTES: 128 MiB covers
+ *   N = 32768 at H = 8 with D = 8 or 32), GT_EHIP when the address lookup fails.
+ *   Every call on one GPU shares that GPU's array and leaves its contents behind
+ *   (nothing in it needs clearing: the kernels write before they read). Calls that
+ *   overlap on one GPU, on different streams or from different threads, race on it:
+ *   order them on one stream.                                                      */
+#define GT_BWD_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+int gt_attn_bwd_static(const void* q, const void* k, const void* v, const uint8_t* spd,
+                       const uint8_t* spd_t, const float* table, const float* out, const float* lse,
+                       const void* dout, float* dq, float* dk, float* dv, float* dtable, int64_t N,
+                       int32_t H, int32_t D, int32_t NB, int32_t dtype, void* stream);
+
 /* ---- Key-block steps (MegaGraph pages, Fig. 4 and its caption: under graph-aware
  * context parallelism each device keeps its query rows while key/value blocks travel
  * around a ring, and each arriving block is paired with the matching column slice of
