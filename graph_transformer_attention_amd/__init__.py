@@ -544,7 +544,7 @@ def stack_fwd_bwd(x0, w, tables, spd, dout, H: int, spd_t=None, workspace=None, 
     return x_last, dx0, dw, dtable
 
 
-KERNEL_COUNT = 16
+KERNEL_COUNT = 17
 
 
 def kernel_names():

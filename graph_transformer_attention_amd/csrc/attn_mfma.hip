@@ -292,8 +292,9 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
                                                                const float* __restrict__ out,
                                                                const uint16_t* __restrict__ dout,
                                                                const float* __restrict__ lse, BwdOps ops,
-                                                               int64_t N, int64_t Nk) {
+                                                               int64_t N, int64_t Nk, uint32_t* __restrict__ flag) {
   const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (x == 0) *flag = 0u;  // the fused pass's code-range flag starts clear
   const int64_t nmax = ops.npq > ops.npk ? ops.npq : ops.npk;
   if (x >= nmax * kH) return;
   const int h = static_cast<int>(x / nmax);
@@ -495,7 +496,10 @@ template <bool kAligned>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
     const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ partial, int64_t N, int64_t Nk, int64_t ldt, int NB, int acc,
-    int64_t qchunk, int64_t gstride, int64_t pstride) {
+    int64_t qchunk, int64_t gstride, int64_t pstride, const uint32_t* __restrict__ gate) {
+  // As a rerun of the fused pass (gate given) it returns at once unless that pass met a
+  // code beyond its private bins.
+  if (gate != nullptr && *gate == 0u) return;
   extern __shared__ __align__(16) unsigned char smem[];
   // workgroup row y of a split launch: queries [y*qchunk, min(N, (y+1)*qchunk)), partial
   // dK, dV at + y*gstride and bucket partials at + y*pstride
@@ -633,6 +637,250 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   }
 }
 
+// Backward in one pass (key-outer with dQ): the key-outer kernel's work and, from the
+// same probabilities, the queries' gradient, so the query-outer pass (a third sweep
+// over the codes with a third exp per entry) is not needed. Work split, staging and the
+// dK/dV contractions are those of bwd_kv_mfma_d8_kernel. Per 32-query tile each wave
+// also:
+//  * writes its packed dS (f16, both heads, 32 keys x 32 queries) row by row into its own
+//    LDS buffer [head][key][query] and reads it back transposed with ds_read_b64_tr_b16:
+//    lane l of a 16-lane group receives element l%4 of the 8-byte chunks that lanes
+//    4e + l/4 address (e = 0..3), so each lane's address names a 4-query chunk of one key
+//    row and its result holds 4 keys of one query;
+//  * contracts those over its 32 keys against K^T (held in registers for the whole
+//    sweep: the wave's keys do not change), dQ^T[d][query] += K^T[d][key] dS^T[key][query];
+//  * adds its result to the other waves' in LDS (a fixed order), and the workgroup writes
+//    one dQ partial row per query for its 128 keys; the backward's last kernel sums the
+//    partials of all key blocks in order, so the result stays bitwise reproducible.
+// dtable bins are lane-private for codes 0..15 only (8 KB per wave): a lane that meets a
+// larger code raises *flag (cleared by the prep kernel), and the three-pass kernels,
+// launched after this one with that flag as their gate, then redo the backward.
+constexpr int kFusedBins = 16;
+constexpr int kDsRow = 40;                        // halves per key row of a transpose buffer (80 B)
+constexpr int kDsHalves = 2 * 32 * kDsRow;        // one wave's buffer: [head][key][query]
+constexpr int kRedFloats = kBwdWaves * 32 * 16;   // [wave][query][head][d] dQ contributions
+
+size_t fused_lds_bytes() {
+  return sizeof(float2) * (kBwdWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kStageHalves +
+         2ull * kBwdWaves * kDsHalves + 4ull * kRedFloats;
+}
+
+template <bool kAligned>
+__global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
+    const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ partial, float* __restrict__ dqpart, int64_t N, int64_t Nk,
+    int64_t ldt, int NB, int64_t qchunk, int64_t gstride, int64_t pstride, int64_t dqstride,
+    uint32_t* __restrict__ flag) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float2* bins = reinterpret_cast<float2*>(smem);                 // [wave][code][lane]
+  float2* tb = bins + kBwdWaves * kFusedBins * 64;                  // [64] by code
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);     // [2][kStageHalves]
+  uint16_t* dsbuf = stage + 2 * kStageHalves;                       // [wave][kDsHalves]
+  float* red = reinterpret_cast<float*>(dsbuf + kBwdWaves * kDsHalves);  // [kRedFloats]
+  const int64_t ib = static_cast<int64_t>(blockIdx.y) * qchunk;
+  N = N - ib < qchunk ? N - ib : qchunk;
+  ops.qa += ib * kH * 16;
+  ops.doa += ib * kH * 16;
+  ops.qt += ib;
+  ops.ot += ib;
+  dk += blockIdx.y * gstride;
+  dv += blockIdx.y * gstride;
+  partial += blockIdx.y * pstride;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float2* mybins = bins + w * (kFusedBins * 64) + lane;
+  uint16_t* mydst = dsbuf + w * kDsHalves;
+
+  const int npad32 = static_cast<int>(ops.npk / 32);
+  const int nkb = (npad32 + kBwdWaves - 1) / kBwdWaves;
+  int kb, hpair;
+  xcd_map(blockIdx.x, nkb, kb, hpair);
+  if (kb < 0) return;
+  const int c = lane & 31, hp = lane >> 5;
+  const int h0 = 2 * hpair;
+  const int64_t jw = static_cast<int64_t>(kb) * (32 * kBwdWaves) + 32 * w;
+  const int64_t j = jw + c;
+  const bool wave_live = jw < ops.npk;
+  const int64_t jj = wave_live ? j : 0;
+  const int64_t jwl = wave_live ? jw : 0;
+  const int64_t npad = ops.npq;
+  const float sqd = sqrtf(static_cast<float>(kD));
+  const float sc2 = kLog2e / sqd;
+
+  for (int b = tid; b < kKvTable; b += kBwdThreads) {
+    const int cb = min(b, NB - 1);
+    tb[b] = make_float2(table[h0 * NB + cb] * kLog2e, table[(h0 + 1) * NB + cb] * kLog2e);
+  }
+  for (int b = 0; b < kFusedBins; ++b) mybins[b * 64] = make_float2(0.f, 0.f);
+  const s16x8 kb0 = load_h8(ops.ka + (jj * kH + h0) * 16 + 8 * hp);
+  const s16x8 kb1 = load_h8(ops.ka + (jj * kH + h0 + 1) * 16 + 8 * hp);
+  const s16x8 vb0 = load_h8(ops.va + (jj * kH + h0) * 16 + 8 * hp);
+  const s16x8 vb1 = load_h8(ops.va + (jj * kH + h0 + 1) * 16 + 8 * hp);
+  // dQ contractions on 16x16x32 MFMAs: rows m = (head m / 8, d m % 8) of both heads,
+  // columns 16 queries, k = 8G + p for lane group G = lane / 16: head G / 2 and key
+  // 16u + 8 (G % 2) + p of the wave (u = 0, 1: the wave's two 16-key halves). The K^T
+  // operand is zero where a row's head is not the k-group's, and is the same every tile.
+  const int G = lane >> 4, m16 = lane & 15;
+  s16x8 kt[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    kt[u] = (m16 >> 3) == (G >> 1)
+                ? load_h8(ops.kt + (static_cast<int64_t>(h0 + (m16 >> 3)) * kD + (m16 & 7)) * ops.npk + jwl + 16 * u +
+                          8 * (G & 1))
+                : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
+  const uint32_t bound = static_cast<uint32_t>(min(NB - 1, kFusedBins - 1));
+  uint32_t over = 0u;
+  const uint8_t* crow = spd_t + (j < Nk ? j : Nk - 1) * ldt + ib;
+  const int64_t cc = 16 * hp;
+  // transposed-read address of this lane (group G, e4 = (lane % 16) / 4, j4 = lane % 4),
+  // for query half qh, key half u and read s: head G / 2, key row 16u + 8 (G % 2) + 4s + e4,
+  // queries 16 qh + 4 j4 .. +3; a lane of group G then receives 4 keys of head G / 2
+  const int e4 = (lane & 15) >> 2, j4 = lane & 3;
+  const int tr_off = (G >> 1) * 32 * kDsRow + (8 * (G & 1) + e4) * kDsRow + 4 * j4;
+  // this thread's share of the workgroup's dQ sum: 2 values of [query][head][d]
+  const int rq = tid >> 3, rh = (tid >> 2) & 1, rd = 2 * (tid & 3);
+
+  StageSrc src;
+  src.row0 = ops.qa + h0 * 16;
+  src.row1 = ops.doa + h0 * 16;
+  src.tr0 = ops.qt + static_cast<int64_t>(h0) * kD * npad;
+  src.tr1 = ops.ot + static_cast<int64_t>(h0) * kD * npad;
+  const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
+  constexpr int kCh = 384;
+  s16x8 sr[stage_per_thread<kCh>()];
+  StageCursor<kCh> cursor;
+  cursor.init(src, npad, tid);
+  cursor.load_next(sr, tid);
+  stage_store<kCh>(stage, sr, tid);
+  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
+  float* dqw = dqpart + static_cast<int64_t>(kb) * dqstride + (ib + rq) * kHD + (h0 + rh) * kD + rd;
+  // the workgroup's dQ for tile tt from the four waves' contributions, in wave order
+  auto reduce_dq = [&](int64_t tt) {
+    const float* slot = red + rq * 16 + rh * 8 + rd;
+    float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int ww = 0; ww < kBwdWaves; ++ww) {
+      const float2 x = *reinterpret_cast<const float2*>(slot + ww * (32 * 16));
+      acc.x += x.x;
+      acc.y += x.y;
+    }
+    const float rs = 1.f / sqd;  // dQ = dS K / sqrt(D)
+    if (tt * 32 + rq < N) *reinterpret_cast<float2*>(dqw + tt * 32 * kHD) = make_float2(acc.x * rs, acc.y * rs);
+  };
+  wait_vm0();
+  __syncthreads();
+
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t i0 = t * 32;
+    const uint16_t* cur = stage + (t & 1) * kStageHalves;
+    u32x4 cwn = cw;
+    if (t + 1 < ntiles) {
+      cursor.load_next(sr, tid);
+      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(crow, i0 + 32 + cc, N)
+                            : codes_at<true, kAligned>(crow, i0 + 32 + cc, N);
+    }
+    float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0;  // this lane's dQ^T, query halves 0 and 1
+    if (wave_live) {
+      const uint16_t* qa_t = cur;
+      const uint16_t* doa_t = cur + kAugHalves;
+      const uint16_t* qt_t = cur + 2 * kAugHalves;
+      const uint16_t* ot_t = qt_t + kTrHalves;
+      over |= (cw[0] | cw[1] | cw[2] | cw[3]) & 0xF0F0F0F0u;
+      uint32_t code[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), bound);
+      f32x16 s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), kb0, f32x16{});
+      f32x16 s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), kb1, f32x16{});
+      f32x16 p0 = mfma_h16(staged_aug(doa_t, c, 0, hp), vb0, f32x16{});
+      f32x16 p1 = mfma_h16(staged_aug(doa_t, c, 1, hp), vb1, f32x16{});
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float2 tv = tb[code[e]];
+        const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, tv.x));
+        const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, tv.y));
+        s0[e] = pa;
+        s1[e] = pb;
+        p0[e] *= pa;
+        p1[e] *= pb;
+        float2 bin = mybins[code[e] * 64];
+        bin.x += p0[e];
+        bin.y += p1[e];
+        mybins[code[e] * 64] = bin;
+      }
+      const s16x8 d0a = pack_f16x8(p0, 0), d0b = pack_f16x8(p0, 8);
+      const s16x8 d1a = pack_f16x8(p1, 0), d1b = pack_f16x8(p1, 8);
+      // dS rows of this lane's key: queries 16hp .. 16hp+15 of both heads
+      *reinterpret_cast<s16x8*>(mydst + c * kDsRow + 16 * hp) = d0a;
+      *reinterpret_cast<s16x8*>(mydst + c * kDsRow + 16 * hp + 8) = d0b;
+      *reinterpret_cast<s16x8*>(mydst + 32 * kDsRow + c * kDsRow + 16 * hp) = d1a;
+      *reinterpret_cast<s16x8*>(mydst + 32 * kDsRow + c * kDsRow + 16 * hp + 8) = d1b;
+#pragma unroll
+      for (int k1 = 0; k1 < 2; ++k1) {
+        const int g = 2 * hp + k1;
+        dv0 = mfma_h16(staged_tr(ot_t, 0, c, g), pack_f16x8(s0, 8 * k1), dv0);
+        dv1 = mfma_h16(staged_tr(ot_t, 1, c, g), pack_f16x8(s1, 8 * k1), dv1);
+        dk0 = mfma_h16(staged_tr(qt_t, 0, c, g), k1 ? d0b : d0a, dk0);
+        dk1 = mfma_h16(staged_tr(qt_t, 1, c, g), k1 ? d1b : d1a, dk1);
+      }
+      // dS^T operands: lane (query 16qh + m16, group G) gets keys 16u + 8 (G % 2) .. +7 of
+      // head G / 2, from two transposed reads of 4 keys each
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4* lds4;
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        f32x4 dq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint16_t* rb = mydst + 16 * u * kDsRow + 16 * qh + tr_off;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb + 4 * kDsRow));
+          const s16x8 bop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kt[u]), __builtin_bit_cast(f16x8, bop),
+                                                      dq, 0, 0, 0);
+        }
+        // rows 4G .. 4G+3 = head G / 2, d 4 (G % 2) .. +3 of query 16qh + m16
+        const float4 v = make_float4(dq[0], dq[1], dq[2], dq[3]);
+        if (qh == 0) q0 = v; else q1 = v;
+      }
+    }
+    // the workgroup's dQ for this tile: every wave's contribution, summed in wave order
+    float* myred = red + w * (32 * 16) + m16 * 16 + 8 * (G >> 1) + 4 * (G & 1);
+    *reinterpret_cast<float4*>(myred) = q0;
+    *reinterpret_cast<float4*>(myred + 16 * 16) = q1;
+    __syncthreads();
+    reduce_dq(t);
+    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kStageHalves, sr, tid);
+    cw = cwn;
+    __syncthreads();
+  }
+  if (wave_live && j < Nk) {
+    const float rs = 1.f / sqd;
+    float* kp = dk + j * kHD + h0 * kD + 4 * hp;
+    float* vp = dv + j * kHD + h0 * kD + 4 * hp;
+    store4(kp, make_float4(dk0[0] * rs, dk0[1] * rs, dk0[2] * rs, dk0[3] * rs), 0);
+    store4(kp + kD, make_float4(dk1[0] * rs, dk1[1] * rs, dk1[2] * rs, dk1[3] * rs), 0);
+    store4(vp, make_float4(dv0[0], dv0[1], dv0[2], dv0[3]), 0);
+    store4(vp + kD, make_float4(dv1[0], dv1[1], dv1[2], dv1[3]), 0);
+  }
+  if (NB > kFusedBins && over != 0u) *flag = 1u;  // every writer stores the same value
+  for (int x = lane; x < 2 * NB; x += 64) {
+    const int hl = x / NB, b = x - hl * NB;
+    float sum = 0.f;
+    if (b < kFusedBins) {
+      const float* srcb = reinterpret_cast<const float*>(bins + w * (kFusedBins * 64)) + b * 128 + hl;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains, fixed order
+#pragma unroll
+      for (int l = 0; l < 64; l += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s4[u] += srcb[2 * (l + u)];
+      }
+      sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    }
+    partial[((jw / 32) * kH + h0 + hl) * NB + b] = sum;
+  }
+}
+
 // Backward, step 3 (query-outer). A workgroup is 4 waves = 128 queries x one head
 // pair (lane c keeps query c); all waves share each staged key tile (augmented k and
 // v rows, transposed k) in LDS, double-buffered. S^T - lse and dP^T - delta come from
@@ -642,7 +890,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
                                                                       const float* __restrict__ table,
                                                                       BwdOps ops, float* __restrict__ dq,
                                                                       int64_t N, int64_t Nk, int64_t ldc, int NB,
-                                                                      int acc, int64_t kchunk, int64_t gstride) {
+                                                                      int acc, int64_t kchunk, int64_t gstride,
+                                                                      const uint32_t* __restrict__ gate) {
+  if (gate != nullptr && *gate == 0u) return;  // rerun of the fused pass, not needed
   __shared__ float2 tb[256];  // both heads' bias for each byte value
   __shared__ __align__(16) uint16_t stage[2 * kStageHalves];
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial dQ
@@ -806,12 +1056,13 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   ops.ot = ops.qt + hq * kD;
   ops.kt = ops.ot + hq * kD;
 
+  uint32_t* flag = reinterpret_cast<uint32_t*>(ws + w.flag_off);
   trace_begin(kTraceBwdDelta, s);
   const int64_t nmax = std::max(ops.npq, ops.npk);
   hipLaunchKernelGGL(bwd_prep_mfma_d8_kernel, dim3(static_cast<unsigned>((nmax * kH + 255) / 256)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.out, static_cast<const uint16_t*>(a.dout), a.lse, ops,
-                     a.N, a.Nk);
+                     a.N, a.Nk, flag);
   hipError_t e = hipGetLastError();
   trace_end(kTraceBwdDelta, s);
   if (e != hipSuccess) return e;
@@ -827,17 +1078,51 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   const int64_t pstride = w.n_kv_blocks * kH * a.NB;
   const int nkb = static_cast<int>((ops.npk / 32 + kBwdWaves - 1) / kBwdWaves);
   const dim3 kgrid(static_cast<unsigned>(xcd_grid(nkb)), static_cast<unsigned>(w.kv.S));
+  const bool kv_aligned = codes_aligned(a.spd_t, a.ld_t);
+  const SumSplits none{nullptr, nullptr, 0, 0, 0};
+  const int dkv = a.acc & kAccDkv;
+  const SumSplits sk = kv_split ? SumSplits{dkp, a.dk, nk_el, w.kv.S, dkv} : none;
+  const SumSplits sv = kv_split ? SumSplits{dvp, a.dv, nk_el, w.kv.S, dkv} : none;
+
+  // One pass when every output is overwritten: dK, dV, dtable partials and per-key-block
+  // dQ partials, then one launch that sums the partials in order. If a code fell outside
+  // the pass's private bins, the three-pass kernels after it (gated on the flag) redo the
+  // backward; with NB <= kFusedBins no code can, and they are not launched.
+  const bool fused = w.fused && a.acc == 0;
+  const uint32_t* gate = nullptr;
+  if (fused) {
+    float* dqpart = reinterpret_cast<float*>(ws + w.dqf_off);
+    const size_t flds = fused_lds_bytes();
+    e = allow_lds_mfma(bwd_fused_mfma_d8_kernel<true>, flds);
+    if (e == hipSuccess) e = allow_lds_mfma(bwd_fused_mfma_d8_kernel<false>, flds);
+    if (e != hipSuccess) return e;
+    trace_begin(kTraceBwdFused, s);
+    if (kv_aligned)
+      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<true>, kgrid, block, flds, s, a.spd_t, a.table, ops, dkp, dvp,
+                         partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
+    else
+      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<false>, kgrid, block, flds, s, a.spd_t, a.table, ops, dkp, dvp,
+                         partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
+    e = hipGetLastError();
+    trace_end(kTraceBwdFused, s);
+    if (e != hipSuccess) return e;
+    const SumSplits sqf{dqpart, a.dq, nq_el, nkb, 0};
+    e = launch_bwd_finish(sk, sv, sqf, partial, a.dtable, w.kv.S * w.n_kv_blocks, kH * a.NB, 0, s);
+    if (e != hipSuccess || a.NB <= kFusedBins) return e;
+    gate = flag;
+  }
+
   const size_t lds = kv_mfma_lds(a.NB);
   e = allow_lds_mfma(bwd_kv_mfma_d8_kernel<true>, lds);
   if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d8_kernel<false>, lds);
   if (e != hipSuccess) return e;
   trace_begin(kTraceBwdKv, s);
-  if (codes_aligned(a.spd_t, a.ld_t))
+  if (kv_aligned)
     hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<true>, kgrid, block, lds, s, a.spd_t, a.table, ops, dkp, dvp, partial,
-                       a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride);
+                       a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride, gate);
   else
     hipLaunchKernelGGL(bwd_kv_mfma_d8_kernel<false>, kgrid, block, lds, s, a.spd_t, a.table, ops, dkp, dvp, partial,
-                       a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride);
+                       a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride, gate);
   e = hipGetLastError();
   trace_end(kTraceBwdKv, s);
   if (e != hipSuccess) return e;
@@ -850,21 +1135,18 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   trace_begin(kTraceBwdQ, s);
   if (codes_aligned(a.spd, a.ld))
     hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<true>, qgrid, block, 0, s, a.spd, a.table, ops, dqp, a.N, a.Nk, a.ld,
-                       a.NB, q_acc, w.q.chunk, nq_el);
+                       a.NB, q_acc, w.q.chunk, nq_el, gate);
   else
     hipLaunchKernelGGL(bwd_q_mfma_d8_kernel<false>, qgrid, block, 0, s, a.spd, a.table, ops, dqp, a.N, a.Nk, a.ld,
-                       a.NB, q_acc, w.q.chunk, nq_el);
+                       a.NB, q_acc, w.q.chunk, nq_el, gate);
   e = hipGetLastError();
   trace_end(kTraceBwdQ, s);
   if (e != hipSuccess) return e;
-  if (!kv_split && !q_split)
+  if (!kv_split && !q_split && gate == nullptr)
     return launch_dtable_reduce(partial, a.dtable, w.n_kv_blocks, kH * a.NB, a.acc & kAccDtable, s);
-  const SumSplits none{nullptr, nullptr, 0, 0, 0};
-  const int dkv = a.acc & kAccDkv;
-  const SumSplits sk = kv_split ? SumSplits{dkp, a.dk, nk_el, w.kv.S, dkv} : none;
-  const SumSplits sv = kv_split ? SumSplits{dvp, a.dv, nk_el, w.kv.S, dkv} : none;
   const SumSplits sq = q_split ? SumSplits{dqp, a.dq, nq_el, w.q.S, a.acc & kAccDq} : none;
-  return launch_bwd_finish(sk, sv, sq, partial, a.dtable, w.kv.S * w.n_kv_blocks, kH * a.NB, a.acc & kAccDtable, s);
+  return launch_bwd_finish(sk, sv, sq, partial, a.dtable, w.kv.S * w.n_kv_blocks, kH * a.NB, a.acc & kAccDtable, s,
+                           gate);
 }
 
 }  // namespace gt

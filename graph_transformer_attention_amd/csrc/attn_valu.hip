@@ -410,7 +410,8 @@ __global__ __launch_bounds__(kThreads) void merge_splits_kernel(const float* __r
 __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(SumSplits a, SumSplits b, SumSplits c, int64_t e0,
                                                               int64_t e1, int64_t e2, const float* __restrict__ partial,
                                                               float* __restrict__ dtable, int64_t nblocks, int HNB,
-                                                              int dacc) {
+                                                              int dacc, const uint32_t* __restrict__ gate) {
+  if (gate != nullptr && *gate == 0u) return;
   const int64_t bid = blockIdx.x;
   if (bid < e2) {
     // select the descriptor by value (workgroup-uniform)
@@ -588,12 +589,12 @@ hipError_t launch_merge_splits(const float* opart, const float* lpart, int S, fl
 }
 
 hipError_t launch_bwd_finish(const SumSplits& a, const SumSplits& b, const SumSplits& c, const float* partial,
-                             float* dtable, int64_t nblocks, int HNB, int dacc, hipStream_t s) {
+                             float* dtable, int64_t nblocks, int HNB, int dacc, hipStream_t s, const uint32_t* gate) {
   auto blocks = [](const SumSplits& g) { return g.S > 0 ? (g.n / 4 + kThreads - 1) / kThreads : 0; };
   const int64_t e0 = blocks(a), e1 = e0 + blocks(b), e2 = e1 + blocks(c);
   trace_begin(kTraceBwdSplits, s);
   hipLaunchKernelGGL(bwd_finish_kernel, dim3(static_cast<unsigned>(e2 + HNB)), dim3(kThreads), 0, s, a, b, c, e0, e1,
-                     e2, partial, dtable, nblocks, HNB, dacc);
+                     e2, partial, dtable, nblocks, HNB, dacc, gate);
   const hipError_t e = hipGetLastError();
   trace_end(kTraceBwdSplits, s);
   return e;

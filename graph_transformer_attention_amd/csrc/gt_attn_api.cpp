@@ -95,7 +95,8 @@ hipEvent_t trace_event() {
 const char* const kKernelNames[GT_KERNEL_COUNT] = {"fwd",        "bwd_delta",  "bwd_kv",     "bwd_q",
                                                    "bwd_dtable", "qkv_fwd",    "qkv_bwd_dx", "qkv_bwd_dw",
                                                    "store",      "merge",      "fwd_merge",  "bwd_finish",
-                                                   "spd_device", "layer_fwd",  "layer_bwd",  "layer_wgrad"};
+                                                   "spd_device", "layer_fwd",  "layer_bwd",  "layer_wgrad",
+                                                   "bwd_fused"};
 
 int check_dtype(int32_t dtype) {
   if (dtype != GT_F32 && dtype != GT_BF16) return fail(GT_EINVAL, "dtype=%d is not GT_F32 or GT_BF16", dtype);
@@ -313,9 +314,10 @@ size_t fwd_workspace_bytes(int64_t N, int64_t Nk, int H, int D, int dtype, bool 
   return up256(static_cast<size_t>(sp.S) * rows * D * sizeof(float)) + up256(static_cast<size_t>(sp.S) * rows * sizeof(float));
 }
 
-BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtype) {
+BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtype, bool fused_ok) {
   BwdWorkspace w{};
   const bool mfma = mfma_supported(H, D, dtype);
+  w.fused = fused_ok && mfma && D == 8;
   const int64_t kb = valu_kv_block(H);
   w.n_kv_blocks = mfma ? (D == 32 ? mfma_d32_kv_blocks(Nk) : mfma_kv_blocks(Nk)) : (Nk + kb - 1) / kb;
   w.kv = inner_split(Nk, N, H, D, dtype, kSplitKv);
@@ -328,7 +330,10 @@ BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtyp
   const size_t dkv = w.kv.S > 1 ? up256(2 * static_cast<size_t>(w.kv.S) * Nk * H * D * f) : 0;
   w.dq_off = w.dkv_off + dkv;
   const size_t dq = w.q.S > 1 ? up256(static_cast<size_t>(w.q.S) * N * H * D * f) : 0;
-  w.flag_off = w.dq_off + dq;  // one device word the kernels of a call share (D = 32 key-outer)
+  w.dqf_off = w.dq_off + dq;
+  // the one-pass backward's dQ partials: one [N][H][D] array per 128-key block
+  const size_t dqf = w.fused ? up256(static_cast<size_t>(mfma_kv_blocks(Nk) / 4) * N * H * D * f) : 0;
+  w.flag_off = w.dqf_off + dqf;  // one device word the kernels of a call share (code-range flag)
   w.bytes = w.flag_off + 256;
   return w;
 }
@@ -440,6 +445,16 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
                 const float* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
                 float* dtable, void* workspace, size_t workspace_bytes, int64_t N, int32_t H,
                 int32_t D, int32_t NB, int32_t dtype, void* stream) {
+  return gt::bwd_call(q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, workspace, workspace_bytes, N, H,
+                      D, NB, dtype, stream, true);
+}
+
+}  // extern "C"
+
+int gt::bwd_call(const void* q, const void* k, const void* v, const uint8_t* spd, const uint8_t* spd_t,
+                 const float* table, const float* out, const float* lse, const void* dout, float* dq, float* dk,
+                 float* dv, float* dtable, void* workspace, size_t workspace_bytes, int64_t N, int32_t H, int32_t D,
+                 int32_t NB, int32_t dtype, void* stream, bool fused_ok) {
   GT_CHECK(check_shape(N, H, D, NB, dtype));
   GT_CHECK(check_ptr(q, "q"));
   GT_CHECK(check_ptr(k, "k"));
@@ -454,12 +469,14 @@ int gt_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* spd,
   GT_CHECK(check_ptr(dk, "dk"));
   GT_CHECK(check_ptr(dv, "dv"));
   GT_CHECK(check_ptr(dtable, "dtable"));
-  const gt::BwdWorkspace w = gt::bwd_workspace(N, N, H, D, NB, dtype);
+  const gt::BwdWorkspace w = gt::bwd_workspace(N, N, H, D, NB, dtype, fused_ok);
   GT_CHECK(check_workspace(workspace, workspace_bytes, w.bytes));
   gt::BwdArgs a{q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, workspace, N, H, D, NB, dtype,
                 N, N, N, 0};
   return hip_status(attn_bwd(a, w, static_cast<hipStream_t>(stream)), "gt_attn_bwd launch");
 }
+
+extern "C" {
 
 size_t gt_attn_fwd_block_workspace_bytes(int64_t Nq, int64_t Nk, int32_t H, int32_t D, int32_t NB, int32_t dtype) {
   const std::string saved = g_error;

@@ -69,9 +69,10 @@ enum { kAccDq = 1, kAccDkv = 2, kAccDtable = 4 };
 // key-outer pass's dK, dV partials [kv.S][2][Nk*H*D] and the query-outer pass's dQ
 // partials [q.S][N*H*D] float.
 struct BwdWorkspace {
-  size_t delta_off, ops_off, partial_off, dkv_off, dq_off, flag_off, bytes;
+  size_t delta_off, ops_off, partial_off, dkv_off, dq_off, dqf_off, flag_off, bytes;
   int64_t n_kv_blocks;  // partial rows of one split
   Split kv, q;
+  bool fused;  // head dimension 8 on the matrix cores: the one-pass backward's dQ partials at dqf_off
 };
 
 // Kernel timing ids (gt_trace_enable); the first five are the header's GT_KERNEL_* ids.
@@ -92,13 +93,16 @@ enum {
   kTraceLayerFwd = 13,
   kTraceLayerBwd = 14,
   kTraceLayerWgrad = 15,
+  kTraceBwdFused = 16,
 };
 
 // Kernel timing hook (gt_trace_enable): bracket one launch with events on its stream.
 void trace_begin(int kernel_id, hipStream_t s);
 void trace_end(int kernel_id, hipStream_t s);
 
-BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtype);
+// fused_ok = false: the three-pass layout only (no room for the one-pass backward's dQ
+// partials, which take N*H*D floats per 128-key block)
+BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtype, bool fused_ok = true);
 
 // Whether every code row base p + i * ld is 16-byte aligned (whole-row vector loads).
 inline bool codes_aligned(const uint8_t* p, int64_t ld) {
@@ -133,8 +137,11 @@ struct SumSplits {
 };
 // The backward's last step after a split launch: up to three partial sums (S = 0 marks
 // an unused one) and the dtable reduction over `nblocks` partial rows, in one launch.
+// gate: when given, the launch does nothing unless *gate is nonzero (the rerun of a pass
+// that met codes beyond its private bins)
 hipError_t launch_bwd_finish(const SumSplits& a, const SumSplits& b, const SumSplits& c, const float* partial,
-                             float* dtable, int64_t nblocks, int HNB, int dacc, hipStream_t s);
+                             float* dtable, int64_t nblocks, int HNB, int dacc, hipStream_t s,
+                             const uint32_t* gate = nullptr);
 // out = merge of two partial attention results over disjoint key sets by their lse
 hipError_t launch_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b, float* out,
                         float* lse, int64_t rows, int D, hipStream_t s);
@@ -200,5 +207,12 @@ hipError_t launch_layer_wgrad(const LayerGradFactors& f, float* partial, float* 
 
 // Message for gt_last_error() on the calling thread (entry points outside gt_attn_api.cpp).
 void set_last_error(const char* msg);
+// gt_attn_bwd with a choice of workspace layout: fused_ok = false takes the three-pass
+// backward, whose workspace (bwd_workspace(..., false)) has no room for the one-pass
+// backward's dQ partials.
+int bwd_call(const void* q, const void* k, const void* v, const uint8_t* spd, const uint8_t* spd_t,
+             const float* table, const float* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+             float* dtable, void* workspace, size_t workspace_bytes, int64_t N, int32_t H, int32_t D, int32_t NB,
+             int32_t dtype, void* stream, bool fused_ok);
 
 }  // namespace gt

@@ -54,12 +54,16 @@ extern "C" int gt_attn_bwd_static(const void* q, const void* k, const void* v, c
     return gt_attn_bwd(q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, nullptr, 0, N, H, D, NB,
                        dtype, stream);
   }
-  if (need > kScratchBytes) {
+  // gt_attn_bwd's own layout when it fits (same kernels, same bits); else the three-pass
+  // layout, which has no room for the one-pass backward's dQ partials
+  const bool fused_fits = need <= kScratchBytes;
+  const size_t need3 = gt::bwd_workspace(N, N, H, D, NB, dtype, false).bytes;
+  if (!fused_fits && need3 > kScratchBytes) {
     char buf[256];
     snprintf(buf, sizeof buf,
              "gt_attn_bwd_static: N=%lld, H=%d, D=%d, NB=%d needs %zu bytes of scratch, more than the fixed "
              "%zu; use gt_attn_bwd with a workspace",
-             (long long)N, H, D, NB, need, kScratchBytes);
+             (long long)N, H, D, NB, need3, kScratchBytes);
     gt::set_last_error(buf);
     return GT_EINVAL;
   }
@@ -71,6 +75,6 @@ extern "C" int gt_attn_bwd_static(const void* q, const void* k, const void* v, c
     gt::set_last_error(buf);
     return GT_EHIP;
   }
-  return gt_attn_bwd(q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, ws, kScratchBytes, N, H, D,
-                     NB, dtype, stream);
+  return gt::bwd_call(q, k, v, spd, spd_t, table, out, lse, dout, dq, dk, dv, dtable, ws, kScratchBytes, N, H, D, NB,
+                      dtype, stream, fused_fits);
 }

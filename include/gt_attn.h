@@ -370,7 +370,8 @@ enum {
   GT_KERNEL_LAYER_FWD = 13,  /* gt_model_fwd_bwd: norm, projections, FFN forward    */
   GT_KERNEL_LAYER_BWD = 14,  /* gt_model_fwd_bwd: their backward (node gradients)   */
   GT_KERNEL_LAYER_WGRAD = 15,/* gt_model_fwd_bwd: parameter gradients              */
-  GT_KERNEL_COUNT = 16
+  GT_KERNEL_BWD_FUSED = 16, /* backward in one pass: dK, dV, dQ partials, buckets  */
+  GT_KERNEL_COUNT = 17
 };
 int gt_trace_enable(int32_t on);
 int gt_trace_collect(int32_t* counts, double* total_ms, int32_t n);

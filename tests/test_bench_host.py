@@ -32,6 +32,10 @@ def test_work_model_per_entry_counts(bench):
     assert ex == E and fl == E * (4 * 2 * D + 5)
     fl, ex, by = bench.work_model("bwd_q", N, H, D, s)
     assert ex == E and fl == E * (3 * 2 * D + 4)
+    # the one-pass backward: one exp per entry for both the key-side and the query-side gradients
+    fl, ex, by = bench.work_model("bwd_fused", N, H, D, s)
+    assert ex == E and fl == E * (5 * 2 * D + 5)
+    assert by == N * N + 4 * node + 2 * N * H * 4 + 3 * f32node
     # the contraction counts behind the MFMA bound agree with the flop model
     for name, n in bench.CONTRACTIONS.items():
         fl, ex, _ = bench.work_model(name, N, H, D, s)
