@@ -656,9 +656,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 // larger code raises *flag (cleared by the prep kernel), and the three-pass kernels,
 // launched after this one with that flag as their gate, then redo the backward.
 constexpr int kFusedBins = 16;
-constexpr int kDsRow = 40;                        // halves per key row of a transpose buffer (80 B)
-constexpr int kDsHalves = 2 * 32 * kDsRow;        // one wave's buffer: [head][key][query]
-constexpr int kRedFloats = kBwdWaves * 32 * 16;   // [wave][query][head][d] dQ contributions
+constexpr int kDsHalves = 2 * 32 * 32;            // one wave's dS buffer: [head][key][query]
+constexpr int kRedRow = 20;                       // floats per query of a dQ slot (16 used)
+constexpr int kRedFloats = kBwdWaves * 32 * kRedRow;  // [wave][query][head][d] dQ contributions
+
+// Position (halves) of queries 8k..8k+7 of key row r in a dS buffer: 64-byte rows whose
+// 16-byte chunks are XOR-swizzled by (r >> 1) & 3, so that the eight lanes of one write
+// cycle (rows r..r+7 at one chunk) and the sixteen 8-byte transposed reads of one lane
+// group (rows r0..r0+3, r0 a multiple of 4, at four chunk offsets) hit distinct banks.
+__device__ __forceinline__ int ds_pos(int r, int k) { return r * 32 + 8 * (k ^ ((r >> 1) & 3)); }
 
 size_t fused_lds_bytes() {
   return sizeof(float2) * (kBwdWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kStageHalves +
@@ -733,10 +739,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   const uint8_t* crow = spd_t + (j < Nk ? j : Nk - 1) * ldt + ib;
   const int64_t cc = 16 * hp;
   // transposed-read address of this lane (group G, e4 = (lane % 16) / 4, j4 = lane % 4),
-  // for query half qh, key half u and read s: head G / 2, key row 16u + 8 (G % 2) + 4s + e4,
-  // queries 16 qh + 4 j4 .. +3; a lane of group G then receives 4 keys of head G / 2
+  // for query half qh, key half u and read s: head G / 2, key row r = 16u + 8 (G % 2) + 4s
+  // + e4, queries 16 qh + 4 j4 .. +3; a lane of group G then receives 4 keys of head G / 2.
+  // With ds_pos's swizzle ((r >> 1) & 3 = 2s + e4 / 2) that is tr_base + 512u + 128s +
+  // 16 (qh ^ s) halves.
   const int e4 = (lane & 15) >> 2, j4 = lane & 3;
-  const int tr_off = (G >> 1) * 32 * kDsRow + (8 * (G & 1) + e4) * kDsRow + 4 * j4;
+  const int tr_base = (G >> 1) * 32 * 32 + (8 * (G & 1) + e4) * 32 + 8 * ((j4 >> 1) ^ (e4 >> 1)) + 4 * (j4 & 1);
   // this thread's share of the workgroup's dQ sum: 2 values of [query][head][d]
   const int rq = tid >> 3, rh = (tid >> 2) & 1, rd = 2 * (tid & 3);
 
@@ -756,11 +764,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   float* dqw = dqpart + static_cast<int64_t>(kb) * dqstride + (ib + rq) * kHD + (h0 + rh) * kD + rd;
   // the workgroup's dQ for tile tt from the four waves' contributions, in wave order
   auto reduce_dq = [&](int64_t tt) {
-    const float* slot = red + rq * 16 + rh * 8 + rd;
+    const float* slot = red + rq * kRedRow + rh * 8 + rd;
     float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
     for (int ww = 0; ww < kBwdWaves; ++ww) {
-      const float2 x = *reinterpret_cast<const float2*>(slot + ww * (32 * 16));
+      const float2 x = *reinterpret_cast<const float2*>(slot + ww * (32 * kRedRow));
       acc.x += x.x;
       acc.y += x.y;
     }
@@ -810,10 +818,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
       const s16x8 d0a = pack_f16x8(p0, 0), d0b = pack_f16x8(p0, 8);
       const s16x8 d1a = pack_f16x8(p1, 0), d1b = pack_f16x8(p1, 8);
       // dS rows of this lane's key: queries 16hp .. 16hp+15 of both heads
-      *reinterpret_cast<s16x8*>(mydst + c * kDsRow + 16 * hp) = d0a;
-      *reinterpret_cast<s16x8*>(mydst + c * kDsRow + 16 * hp + 8) = d0b;
-      *reinterpret_cast<s16x8*>(mydst + 32 * kDsRow + c * kDsRow + 16 * hp) = d1a;
-      *reinterpret_cast<s16x8*>(mydst + 32 * kDsRow + c * kDsRow + 16 * hp + 8) = d1b;
+      *reinterpret_cast<s16x8*>(mydst + ds_pos(c, 2 * hp)) = d0a;
+      *reinterpret_cast<s16x8*>(mydst + ds_pos(c, 2 * hp + 1)) = d0b;
+      *reinterpret_cast<s16x8*>(mydst + 32 * 32 + ds_pos(c, 2 * hp)) = d1a;
+      *reinterpret_cast<s16x8*>(mydst + 32 * 32 + ds_pos(c, 2 * hp + 1)) = d1b;
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
         const int g = 2 * hp + k1;
@@ -832,9 +840,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
         f32x4 dq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const uint16_t* rb = mydst + 16 * u * kDsRow + 16 * qh + tr_off;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb + 4 * kDsRow));
+          const uint16_t* rb = mydst + tr_base + 512 * u;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb + 16 * qh));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb + 128 + 16 * (qh ^ 1)));
           const s16x8 bop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kt[u]), __builtin_bit_cast(f16x8, bop),
                                                       dq, 0, 0, 0);
@@ -845,9 +853,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
       }
     }
     // the workgroup's dQ for this tile: every wave's contribution, summed in wave order
-    float* myred = red + w * (32 * 16) + m16 * 16 + 8 * (G >> 1) + 4 * (G & 1);
+    float* myred = red + w * (32 * kRedRow) + m16 * kRedRow + 8 * (G >> 1) + 4 * (G & 1);
     *reinterpret_cast<float4*>(myred) = q0;
-    *reinterpret_cast<float4*>(myred + 16 * 16) = q1;
+    *reinterpret_cast<float4*>(myred + 16 * kRedRow) = q1;
     __syncthreads();
     reduce_dq(t);
     if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kStageHalves, sr, tid);
