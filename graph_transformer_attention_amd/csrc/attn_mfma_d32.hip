@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
                                                                 float* __restrict__ out, float* __restrict__ lse,
                                                                 int64_t N, int64_t Nk, int64_t ldc, int NB,
                                                                 int64_t kchunk, int64_t ostride, int64_t lstride) {
-  __shared__ float2 tb[256];  // both heads' bias * sqrt(D) for each byte value
+  __shared__ float2 tb[256];  // both heads' bias for each byte value (forward: * sqrt(D), query-outer: * log2e)
   __shared__ __align__(16) uint16_t vt[2][2 * kVtHead];  // [buffer][head][d][key], rows of kVtRow
   __shared__ __align__(16) uint16_t kt[2][kRowTile];     // [buffer] k row tile
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
                                                                   int64_t ldc, int NB, int acc, int64_t kchunk,
                                                                   int64_t gstride) {
   using Set = StageSetD32<2, 1>;
-  __shared__ float2 tb[256];  // both heads' bias * sqrt(D) for each byte value
+  __shared__ float2 tb[256];  // both heads' bias for each byte value (forward: * sqrt(D), query-outer: * log2e)
   __shared__ __align__(16) uint16_t stage[2 * Set::kHalves];
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial dQ
   // at dq + y*gstride
@@ -686,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
 
   for (int b = tid; b < 256; b += kThreads) {
     const int c = min(b, NB - 1);
-    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
+    tb[b] = make_float2(table[h0 * NB + c] * kLog2e, table[(h0 + 1) * NB + c] * kLog2e);
   }
   s16x8 qop[2][2], oop[2][2], qaug[2], oaug[2];
   const uint16_t one = 0x3C00u, ninf = 0xFC00u;
@@ -733,13 +733,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
       const uint16_t* k_t = cur;
       const uint16_t* v_t = cur + kRowTile;
       const uint16_t* kt_t = cur + 2 * kRowTile;
-      f32x16 s0, s1;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float2 t = tb[code_byte(cw, e)];
-        s0[e] = t.x;
-        s1[e] = t.y;
-      }
+      f32x16 s0 = {}, s1 = {};
       f32x16 p0 = {}, p1 = {};
 #pragma unroll
       for (int ci = 0; ci < 2; ++ci) {
@@ -755,8 +749,9 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
       p1 = mfma_h16(vaug, oaug[1], p1);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p0[e] *= __builtin_amdgcn_exp2f(s0[e] * sc2);
-        p1[e] *= __builtin_amdgcn_exp2f(s1[e] * sc2);
+        const float2 t = tb[code_byte(cw, e)];  // both heads' log2e-scaled bias: the FMA addends
+        p0[e] *= __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, t.x));
+        p1[e] *= __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, t.y));
       }
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
