@@ -24,7 +24,9 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgt_attn.so")
+# GT_ATTN_LIBRARY selects another build of the same library (the host-sanitizer build).
+LIB_PATH = os.environ.get("GT_ATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libgt_attn.so")
 GT_F32, GT_BF16 = 0, 1
 GT_OK, GT_EINVAL, GT_EUNSUPPORTED, GT_EHIP = 0, -1, -2, -3
 ACC_DQ, ACC_DKV, ACC_DTABLE, ACC_ALL = 1, 2, 4, 7   # gt_attn_bwd_block accumulate bits
