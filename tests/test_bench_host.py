@@ -64,11 +64,13 @@ def test_traffic_record_is_tied_to_the_kernel_sources(bench, tmp_path, monkeypat
     path = os.path.join(ROOT, "profiles", "traffic_ba32768-bf16.json")
     with open(path) as f:
         rec = json.load(f)
-    for k in ("fwd", "bwd_kv", "bwd_q"):
+    # the kernels of the default step: the forward and the one-pass backward
+    for k in ("fwd", "bwd_fused"):
         assert rec["kernels"][k]["hbm_bytes_per_launch"] > 0
     if rec["source_hash"] == bench.kernel_source_hash():
-        assert bench.recorded_traffic("bwd_kv", "ba32768-bf16") == rec["kernels"]["bwd_kv"]["hbm_bytes_per_launch"]
-    assert bench.recorded_traffic("bwd_kv", "no-such-workload") is None
+        assert (bench.recorded_traffic("bwd_fused", "ba32768-bf16")
+                == rec["kernels"]["bwd_fused"]["hbm_bytes_per_launch"])
+    assert bench.recorded_traffic("bwd_fused", "no-such-workload") is None
     # the head-dimension-32 record is checked against that path's sources
     with open(os.path.join(ROOT, "profiles", "traffic_sbm65536-d32-bf16.json")) as f:
         rec32 = json.load(f)
@@ -83,7 +85,7 @@ def test_traffic_record_is_tied_to_the_kernel_sources(bench, tmp_path, monkeypat
     (tmp_path / "profiles" / "traffic_ba32768-bf16.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda D=8: "f" * 16)
-    assert bench.recorded_traffic("bwd_kv", "ba32768-bf16") is None
+    assert bench.recorded_traffic("bwd_fused", "ba32768-bf16") is None
 
 
 def test_more_than_one_gpu_is_refused():
