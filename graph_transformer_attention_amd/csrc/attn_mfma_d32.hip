@@ -38,11 +38,18 @@ constexpr int kThreads = 64 * kWaves;
 //   transposed    [head][d][32 nodes] half: 64 rows of 64 bytes, chunk g of row r at
 //                 g ^ tswz(r)
 // Both swizzles give the 8 (or 16) lanes of one LDS cycle distinct bank groups when
-// they read consecutive rows at one chunk index.
+// they read consecutive rows at one chunk index. The row swizzle t = (s >> 1) & 7 also
+// has bit 2 flipped when bit 0 is set (a permutation of 0..7, so the property above
+// holds): the key-outer pass reads its query row tiles transposed, 4 consecutive slots
+// s0..s0+3 (s0 a multiple of 4) at a time, and the flip moves slots s0+2 and s0+3 to the
+// other head's half of the row, so those reads cover all 64 banks once.
 constexpr int kRowTile = 32 * 2 * kD;  // halves
 constexpr int kTrTile = 2 * kD * 32;   // halves
 
-__device__ __forceinline__ int rswz(int s) { return (s >> 1) & 7; }
+__device__ __forceinline__ int rswz(int s) {
+  const int t = (s >> 1) & 7;
+  return t ^ ((t & 1) << 2);
+}
 __device__ __forceinline__ int tswz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int row_pos(int slot, int chunk) { return slot * 64 + 8 * (chunk ^ rswz(slot)); }
 __device__ __forceinline__ int tr_pos(int row, int g) { return row * 32 + 8 * (g ^ tswz(row)); }
@@ -262,7 +269,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
 // delta) for the N queries rounded up to 32 (npq), key-side arrays (k, v) for the Nk
 // keys rounded up to 32 (npk); padded rows are zero:
 //   qd, kd, vd, od   [node][head][32] half      q, k, v, dout
-//   qt, kt, ot       [head][32][node] half      transposed q, k, dout
+//   kt               [head][32][node] half      transposed k (the key-outer pass reads q
+//                                               and dout transposed from their row tiles)
 //   lq, dl           [head][node] two halves    (-L_hi, -L_lo), L = lse*sqrt(D), and
 //                                               (-delta_hi, -delta_lo), delta = <dout, out>
 // The score MFMAs contract over 48: the 32 head dimensions, then a chunk holding
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
 // [-delta_hi, -delta_lo, 0...] against [1, 1, 0...] gives dout.v - delta. Padded
 // queries get -L_hi = -inf.
 struct OpsD32 {
-  uint16_t *qd, *kd, *vd, *od, *qt, *kt, *ot;
+  uint16_t *qd, *kd, *vd, *od, *kt;
   uint32_t *lq, *dl;
   int64_t npq, npk;
 };
@@ -340,16 +348,16 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* 
   if (n < ops.npq) {
     const int64_t lrow = static_cast<int64_t>(h) * ops.npq + n;
     if (n < N) {
-      copy(q, ops.qd, ops.qt, ops.npq, nullptr);
-      const float delta = copy(dout, ops.od, ops.ot, ops.npq, out);
+      copy(q, ops.qd, nullptr, ops.npq, nullptr);
+      const float delta = copy(dout, ops.od, nullptr, ops.npq, out);
       const float L = lse[n * kH + h] * sqrtf(static_cast<float>(kD));
       const _Float16 lh = to_half_or_nan(L);
       ops.lq[lrow] = pack2(hbits(-static_cast<float>(lh)), half_bits_or_nan(-(L - static_cast<float>(lh))));
       const _Float16 dh = to_half_or_nan(delta);
       ops.dl[lrow] = pack2(hbits(-static_cast<float>(dh)), half_bits_or_nan(-(delta - static_cast<float>(dh))));
     } else {
-      zero(ops.qd, ops.qt, ops.npq);
-      zero(ops.od, ops.ot, ops.npq);
+      zero(ops.qd, nullptr, ops.npq);
+      zero(ops.od, nullptr, ops.npq);
       ops.lq[lrow] = pack2(ninf, 0);
       ops.dl[lrow] = 0u;
     }
@@ -414,11 +422,12 @@ __device__ __forceinline__ s16x8 aug_chunk(uint32_t ab, uint16_t cc, int hp) {
 
 // ---------------------------------------------------------------------------------
 // Backward, key-outer: a wave owns 32 keys (lane c keeps key c) and a head pair; the
-// 4 waves share each staged query tile (q and dout rows, q^T and dout^T), staged
-// once per tile in LDS. S and dP - delta come from 3 MFMAs each (rows = queries,
-// columns = keys), P = exp2(S log2e / sqrt(D)), dS = P (dP - delta); dV^T += dO^T P
-// and dK^T += Q^T dS contract over the tile's queries. Bucket sums of dS go to LDS bins
-// in one of two layouts:
+// 4 waves share each staged query tile (q and dout rows, 8 KB), staged once per tile in
+// LDS. S and dP - delta come from 3 MFMAs each (rows = queries, columns = keys),
+// P = exp2(S log2e / sqrt(D)), dS = P (dP - delta); dV^T += dO^T P and dK^T += Q^T dS
+// contract over the tile's queries, their dO^T and Q^T operands read from the same row
+// tiles with ds_read_b64_tr_b16 (below), so no transposed copy is staged. Bucket sums of
+// dS go to LDS bins in one of two layouts:
 //  * kPrivate: [bucket][64 lanes][2 heads], one bin row per lane, so every lane updates
 //    its own bins in the same instruction. Only buckets below kPrivBins fit in LDS at this
 //    occupancy; a lane that meets a larger code raises *flag, and the launch is then
@@ -429,6 +438,29 @@ __device__ __forceinline__ s16x8 aug_chunk(uint32_t ab, uint16_t cc, int hp) {
 //    *flag was raised.
 constexpr int kKvTbD32 = 64;  // key-outer table entries (float2: both heads), codes clamped to NB-1 <= 63
 constexpr int kPrivBins = 16;  // buckets of the private layout
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+
+// Transposed operand from a row tile: 4 consecutive nodes of one d for each lane. In a
+// 16-lane group, ds_read_b64_tr_b16 gives lane j element j % 4 of the 8-byte pieces that
+// lanes 4e + j / 4 address (e = 0..3): when lane 4e + r of group G addresses node n0 + e,
+// head hl, d = 16 (G % 2) + 4r .. +3, lane j receives nodes n0 .. n0+3 at d = 16 (G % 2) + j,
+// i.e. at its own column c. tr_lane_base gives that address (halves) for the 4-node group
+// n0 = 16 (G / 2) + 8 k1 + 4 half without its slot term 512 (2 k1 + half): the row
+// swizzle makes the rest depend on (hl, half) only through hl ^ half (x below).
+__device__ __forceinline__ int tr_lane_base(int lane, int x) {
+  const int G = lane >> 4, e4 = (lane >> 2) & 3, r4 = lane & 3;
+  const int pos = ((r4 >> 1) ^ (e4 >> 1)) | (((G & 1) ^ (G >> 1)) << 1) | (((e4 >> 1) ^ x) << 2);
+  return 64 * (4 * (G >> 1) + e4) + 8 * pos + 4 * (r4 & 1);
+}
+// 8 consecutive nodes 16 hp + 8 k1 .. +7 of head hl at the lane's d, as an MFMA operand
+__device__ __forceinline__ s16x8 tr_row_op(const uint16_t* tile, int tb0, int tb1, int hl, int k1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(tile + 512 * (2 * k1) + (hl ? tb1 : tb0)));
+  const s16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(tile + 512 * (2 * k1 + 1) + (hl ? tb0 : tb1)));
+  return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
 
 template <bool kAligned, bool kPrivate>
 __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t* __restrict__ spd_t,
@@ -446,8 +478,6 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   N = N - ib < qchunk ? N - ib : qchunk;
   ops.qd += ib * kH * kD;
   ops.od += ib * kH * kD;
-  ops.qt += ib;
-  ops.ot += ib;
   ops.lq += ib;
   ops.dl += ib;
   dk += blockIdx.y * gstride;
@@ -502,15 +532,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   const int64_t cc = 16 * hp;
   const int qr = node_of_row(c);
 
-  StageSetD32<2, 2> set;
+  StageSetD32<2, 0> set;
   set.rows[0] = ops.qd;
   set.rows[1] = ops.od;
-  set.trs[0] = ops.qt;
-  set.trs[1] = ops.ot;
   set.h0 = h0;
   set.npad = npad;
+  const int tb0 = tr_lane_base(lane, 0), tb1 = tr_lane_base(lane, 1);
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
-  s16x8 sr[StageSetD32<2, 2>::kPer];
+  s16x8 sr[StageSetD32<2, 0>::kPer];
   set.load(sr, 0, tid);
   u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
   uint32_t lw0 = ops.lq[static_cast<int64_t>(h0) * npad + qr], lw1 = ops.lq[static_cast<int64_t>(h0 + 1) * npad + qr];
@@ -536,8 +565,6 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
     if (wave_live) {
       const uint16_t* q_t = stage;
       const uint16_t* o_t = stage + kRowTile;
-      const uint16_t* qt_t = stage + 2 * kRowTile;
-      const uint16_t* ot_t = qt_t + kTrTile;
       f32x16 s0, s1;
       uint32_t code[16];
 #pragma unroll
@@ -595,11 +622,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
       }
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
-        const int g = 2 * hp + k1;
-        dv0 = mfma_h16(tr_op(ot_t, 0, c, g), pack_f16x8(s0, 8 * k1), dv0);
-        dv1 = mfma_h16(tr_op(ot_t, 1, c, g), pack_f16x8(s1, 8 * k1), dv1);
-        dk0 = mfma_h16(tr_op(qt_t, 0, c, g), pack_f16x8(p0, 8 * k1), dk0);
-        dk1 = mfma_h16(tr_op(qt_t, 1, c, g), pack_f16x8(p1, 8 * k1), dk1);
+        dv0 = mfma_h16(tr_row_op(o_t, tb0, tb1, 0, k1), pack_f16x8(s0, 8 * k1), dv0);
+        dv1 = mfma_h16(tr_row_op(o_t, tb0, tb1, 1, k1), pack_f16x8(s1, 8 * k1), dv1);
+        dk0 = mfma_h16(tr_row_op(q_t, tb0, tb1, 0, k1), pack_f16x8(p0, 8 * k1), dk0);
+        dk1 = mfma_h16(tr_row_op(q_t, tb0, tb1, 1, k1), pack_f16x8(p1, 8 * k1), dk1);
       }
     }
     cw = cwn;
@@ -786,9 +812,7 @@ OpsD32 carve_ops_d32(void* base, int64_t N, int64_t Nk) {
   uint16_t* p = static_cast<uint16_t*>(base);
   o.qd = p;
   o.od = o.qd + nq;
-  o.qt = o.od + nq;
-  o.ot = o.qt + nq;
-  o.kd = o.ot + nq;
+  o.kd = o.od + nq;
   o.vd = o.kd + nk;
   o.kt = o.vd + nk;
   o.lq = reinterpret_cast<uint32_t*>(o.kt + nk);
@@ -798,14 +822,14 @@ OpsD32 carve_ops_d32(void* base, int64_t N, int64_t Nk) {
 
 size_t kv_d32_lds(int NB, bool priv) {
   const size_t bins = priv ? 4ull * kWaves * 2 * kPrivBins * 64 : 4ull * kWaves * 2 * NB * 32;
-  return bins + sizeof(float2) * kKvTbD32 + 2ull * StageSetD32<2, 2>::kHalves;
+  return bins + sizeof(float2) * kKvTbD32 + 2ull * StageSetD32<2, 0>::kHalves;
 }
 
 }  // namespace
 
 size_t mfma_d32_ops_bytes(int64_t N, int64_t Nk) {
   const size_t npq = static_cast<size_t>((N + 31) / 32 * 32), npk = static_cast<size_t>((Nk + 31) / 32 * 32);
-  return (4 * npq + 3 * npk) * kH * kD * 2 + npq * kH * 4 * 2;
+  return (2 * npq + 3 * npk) * kH * kD * 2 + npq * kH * 4 * 2;
 }
 
 int64_t mfma_d32_kv_blocks(int64_t Nk) {
