@@ -32,27 +32,22 @@ constexpr int kThreads = 64 * kWaves;
 
 // ---------------------------------------------------------------------------------
 // Staged tiles: one 32-node tile of a head pair, 16-byte chunks (the forward stages
-// k as a row tile, the backward its operand copies).
+// k as a row tile, the backward its operand copies):
 //   row tile      [slot][head][32] half, slot s holding node a(s): 32 rows of 128 bytes,
 //                 chunk k of row s stored at chunk position k ^ rswz(s)
-//   transposed    [head][d][32 nodes] half: 64 rows of 64 bytes, chunk g of row r at
-//                 g ^ tswz(r)
-// Both swizzles give the 8 (or 16) lanes of one LDS cycle distinct bank groups when
-// they read consecutive rows at one chunk index. The row swizzle t = (s >> 1) & 7 also
-// has bit 2 flipped when bit 0 is set (a permutation of 0..7, so the property above
-// holds): the key-outer pass reads its query row tiles transposed, 4 consecutive slots
-// s0..s0+3 (s0 a multiple of 4) at a time, and the flip moves slots s0+2 and s0+3 to the
-// other head's half of the row, so those reads cover all 64 banks once.
+// The swizzle gives the 8 (or 16) lanes of one LDS cycle distinct bank groups when they
+// read consecutive rows at one chunk index: t = (s >> 1) & 7, with bit 2 flipped when
+// bit 0 is set (a permutation of 0..7). The backward also reads row tiles transposed
+// (ds_read_b64_tr_b16), 4 consecutive slots s0..s0+3 (s0 a multiple of 4) at a time; the
+// flip moves slots s0+2 and s0+3 to the other head's half of the row, so those reads
+// cover all 64 banks once.
 constexpr int kRowTile = 32 * 2 * kD;  // halves
-constexpr int kTrTile = 2 * kD * 32;   // halves
 
 __device__ __forceinline__ int rswz(int s) {
   const int t = (s >> 1) & 7;
   return t ^ ((t & 1) << 2);
 }
-__device__ __forceinline__ int tswz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int row_pos(int slot, int chunk) { return slot * 64 + 8 * (chunk ^ rswz(slot)); }
-__device__ __forceinline__ int tr_pos(int row, int g) { return row * 32 + 8 * (g ^ tswz(row)); }
 
 // global chunk x of a row tile: node = x >> 3, chunk = x & 7 (head = chunk >> 2, 8 halves of d)
 __device__ __forceinline__ const uint16_t* row_src(const uint16_t* base, int64_t n0, int h0, int x) {
@@ -268,9 +263,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
 // Backward operand copies, written once per call: query-side arrays (q, dout, lse,
 // delta) for the N queries rounded up to 32 (npq), key-side arrays (k, v) for the Nk
 // keys rounded up to 32 (npk); padded rows are zero:
-//   qd, kd, vd, od   [node][head][32] half      q, k, v, dout
-//   kt               [head][32][node] half      transposed k (the key-outer pass reads q
-//                                               and dout transposed from their row tiles)
+//   qd, kd, vd, od   [node][head][32] half      q, k, v, dout (the contractions over
+//                                               nodes read them transposed from their
+//                                               staged row tiles)
 //   lq, dl           [head][node] two halves    (-L_hi, -L_lo), L = lse*sqrt(D), and
 //                                               (-delta_hi, -delta_lo), delta = <dout, out>
 // The score MFMAs contract over 48: the 32 head dimensions, then a chunk holding
@@ -279,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
 // [-delta_hi, -delta_lo, 0...] against [1, 1, 0...] gives dout.v - delta. Padded
 // queries get -L_hi = -inf.
 struct OpsD32 {
-  uint16_t *qd, *kd, *vd, *od, *kt;
+  uint16_t *qd, *kd, *vd, *od;
   uint32_t *lq, *dl;
   int64_t npq, npk;
 };
@@ -305,9 +300,8 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* 
   const int64_t n = x - h * nmax;
   const int64_t row = (n * kH + h) * kD;
   const uint16_t ninf = hbits(-INFINITY);
-  // One node's row of 32 bf16 values -> half row (and its transposed column when tr is
-  // given, over npad nodes); with o given, also returns <row, o's row>.
-  auto copy = [&](const uint16_t* src, uint16_t* dst, uint16_t* tr, int64_t npad, const float* o) {
+  // One node's row of 32 bf16 values -> half row; with o given, also returns <row, o's row>.
+  auto copy = [&](const uint16_t* src, uint16_t* dst, const float* o) {
     float dot = 0.f;
 #pragma unroll
     for (int part = 0; part < 4; ++part) {
@@ -328,89 +322,60 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d32_kernel(const uint16_t* 
         dot = fmaf(bf16_lo(wv[3]), ob.z, dot);
         dot = fmaf(bf16_hi(wv[3]), ob.w, dot);
       }
-      if (tr != nullptr) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t word = hv[e >> 1];
-          tr[(static_cast<int64_t>(h) * kD + 8 * part + e) * npad + n] =
-              static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
-        }
-      }
     }
     return dot;
   };
-  auto zero = [&](uint16_t* dst, uint16_t* tr, int64_t npad) {
+  auto zero = [&](uint16_t* dst) {
 #pragma unroll
     for (int part = 0; part < 4; ++part) *reinterpret_cast<u32x4*>(dst + row + 8 * part) = u32x4{0u, 0u, 0u, 0u};
-    if (tr != nullptr)
-      for (int d = 0; d < kD; ++d) tr[(static_cast<int64_t>(h) * kD + d) * npad + n] = 0;
   };
   if (n < ops.npq) {
     const int64_t lrow = static_cast<int64_t>(h) * ops.npq + n;
     if (n < N) {
-      copy(q, ops.qd, nullptr, ops.npq, nullptr);
-      const float delta = copy(dout, ops.od, nullptr, ops.npq, out);
+      copy(q, ops.qd, nullptr);
+      const float delta = copy(dout, ops.od, out);
       const float L = lse[n * kH + h] * sqrtf(static_cast<float>(kD));
       const _Float16 lh = to_half_or_nan(L);
       ops.lq[lrow] = pack2(hbits(-static_cast<float>(lh)), half_bits_or_nan(-(L - static_cast<float>(lh))));
       const _Float16 dh = to_half_or_nan(delta);
       ops.dl[lrow] = pack2(hbits(-static_cast<float>(dh)), half_bits_or_nan(-(delta - static_cast<float>(dh))));
     } else {
-      zero(ops.qd, nullptr, ops.npq);
-      zero(ops.od, nullptr, ops.npq);
+      zero(ops.qd);
+      zero(ops.od);
       ops.lq[lrow] = pack2(ninf, 0);
       ops.dl[lrow] = 0u;
     }
   }
   if (n < ops.npk) {
     if (n < Nk) {
-      copy(k, ops.kd, ops.kt, ops.npk, nullptr);
-      copy(v, ops.vd, nullptr, ops.npk, nullptr);
+      copy(k, ops.kd, nullptr);
+      copy(v, ops.vd, nullptr);
     } else {
-      zero(ops.kd, ops.kt, ops.npk);
-      zero(ops.vd, nullptr, ops.npk);
+      zero(ops.kd);
+      zero(ops.vd);
     }
   }
 }
 
-// global chunk x of a transposed tile: row = x >> 2 (head = row >> 5, d = row & 31), nodes 8*(x & 3)
-__device__ __forceinline__ const uint16_t* tr_src(const uint16_t* base, int64_t npad, int64_t n0, int h0, int x) {
-  return base + (static_cast<int64_t>(h0) * kD + (x >> 2)) * npad + n0 + 8 * (x & 3);
-}
-
-// A tile set: kRows row tiles followed by kTrs transposed tiles; 256 chunks each, so
-// thread tid (of kThreads = 256) moves chunk tid of every tile.
-template <int kRows, int kTrs>
+// A tile set: kRows row tiles of 256 chunks each, so thread tid (of kThreads = 256)
+// moves chunk tid of every tile.
+template <int kRows>
 struct StageSetD32 {
-  static constexpr int kChunks = 256 * (kRows + kTrs);
-  static constexpr int kPer = kChunks / kThreads;
-  static constexpr int kHalves = kRows * kRowTile + kTrs * kTrTile;
-  const uint16_t* rows[kRows > 0 ? kRows : 1];
-  const uint16_t* trs[kTrs > 0 ? kTrs : 1];
+  static constexpr int kPer = kRows;
+  static constexpr int kHalves = kRows * kRowTile;
+  const uint16_t* rows[kRows];
   int h0;
-  int64_t npad;
 
   __device__ __forceinline__ void load(s16x8 (&r)[kPer], int64_t n0, int tid) const {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {  // thread tid moves chunk tid of tile u
-      r[u] = u < kRows ? load_h8(row_src(rows[u < kRows ? u : 0], n0, h0, tid))
-                       : load_h8(tr_src(trs[u < kRows ? 0 : u - kRows], npad, n0, h0, tid));
-    }
+    for (int u = 0; u < kPer; ++u) r[u] = load_h8(row_src(rows[u], n0, h0, tid));  // chunk tid of tile u
   }
   __device__ __forceinline__ void store(uint16_t* buf, const s16x8 (&r)[kPer], int tid) const {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pos = u < kRows ? u * kRowTile + row_pos(slot_of_node(tid >> 3), tid & 7)
-                                : kRows * kRowTile + (u - kRows) * kTrTile + tr_pos(tid >> 2, tid & 3);
-      *reinterpret_cast<s16x8*>(buf + pos) = r[u];
-    }
+    for (int u = 0; u < kPer; ++u)
+      *reinterpret_cast<s16x8*>(buf + u * kRowTile + row_pos(slot_of_node(tid >> 3), tid & 7)) = r[u];
   }
 };
-
-// Transposed operand: head hl, d = m (0..31), nodes 8g .. 8g+7.
-__device__ __forceinline__ s16x8 tr_op(const uint16_t* tile, int hl, int m, int g) {
-  return load_h8(tile + tr_pos(hl * kD + m, g));
-}
 
 // The third 16-deep contraction chunk of a lane: lanes of half 0 carry
 // [a, b, c, 0, 0, 0, 0, 0] (halves), lanes of half 1 carry zeros.
@@ -532,14 +497,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   const int64_t cc = 16 * hp;
   const int qr = node_of_row(c);
 
-  StageSetD32<2, 0> set;
+  StageSetD32<2> set;
   set.rows[0] = ops.qd;
   set.rows[1] = ops.od;
   set.h0 = h0;
-  set.npad = npad;
   const int tb0 = tr_lane_base(lane, 0), tb1 = tr_lane_base(lane, 1);
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
-  s16x8 sr[StageSetD32<2, 0>::kPer];
+  s16x8 sr[StageSetD32<2>::kPer];
   set.load(sr, 0, tid);
   u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
   uint32_t lw0 = ops.lq[static_cast<int64_t>(h0) * npad + qr], lw1 = ops.lq[static_cast<int64_t>(h0 + 1) * npad + qr];
@@ -672,16 +636,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
 
 // ---------------------------------------------------------------------------------
 // Backward, query-outer: a wave owns 32 queries (lane c keeps query c) and a head
-// pair; the 4 waves share each staged key tile (k and v rows, k^T), double-buffered.
+// pair; the 4 waves share each staged key tile (k and v rows), double-buffered.
 // S^T and dP^T - delta come from 3 MFMAs each (rows = keys, columns = queries);
-// dQ^T += K^T dS^T per key tile.
+// dQ^T += K^T dS^T per key tile, K^T read from the k row tile with ds_read_b64_tr_b16
+// as in the key-outer pass.
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t* __restrict__ spd,
                                                                   const float* __restrict__ table, OpsD32 ops,
                                                                   float* __restrict__ dq, int64_t N, int64_t Nk,
                                                                   int64_t ldc, int NB, int acc, int64_t kchunk,
                                                                   int64_t gstride) {
-  using Set = StageSetD32<2, 1>;
+  using Set = StageSetD32<2>;
   __shared__ float2 tb[256];  // both heads' bias for each byte value (forward: * sqrt(D), query-outer: * log2e)
   __shared__ __align__(16) uint16_t stage[2 * Set::kHalves];
   // workgroup row y of a split launch: keys [y*kchunk, min(Nk, (y+1)*kchunk)), partial dQ
@@ -690,7 +655,6 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
   Nk = Nk - jb < kchunk ? Nk - jb : kchunk;
   ops.kd += jb * kH * kD;
   ops.vd += jb * kH * kD;
-  ops.kt += jb;
   spd += jb;
   dq += blockIdx.y * gstride;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -706,7 +670,6 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
   const bool wave_live = iw < ops.npq;
   const int64_t ii = wave_live ? i : 0;
   const bool qvalid = i < N;
-  const int64_t npad = ops.npk;  // staged tiles are key tiles
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
@@ -735,9 +698,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
   Set set;
   set.rows[0] = ops.kd;
   set.rows[1] = ops.vd;
-  set.trs[0] = ops.kt;
   set.h0 = h0;
-  set.npad = npad;
+  const int tb0 = tr_lane_base(lane, 0), tb1 = tr_lane_base(lane, 1);
   const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
   s16x8 sr[Set::kPer];
   set.load(sr, 0, tid);
@@ -758,7 +720,6 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
     if (wave_live) {
       const uint16_t* k_t = cur;
       const uint16_t* v_t = cur + kRowTile;
-      const uint16_t* kt_t = cur + 2 * kRowTile;
       f32x16 s0 = {}, s1 = {};
       f32x16 p0 = {}, p1 = {};
 #pragma unroll
@@ -781,9 +742,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
       }
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
-        const int g = 2 * hp + k1;
-        dq0 = mfma_h16(tr_op(kt_t, 0, c, g), pack_f16x8(p0, 8 * k1), dq0);
-        dq1 = mfma_h16(tr_op(kt_t, 1, c, g), pack_f16x8(p1, 8 * k1), dq1);
+        dq0 = mfma_h16(tr_row_op(k_t, tb0, tb1, 0, k1), pack_f16x8(p0, 8 * k1), dq0);
+        dq1 = mfma_h16(tr_row_op(k_t, tb0, tb1, 1, k1), pack_f16x8(p1, 8 * k1), dq1);
       }
     }
     if (t + 1 < ntiles) set.store(stage + ((t + 1) & 1) * Set::kHalves, sr, tid);
@@ -814,22 +774,21 @@ OpsD32 carve_ops_d32(void* base, int64_t N, int64_t Nk) {
   o.od = o.qd + nq;
   o.kd = o.od + nq;
   o.vd = o.kd + nk;
-  o.kt = o.vd + nk;
-  o.lq = reinterpret_cast<uint32_t*>(o.kt + nk);
+  o.lq = reinterpret_cast<uint32_t*>(o.vd + nk);
   o.dl = o.lq + static_cast<size_t>(o.npq) * kH;
   return o;
 }
 
 size_t kv_d32_lds(int NB, bool priv) {
   const size_t bins = priv ? 4ull * kWaves * 2 * kPrivBins * 64 : 4ull * kWaves * 2 * NB * 32;
-  return bins + sizeof(float2) * kKvTbD32 + 2ull * StageSetD32<2, 0>::kHalves;
+  return bins + sizeof(float2) * kKvTbD32 + 2ull * StageSetD32<2>::kHalves;
 }
 
 }  // namespace
 
 size_t mfma_d32_ops_bytes(int64_t N, int64_t Nk) {
   const size_t npq = static_cast<size_t>((N + 31) / 32 * 32), npk = static_cast<size_t>((Nk + 31) / 32 * 32);
-  return (2 * npq + 3 * npk) * kH * kD * 2 + npq * kH * 4 * 2;
+  return (2 * npq + 2 * npk) * kH * kD * 2 + npq * kH * 4 * 2;
 }
 
 int64_t mfma_d32_kv_blocks(int64_t Nk) {
