@@ -639,8 +639,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 
 // Backward in one pass (key-outer with dQ): the key-outer kernel's work and, from the
 // same probabilities, the queries' gradient, so the query-outer pass (a third sweep
-// over the codes with a third exp per entry) is not needed. Work split, staging and the
-// dK/dV contractions are those of bwd_kv_mfma_d8_kernel. Per 32-query tile each wave
+// over the codes with a third exp per entry) is not needed. Work split and the dK/dV
+// contractions are those of bwd_kv_mfma_d8_kernel, but only the two augmented row
+// tiles are staged (4 KB per tile): the dK^T and dV^T contractions read Q^T and dO^T
+// from them with ds_read_b64_tr_b16 (tr_aug_base below). Per 32-query tile each wave
 // also:
 //  * writes its packed dS (f16, both heads, 32 keys x 32 queries) row by row into its own
 //    LDS buffer [head][key][query] and reads it back transposed with ds_read_b64_tr_b16:
@@ -656,6 +658,28 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 // larger code raises *flag (cleared by the prep kernel), and the three-pass kernels,
 // launched after this one with that flag as their gate, then redo the backward.
 constexpr int kFusedBins = 16;
+constexpr int kFusedStageHalves = 2 * kAugHalves;  // one stage buffer: the qa and doa row tiles
+
+// Transposed read of an augmented row tile (32 slots x [2 heads][16 halves], swz): in a
+// 16-lane group, ds_read_b64_tr_b16 gives lane j element j % 4 of the 8-byte pieces that
+// lanes 4e + j / 4 address (e = 0..3). Lane 4e + r addresses node n0 + e, head hl,
+// columns 4r .. 4r+3 of the node's 16-half row, so lane j receives nodes n0 .. n0+3 of
+// column j: for j < 8 that is d = j, the MFMA row of lane c = j; columns 8..15 (the
+// augmented terms) and lanes 16..31 (which repeat lanes 0..15) only feed accumulator rows
+// 8..31, which are never stored. n0 = 16 hp + 8 k1 + 4 half; the slot term
+// 512 k1 + 256 half is left out here, and with swz's swizzle the rest depends on hl only.
+__device__ __forceinline__ int tr_aug_base(int lane, int hl) {
+  const int hp = lane >> 5, e = (lane >> 2) & 3, r = lane & 3;
+  return 128 * hp + 32 * e + 8 * (2 * (hl ^ hp) + ((r >> 1) ^ (e >> 1))) + 4 * (r & 1);
+}
+// 8 consecutive nodes 16 hp + 8 k1 .. +7 at the lane's d (rows 0..7), as an MFMA operand
+__device__ __forceinline__ s16x8 tr_aug_op(const uint16_t* aug, int base, int k1) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lds4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(aug + 512 * k1 + base));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(aug + 512 * k1 + 256 + base));
+  return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
 constexpr int kDsHalves = 2 * 32 * 32;            // one wave's dS buffer: [head][key][query]
 constexpr int kRedRow = 20;                       // floats per query of a dQ slot (16 used)
 constexpr int kRedFloats = kBwdWaves * 32 * kRedRow;  // [wave][query][head][d] dQ contributions
@@ -667,7 +691,7 @@ constexpr int kRedFloats = kBwdWaves * 32 * kRedRow;  // [wave][query][head][d] 
 __device__ __forceinline__ int ds_pos(int r, int k) { return r * 32 + 8 * (k ^ ((r >> 1) & 3)); }
 
 size_t fused_lds_bytes() {
-  return sizeof(float2) * (kBwdWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kStageHalves +
+  return sizeof(float2) * (kBwdWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kFusedStageHalves +
          2ull * kBwdWaves * kDsHalves + 4ull * kRedFloats;
 }
 
@@ -680,8 +704,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   float2* bins = reinterpret_cast<float2*>(smem);                 // [wave][code][lane]
   float2* tb = bins + kBwdWaves * kFusedBins * 64;                  // [64] by code
-  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);     // [2][kStageHalves]
-  uint16_t* dsbuf = stage + 2 * kStageHalves;                       // [wave][kDsHalves]
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);     // [2][kFusedStageHalves]
+  uint16_t* dsbuf = stage + 2 * kFusedStageHalves;                  // [wave][kDsHalves]
   float* red = reinterpret_cast<float*>(dsbuf + kBwdWaves * kDsHalves);  // [kRedFloats]
   const int64_t ib = static_cast<int64_t>(blockIdx.y) * qchunk;
   N = N - ib < qchunk ? N - ib : qchunk;
@@ -751,10 +775,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   StageSrc src;
   src.row0 = ops.qa + h0 * 16;
   src.row1 = ops.doa + h0 * 16;
-  src.tr0 = ops.qt + static_cast<int64_t>(h0) * kD * npad;
-  src.tr1 = ops.ot + static_cast<int64_t>(h0) * kD * npad;
+  src.tr0 = nullptr;  // no transposed tile is staged
+  src.tr1 = nullptr;
+  const int tb_h0 = tr_aug_base(lane, 0), tb_h1 = tr_aug_base(lane, 1);
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
-  constexpr int kCh = 384;
+  constexpr int kCh = 256;  // qa, doa
   s16x8 sr[stage_per_thread<kCh>()];
   StageCursor<kCh> cursor;
   cursor.init(src, npad, tid);
@@ -780,7 +805,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
 
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t i0 = t * 32;
-    const uint16_t* cur = stage + (t & 1) * kStageHalves;
+    const uint16_t* cur = stage + (t & 1) * kFusedStageHalves;
     u32x4 cwn = cw;
     if (t + 1 < ntiles) {
       cursor.load_next(sr, tid);
@@ -791,8 +816,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
     if (wave_live) {
       const uint16_t* qa_t = cur;
       const uint16_t* doa_t = cur + kAugHalves;
-      const uint16_t* qt_t = cur + 2 * kAugHalves;
-      const uint16_t* ot_t = qt_t + kTrHalves;
       over |= (cw[0] | cw[1] | cw[2] | cw[3]) & 0xF0F0F0F0u;
       uint32_t code[16];
 #pragma unroll
@@ -824,11 +847,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
       *reinterpret_cast<s16x8*>(mydst + 32 * 32 + ds_pos(c, 2 * hp + 1)) = d1b;
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
-        const int g = 2 * hp + k1;
-        dv0 = mfma_h16(staged_tr(ot_t, 0, c, g), pack_f16x8(s0, 8 * k1), dv0);
-        dv1 = mfma_h16(staged_tr(ot_t, 1, c, g), pack_f16x8(s1, 8 * k1), dv1);
-        dk0 = mfma_h16(staged_tr(qt_t, 0, c, g), k1 ? d0b : d0a, dk0);
-        dk1 = mfma_h16(staged_tr(qt_t, 1, c, g), k1 ? d1b : d1a, dk1);
+        dv0 = mfma_h16(tr_aug_op(doa_t, tb_h0, k1), pack_f16x8(s0, 8 * k1), dv0);
+        dv1 = mfma_h16(tr_aug_op(doa_t, tb_h1, k1), pack_f16x8(s1, 8 * k1), dv1);
+        dk0 = mfma_h16(tr_aug_op(qa_t, tb_h0, k1), k1 ? d0b : d0a, dk0);
+        dk1 = mfma_h16(tr_aug_op(qa_t, tb_h1, k1), k1 ? d1b : d1a, dk1);
       }
       // dS^T operands: lane (query 16qh + m16, group G) gets keys 16u + 8 (G % 2) .. +7 of
       // head G / 2, from two transposed reads of 4 keys each
@@ -858,7 +880,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
     *reinterpret_cast<float4*>(myred + 16 * kRedRow) = q1;
     __syncthreads();
     reduce_dq(t);
-    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kStageHalves, sr, tid);
+    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kFusedStageHalves, sr, tid);
     cw = cwn;
     __syncthreads();
   }
