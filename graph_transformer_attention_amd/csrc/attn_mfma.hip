@@ -278,11 +278,11 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
 // inputs are exact in half precision, so the score products carry no rounding; the scale
 // log2(e)/sqrt(D) is applied in float32 before the exp2 (folding it into q would round
 // q to half precision and cost about 1e-3 of P). Padded
-// queries get -L_hi = -inf. Transposed half copies [head][d][node] of q, k and dout
-// (q and dout over npq nodes, k over npk) are the A operands of the contractions over
-// nodes.
+// queries get -L_hi = -inf. The contractions over queries read Q^T and dO^T from the
+// staged qa and doa row tiles transposed (ds_read_b64_tr_b16); a transposed half copy
+// kt [head][d][node] of k (over npk nodes) serves the contraction over keys.
 struct BwdOps {
-  uint16_t *qa, *ka, *doa, *va, *qt, *kt, *ot;
+  uint16_t *qa, *ka, *doa, *va, *kt;
   int64_t npq, npk;
 };
 
@@ -348,12 +348,6 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
     }
     put_row(ops.qa, qa);
     put_row(ops.doa, da);
-#pragma unroll
-    for (int d = 0; d < kD; ++d) {
-      const int64_t t = (static_cast<int64_t>(h) * kD + d) * ops.npq + n;
-      ops.qt[t] = qa[d];
-      ops.ot[t] = da[d];
-    }
   }
   if (n < ops.npk) {
     uint16_t ka[16] = {}, va[16] = {};
@@ -481,6 +475,29 @@ __device__ __forceinline__ s16x8 staged_tr(const uint16_t* tr, int hl, int m, in
   return *reinterpret_cast<const s16x8*>(tr + swz(hl * kD + (m & 7), g));
 }
 
+constexpr int kAugStageHalves = 2 * kAugHalves;  // a stage buffer of the two augmented row tiles only
+
+// Transposed read of an augmented row tile (32 slots x [2 heads][16 halves], swz): in a
+// 16-lane group, ds_read_b64_tr_b16 gives lane j element j % 4 of the 8-byte pieces that
+// lanes 4e + j / 4 address (e = 0..3). Lane 4e + r addresses node n0 + e, head hl,
+// columns 4r .. 4r+3 of the node's 16-half row, so lane j receives nodes n0 .. n0+3 of
+// column j: for j < 8 that is d = j, the MFMA row of lane c = j; columns 8..15 (the
+// augmented terms) and lanes 16..31 (which repeat lanes 0..15) only feed accumulator rows
+// 8..31, which are never stored. n0 = 16 hp + 8 k1 + 4 half; the slot term
+// 512 k1 + 256 half is left out here, and with swz's swizzle the rest depends on hl only.
+__device__ __forceinline__ int tr_aug_base(int lane, int hl) {
+  const int hp = lane >> 5, e = (lane >> 2) & 3, r = lane & 3;
+  return 128 * hp + 32 * e + 8 * (2 * (hl ^ hp) + ((r >> 1) ^ (e >> 1))) + 4 * (r & 1);
+}
+// 8 consecutive nodes 16 hp + 8 k1 .. +7 at the lane's d (rows 0..7), as an MFMA operand
+__device__ __forceinline__ s16x8 tr_aug_op(const uint16_t* aug, int base, int k1) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lds4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(aug + 512 * k1 + base));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(aug + 512 * k1 + 256 + base));
+  return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // Backward, step 2 (key-outer). A workgroup is 4 waves = 128 keys x one head pair;
 // each wave owns 32 keys (lane c keeps key c for the whole sweep) and all waves share
 // each staged query tile (augmented q and dout rows, transposed q and dout) in LDS,
@@ -507,15 +524,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   N = N - ib < qchunk ? N - ib : qchunk;
   ops.qa += ib * kH * 16;
   ops.doa += ib * kH * 16;
-  ops.qt += ib;
-  ops.ot += ib;
   dk += blockIdx.y * gstride;
   dv += blockIdx.y * gstride;
   partial += blockIdx.y * pstride;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* bins = reinterpret_cast<float*>(smem) + w * (2 * NB * 64);      // [NB][64 lanes][2 heads] per wave
   float2* tb = reinterpret_cast<float2*>(reinterpret_cast<float*>(smem) + kBwdWaves * 2 * NB * 64);  // [64] by code
-  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);           // [2][kStageHalves]
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);           // [2][kAugStageHalves]
 
   const int npad32 = static_cast<int>(ops.npk / 32);
   const int nkb = (npad32 + kBwdWaves - 1) / kBwdWaves;
@@ -550,10 +565,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   StageSrc src;
   src.row0 = ops.qa + h0 * 16;
   src.row1 = ops.doa + h0 * 16;
-  src.tr0 = ops.qt + static_cast<int64_t>(h0) * kD * npad;
-  src.tr1 = ops.ot + static_cast<int64_t>(h0) * kD * npad;
+  src.tr0 = nullptr;  // Q^T and dO^T are read transposed from the row tiles
+  src.tr1 = nullptr;
+  const int tb_h0 = tr_aug_base(lane, 0), tb_h1 = tr_aug_base(lane, 1);
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
-  constexpr int kCh = 384;  // qa, doa, q^T, dout^T
+  constexpr int kCh = 256;  // qa, doa
   s16x8 sr[stage_per_thread<kCh>()];
   StageCursor<kCh> cursor;
   cursor.init(src, npad, tid);
@@ -565,7 +581,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t i0 = t * 32;
-    const uint16_t* cur = stage + (t & 1) * kStageHalves;
+    const uint16_t* cur = stage + (t & 1) * kAugStageHalves;
     u32x4 cwn = cw;
     if (t + 1 < ntiles) {
       cursor.load_next(sr, tid);
@@ -575,8 +591,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
     if (wave_live) {
       const uint16_t* qa_t = cur;
       const uint16_t* doa_t = cur + kAugHalves;
-      const uint16_t* qt_t = cur + 2 * kAugHalves;
-      const uint16_t* ot_t = qt_t + kTrHalves;
       uint32_t code[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), nbm1);
@@ -601,14 +615,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
       }
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
-        const int g = 2 * hp + k1;
-        dv0 = mfma_h16(staged_tr(ot_t, 0, c, g), pack_f16x8(s0, 8 * k1), dv0);
-        dv1 = mfma_h16(staged_tr(ot_t, 1, c, g), pack_f16x8(s1, 8 * k1), dv1);
-        dk0 = mfma_h16(staged_tr(qt_t, 0, c, g), pack_f16x8(p0, 8 * k1), dk0);
-        dk1 = mfma_h16(staged_tr(qt_t, 1, c, g), pack_f16x8(p1, 8 * k1), dk1);
+        dv0 = mfma_h16(tr_aug_op(doa_t, tb_h0, k1), pack_f16x8(s0, 8 * k1), dv0);
+        dv1 = mfma_h16(tr_aug_op(doa_t, tb_h1, k1), pack_f16x8(s1, 8 * k1), dv1);
+        dk0 = mfma_h16(tr_aug_op(qa_t, tb_h0, k1), pack_f16x8(p0, 8 * k1), dk0);
+        dk1 = mfma_h16(tr_aug_op(qa_t, tb_h1, k1), pack_f16x8(p1, 8 * k1), dk1);
       }
     }
-    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kStageHalves, sr, tid);
+    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kAugStageHalves, sr, tid);
     cw = cwn;
     __syncthreads();
   }
@@ -658,28 +671,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 // larger code raises *flag (cleared by the prep kernel), and the three-pass kernels,
 // launched after this one with that flag as their gate, then redo the backward.
 constexpr int kFusedBins = 16;
-constexpr int kFusedStageHalves = 2 * kAugHalves;  // one stage buffer: the qa and doa row tiles
 
-// Transposed read of an augmented row tile (32 slots x [2 heads][16 halves], swz): in a
-// 16-lane group, ds_read_b64_tr_b16 gives lane j element j % 4 of the 8-byte pieces that
-// lanes 4e + j / 4 address (e = 0..3). Lane 4e + r addresses node n0 + e, head hl,
-// columns 4r .. 4r+3 of the node's 16-half row, so lane j receives nodes n0 .. n0+3 of
-// column j: for j < 8 that is d = j, the MFMA row of lane c = j; columns 8..15 (the
-// augmented terms) and lanes 16..31 (which repeat lanes 0..15) only feed accumulator rows
-// 8..31, which are never stored. n0 = 16 hp + 8 k1 + 4 half; the slot term
-// 512 k1 + 256 half is left out here, and with swz's swizzle the rest depends on hl only.
-__device__ __forceinline__ int tr_aug_base(int lane, int hl) {
-  const int hp = lane >> 5, e = (lane >> 2) & 3, r = lane & 3;
-  return 128 * hp + 32 * e + 8 * (2 * (hl ^ hp) + ((r >> 1) ^ (e >> 1))) + 4 * (r & 1);
-}
-// 8 consecutive nodes 16 hp + 8 k1 .. +7 at the lane's d (rows 0..7), as an MFMA operand
-__device__ __forceinline__ s16x8 tr_aug_op(const uint16_t* aug, int base, int k1) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4* lds4;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(aug + 512 * k1 + base));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(aug + 512 * k1 + 256 + base));
-  return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
 constexpr int kDsHalves = 2 * 32 * 32;            // one wave's dS buffer: [head][key][query]
 constexpr int kRedRow = 20;                       // floats per query of a dQ slot (16 used)
 constexpr int kRedFloats = kBwdWaves * 32 * kRedRow;  // [wave][query][head][d] dQ contributions
@@ -691,7 +683,7 @@ constexpr int kRedFloats = kBwdWaves * 32 * kRedRow;  // [wave][query][head][d] 
 __device__ __forceinline__ int ds_pos(int r, int k) { return r * 32 + 8 * (k ^ ((r >> 1) & 3)); }
 
 size_t fused_lds_bytes() {
-  return sizeof(float2) * (kBwdWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kFusedStageHalves +
+  return sizeof(float2) * (kBwdWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kAugStageHalves +
          2ull * kBwdWaves * kDsHalves + 4ull * kRedFloats;
 }
 
@@ -704,15 +696,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   float2* bins = reinterpret_cast<float2*>(smem);                 // [wave][code][lane]
   float2* tb = bins + kBwdWaves * kFusedBins * 64;                  // [64] by code
-  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);     // [2][kFusedStageHalves]
-  uint16_t* dsbuf = stage + 2 * kFusedStageHalves;                  // [wave][kDsHalves]
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);     // [2][kAugStageHalves]
+  uint16_t* dsbuf = stage + 2 * kAugStageHalves;                  // [wave][kDsHalves]
   float* red = reinterpret_cast<float*>(dsbuf + kBwdWaves * kDsHalves);  // [kRedFloats]
   const int64_t ib = static_cast<int64_t>(blockIdx.y) * qchunk;
   N = N - ib < qchunk ? N - ib : qchunk;
   ops.qa += ib * kH * 16;
   ops.doa += ib * kH * 16;
-  ops.qt += ib;
-  ops.ot += ib;
   dk += blockIdx.y * gstride;
   dv += blockIdx.y * gstride;
   partial += blockIdx.y * pstride;
@@ -805,7 +795,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
 
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t i0 = t * 32;
-    const uint16_t* cur = stage + (t & 1) * kFusedStageHalves;
+    const uint16_t* cur = stage + (t & 1) * kAugStageHalves;
     u32x4 cwn = cw;
     if (t + 1 < ntiles) {
       cursor.load_next(sr, tid);
@@ -880,7 +870,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
     *reinterpret_cast<float4*>(myred + 16 * kRedRow) = q1;
     __syncthreads();
     reduce_dq(t);
-    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kFusedStageHalves, sr, tid);
+    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kAugStageHalves, sr, tid);
     cw = cwn;
     __syncthreads();
   }
@@ -1022,7 +1012,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
 }
 
 size_t kv_mfma_lds(int NB) {
-  return 4ull * kBwdWaves * 2 * NB * 64 + sizeof(float2) * kKvTable + 2ull * 2 * kStageHalves;
+  return 4ull * kBwdWaves * 2 * NB * 64 + sizeof(float2) * kKvTable + 2ull * 2 * kAugStageHalves;
 }
 
 }  // namespace
@@ -1039,7 +1029,7 @@ int64_t mfma_kv_blocks(int64_t Nk) {
 
 size_t mfma_ops_bytes(int64_t N, int64_t Nk) {
   const size_t npq = static_cast<size_t>(mfma_npad(N)), npk = static_cast<size_t>(mfma_npad(Nk));
-  return 2 * (npq + npk) * kH * 16 * 2 + (2 * npq + npk) * kH * kD * 2;
+  return 2 * (npq + npk) * kH * 16 * 2 + npk * kH * kD * 2;
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
@@ -1082,9 +1072,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   ops.doa = ops.qa + hq * 16;
   ops.ka = ops.doa + hq * 16;
   ops.va = ops.ka + hk * 16;
-  ops.qt = ops.va + hk * 16;
-  ops.ot = ops.qt + hq * kD;
-  ops.kt = ops.ot + hq * kD;
+  ops.kt = ops.va + hk * 16;
 
   uint32_t* flag = reinterpret_cast<uint32_t*>(ws + w.flag_off);
   trace_begin(kTraceBwdDelta, s);
