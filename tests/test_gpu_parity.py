@@ -126,6 +126,31 @@ def test_d32_backward_is_bitwise_reproducible(N, family):
         check(name, host64(got), r, "bf16")
 
 
+@pytest.mark.parametrize("N,family", [(300, "er"), (40, "path")])
+def test_d8_backward_is_bitwise_reproducible(N, family):
+    """Head dimension 8: the one-pass backward keeps private dtable bins for codes 0..15 (the
+    connected ER graph stays there); a larger code (the 40-node path reaches 30, NB = 31)
+    raises its flag and the three-pass kernels redo the backward. Either way two calls give
+    identical bits, and match the oracle."""
+    inp = small_case(N, 8, 8, 30, "bf16", seed=5, family=family, avg_degree=12.0)
+    codes = oracle.bfs_codes(inp.indptr, inp.indices, 30, range(N))
+    assert (codes.max() >= 16) == (family == "path")
+    q, k, v, do, table = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.dout), dev(inp.table)
+    spd = torch.from_numpy(codes).cuda()
+    runs = []
+    for _ in range(2):
+        out, lse = gta.fwd(q, k, v, spd, table)
+        g = gta.bwd(q, k, v, spd, table, out, lse, do)
+        torch.cuda.synchronize()
+        runs.append([x.clone() for x in (out, lse) + tuple(g)])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+    ref = oracle.full_backward(inp.q.value, inp.k.value, inp.v.value, codes, inp.table.value,
+                               inp.dout.value)
+    for name, got, r in zip(["out", "lse", "dq", "dk", "dv", "dtable"], runs[0], ref):
+        check(name, host64(got), r, "bf16")
+
+
 def test_code_clamp_and_determinism():
     """Codes >= NB clamp to NB-1 like the oracle; two runs are bitwise identical."""
     inp = small_case(150, 8, 8, 6, "bf16", seed=3)
