@@ -275,12 +275,18 @@ void trace_end(int kernel_id, hipStream_t s) {
 // are a fixed ~10-20 us plus ~1.7-1.8 us per tile, so the fixed part is about 12 tiles.
 // This both fills the GPU when the outer dimension is short and evens out the last
 // round when W is not a multiple of R.
+// The forward's CUs do not finish a round together: launched as exactly one round at
+// 32768 nodes, it kept 11 of 16 waves resident on average, the rest idle at the tail;
+// smaller workgroups in more rounds let the faster CUs take more of them (4 key splits:
+// 1.72 -> 1.59 ms). The model charges the forward's last round a tail of 2/10 of a
+// workgroup's tiles (the backward kernels kept 7.4 of 8 waves resident: no tail term).
 constexpr int64_t kSplitMinInner = 256;
 constexpr int64_t kSplitFixedTiles = 12;
+constexpr int64_t kFwdTailTenths = 2;
 
 // 4-wave workgroups resident per CU, from each kernel's VGPR use (512 per SIMD lane):
-// D = 8: forward 128 -> 4, key-outer 203 -> 2, query-outer 140 -> 3; D = 32: forward 156
-// -> 3, key-outer 252 and query-outer 200 -> 2.
+// D = 8: forward 128 -> 4, key-outer 192-212 -> 2, query-outer 142 -> 3; D = 32: forward 156
+// -> 3, key-outer 238-243 and query-outer 226 -> 2.
 int64_t resident_wgs(int kind, int D) {
   const int per_cu = D == 32 ? (kind == kSplitFwd ? 3 : 2) : (kind == kSplitFwd ? 4 : kind == kSplitKv ? 2 : 3);
   return 256 * per_cu;
@@ -297,7 +303,8 @@ Split inner_split(int64_t outer, int64_t inner, int H, int D, int dtype, int kin
     const int64_t chunk = S == 1 ? inner : ((inner + S - 1) / S + 31) / 32 * 32;
     const int64_t parts = (inner + chunk - 1) / chunk;
     const int64_t rounds = (W * parts + R - 1) / R;
-    const int64_t t = rounds * (kSplitFixedTiles + (chunk + 31) / 32);
+    const int64_t tiles = (chunk + 31) / 32;
+    const int64_t t = 10 * rounds * (kSplitFixedTiles + tiles) + (kind == kSplitFwd ? kFwdTailTenths * tiles : 0);
     if (best_t < 0 || t < best_t) {
       best_t = t;
       sp.S = static_cast<int>(parts);

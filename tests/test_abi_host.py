@@ -86,10 +86,12 @@ def test_bwd_argument_errors():
 
 def test_split_workspaces():
     """Launches whose workgroups would not fill whole rounds split the inner loop: the
-    forward then needs a workspace for its partial results, and the backward's grows;
-    at 32768 nodes (D = 8) the forward and key-outer passes fill whole rounds and do not split."""
+    forward then needs a workspace for its partial results, and the backward's grows.
+    At 32768 nodes (D = 8) the forward's 1024 workgroups would be one full round, whose tail
+    the model charges, so it splits 4 ways (4 rounds of 256 tiles)."""
     L = gta.lib()
-    assert L.gt_attn_fwd_workspace_bytes(32768, 8, 8, 33, 1) == 0    # 1024 workgroups: one full round
+    rows = 32768 * 8
+    assert L.gt_attn_fwd_workspace_bytes(32768, 8, 8, 33, 1) == 4 * (rows * 8 * 4 + rows * 4)
     # D = 32, 65536 nodes: 2048 workgroups at 3 per CU would leave the third round two thirds
     # full; three key splits (8 rounds of 683 tiles) cost less than 3 rounds of 2048 tiles
     rows = 65536 * 8
