@@ -380,25 +380,25 @@ constexpr int kKvTable = 64;              // key-outer table entries (codes clam
 constexpr int kBwdThreads = 64 * kBwdWaves;
 
 // One 32-node tile of backward operands of a head pair, staged into LDS: two
-// augmented-row tiles and one or two transposed tiles. Each tile is 32 rows of 64
-// bytes (4 chunks of 16 bytes):
+// augmented-row tiles, and for the query-outer kernel a transposed k tile. Each tile is
+// 32 rows of 64 bytes (4 chunks of 16 bytes):
 //   augmented:  row = slot s holding node a(s) (the MFMA row order), chunk = 2*head + half
 //   transposed: row = 8*head + d, chunk = 8-node group
 // Chunk k of row r is stored at chunk position k ^ ((r >> 1) & 3), so that the eight
 // lanes of one LDS cycle, which read rows 0..7 (or 8..15, ...) at one chunk index,
 // hit 8 distinct 16-byte bank groups instead of two.
 // The global source is cut into 16-byte chunks x: [0,128) first augmented, [128,256)
-// second augmented, [256,320) first transposed, [320,384) second transposed; thread t
-// moves chunks t, t + 256, ...
+// second augmented, [256,320) the transposed tile; thread t moves chunks t, t + 256.
+// The key-outer kernels stage the two augmented tiles only and read Q^T and dO^T from
+// them transposed (tr_aug_op).
 constexpr int kAugHalves = 32 * 32;             // one augmented tile, halves
 constexpr int kTrHalves = 2 * kD * 32;          // one transposed tile [2 heads][8][32], halves
-constexpr int kStageHalves = 2 * kAugHalves + 2 * kTrHalves;  // one buffer of the double buffer
+constexpr int kStageHalves = 2 * kAugHalves + kTrHalves;  // one buffer of the query-outer's double buffer
 
 struct StageSrc {
   const uint16_t* row0;  // first augmented rows (qa or ka) at node 0, head h0
   const uint16_t* row1;  // second augmented rows (doa or va) at node 0, head h0
-  const uint16_t* tr0;   // first transposed copy at head h0, d 0, node 0
-  const uint16_t* tr1;   // second transposed copy (unused when only one is staged)
+  const uint16_t* tr;    // transposed copy at head h0, d 0, node 0 (null when none is staged)
 };
 
 // global chunk c of an augmented tile: node = c >> 2, chunk = c & 3 (head = bit 1, half = bit 0)
@@ -412,8 +412,7 @@ __device__ __forceinline__ const uint16_t* tr_chunk(const uint16_t* base, int64_
 __device__ __forceinline__ const uint16_t* stage_chunk(const StageSrc& s, int64_t npad, int64_t n0, int x) {
   if (x < 128) return aug_chunk(s.row0, n0, x);
   if (x < 256) return aug_chunk(s.row1, n0, x - 128);
-  if (x < 320) return tr_chunk(s.tr0, npad, n0, x - 256);
-  return tr_chunk(s.tr1, npad, n0, x - 320);
+  return tr_chunk(s.tr, npad, n0, x - 256);
 }
 // LDS position (halves) of global chunk x within one stage buffer
 __device__ __forceinline__ int stage_pos(int x) {
@@ -421,8 +420,8 @@ __device__ __forceinline__ int stage_pos(int x) {
     const int c = x & 127;
     return (x >> 7) * kAugHalves + swz(slot_of_node(c >> 2), c & 3);
   }
-  const int c = (x - 256) & 63;
-  return 2 * kAugHalves + ((x - 256) >> 6) * kTrHalves + swz(c >> 2, c & 3);
+  const int c = x - 256;  // the transposed tile (chunks 256..319)
+  return 2 * kAugHalves + swz(c >> 2, c & 3);
 }
 
 template <int kChunks>
@@ -500,13 +499,14 @@ __device__ __forceinline__ s16x8 tr_aug_op(const uint16_t* aug, int base, int k1
 
 // Backward, step 2 (key-outer). A workgroup is 4 waves = 128 keys x one head pair;
 // each wave owns 32 keys (lane c keeps key c for the whole sweep) and all waves share
-// each staged query tile (augmented q and dout rows, transposed q and dout) in LDS,
-// double-buffered. Codes come along rows of the transposed code matrix.
+// each staged query tile (augmented q and dout rows) in LDS, double-buffered. Codes
+// come along rows of the transposed code matrix.
 // S = Q K^T - lse and dP - delta = dO V^T - delta come out of two augmented MFMAs with
 // rows = queries (order a(r)) and columns = keys, so a lane's accumulator entries
 // are queries 16*hp + 0..15; then P = exp2(S log2e / sqrt(D)) and dS = P (dP - delta)
 // take one multiply each. dV^T += dO^T P and dK^T += Q^T dS contract over those
-// queries. Bucket sums of dS go to per-lane LDS bins laid out [bucket][lane][head]
+// queries, Q^T and dO^T read from the staged rows with ds_read_b64_tr_b16. Bucket sums
+// of dS go to per-lane LDS bins laid out [bucket][lane][head]
 // (no two lanes share an address, so a plain read-add-write suffices; one 8-byte
 // read-add-write updates both heads), reduced in a fixed order at the end.
 template <bool kAligned>
@@ -565,8 +565,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   StageSrc src;
   src.row0 = ops.qa + h0 * 16;
   src.row1 = ops.doa + h0 * 16;
-  src.tr0 = nullptr;  // Q^T and dO^T are read transposed from the row tiles
-  src.tr1 = nullptr;
+  src.tr = nullptr;  // Q^T and dO^T are read transposed from the row tiles
   const int tb_h0 = tr_aug_base(lane, 0), tb_h1 = tr_aug_base(lane, 1);
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
   constexpr int kCh = 256;  // qa, doa
@@ -765,8 +764,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   StageSrc src;
   src.row0 = ops.qa + h0 * 16;
   src.row1 = ops.doa + h0 * 16;
-  src.tr0 = nullptr;  // no transposed tile is staged
-  src.tr1 = nullptr;
+  src.tr = nullptr;  // no transposed tile is staged
   const int tb_h0 = tr_aug_base(lane, 0), tb_h1 = tr_aug_base(lane, 1);
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
   constexpr int kCh = 256;  // qa, doa
@@ -956,8 +954,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_d8_kernel(const uint8_
   StageSrc src;
   src.row0 = ops.ka + h0 * 16;
   src.row1 = ops.va + h0 * 16;
-  src.tr0 = ops.kt + static_cast<int64_t>(h0) * kD * npad;
-  src.tr1 = nullptr;
+  src.tr = ops.kt + static_cast<int64_t>(h0) * kD * npad;
   const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
   constexpr int kCh = 320;  // ka, va, k^T
   s16x8 sr[stage_per_thread<kCh>()];
