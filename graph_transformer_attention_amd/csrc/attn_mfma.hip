@@ -378,6 +378,15 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
 constexpr int kBwdWaves = 4;              // waves per backward workgroup: 4 x 32 nodes, one head pair
 constexpr int kKvTable = 64;              // key-outer table entries (codes clamped to NB-1 <= 63)
 constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kFusedWaves = 8;            // waves per one-pass workgroup: 8 x 32 keys, one head pair
+constexpr int kFusedThreads = 64 * kFusedWaves;
+
+// 32-key blocks of dtable partial rows, padded to whole one-pass workgroups (a multiple
+// of 8, so of the 4-wave kernels' blocks too); every key-outer kernel covers them all, a
+// wave past the last key writing zero rows, so each row is defined whichever ran.
+__host__ __device__ constexpr int64_t kv_row_blocks(int64_t npad32) {
+  return (npad32 + kFusedWaves - 1) / kFusedWaves * kFusedWaves;
+}
 
 // One 32-node tile of backward operands of a head pair, staged into LDS: two
 // augmented-row tiles, and for the query-outer kernel a transposed k tile. Each tile is
@@ -532,8 +541,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
   float2* tb = reinterpret_cast<float2*>(reinterpret_cast<float*>(smem) + kBwdWaves * 2 * NB * 64);  // [64] by code
   uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);           // [2][kAugStageHalves]
 
-  const int npad32 = static_cast<int>(ops.npk / 32);
-  const int nkb = (npad32 + kBwdWaves - 1) / kBwdWaves;
+  const int nkb = static_cast<int>(kv_row_blocks(ops.npk / 32) / kBwdWaves);
   int kb, hpair;
   xcd_map(blockIdx.x, nkb, kb, hpair);
   if (kb < 0) return;
@@ -651,11 +659,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 
 // Backward in one pass (key-outer with dQ): the key-outer kernel's work and, from the
 // same probabilities, the queries' gradient, so the query-outer pass (a third sweep
-// over the codes with a third exp per entry) is not needed. Work split and the dK/dV
-// contractions are those of bwd_kv_mfma_d8_kernel, but only the two augmented row
-// tiles are staged (4 KB per tile): the dK^T and dV^T contractions read Q^T and dO^T
-// from them with ds_read_b64_tr_b16 (tr_aug_base below). Per 32-query tile each wave
-// also:
+// over the codes with a third exp per entry) is not needed. The dK/dV contractions are
+// those of bwd_kv_mfma_d8_kernel, with 8-wave workgroups (256 keys x one head pair, one
+// workgroup per CU): the staged query tile then serves twice the keys, and each
+// workgroup's dQ partial covers 256 keys, which halves the partials written and summed.
+// Only the two augmented row tiles are staged (4 KB per tile): the dK^T and dV^T
+// contractions read Q^T and dO^T from them with ds_read_b64_tr_b16 (tr_aug_base). Per
+// 32-query tile each wave also:
 //  * writes its packed dS (f16, both heads, 32 keys x 32 queries) row by row into its own
 //    LDS buffer [head][key][query] and reads it back transposed with ds_read_b64_tr_b16:
 //    lane l of a 16-lane group receives element l%4 of the 8-byte chunks that lanes
@@ -673,7 +683,7 @@ constexpr int kFusedBins = 16;
 
 constexpr int kDsHalves = 2 * 32 * 32;            // one wave's dS buffer: [head][key][query]
 constexpr int kRedRow = 20;                       // floats per query of a dQ slot (16 used)
-constexpr int kRedFloats = kBwdWaves * 32 * kRedRow;  // [wave][query][head][d] dQ contributions
+constexpr int kRedFloats = kFusedWaves * 32 * kRedRow;  // [wave][query][head][d] dQ contributions
 
 // Position (halves) of queries 8k..8k+7 of key row r in a dS buffer: 64-byte rows whose
 // 16-byte chunks are XOR-swizzled by (r >> 1) & 3, so that the eight lanes of one write
@@ -682,22 +692,22 @@ constexpr int kRedFloats = kBwdWaves * 32 * kRedRow;  // [wave][query][head][d] 
 __device__ __forceinline__ int ds_pos(int r, int k) { return r * 32 + 8 * (k ^ ((r >> 1) & 3)); }
 
 size_t fused_lds_bytes() {
-  return sizeof(float2) * (kBwdWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kAugStageHalves +
-         2ull * kBwdWaves * kDsHalves + 4ull * kRedFloats;
+  return sizeof(float2) * (kFusedWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kAugStageHalves +
+         2ull * kFusedWaves * kDsHalves + 4ull * kRedFloats;
 }
 
 template <bool kAligned>
-__global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
+__global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
     const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ partial, float* __restrict__ dqpart, int64_t N, int64_t Nk,
     int64_t ldt, int NB, int64_t qchunk, int64_t gstride, int64_t pstride, int64_t dqstride,
     uint32_t* __restrict__ flag) {
   extern __shared__ __align__(16) unsigned char smem[];
   float2* bins = reinterpret_cast<float2*>(smem);                 // [wave][code][lane]
-  float2* tb = bins + kBwdWaves * kFusedBins * 64;                  // [64] by code
+  float2* tb = bins + kFusedWaves * kFusedBins * 64;                // [64] by code
   uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);     // [2][kAugStageHalves]
   uint16_t* dsbuf = stage + 2 * kAugStageHalves;                  // [wave][kDsHalves]
-  float* red = reinterpret_cast<float*>(dsbuf + kBwdWaves * kDsHalves);  // [kRedFloats]
+  float* red = reinterpret_cast<float*>(dsbuf + kFusedWaves * kDsHalves);  // [kRedFloats]
   const int64_t ib = static_cast<int64_t>(blockIdx.y) * qchunk;
   N = N - ib < qchunk ? N - ib : qchunk;
   ops.qa += ib * kH * 16;
@@ -709,14 +719,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   float2* mybins = bins + w * (kFusedBins * 64) + lane;
   uint16_t* mydst = dsbuf + w * kDsHalves;
 
-  const int npad32 = static_cast<int>(ops.npk / 32);
-  const int nkb = (npad32 + kBwdWaves - 1) / kBwdWaves;
+  const int nkb = static_cast<int>(kv_row_blocks(ops.npk / 32) / kFusedWaves);
   int kb, hpair;
   xcd_map(blockIdx.x, nkb, kb, hpair);
   if (kb < 0) return;
   const int c = lane & 31, hp = lane >> 5;
   const int h0 = 2 * hpair;
-  const int64_t jw = static_cast<int64_t>(kb) * (32 * kBwdWaves) + 32 * w;
+  const int64_t jw = static_cast<int64_t>(kb) * (32 * kFusedWaves) + 32 * w;
   const int64_t j = jw + c;
   const bool wave_live = jw < ops.npk;
   const int64_t jj = wave_live ? j : 0;
@@ -725,7 +734,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
 
-  for (int b = tid; b < kKvTable; b += kBwdThreads) {
+  for (int b = tid; b < kKvTable; b += kFusedThreads) {
     const int cb = min(b, NB - 1);
     tb[b] = make_float2(table[h0 * NB + cb] * kLog2e, table[(h0 + 1) * NB + cb] * kLog2e);
   }
@@ -758,8 +767,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   // 16 (qh ^ s) halves.
   const int e4 = (lane & 15) >> 2, j4 = lane & 3;
   const int tr_base = (G >> 1) * 32 * 32 + (8 * (G & 1) + e4) * 32 + 8 * ((j4 >> 1) ^ (e4 >> 1)) + 4 * (j4 & 1);
-  // this thread's share of the workgroup's dQ sum: 2 values of [query][head][d]
-  const int rq = tid >> 3, rh = (tid >> 2) & 1, rd = 2 * (tid & 3);
+  // this thread's share of the workgroup's dQ sum: one value of [query][head][d]
+  const int rq = tid >> 4, rh = (tid >> 3) & 1, rd = tid & 7;
 
   StageSrc src;
   src.row0 = ops.qa + h0 * 16;
@@ -775,18 +784,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fused_mfma_d8_kernel(
   stage_store<kCh>(stage, sr, tid);
   u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
   float* dqw = dqpart + static_cast<int64_t>(kb) * dqstride + (ib + rq) * kHD + (h0 + rh) * kD + rd;
-  // the workgroup's dQ for tile tt from the four waves' contributions, in wave order
+  // the workgroup's dQ for tile tt from the eight waves' contributions, in wave order
   auto reduce_dq = [&](int64_t tt) {
     const float* slot = red + rq * kRedRow + rh * 8 + rd;
-    float2 acc = make_float2(0.f, 0.f);
+    float acc = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kBwdWaves; ++ww) {
-      const float2 x = *reinterpret_cast<const float2*>(slot + ww * (32 * kRedRow));
-      acc.x += x.x;
-      acc.y += x.y;
-    }
+    for (int ww = 0; ww < kFusedWaves; ++ww) acc += slot[ww * (32 * kRedRow)];
     const float rs = 1.f / sqd;  // dQ = dS K / sqrt(D)
-    if (tt * 32 + rq < N) *reinterpret_cast<float2*>(dqw + tt * 32 * kHD) = make_float2(acc.x * rs, acc.y * rs);
+    if (tt * 32 + rq < N) dqw[tt * 32 * kHD] = acc * rs;
   };
   wait_vm0();
   __syncthreads();
@@ -1018,11 +1023,11 @@ bool mfma_supported(int H, int D, int dtype) { return H == kH && (D == 8 || D ==
 
 int64_t mfma_npad(int64_t N) { return (N + 31) / 32 * 32; }
 
-// dtable partial rows: one per 32-key block (padded to whole key workgroups)
-int64_t mfma_kv_blocks(int64_t Nk) {
-  const int64_t nblk = (mfma_npad(Nk) / 32 + kBwdWaves - 1) / kBwdWaves;
-  return nblk * kBwdWaves;
-}
+// dtable partial rows: one per 32-key block (padded to whole one-pass workgroups)
+int64_t mfma_kv_blocks(int64_t Nk) { return kv_row_blocks(mfma_npad(Nk) / 32); }
+
+// dQ partials of the one-pass backward: one per workgroup's 256 keys
+int64_t mfma_fused_dq_parts(int64_t Nk) { return mfma_kv_blocks(Nk) / kFusedWaves; }
 
 size_t mfma_ops_bytes(int64_t N, int64_t Nk) {
   const size_t npq = static_cast<size_t>(mfma_npad(N)), npk = static_cast<size_t>(mfma_npad(Nk));
@@ -1091,7 +1096,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   float* dvp = kv_split ? dkp + static_cast<size_t>(w.kv.S) * nk_el : a.dv;
   const int kv_acc = kv_split ? 0 : (a.acc & kAccDkv);
   const int64_t pstride = w.n_kv_blocks * kH * a.NB;
-  const int nkb = static_cast<int>((ops.npk / 32 + kBwdWaves - 1) / kBwdWaves);
+  const int nkb = static_cast<int>(mfma_kv_blocks(a.Nk) / kBwdWaves);
   const dim3 kgrid(static_cast<unsigned>(xcd_grid(nkb)), static_cast<unsigned>(w.kv.S));
   const bool kv_aligned = codes_aligned(a.spd_t, a.ld_t);
   const SumSplits none{nullptr, nullptr, 0, 0, 0};
@@ -1107,21 +1112,23 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
   const uint32_t* gate = nullptr;
   if (fused) {
     float* dqpart = reinterpret_cast<float*>(ws + w.dqf_off);
+    const int nfb = static_cast<int>(mfma_fused_dq_parts(a.Nk));
+    const dim3 fgrid(static_cast<unsigned>(xcd_grid(nfb)), static_cast<unsigned>(w.kv.S));
     const size_t flds = fused_lds_bytes();
     e = allow_lds_mfma(bwd_fused_mfma_d8_kernel<true>, flds);
     if (e == hipSuccess) e = allow_lds_mfma(bwd_fused_mfma_d8_kernel<false>, flds);
     if (e != hipSuccess) return e;
     trace_begin(kTraceBwdFused, s);
     if (kv_aligned)
-      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<true>, kgrid, block, flds, s, a.spd_t, a.table, ops, dkp, dvp,
-                         partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
+      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<true>, fgrid, dim3(kFusedThreads), flds, s, a.spd_t, a.table, ops,
+                         dkp, dvp, partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
     else
-      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<false>, kgrid, block, flds, s, a.spd_t, a.table, ops, dkp, dvp,
-                         partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
+      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<false>, fgrid, dim3(kFusedThreads), flds, s, a.spd_t, a.table, ops,
+                         dkp, dvp, partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
     e = hipGetLastError();
     trace_end(kTraceBwdFused, s);
     if (e != hipSuccess) return e;
-    const SumSplits sqf{dqpart, a.dq, nq_el, nkb, 0};
+    const SumSplits sqf{dqpart, a.dq, nq_el, nfb, 0};
     e = launch_bwd_finish(sk, sv, sqf, partial, a.dtable, w.kv.S * w.n_kv_blocks, kH * a.NB, 0, s);
     if (e != hipSuccess || a.NB <= kFusedBins) return e;
     gate = flag;

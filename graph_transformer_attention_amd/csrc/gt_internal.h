@@ -114,6 +114,7 @@ hipError_t launch_fwd_valu(const FwdArgs& a, hipStream_t s);
 bool mfma_supported(int H, int D, int dtype);
 int64_t mfma_npad(int64_t N);
 int64_t mfma_kv_blocks(int64_t Nk);
+int64_t mfma_fused_dq_parts(int64_t Nk);
 size_t mfma_ops_bytes(int64_t N, int64_t Nk);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
