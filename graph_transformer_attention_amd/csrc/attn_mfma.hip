@@ -693,7 +693,7 @@ __device__ __forceinline__ int ds_pos(int r, int k) { return r * 32 + 8 * (k ^ (
 
 size_t fused_lds_bytes() {
   return sizeof(float2) * (kFusedWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kAugStageHalves +
-         2ull * kFusedWaves * kDsHalves + 4ull * kRedFloats;
+         2ull * kFusedWaves * kDsHalves + 4ull * 2 * kRedFloats;
 }
 
 template <bool kAligned>
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   float2* tb = bins + kFusedWaves * kFusedBins * 64;                // [64] by code
   uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);     // [2][kAugStageHalves]
   uint16_t* dsbuf = stage + 2 * kAugStageHalves;                  // [wave][kDsHalves]
-  float* red = reinterpret_cast<float*>(dsbuf + kFusedWaves * kDsHalves);  // [kRedFloats]
+  float* red = reinterpret_cast<float*>(dsbuf + kFusedWaves * kDsHalves);  // [2][kRedFloats]
   const int64_t ib = static_cast<int64_t>(blockIdx.y) * qchunk;
   N = N - ib < qchunk ? N - ib : qchunk;
   ops.qa += ib * kH * 16;
@@ -786,7 +786,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   float* dqw = dqpart + static_cast<int64_t>(kb) * dqstride + (ib + rq) * kHD + (h0 + rh) * kD + rd;
   // the workgroup's dQ for tile tt from the eight waves' contributions, in wave order
   auto reduce_dq = [&](int64_t tt) {
-    const float* slot = red + rq * kRedRow + rh * 8 + rd;
+    const float* slot = red + (tt & 1) * kRedFloats + rq * kRedRow + rh * 8 + rd;
     float acc = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kFusedWaves; ++ww) acc += slot[ww * (32 * kRedRow)];
@@ -867,15 +867,17 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
         if (qh == 0) q0 = v; else q1 = v;
       }
     }
-    // the workgroup's dQ for this tile: every wave's contribution, summed in wave order
-    float* myred = red + w * (32 * kRedRow) + m16 * kRedRow + 8 * (G >> 1) + 4 * (G & 1);
+    // the workgroup's dQ for this tile: every wave's contribution, summed in wave order.
+    // The contributions of tile t go to buffer t & 1 and one barrier per tile orders
+    // everything: after it, tile t's contributions and tile t+1's stage are complete, and
+    // the buffers written next (contributions of t+1, stage of t+2) were last read before it.
+    float* myred = red + (t & 1) * kRedFloats + w * (32 * kRedRow) + m16 * kRedRow + 8 * (G >> 1) + 4 * (G & 1);
     *reinterpret_cast<float4*>(myred) = q0;
     *reinterpret_cast<float4*>(myred + 16 * kRedRow) = q1;
-    __syncthreads();
-    reduce_dq(t);
     if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kAugStageHalves, sr, tid);
     cw = cwn;
     __syncthreads();
+    reduce_dq(t);
   }
   if (wave_live && j < Nk) {
     const float rs = 1.f / sqd;
