@@ -691,23 +691,20 @@ constexpr int kRedFloats = kFusedWaves * 32 * kRedRow;  // [wave][query][head][d
 // group (rows r0..r0+3, r0 a multiple of 4, at four chunk offsets) hit distinct banks.
 __device__ __forceinline__ int ds_pos(int r, int k) { return r * 32 + 8 * (k ^ ((r >> 1) & 3)); }
 
-size_t fused_lds_bytes() {
-  return sizeof(float2) * (kFusedWaves * kFusedBins * 64 + kKvTable) + 2ull * 2 * kAugStageHalves +
-         2ull * kFusedWaves * kDsHalves + 4ull * 2 * kRedFloats;
-}
-
 template <bool kAligned>
 __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
     const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ partial, float* __restrict__ dqpart, int64_t N, int64_t Nk,
     int64_t ldt, int NB, int64_t qchunk, int64_t gstride, int64_t pstride, int64_t dqstride,
     uint32_t* __restrict__ flag) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float2* bins = reinterpret_cast<float2*>(smem);                 // [wave][code][lane]
-  float2* tb = bins + kFusedWaves * kFusedBins * 64;                // [64] by code
-  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTable);     // [2][kAugStageHalves]
-  uint16_t* dsbuf = stage + 2 * kAugStageHalves;                  // [wave][kDsHalves]
-  float* red = reinterpret_cast<float*>(dsbuf + kFusedWaves * kDsHalves);  // [2][kRedFloats]
+  // Five separate LDS arrays (144.5 KB): as distinct objects the compiler knows that
+  // accesses to different ones never overlap, so it may interleave the bin updates with
+  // the other arrays' reads and writes instead of keeping all of them in program order.
+  __shared__ __align__(16) float2 bins[kFusedWaves * kFusedBins * 64];  // [wave][code][lane]
+  __shared__ __align__(16) float2 tb[kKvTable];                         // by code
+  __shared__ __align__(16) uint16_t stage[2 * kAugStageHalves];         // [2][kAugStageHalves]
+  __shared__ __align__(16) uint16_t dsbuf[kFusedWaves * kDsHalves];     // [wave][kDsHalves]
+  __shared__ __align__(16) float red[2 * kRedFloats];                   // [2][kRedFloats]
   const int64_t ib = static_cast<int64_t>(blockIdx.y) * qchunk;
   N = N - ib < qchunk ? N - ib : qchunk;
   ops.qa += ib * kH * 16;
@@ -813,19 +810,27 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
       uint32_t code[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), bound);
+      // All 16 bias reads are issued before the first bin update: the table and the bins
+      // share the LDS array, so a table read placed after a bin store must wait behind it,
+      // which would chain every entry's read, exp and store into one serial LDS round trip.
+      float2 tv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tv[e] = tb[code[e]];
       f32x16 s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), kb0, f32x16{});
       f32x16 s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), kb1, f32x16{});
       f32x16 p0 = mfma_h16(staged_aug(doa_t, c, 0, hp), vb0, f32x16{});
       f32x16 p1 = mfma_h16(staged_aug(doa_t, c, 1, hp), vb1, f32x16{});
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float2 tv = tb[code[e]];
-        const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, tv.x));
-        const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, tv.y));
+        const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, tv[e].x));
+        const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, tv[e].y));
         s0[e] = pa;
         s1[e] = pb;
         p0[e] *= pa;
         p1[e] *= pb;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
         float2 bin = mybins[code[e] * 64];
         bin.x += p0[e];
         bin.y += p1[e];
@@ -1116,16 +1121,12 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
     float* dqpart = reinterpret_cast<float*>(ws + w.dqf_off);
     const int nfb = static_cast<int>(mfma_fused_dq_parts(a.Nk));
     const dim3 fgrid(static_cast<unsigned>(xcd_grid(nfb)), static_cast<unsigned>(w.kv.S));
-    const size_t flds = fused_lds_bytes();
-    e = allow_lds_mfma(bwd_fused_mfma_d8_kernel<true>, flds);
-    if (e == hipSuccess) e = allow_lds_mfma(bwd_fused_mfma_d8_kernel<false>, flds);
-    if (e != hipSuccess) return e;
     trace_begin(kTraceBwdFused, s);
     if (kv_aligned)
-      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<true>, fgrid, dim3(kFusedThreads), flds, s, a.spd_t, a.table, ops,
+      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<true>, fgrid, dim3(kFusedThreads), 0, s, a.spd_t, a.table, ops,
                          dkp, dvp, partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
     else
-      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<false>, fgrid, dim3(kFusedThreads), flds, s, a.spd_t, a.table, ops,
+      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<false>, fgrid, dim3(kFusedThreads), 0, s, a.spd_t, a.table, ops,
                          dkp, dvp, partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
     e = hipGetLastError();
     trace_end(kTraceBwdFused, s);
