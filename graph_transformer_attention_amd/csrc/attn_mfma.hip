@@ -601,24 +601,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
       uint32_t code[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), nbm1);
+      // Every LDS read of the tile (bias, then the dK/dV operands) precedes the bin
+      // updates in program order: the bins share the LDS array with the table and the
+      // stage, so a read placed after a bin store would wait behind it.
+      float2 tv[16];  // both heads' log2e-scaled bias, the FMA addends
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tv[e] = tb[code[e]];
       f32x16 s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), kb0, f32x16{});
       f32x16 s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), kb1, f32x16{});
       f32x16 p0 = mfma_h16(staged_aug(doa_t, c, 0, hp), vb0, f32x16{});
       f32x16 p1 = mfma_h16(staged_aug(doa_t, c, 1, hp), vb1, f32x16{});
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        // both heads' log2e-scaled bias in one 8-byte read, used as the FMA addends
-        const float2 t = tb[code[e]];
-        const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, t.x));
-        const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, t.y));
+        const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, tv[e].x));
+        const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, tv[e].y));
         s0[e] = pa;
         s1[e] = pb;
         p0[e] *= pa;
         p1[e] *= pb;
-        float2 bin = mybins[code[e] * 64];
-        bin.x += p0[e];
-        bin.y += p1[e];
-        mybins[code[e] * 64] = bin;
       }
 #pragma unroll
       for (int k1 = 0; k1 < 2; ++k1) {
@@ -626,6 +626,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
         dv1 = mfma_h16(tr_aug_op(doa_t, tb_h1, k1), pack_f16x8(s1, 8 * k1), dv1);
         dk0 = mfma_h16(tr_aug_op(qa_t, tb_h0, k1), pack_f16x8(p0, 8 * k1), dk0);
         dk1 = mfma_h16(tr_aug_op(qa_t, tb_h1, k1), pack_f16x8(p1, 8 * k1), dk1);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float2 bin = mybins[code[e] * 64];
+        bin.x += p0[e];
+        bin.y += p1[e];
+        mybins[code[e] * 64] = bin;
       }
     }
     if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kAugStageHalves, sr, tid);

@@ -435,7 +435,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
                                                                    int64_t ldt, int NB, int acc, int64_t qchunk,
                                                                    int64_t gstride, int64_t pstride,
                                                                    uint32_t* __restrict__ flag) {
-  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kBinLanes = kPrivate ? 64 : 32;                          // bin rows per bucket
+  // Three separate LDS arrays (bins sized for the layout's largest bucket count, NB <= 64):
+  // as distinct objects the compiler knows the bin updates never touch the table or the
+  // staged tile, so it may issue the stage reads of the dK/dV operands among them.
+  __shared__ __align__(16) float bins_all[kWaves * 2 * (kPrivate ? kPrivBins : kKvTbD32) * kBinLanes];
+  __shared__ __align__(16) float2 tb[kKvTbD32];
+  __shared__ __align__(16) uint16_t stage[StageSetD32<2>::kHalves];
   if (!kPrivate && flag != nullptr && *flag == 0u) return;  // the private launch was exact
   // workgroup row y of a split launch: queries [y*qchunk, min(N, (y+1)*qchunk)), partial
   // dK, dV at + y*gstride and bucket partials at + y*pstride
@@ -449,11 +455,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   dv += blockIdx.y * gstride;
   partial += blockIdx.y * pstride;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  constexpr int kBinLanes = kPrivate ? 64 : 32;                          // bin rows per bucket
   const int nbins = kPrivate ? kPrivBins : NB;
-  float* bins = reinterpret_cast<float*>(smem) + w * (2 * nbins * kBinLanes);  // [nbins][rows][2 heads] per wave
-  float2* tb = reinterpret_cast<float2*>(reinterpret_cast<float*>(smem) + kWaves * 2 * nbins * kBinLanes);
-  uint16_t* stage = reinterpret_cast<uint16_t*>(tb + kKvTbD32);
+  float* bins = bins_all + w * (2 * nbins * kBinLanes);  // [nbins][rows][2 heads] per wave
 
   const int npad32 = static_cast<int>(ops.npk / 32);
   const int nkb = (npad32 + kWaves - 1) / kWaves;
@@ -779,11 +782,6 @@ OpsD32 carve_ops_d32(void* base, int64_t N, int64_t Nk) {
   return o;
 }
 
-size_t kv_d32_lds(int NB, bool priv) {
-  const size_t bins = priv ? 4ull * kWaves * 2 * kPrivBins * 64 : 4ull * kWaves * 2 * NB * 32;
-  return bins + sizeof(float2) * kKvTbD32 + 2ull * StageSetD32<2>::kHalves;
-}
-
 }  // namespace
 
 size_t mfma_d32_ops_bytes(int64_t N, int64_t Nk) {
@@ -854,20 +852,13 @@ hipError_t launch_bwd_mfma_d32(const BwdArgs& a, const BwdWorkspace& w, hipStrea
   // private bins (never when NB <= kPrivBins, so it is then not launched).
   const bool priv = kv_acc == 0;
   const bool aligned = codes_aligned(a.spd_t, a.ld_t);
-  const size_t lds_priv = kv_d32_lds(a.NB, true), lds_shared = kv_d32_lds(a.NB, false);
-  e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<true, false>, lds_shared);
-  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<false, false>, lds_shared);
-  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<true, true>, lds_priv);
-  if (e == hipSuccess) e = allow_lds_mfma(bwd_kv_mfma_d32_kernel<false, true>, lds_priv);
-  if (e != hipSuccess) return e;
   auto kv_launch = [&](auto private_tag, uint32_t* f) {
     constexpr bool kP = decltype(private_tag)::value;
-    const size_t lds = kP ? lds_priv : lds_shared;
     if (aligned)
-      hipLaunchKernelGGL((bwd_kv_mfma_d32_kernel<true, kP>), kgrid, dim3(kThreads), lds, s, a.spd_t, a.table, ops,
+      hipLaunchKernelGGL((bwd_kv_mfma_d32_kernel<true, kP>), kgrid, dim3(kThreads), 0, s, a.spd_t, a.table, ops,
                          dkp, dvp, partial, a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride, f);
     else
-      hipLaunchKernelGGL((bwd_kv_mfma_d32_kernel<false, kP>), kgrid, dim3(kThreads), lds, s, a.spd_t, a.table, ops,
+      hipLaunchKernelGGL((bwd_kv_mfma_d32_kernel<false, kP>), kgrid, dim3(kThreads), 0, s, a.spd_t, a.table, ops,
                          dkp, dvp, partial, a.N, a.Nk, a.ld_t, a.NB, kv_acc, w.kv.chunk, nk_el, pstride, f);
   };
   trace_begin(kTraceBwdKv, s);
