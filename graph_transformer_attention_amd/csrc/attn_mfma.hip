@@ -817,9 +817,8 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
       uint32_t code[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), bound);
-      // All 16 bias reads are issued before the first bin update: the table and the bins
-      // share the LDS array, so a table read placed after a bin store must wait behind it,
-      // which would chain every entry's read, exp and store into one serial LDS round trip.
+      // All 16 bias reads are issued together, before the bin updates: one LDS round trip
+      // for the tile's exp arguments instead of one per entry.
       float2 tv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) tv[e] = tb[code[e]];
