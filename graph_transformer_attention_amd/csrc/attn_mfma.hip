@@ -51,9 +51,10 @@ constexpr int kHD = kH * kD;
 // while it computes the current one. Only the last key tile can be partial, so only it
 // takes the guarded loads and the -inf mask.
 //
-// The running max is updated lazily: a wave rescales its accumulators only when some
-// lane's tile max exceeds its current max by more than kLazy (in log2 units), so the
-// probabilities fed to the MFMA stay below 2^kLazy and rescales are rare.
+// The running max is updated lazily: the first tile sets it, and a wave rescales its
+// accumulators only when some lane's score exceeds it by more than kLazy (in log2 units),
+// so the probabilities fed to the MFMA stay below 2^kLazy and rescales are rare. The test
+// reads the exp2 arguments, which carry the shift already: no per-tile threshold.
 constexpr int kFwdWaves = 4;
 
 struct FwdTile {
@@ -128,7 +129,6 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
   const int64_t irow = qvalid ? i : N - 1;
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
-  const float lazy_raw = kLazy / sc2;
 
   for (int b = tid; b < 256; b += 64 * kFwdWaves) {
     const int c = min(b, NB - 1);
@@ -171,12 +171,16 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
   __syncthreads();
 
   f32x16 o0 = {}, o1 = {};
-  float m0 = -INFINITY, m1 = -INFINITY;
+  // The softmax shift of both heads, kept as the exp2 argument's addend: -m * log2(e)/sqrt(D)
+  // for the running max m of the raw scores (set by the first tile).
+  float nb0 = 0.f, nb1 = 0.f;
   // One key tile; kMask (the partial last tile only) sets the scores of keys past Nk to
   // -inf. The full tiles run without that code: kept in the loop, the compiler turns the
-  // tile-uniform test into per-entry selects executed on every tile.
-  auto tile = [&](int64_t t, auto mask_tag) __attribute__((always_inline)) {
+  // tile-uniform test into per-entry selects executed on every tile. kFirst: the first
+  // tile, which sets the shift from its largest score.
+  auto tile = [&](int64_t t, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
+    constexpr bool kFirst = decltype(first_tag)::value;
     const int64_t j0 = t * 32;
     const int buf = static_cast<int>(t & 1);
     if (t + 1 < nfull)
@@ -203,36 +207,59 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
         for (int e = 0; e < 16; ++e)
           if (8 * g + (e >> 1) >= lim) sg[g][e] = -INFINITY;
     }
-    float x0 = sg[0][0], x1 = sg[0][1];
+    if constexpr (kFirst) {  // the shift starts at the query column's largest score of this tile
+      float x0 = sg[0][0], x1 = sg[0][1];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) {
-      x0 = fmaxf(x0, sg[j >> 3][2 * (j & 7)]);
-      x1 = fmaxf(x1, sg[j >> 3][2 * (j & 7) + 1]);
-    }
-    // Each lane tests its own 16 keys; the two lane halves of a query column are combined
-    // only on the rare rescale path, so the common path has no cross-lane step.
-    if (__builtin_expect(__any(x0 > m0 + lazy_raw || x1 > m1 + lazy_raw), 0)) {  // rare: keep it a branch
-      x0 = fmaxf(x0, __shfl_xor(x0, 32));
-      x1 = fmaxf(x1, __shfl_xor(x1, 32));
-      const float n0 = fmaxf(m0, x0), n1 = fmaxf(m1, x1);
-      const float a0 = __builtin_amdgcn_exp2f((m0 - n0) * sc2);
-      const float a1 = __builtin_amdgcn_exp2f((m1 - n1) * sc2);
-#pragma unroll
-      for (int e = 0; e < 5; ++e) {
-        o0[e] *= a0;
-        o1[e] *= a1;
+      for (int j = 1; j < 16; ++j) {
+        x0 = fmaxf(x0, sg[j >> 3][2 * (j & 7)]);
+        x1 = fmaxf(x1, sg[j >> 3][2 * (j & 7) + 1]);
       }
-      m0 = n0;
-      m1 = n1;
+      nb0 = -fmaxf(x0, __shfl_xor(x0, 32)) * sc2;
+      nb1 = -fmaxf(x1, __shfl_xor(x1, 32)) * sc2;
     }
-    const float b0 = -m0 * sc2, b1 = -m1 * sc2;
+    // exp2 arguments against the current shift
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        sg[g][e] = __builtin_amdgcn_exp2f(fmaf(sg[g][e], sc2, b0));
-        sg[g][e + 1] = __builtin_amdgcn_exp2f(fmaf(sg[g][e + 1], sc2, b1));
+        sg[g][e] = fmaf(sg[g][e], sc2, nb0);
+        sg[g][e + 1] = fmaf(sg[g][e + 1], sc2, nb1);
       }
+    if constexpr (!kFirst) {
+      // The running max is tested on the arguments: an argument above kLazy means a score
+      // that far above the shift. Each lane tests its own 16 keys; the two lane halves of
+      // a query column are combined only on the rare rescale path.
+      float x0 = sg[0][0], x1 = sg[0][1];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) {
+        x0 = fmaxf(x0, sg[j >> 3][2 * (j & 7)]);
+        x1 = fmaxf(x1, sg[j >> 3][2 * (j & 7) + 1]);
+      }
+      if (__builtin_expect(__any(x0 > kLazy || x1 > kLazy), 0)) {  // rare: keep it a branch
+        // the shift rises by d to the column's largest score (whose argument becomes 0)
+        const float d0 = fmaxf(fmaxf(x0, __shfl_xor(x0, 32)), 0.f);
+        const float d1 = fmaxf(fmaxf(x1, __shfl_xor(x1, 32)), 0.f);
+        const float a0 = __builtin_amdgcn_exp2f(-d0), a1 = __builtin_amdgcn_exp2f(-d1);
+#pragma unroll
+        for (int e = 0; e < 5; ++e) {
+          o0[e] *= a0;
+          o1[e] *= a1;
+        }
+        nb0 -= d0;
+        nb1 -= d1;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            sg[g][e] -= d0;
+            sg[g][e + 1] -= d1;
+          }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sg[g][e] = __builtin_amdgcn_exp2f(sg[g][e]);
     // rows >= 9 of the V^T operand only feed output rows that are never read; PV MFMA g
     // contracts over keys 16*hp + 8g .. +7 (k-group hp), the lane's keys of score MFMA g
     const int vr = min(c, kD);
@@ -249,8 +276,14 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
     }
     __syncthreads();
   };
-  for (int64_t t = 0; t < nfull; ++t) tile(t, std::false_type{});
-  if (nfull < ntiles) tile(nfull, std::true_type{});
+  if (nfull > 0) tile(0, std::false_type{}, std::true_type{});
+  for (int64_t t = 1; t < nfull; ++t) tile(t, std::false_type{}, std::false_type{});
+  if (nfull < ntiles) {
+    if (nfull == 0)
+      tile(nfull, std::true_type{}, std::true_type{});
+    else
+      tile(nfull, std::true_type{}, std::false_type{});
+  }
   // O^T rows: d = 4hp + e in entries e = 0..3; row 8 (lane half 0, entry 4) is l.
   const float l0 = __shfl(o0[4], c), l1 = __shfl(o1[4], c);
   if (qvalid) {
@@ -259,8 +292,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
     *reinterpret_cast<float4*>(op) = make_float4(o0[0] * r0, o0[1] * r0, o0[2] * r0, o0[3] * r0);
     *reinterpret_cast<float4*>(op + kD) = make_float4(o1[0] * r1, o1[1] * r1, o1[2] * r1, o1[3] * r1);
     if (hp == 0) {
-      lse[i * kH + h0] = (m0 * sc2 + log2f(l0)) * kLn2;
-      lse[i * kH + h0 + 1] = (m1 * sc2 + log2f(l1)) * kLn2;
+      lse[i * kH + h0] = (log2f(l0) - nb0) * kLn2;
+      lse[i * kH + h0 + 1] = (log2f(l1) - nb1) * kLn2;
     }
   }
 }
