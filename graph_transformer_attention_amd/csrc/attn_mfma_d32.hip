@@ -123,7 +123,6 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
   const int64_t irow = qvalid ? i : N - 1;
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
-  const float lazy_raw = kLazy / sc2;
 
   for (int b = tid; b < 256; b += kThreads) {
     const int c = min(b, NB - 1);
@@ -166,8 +165,15 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
   __syncthreads();
 
   f32x16 o0 = {}, o1 = {};
-  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
-  for (int64_t t = 0; t < ntiles; ++t) {
+  // nb0, nb1: the softmax shift of both heads as the exp2 argument's addend,
+  // -m * log2(e)/sqrt(D) for the running max m of the raw scores (set by the first tile);
+  // l0, l1: this lane half's share of the row sums, from the half-precision P that the
+  // P.V MFMAs take (packed dot products with (1, 1)).
+  float nb0 = 0.f, nb1 = 0.f, l0 = 0.f, l1 = 0.f;
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 ones2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  auto tile = [&](int64_t t, auto first_tag) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_tag)::value;
     const int64_t j0 = t * 32;
     const int buf = static_cast<int>(t & 1);
     if (t + 1 < nfull)
@@ -194,41 +200,69 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
         }
       }
     }
-    float x0 = s0[0], x1 = s1[0];
+    if constexpr (kFirst) {  // the shift starts at the query column's largest score of this tile
+      float x0 = s0[0], x1 = s1[0];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) {
-      x0 = fmaxf(x0, s0[e]);
-      x1 = fmaxf(x1, s1[e]);
-    }
-    x0 = fmaxf(x0, __shfl_xor(x0, 32));
-    x1 = fmaxf(x1, __shfl_xor(x1, 32));
-    if (__any(x0 > m0 + lazy_raw || x1 > m1 + lazy_raw)) {
-      const float n0 = fmaxf(m0, x0), n1 = fmaxf(m1, x1);
-      const float a0 = __builtin_amdgcn_exp2f((m0 - n0) * sc2);
-      const float a1 = __builtin_amdgcn_exp2f((m1 - n1) * sc2);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        o0[e] *= a0;
-        o1[e] *= a1;
+      for (int e = 1; e < 16; ++e) {
+        x0 = fmaxf(x0, s0[e]);
+        x1 = fmaxf(x1, s1[e]);
       }
-      l0 *= a0;
-      l1 *= a1;
-      m0 = n0;
-      m1 = n1;
+      nb0 = -fmaxf(x0, __shfl_xor(x0, 32)) * sc2;
+      nb1 = -fmaxf(x1, __shfl_xor(x1, 32)) * sc2;
     }
-    const float b0 = -m0 * sc2, b1 = -m1 * sc2;
+    // exp2 arguments against the current shift
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, b0));
-      s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, b1));
-      l0 += s0[e];
-      l1 += s1[e];
+      s0[e] = fmaf(s0[e], sc2, nb0);
+      s1[e] = fmaf(s1[e], sc2, nb1);
+    }
+    if constexpr (!kFirst) {
+      // The lazy running max, tested on the arguments: one above kLazy is a score that far
+      // above the shift. Each lane tests its own 16 keys; the two lane halves of a query
+      // column are combined only on the rare rescale path.
+      float x0 = s0[0], x1 = s1[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) {
+        x0 = fmaxf(x0, s0[e]);
+        x1 = fmaxf(x1, s1[e]);
+      }
+      if (__builtin_expect(__any(x0 > kLazy || x1 > kLazy), 0)) {  // rare: keep it a branch
+        // the shift rises by d to the column's largest score (whose argument becomes 0)
+        const float d0 = fmaxf(fmaxf(x0, __shfl_xor(x0, 32)), 0.f);
+        const float d1 = fmaxf(fmaxf(x1, __shfl_xor(x1, 32)), 0.f);
+        const float a0 = __builtin_amdgcn_exp2f(-d0), a1 = __builtin_amdgcn_exp2f(-d1);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          o0[e] *= a0;
+          o1[e] *= a1;
+          s0[e] -= d0;
+          s1[e] -= d1;
+        }
+        l0 *= a0;
+        l1 *= a1;
+        nb0 -= d0;
+        nb1 -= d1;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s0[e] = __builtin_amdgcn_exp2f(s0[e]);
+      s1[e] = __builtin_amdgcn_exp2f(s1[e]);
     }
     const uint16_t* vb0 = &vt[buf][c * kVtRow + 16 * hp];
 #pragma unroll
     for (int k1 = 0; k1 < 2; ++k1) {
-      o0 = mfma_h16(load_h8(vb0 + 8 * k1), pack_f16x8(s0, 8 * k1), o0);
-      o1 = mfma_h16(load_h8(vb0 + kVtHead + 8 * k1), pack_f16x8(s1, 8 * k1), o1);
+      const s16x8 p0 = pack_f16x8(s0, 8 * k1), p1 = pack_f16x8(s1, 8 * k1);
+      o0 = mfma_h16(load_h8(vb0 + 8 * k1), p0, o0);
+      o1 = mfma_h16(load_h8(vb0 + kVtHead + 8 * k1), p1, o1);
+      const u32x4 w0 = __builtin_bit_cast(u32x4, p0), w1 = __builtin_bit_cast(u32x4, p1);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        // scalar copies first: hipcc bit-casts a vector element named in place as element 0
+        const uint32_t a = w0[x], b = w1[x];
+        l0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), ones2, l0, false);
+        l1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, b), ones2, l1, false);
+      }
     }
     if (t + 1 < ntiles) {
       stage(buf ^ 1, nxt.va, nxt.vb);
@@ -236,7 +270,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
       cur = nxt;
     }
     __syncthreads();
-  }
+  };
+  tile(0, std::true_type{});
+  for (int64_t t = 1; t < ntiles; ++t) tile(t, std::false_type{});
   // each lane half summed its 16 keys of every tile
   l0 += __shfl_xor(l0, 32);
   l1 += __shfl_xor(l1, 32);
@@ -253,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
           make_float4(o1[4 * jq] * r1, o1[4 * jq + 1] * r1, o1[4 * jq + 2] * r1, o1[4 * jq + 3] * r1);
     }
     if (hp == 0) {
-      lse[i * kH + h0] = (m0 * sc2 + log2f(l0)) * kLn2;
-      lse[i * kH + h0 + 1] = (m1 * sc2 + log2f(l1)) * kLn2;
+      lse[i * kH + h0] = (log2f(l0) - nb0) * kLn2;
+      lse[i * kH + h0 + 1] = (log2f(l1) - nb1) * kLn2;
     }
   }
 }
