@@ -167,11 +167,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
   f32x16 o0 = {}, o1 = {};
   // nb0, nb1: the softmax shift of both heads as the exp2 argument's addend,
   // -m * log2(e)/sqrt(D) for the running max m of the raw scores (set by the first tile);
-  // l0, l1: this lane half's share of the row sums, from the half-precision P that the
-  // P.V MFMAs take (packed dot products with (1, 1)).
+  // l0, l1: this lane half's share of the row sums, in float32 from the unrounded P (a sum
+  // of the half-precision P would carry their rounding into lse).
   float nb0 = 0.f, nb1 = 0.f, l0 = 0.f, l1 = 0.f;
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  const f16x2 ones2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
   auto tile = [&](int64_t t, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value;
     const int64_t j0 = t * 32;
@@ -248,21 +246,14 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     for (int e = 0; e < 16; ++e) {
       s0[e] = __builtin_amdgcn_exp2f(s0[e]);
       s1[e] = __builtin_amdgcn_exp2f(s1[e]);
+      l0 += s0[e];
+      l1 += s1[e];
     }
     const uint16_t* vb0 = &vt[buf][c * kVtRow + 16 * hp];
 #pragma unroll
     for (int k1 = 0; k1 < 2; ++k1) {
-      const s16x8 p0 = pack_f16x8(s0, 8 * k1), p1 = pack_f16x8(s1, 8 * k1);
-      o0 = mfma_h16(load_h8(vb0 + 8 * k1), p0, o0);
-      o1 = mfma_h16(load_h8(vb0 + kVtHead + 8 * k1), p1, o1);
-      const u32x4 w0 = __builtin_bit_cast(u32x4, p0), w1 = __builtin_bit_cast(u32x4, p1);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        // scalar copies first: hipcc bit-casts a vector element named in place as element 0
-        const uint32_t a = w0[x], b = w1[x];
-        l0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), ones2, l0, false);
-        l1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, b), ones2, l1, false);
-      }
+      o0 = mfma_h16(load_h8(vb0 + 8 * k1), pack_f16x8(s0, 8 * k1), o0);
+      o1 = mfma_h16(load_h8(vb0 + kVtHead + 8 * k1), pack_f16x8(s1, 8 * k1), o1);
     }
     if (t + 1 < ntiles) {
       stage(buf ^ 1, nxt.va, nxt.vb);
