@@ -75,6 +75,15 @@ def test_er256_f32_full():
     (16, 8, 32, 20, "bf16", "path"),
     (17, 8, 32, 20, "bf16", "path"),
     (1000, 8, 32, 30, "bf16", "path"),
+    # the same edges of the D = 8 one-pass backward's private bins (codes 0..15): a 16-node
+    # path tops out at code 15 (one pass), a 17-node path reaches code 16 (the flag, then
+    # the three-pass rerun); with NB = 13 <= 16 the rerun is not launched at all: a 12-node
+    # path (codes 0..11), and 40 isolated nodes (code 0 on the diagonal, the clip code 12
+    # everywhere else)
+    (16, 8, 8, 20, "bf16", "path"),
+    (17, 8, 8, 20, "bf16", "path"),
+    (12, 8, 8, 12, "bf16", "path"),
+    (40, 8, 8, 12, "bf16", "empty"),
     # graphs too small to fill the GPU by rows: every matrix-core kernel splits its inner
     # loop (3 splits here, the last one ragged) and partial results are combined
     (777, 8, 8, 20, "bf16", "er"),
