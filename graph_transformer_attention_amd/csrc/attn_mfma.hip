@@ -15,8 +15,9 @@
 // table[h, code] read from LDS by the uint8 code, so adding the bias costs no vector
 // instruction.
 //
-// Work split: workgroups of 4 waves; each wave owns 32 nodes of its outer loop and
-// two heads (the head pair follows from the workgroup order, xcd_map). Lane l holds
+// Work split: workgroups of 4 waves (8 in the one-pass backward); each wave owns 32
+// nodes of its outer loop and two heads (the head pair follows from the workgroup
+// order, xcd_map). Lane l holds
 // column c = l % 32 of every 32x32 tile and one half hp = l / 32 of its rows. In the
 // backward, rows follow node_of_row (mfma_common.h): the lane's 16 accumulator entries
 // are 16 consecutive nodes, so its codes are one 16-byte load and each 8-entry half of
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 //  * contracts those over its 32 keys against K^T (held in registers for the whole
 //    sweep: the wave's keys do not change), dQ^T[d][query] += K^T[d][key] dS^T[key][query];
 //  * adds its result to the other waves' in LDS (a fixed order), and the workgroup writes
-//    one dQ partial row per query for its 128 keys; the backward's last kernel sums the
+//    one dQ partial row per query for its 256 keys; the backward's last kernel sums the
 //    partials of all key blocks in order, so the result stays bitwise reproducible.
 // dtable bins are lane-private for codes 0..15 only (8 KB per wave): a lane that meets a
 // larger code raises *flag (cleared by the prep kernel), and the three-pass kernels,
