@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
     return *reinterpret_cast<const s16x8*>(p);
   };
 
-  const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
+  const int ntiles = static_cast<int>((Nk + 31) / 32), nfull = static_cast<int>(Nk / 32);
   FwdTile cur, nxt;
   if (nfull > 0)
     fwd_load<false, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, sk, shl, sdp);
@@ -179,11 +179,11 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
   // -inf. The full tiles run without that code: kept in the loop, the compiler turns the
   // tile-uniform test into per-entry selects executed on every tile. kFirst: the first
   // tile, which sets the shift from its largest score.
-  auto tile = [&](int64_t t, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
+  auto tile = [&](int t, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     constexpr bool kFirst = decltype(first_tag)::value;
-    const int64_t j0 = t * 32;
-    const int buf = static_cast<int>(t & 1);
+    const int64_t j0 = static_cast<int64_t>(t) * 32;
+    const int buf = t & 1;
     if (t + 1 < nfull)
       fwd_load<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, sk, shl, sdp);
     else if (t + 1 < ntiles)
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4) void fwd_mfma_d8_kernel(const ui
     __syncthreads();
   };
   if (nfull > 0) tile(0, std::false_type{}, std::true_type{});
-  for (int64_t t = 1; t < nfull; ++t) tile(t, std::false_type{}, std::false_type{});
+  for (int t = 1; t < nfull; ++t) tile(t, std::false_type{}, std::false_type{});
   if (nfull < ntiles) {
     if (nfull == 0)
       tile(nfull, std::true_type{}, std::true_type{});
