@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
   const int kpos = row_pos(slot_of_node(tid >> 3), tid & 7);
   auto stage_k = [&](int buf, const s16x8& ks) { *reinterpret_cast<s16x8*>(&kt[buf][kpos]) = ks; };
 
-  const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
+  const int ntiles = static_cast<int>((Nk + 31) / 32), nfull = static_cast<int>(Nk / 32);  // scalar loop tests
   FwdTileD32 cur, nxt;
   if (nfull > 0)
     fwd_load_d32<false, kAligned>(cur, srow, k, v, 0, Nk, h0, hp, tid, shl, sdq, skp);
@@ -170,10 +170,10 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
   // l0, l1: this lane half's share of the row sums, in float32 from the unrounded P (a sum
   // of the half-precision P would carry their rounding into lse).
   float nb0 = 0.f, nb1 = 0.f, l0 = 0.f, l1 = 0.f;
-  auto tile = [&](int64_t t, auto first_tag) __attribute__((always_inline)) {
+  auto tile = [&](int t, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value;
-    const int64_t j0 = t * 32;
-    const int buf = static_cast<int>(t & 1);
+    const int64_t j0 = static_cast<int64_t>(t) * 32;
+    const int buf = t & 1;
     if (t + 1 < nfull)
       fwd_load_d32<false, kAligned>(nxt, srow, k, v, j0 + 32, Nk, h0, hp, tid, shl, sdq, skp);
     else if (t + 1 < ntiles)
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_d32_kernel(const uint16_t* 
     __syncthreads();
   };
   tile(0, std::true_type{});
-  for (int64_t t = 1; t < ntiles; ++t) tile(t, std::false_type{});
+  for (int t = 1; t < ntiles; ++t) tile(t, std::false_type{});
   // each lane half summed its 16 keys of every tile
   l0 += __shfl_xor(l0, 32);
   l1 += __shfl_xor(l1, 32);
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   set.rows[1] = ops.od;
   set.h0 = h0;
   const int tb0 = tr_lane_base(lane, 0), tb1 = tr_lane_base(lane, 1);
-  const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
+  const int ntiles = static_cast<int>((N + 31) / 32), nfull = static_cast<int>(N / 32);  // scalar loop tests
   s16x8 sr[StageSetD32<2>::kPer];
   set.load(sr, 0, tid);
   u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
@@ -540,8 +540,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   uint32_t dw0 = ops.dl[static_cast<int64_t>(h0) * npad + qr], dw1 = ops.dl[static_cast<int64_t>(h0 + 1) * npad + qr];
   wait_vm0();
 
-  for (int64_t t = 0; t < ntiles; ++t) {
-    const int64_t i0 = t * 32;
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t i0 = static_cast<int64_t>(t) * 32;
     set.store(stage, sr, tid);
     __syncthreads();
     u32x4 cwn = cw;
@@ -730,7 +730,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
   set.rows[1] = ops.vd;
   set.h0 = h0;
   const int tb0 = tr_lane_base(lane, 0), tb1 = tr_lane_base(lane, 1);
-  const int64_t ntiles = (Nk + 31) / 32, nfull = Nk / 32;
+  const int ntiles = static_cast<int>((Nk + 31) / 32), nfull = static_cast<int>(Nk / 32);  // scalar loop tests
   s16x8 sr[Set::kPer];
   set.load(sr, 0, tid);
   set.store(stage, sr, tid);
@@ -738,8 +738,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_mfma_d32_kernel(const uint8_t*
   wait_vm0();
   __syncthreads();
 
-  for (int64_t t = 0; t < ntiles; ++t) {
-    const int64_t j0 = t * 32;
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t j0 = static_cast<int64_t>(t) * 32;
     const uint16_t* cur = stage + (t & 1) * Set::kHalves;
     u32x4 cwn = cw;
     if (t + 1 < ntiles) {
