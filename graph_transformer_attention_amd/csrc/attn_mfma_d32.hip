@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
   // as distinct objects the compiler knows the bin updates never touch the table or the
   // staged tile, so it may issue the stage reads of the dK/dV operands among them.
   __shared__ __align__(16) float bins_all[kWaves * 2 * (kPrivate ? kPrivBins : kKvTbD32) * kBinLanes];
-  __shared__ __align__(16) float2 tb[kKvTbD32];
+  __shared__ __align__(16) float2 tb[kKvTbD32];  // both heads' bias * log2e: the exp2 arguments' addends
   __shared__ __align__(16) uint16_t stage[StageSetD32<2>::kHalves];
   if (!kPrivate && flag != nullptr && *flag == 0u) return;  // the private launch was exact
   // workgroup row y of a split launch: queries [y*qchunk, min(N, (y+1)*qchunk)), partial
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
 
   for (int b = tid; b < kKvTbD32; b += kThreads) {
     const int c = min(b, NB - 1);
-    tb[b] = make_float2(table[h0 * NB + c] * sqd, table[(h0 + 1) * NB + c] * sqd);
+    tb[b] = make_float2(table[h0 * NB + c] * kLog2e, table[(h0 + 1) * NB + c] * kLog2e);
   }
   for (int x = lane; x < 2 * nbins * kBinLanes; x += 64) bins[x] = 0.f;
   s16x8 kop[2][2], vop[2][2];
@@ -559,15 +559,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
     if (wave_live) {
       const uint16_t* q_t = stage;
       const uint16_t* o_t = stage + kRowTile;
-      f32x16 s0, s1;
       uint32_t code[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        code[e] = min(code_byte(cw, e), nbm1);
-        const float2 t = tb[code[e]];
-        s0[e] = t.x;
-        s1[e] = t.y;
-      }
+      for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), nbm1);
+      f32x16 s0 = {}, s1 = {};
       if (check_range) over |= (cw[0] | cw[1] | cw[2] | cw[3]) & 0xF0F0F0F0u;
       f32x16 p0 = {}, p1 = {};
 #pragma unroll
@@ -583,8 +578,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_mfma_d32_kernel(const uint8_t
       p1 = mfma_h16(aug_chunk(dw1, 0, hp), vaug, p1);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pa = __builtin_amdgcn_exp2f(s0[e] * sc2);
-        const float pb = __builtin_amdgcn_exp2f(s1[e] * sc2);
+        const float2 tv = tb[code[e]];  // read straight into the FMAs' addends: no moves
+        const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, tv.x));
+        const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, tv.y));
         s0[e] = pa;
         s1[e] = pb;
         p0[e] *= pa;
