@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import graph_transformer_attention_amd as gta
-from workloads import make_inputs, small_case
+from workloads import graphs, make_inputs, small_case, store
 
 from gpu_util import check, dev, host64
 
@@ -99,6 +99,25 @@ def test_er256_f32_full():
 ])
 def test_small_cases(N, H, D, C, dtype, family):
     inp = small_case(N, H, D, C, dtype, seed=11, family=family)
+    got, codes = _run(inp)
+    _compare(inp, got, codes)
+
+
+@pytest.mark.parametrize("N,D", [(300, 8), (1000, 8), (1000, 32)])
+def test_scores_rising_along_the_keys(N, D):
+    """The matrix-core forwards set the softmax shift from a key range's first tile and
+    rescale only when a later score passes it by more than 8 in log2 units. Here the bias
+    climbs along the keys: on a chain of 32-node cliques a query's distance to the keys of
+    each later 32-key tile grows by about 2, and the table rises by 4 per code on heads 0-3
+    (falls on heads 4-7), so on half of the rows every tile passes the shift by about 8 and
+    the rescale runs tile after tile, in each key split too (these sizes split the key
+    range and merge the partial results). Q and K stay N(0, 1); codes reach 62 at N = 1000,
+    so the backward's reruns for codes of 16 and more run as well."""
+    C = 63
+    inp = small_case(N, 8, D, C, "bf16", seed=17, family="empty")
+    inp.indptr, inp.indices = graphs.clique_chain(N)
+    sign = np.where(np.arange(8) < 4, 1.0, -1.0)
+    inp.table = store(4.0 * sign[:, None] * np.arange(C + 1)[None, :], "f32")
     got, codes = _run(inp)
     _compare(inp, got, codes)
 

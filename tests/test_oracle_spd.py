@@ -113,6 +113,26 @@ def test_clip_on_path_graph():
     np.testing.assert_array_equal(codes, np.minimum(np.abs(i - j), C - 1))
 
 
+def test_clique_chain_distances():
+    # cliques of 32 consecutive ids, clique k's last id joined to clique k+1's first: from
+    # i in clique a to j in a later clique b, leave a at its last id (one step unless i is
+    # it), cross each join (b - a joins) and each clique in between (first to last), then
+    # reach j from b's first id (one step unless j is it)
+    n, s, C = 100, 32, 63
+    indptr, indices = graphs.clique_chain(n, s)
+    codes = oracle.bfs_codes(indptr, indices, C, range(n))
+    want = np.zeros((n, n), np.int64)
+    for i in range(n):
+        for j in range(n):
+            a, b = sorted((i // s, j // s))
+            lo, hi = (i, j) if i // s <= j // s else (j, i)
+            if a == b:
+                want[i, j] = int(i != j)
+            else:
+                want[i, j] = int(lo != a * s + s - 1) + (b - a) + (b - a - 1) + int(hi != b * s)
+    np.testing.assert_array_equal(codes, np.minimum(want, C - 1))
+
+
 def test_unreachable_bucket():
     # two components {0,1,2} and {3,4}, plus an isolated node 5
     indptr, indices = _csr(6, [(0, 1), (1, 2), (3, 4)])

@@ -116,5 +116,21 @@ def path_graph(n: int):
     return csr_from_edges(n, a, a + 1)
 
 
+def clique_chain(n: int, size: int = 32):
+    """Cliques of `size` consecutive ids (the last one ragged), each joined to the next by
+    one edge (last id of a clique to the first of the next): the distance from a node to
+    the nodes of the clique k places away grows by about 2 per clique."""
+    u, v = [], []
+    for c0 in range(0, n, size):
+        ids = np.arange(c0, min(n, c0 + size))
+        a, b = np.triu_indices(len(ids), 1)
+        u.append(ids[a])
+        v.append(ids[b])
+        if c0 + size < n:
+            u.append(np.array([c0 + size - 1]))
+            v.append(np.array([c0 + size]))
+    return csr_from_edges(n, np.concatenate(u), np.concatenate(v))
+
+
 def degrees(indptr: np.ndarray) -> np.ndarray:
     return np.diff(indptr)
