@@ -412,14 +412,17 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
 constexpr int kBwdWaves = 4;              // waves per backward workgroup: 4 x 32 nodes, one head pair
 constexpr int kKvTable = 64;              // key-outer table entries (codes clamped to NB-1 <= 63)
 constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kFusedWaves = 8;            // waves per one-pass workgroup: 8 x 32 keys, one head pair
+constexpr int kFusedWaves = 8;            // waves per one-pass workgroup: 8 x 2 x 32 keys, one head pair
 constexpr int kFusedThreads = 64 * kFusedWaves;
 
+constexpr int kFusedSets = 2;             // 32-key sets per one-pass wave
+constexpr int kFusedBlocks = kFusedWaves * kFusedSets;  // 32-key blocks per one-pass workgroup
+
 // 32-key blocks of dtable partial rows, padded to whole one-pass workgroups (a multiple
-// of 8, so of the 4-wave kernels' blocks too); every key-outer kernel covers them all, a
+// of 16, so of the 4-wave kernels' blocks too); every key-outer kernel covers them all, a
 // wave past the last key writing zero rows, so each row is defined whichever ran.
 __host__ __device__ constexpr int64_t kv_row_blocks(int64_t npad32) {
-  return (npad32 + kFusedWaves - 1) / kFusedWaves * kFusedWaves;
+  return (npad32 + kFusedBlocks - 1) / kFusedBlocks * kFusedBlocks;
 }
 
 // One 32-node tile of backward operands of a head pair, staged into LDS: two
@@ -538,6 +541,26 @@ __device__ __forceinline__ s16x8 tr_aug_op(const uint16_t* aug, int base, int k1
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(aug + 512 * k1 + base));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(aug + 512 * k1 + 256 + base));
   return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// The same read for a 16x16x32 MFMA whose rows are (key half u, d) = 8u + d and whose
+// contraction index is k = 8G + p for lane group G = lane / 16 (nodes 16 (G / 2) + 8 k1 + p):
+// that operand is block-diagonal, node k pairing with keys of half G % 2 only. Lane 4e + r of
+// group G addresses columns 4 (r % 2) .. +3 of node 4e' + e's row (as above) when r / 2 = G % 2,
+// so lanes j = 8u + d of the group receive column d for u = G % 2; otherwise it addresses
+// columns 12..15, which are zero in every augmented row (the extra terms sit in columns
+// 8..10), so the lanes of the other key half receive zeros.
+__device__ __forceinline__ int tr_aug_base16(int lane, int hl) {
+  const int G = lane >> 4, hp = lane >> 5, e = (lane >> 2) & 3, r = lane & 3;
+  const bool data = (r >> 1) == (G & 1);
+  const int hb = data ? 0 : 1, off = data ? 4 * (r & 1) : 4;
+  return 128 * hp + 32 * e + 8 * (2 * (hl ^ hp) + (hb ^ (e >> 1))) + off;
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma_h16x16(s16x8 a, s16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
 }
 
 // Backward, step 2 (key-outer). A workgroup is 4 waves = 128 keys x one head pair;
@@ -701,21 +724,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 // Backward in one pass (key-outer with dQ): the key-outer kernel's work and, from the
 // same probabilities, the queries' gradient, so the query-outer pass (a third sweep
 // over the codes with a third exp per entry) is not needed. The dK/dV contractions are
-// those of bwd_kv_mfma_d8_kernel, with 8-wave workgroups (256 keys x one head pair, one
-// workgroup per CU): the staged query tile then serves twice the keys, and each
-// workgroup's dQ partial covers 256 keys, which halves the partials written and summed.
+// those of bwd_kv_mfma_d8_kernel, with 8-wave workgroups of 512 keys x one head pair, one
+// workgroup per CU: each wave owns two sets of 32 keys and runs them one after the other on
+// every staged query tile. The tile, its barrier and the cross-wave dQ sum then serve four
+// times the keys of a 4-wave, one-set workgroup, and each workgroup's dQ partial covers 512
+// keys (0.54 GB of partials at N = 32768 instead of 2.1 GB at 128 keys). dK and dV contract
+// on 16x16x32 MFMAs, which leaves the registers for the second set.
 // Only the two augmented row tiles are staged (4 KB per tile): the dK^T and dV^T
-// contractions read Q^T and dO^T from them with ds_read_b64_tr_b16 (tr_aug_base). Per
-// 32-query tile each wave also:
-//  * writes its packed dS (f16, both heads, 32 keys x 32 queries) row by row into its own
-//    LDS buffer [head][key][query] and reads it back transposed with ds_read_b64_tr_b16:
+// contractions read Q^T and dO^T from them with ds_read_b64_tr_b16 (tr_aug_base16). Per
+// 32-query tile each of a wave's sets also:
+//  * writes its packed dS (f16, both heads, 32 keys x 32 queries) row by row into the
+//    wave's LDS buffer [head][key][query] and reads it back transposed with ds_read_b64_tr_b16:
 //    lane l of a 16-lane group receives element l%4 of the 8-byte chunks that lanes
 //    4e + l/4 address (e = 0..3), so each lane's address names a 4-query chunk of one key
 //    row and its result holds 4 keys of one query;
 //  * contracts those over its 32 keys against K^T (held in registers for the whole
 //    sweep: the wave's keys do not change), dQ^T[d][query] += K^T[d][key] dS^T[key][query];
-//  * adds its result to the other waves' in LDS (a fixed order), and the workgroup writes
-//    one dQ partial row per query for its 256 keys; the backward's last kernel sums the
+//  * adds its result to the wave's, which goes to LDS beside the other waves' (summed in a
+//    fixed order), and the workgroup writes
+//    one dQ partial row per query for its 512 keys; the backward's last kernel sums the
 //    partials of all key blocks in order, so the result stays bitwise reproducible.
 // dtable bins are lane-private for codes 0..15 only (8 KB per wave): a lane that meets a
 // larger code raises *flag (cleared by the prep kernel), and the three-pass kernels,
@@ -731,6 +758,16 @@ constexpr int kRedFloats = kFusedWaves * 32 * kRedRow;  // [wave][query][head][d
 // cycle (rows r..r+7 at one chunk) and the sixteen 8-byte transposed reads of one lane
 // group (rows r0..r0+3, r0 a multiple of 4, at four chunk offsets) hit distinct banks.
 __device__ __forceinline__ int ds_pos(int r, int k) { return r * 32 + 8 * (k ^ ((r >> 1) & 3)); }
+
+// One 32-key set of a one-pass wave: its keys' operands, its dK/dV accumulators and its
+// code row (the keys stay the wave's for the whole sweep).
+struct FusedSet {
+  s16x8 kb0, kb1, vb0, vb1;  // augmented k and v rows of both heads (score MFMA operands)
+  s16x8 kt[2];               // K^T operands of the dQ contractions (16-key halves)
+  f32x4 dv0, dv1, dk0, dk1;  // dV^T and dK^T of both heads (tr_aug_base16 layout)
+  const uint8_t* crow;       // this lane's code row (its key, the launch's query range)
+  u32x4 cw, cwn;             // codes of the current and the next query tile
+};
 
 template <bool kAligned>
 __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
@@ -757,17 +794,15 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   float2* mybins = bins + w * (kFusedBins * 64) + lane;
   uint16_t* mydst = dsbuf + w * kDsHalves;
 
-  const int nkb = static_cast<int>(kv_row_blocks(ops.npk / 32) / kFusedWaves);
+  const int nkb = static_cast<int>(kv_row_blocks(ops.npk / 32) / kFusedBlocks);
   int kb, hpair;
   xcd_map(blockIdx.x, nkb, kb, hpair);
   if (kb < 0) return;
   const int c = lane & 31, hp = lane >> 5;
   const int h0 = 2 * hpair;
-  const int64_t jw = static_cast<int64_t>(kb) * (32 * kFusedWaves) + 32 * w;
-  const int64_t j = jw + c;
-  const bool wave_live = jw < ops.npk;
-  const int64_t jj = wave_live ? j : 0;
-  const int64_t jwl = wave_live ? jw : 0;
+  // the wave's keys: set s (s = 0, 1) holds the 32 keys from jw + 32 s
+  const int64_t jw = static_cast<int64_t>(kb) * (32 * kFusedBlocks) + 32 * kFusedSets * w;
+  const int nlive = jw + 32 < ops.npk ? 2 : (jw < ops.npk ? 1 : 0);  // live sets (wave-uniform)
   const int64_t npad = ops.npq;
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
@@ -777,27 +812,35 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
     tb[b] = make_float2(table[h0 * NB + cb] * kLog2e, table[(h0 + 1) * NB + cb] * kLog2e);
   }
   for (int b = 0; b < kFusedBins; ++b) mybins[b * 64] = make_float2(0.f, 0.f);
-  const s16x8 kb0 = load_h8(ops.ka + (jj * kH + h0) * 16 + 8 * hp);
-  const s16x8 kb1 = load_h8(ops.ka + (jj * kH + h0 + 1) * 16 + 8 * hp);
-  const s16x8 vb0 = load_h8(ops.va + (jj * kH + h0) * 16 + 8 * hp);
-  const s16x8 vb1 = load_h8(ops.va + (jj * kH + h0 + 1) * 16 + 8 * hp);
   // dQ contractions on 16x16x32 MFMAs: rows m = (head m / 8, d m % 8) of both heads,
   // columns 16 queries, k = 8G + p for lane group G = lane / 16: head G / 2 and key
-  // 16u + 8 (G % 2) + p of the wave (u = 0, 1: the wave's two 16-key halves). The K^T
-  // operand is zero where a row's head is not the k-group's, and is the same every tile.
+  // 16u + 8 (G % 2) + p of the set (u = 0, 1: its two 16-key halves). The K^T operand is
+  // zero where a row's head is not the k-group's, and is the same every tile.
   const int G = lane >> 4, m16 = lane & 15;
-  s16x8 kt[2];
+  const int64_t cc = 16 * hp;
+  FusedSet set[kFusedSets];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-    kt[u] = (m16 >> 3) == (G >> 1)
-                ? load_h8(ops.kt + (static_cast<int64_t>(h0 + (m16 >> 3)) * kD + (m16 & 7)) * ops.npk + jwl + 16 * u +
-                          8 * (G & 1))
-                : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
+  for (int si = 0; si < kFusedSets; ++si) {
+    FusedSet& st = set[si];
+    const int64_t js = jw + 32 * si;
+    const bool live = js < ops.npk;
+    const int64_t jj = live ? js + c : 0, jsl = live ? js : 0;
+    st.kb0 = load_h8(ops.ka + (jj * kH + h0) * 16 + 8 * hp);
+    st.kb1 = load_h8(ops.ka + (jj * kH + h0 + 1) * 16 + 8 * hp);
+    st.vb0 = load_h8(ops.va + (jj * kH + h0) * 16 + 8 * hp);
+    st.vb1 = load_h8(ops.va + (jj * kH + h0 + 1) * 16 + 8 * hp);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      st.kt[u] = (m16 >> 3) == (G >> 1)
+                     ? load_h8(ops.kt + (static_cast<int64_t>(h0 + (m16 >> 3)) * kD + (m16 & 7)) * ops.npk + jsl +
+                               16 * u + 8 * (G & 1))
+                     : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    st.dv0 = st.dv1 = st.dk0 = st.dk1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t j = js + c;
+    st.crow = spd_t + (j < Nk ? j : Nk - 1) * ldt + ib;
+  }
   const uint32_t bound = static_cast<uint32_t>(min(NB - 1, kFusedBins - 1));
   uint32_t over = 0u;
-  const uint8_t* crow = spd_t + (j < Nk ? j : Nk - 1) * ldt + ib;
-  const int64_t cc = 16 * hp;
   // transposed-read address of this lane (group G, e4 = (lane % 16) / 4, j4 = lane % 4),
   // for query half qh, key half u and read s: head G / 2, key row r = 16u + 8 (G % 2) + 4s
   // + e4, queries 16 qh + 4 j4 .. +3; a lane of group G then receives 4 keys of head G / 2.
@@ -812,7 +855,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   src.row0 = ops.qa + h0 * 16;
   src.row1 = ops.doa + h0 * 16;
   src.tr = nullptr;  // no transposed tile is staged
-  const int tb_h0 = tr_aug_base(lane, 0), tb_h1 = tr_aug_base(lane, 1);
+  const int tb_h0 = tr_aug_base16(lane, 0), tb_h1 = tr_aug_base16(lane, 1);
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
   constexpr int kCh = 256;  // qa, doa
   s16x8 sr[stage_per_thread<kCh>()];
@@ -820,7 +863,10 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   cursor.init(src, npad, tid);
   cursor.load_next(sr, tid);
   stage_store<kCh>(stage, sr, tid);
-  u32x4 cw = nfull > 0 ? codes_at<false, kAligned>(crow, cc, N) : codes_at<true, kAligned>(crow, cc, N);
+#pragma unroll
+  for (int si = 0; si < kFusedSets; ++si)
+    set[si].cw =
+        nfull > 0 ? codes_at<false, kAligned>(set[si].crow, cc, N) : codes_at<true, kAligned>(set[si].crow, cc, N);
   float* dqw = dqpart + static_cast<int64_t>(kb) * dqstride + (ib + rq) * kHD + (h0 + rh) * kD + rd;
   // the workgroup's dQ for tile tt from the eight waves' contributions, in wave order
   auto reduce_dq = [&](int64_t tt) {
@@ -834,106 +880,131 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   wait_vm0();
   __syncthreads();
 
-  for (int64_t t = 0; t < ntiles; ++t) {
-    const int64_t i0 = t * 32;
-    const uint16_t* cur = stage + (t & 1) * kAugStageHalves;
-    u32x4 cwn = cw;
-    if (t + 1 < ntiles) {
-      cursor.load_next(sr, tid);
-      cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(crow, i0 + 32 + cc, N)
-                            : codes_at<true, kAligned>(crow, i0 + 32 + cc, N);
+  // One 32-key set's work on the staged query tile: scores, P and dS, the dtable bins, the
+  // dK/dV contractions, and its share of the tile's dQ^T (added to dq).
+  auto set_tile = [&](FusedSet& st, const uint16_t* cur, f32x4(&dq)[2]) __attribute__((always_inline)) {
+    const uint16_t* qa_t = cur;
+    const uint16_t* doa_t = cur + kAugHalves;
+    const u32x4 cw = st.cw;
+    over |= (cw[0] | cw[1] | cw[2] | cw[3]) & 0xF0F0F0F0u;
+    uint32_t code[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), bound);
+    // All 16 bias reads are issued together, before the bin updates: one LDS round trip
+    // for the tile's exp arguments instead of one per entry.
+    float2 tv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tv[e] = tb[code[e]];
+    f32x16 s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), st.kb0, f32x16{});
+    f32x16 s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), st.kb1, f32x16{});
+    f32x16 p0 = mfma_h16(staged_aug(doa_t, c, 0, hp), st.vb0, f32x16{});
+    f32x16 p1 = mfma_h16(staged_aug(doa_t, c, 1, hp), st.vb1, f32x16{});
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, tv[e].x));
+      const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, tv[e].y));
+      s0[e] = pa;
+      s1[e] = pb;
+      p0[e] *= pa;
+      p1[e] *= pb;
     }
-    float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0;  // this lane's dQ^T, query halves 0 and 1
-    if (wave_live) {
-      const uint16_t* qa_t = cur;
-      const uint16_t* doa_t = cur + kAugHalves;
-      over |= (cw[0] | cw[1] | cw[2] | cw[3]) & 0xF0F0F0F0u;
-      uint32_t code[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) code[e] = min(code_byte(cw, e), bound);
-      // All 16 bias reads are issued together, before the bin updates: one LDS round trip
-      // for the tile's exp arguments instead of one per entry.
-      float2 tv[16];
+    for (int e = 0; e < 16; ++e) {
+      float2 bin = mybins[code[e] * 64];
+      bin.x += p0[e];
+      bin.y += p1[e];
+      mybins[code[e] * 64] = bin;
+    }
+    const s16x8 d0a = pack_f16x8(p0, 0), d0b = pack_f16x8(p0, 8);
+    const s16x8 d1a = pack_f16x8(p1, 0), d1b = pack_f16x8(p1, 8);
+    // dS rows of this lane's key: queries 16hp .. 16hp+15 of both heads (the wave's next
+    // set reuses the buffer: the LDS operations of one wave complete in order)
+    *reinterpret_cast<s16x8*>(mydst + ds_pos(c, 2 * hp)) = d0a;
+    *reinterpret_cast<s16x8*>(mydst + ds_pos(c, 2 * hp + 1)) = d0b;
+    *reinterpret_cast<s16x8*>(mydst + 32 * 32 + ds_pos(c, 2 * hp)) = d1a;
+    *reinterpret_cast<s16x8*>(mydst + 32 * 32 + ds_pos(c, 2 * hp + 1)) = d1b;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tv[e] = tb[code[e]];
-      f32x16 s0 = mfma_h16(staged_aug(qa_t, c, 0, hp), kb0, f32x16{});
-      f32x16 s1 = mfma_h16(staged_aug(qa_t, c, 1, hp), kb1, f32x16{});
-      f32x16 p0 = mfma_h16(staged_aug(doa_t, c, 0, hp), vb0, f32x16{});
-      f32x16 p1 = mfma_h16(staged_aug(doa_t, c, 1, hp), vb1, f32x16{});
+    for (int k1 = 0; k1 < 2; ++k1) {
+      st.dv0 = mfma_h16x16(tr_aug_op(doa_t, tb_h0, k1), pack_f16x8(s0, 8 * k1), st.dv0);
+      st.dv1 = mfma_h16x16(tr_aug_op(doa_t, tb_h1, k1), pack_f16x8(s1, 8 * k1), st.dv1);
+      st.dk0 = mfma_h16x16(tr_aug_op(qa_t, tb_h0, k1), k1 ? d0b : d0a, st.dk0);
+      st.dk1 = mfma_h16x16(tr_aug_op(qa_t, tb_h1, k1), k1 ? d1b : d1a, st.dk1);
+    }
+    // dS^T operands: lane (query 16qh + m16, group G) gets keys 16u + 8 (G % 2) .. +7 of
+    // head G / 2, from two transposed reads of 4 keys each
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* lds4;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pa = __builtin_amdgcn_exp2f(fmaf(s0[e], sc2, tv[e].x));
-        const float pb = __builtin_amdgcn_exp2f(fmaf(s1[e], sc2, tv[e].y));
-        s0[e] = pa;
-        s1[e] = pb;
-        p0[e] *= pa;
-        p1[e] *= pb;
-      }
+    for (int qh = 0; qh < 2; ++qh) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float2 bin = mybins[code[e] * 64];
-        bin.x += p0[e];
-        bin.y += p1[e];
-        mybins[code[e] * 64] = bin;
-      }
-      const s16x8 d0a = pack_f16x8(p0, 0), d0b = pack_f16x8(p0, 8);
-      const s16x8 d1a = pack_f16x8(p1, 0), d1b = pack_f16x8(p1, 8);
-      // dS rows of this lane's key: queries 16hp .. 16hp+15 of both heads
-      *reinterpret_cast<s16x8*>(mydst + ds_pos(c, 2 * hp)) = d0a;
-      *reinterpret_cast<s16x8*>(mydst + ds_pos(c, 2 * hp + 1)) = d0b;
-      *reinterpret_cast<s16x8*>(mydst + 32 * 32 + ds_pos(c, 2 * hp)) = d1a;
-      *reinterpret_cast<s16x8*>(mydst + 32 * 32 + ds_pos(c, 2 * hp + 1)) = d1b;
-#pragma unroll
-      for (int k1 = 0; k1 < 2; ++k1) {
-        dv0 = mfma_h16(tr_aug_op(doa_t, tb_h0, k1), pack_f16x8(s0, 8 * k1), dv0);
-        dv1 = mfma_h16(tr_aug_op(doa_t, tb_h1, k1), pack_f16x8(s1, 8 * k1), dv1);
-        dk0 = mfma_h16(tr_aug_op(qa_t, tb_h0, k1), k1 ? d0b : d0a, dk0);
-        dk1 = mfma_h16(tr_aug_op(qa_t, tb_h1, k1), k1 ? d1b : d1a, dk1);
-      }
-      // dS^T operands: lane (query 16qh + m16, group G) gets keys 16u + 8 (G % 2) .. +7 of
-      // head G / 2, from two transposed reads of 4 keys each
-      typedef short s16x4 __attribute__((ext_vector_type(4)));
-      typedef float f32x4 __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(3))) s16x4* lds4;
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        f32x4 dq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint16_t* rb = mydst + tr_base + 512 * u;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb + 16 * qh));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb + 128 + 16 * (qh ^ 1)));
-          const s16x8 bop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kt[u]), __builtin_bit_cast(f16x8, bop),
-                                                      dq, 0, 0, 0);
-        }
-        // rows 4G .. 4G+3 = head G / 2, d 4 (G % 2) .. +3 of query 16qh + m16
-        const float4 v = make_float4(dq[0], dq[1], dq[2], dq[3]);
-        if (qh == 0) q0 = v; else q1 = v;
+      for (int u = 0; u < 2; ++u) {
+        const uint16_t* rb = mydst + tr_base + 512 * u;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb + 16 * qh));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4)(rb + 128 + 16 * (qh ^ 1)));
+        const s16x8 bop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dq[qh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, st.kt[u]),
+                                                        __builtin_bit_cast(f16x8, bop), dq[qh], 0, 0, 0);
       }
     }
-    // the workgroup's dQ for this tile: every wave's contribution, summed in wave order.
-    // The contributions of tile t go to buffer t & 1 and one barrier per tile orders
-    // everything: after it, tile t's contributions and tile t+1's stage are complete, and
-    // the buffers written next (contributions of t+1, stage of t+2) were last read before it.
-    float* myred = red + (t & 1) * kRedFloats + w * (32 * kRedRow) + m16 * kRedRow + 8 * (G >> 1) + 4 * (G & 1);
-    *reinterpret_cast<float4*>(myred) = q0;
-    *reinterpret_cast<float4*>(myred + 16 * kRedRow) = q1;
-    if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kAugStageHalves, sr, tid);
-    cw = cwn;
-    __syncthreads();
-    reduce_dq(t);
-  }
-  if (wave_live && j < Nk) {
-    const float rs = 1.f / sqd;
-    float* kp = dk + j * kHD + h0 * kD + 4 * hp;
-    float* vp = dv + j * kHD + h0 * kD + 4 * hp;
-    store4(kp, make_float4(dk0[0] * rs, dk0[1] * rs, dk0[2] * rs, dk0[3] * rs), 0);
-    store4(kp + kD, make_float4(dk1[0] * rs, dk1[1] * rs, dk1[2] * rs, dk1[3] * rs), 0);
-    store4(vp, make_float4(dv0[0], dv0[1], dv0[2], dv0[3]), 0);
-    store4(vp + kD, make_float4(dv1[0], dv1[1], dv1[2], dv1[3]), 0);
+  };
+
+  // The query sweep of a wave with kLive live sets (2, 1 or 0: only the last workgroup's
+  // waves can have fewer than 2); the sets' work on a tile runs one after the other.
+  auto sweep = [&](auto live_tag) __attribute__((always_inline)) {
+    constexpr int kLive = decltype(live_tag)::value;
+    for (int64_t t = 0; t < ntiles; ++t) {
+      const int64_t i0 = t * 32;
+      const uint16_t* cur = stage + (t & 1) * kAugStageHalves;
+      if (t + 1 < ntiles) {
+        cursor.load_next(sr, tid);
+#pragma unroll
+        for (int si = 0; si < kLive; ++si)
+          set[si].cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(set[si].crow, i0 + 32 + cc, N)
+                                        : codes_at<true, kAligned>(set[si].crow, i0 + 32 + cc, N);
+      }
+      // rows 4G .. 4G+3 = head G / 2, d 4 (G % 2) .. +3 of query 16qh + m16: this lane's dQ^T
+      f32x4 dq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int si = 0; si < kLive; ++si) set_tile(set[si], cur, dq);
+      // the workgroup's dQ for this tile: every wave's contribution, summed in wave order.
+      // The contributions of tile t go to buffer t & 1 and one barrier per tile orders
+      // everything: after it, tile t's contributions and tile t+1's stage are complete, and
+      // the buffers written next (contributions of t+1, stage of t+2) were last read before it.
+      float* myred = red + (t & 1) * kRedFloats + w * (32 * kRedRow) + m16 * kRedRow + 8 * (G >> 1) + 4 * (G & 1);
+      *reinterpret_cast<float4*>(myred) = make_float4(dq[0][0], dq[0][1], dq[0][2], dq[0][3]);
+      *reinterpret_cast<float4*>(myred + 16 * kRedRow) = make_float4(dq[1][0], dq[1][1], dq[1][2], dq[1][3]);
+      if (t + 1 < ntiles) stage_store<kCh>(stage + ((t + 1) & 1) * kAugStageHalves, sr, tid);
+#pragma unroll
+      for (int si = 0; si < kLive; ++si) set[si].cw = set[si].cwn;
+      __syncthreads();
+      reduce_dq(t);
+    }
+  };
+  if (nlive == 2)
+    sweep(std::integral_constant<int, 2>{});
+  else if (nlive == 1)
+    sweep(std::integral_constant<int, 1>{});
+  else
+    sweep(std::integral_constant<int, 0>{});
+
+  const float rs = 1.f / sqd;
+  const int dg = 4 * ((lane >> 4) & 1);
+#pragma unroll
+  for (int si = 0; si < kFusedSets; ++si) {
+    const FusedSet& st = set[si];
+    const int64_t jo = jw + 32 * si + 16 * hp + (lane & 15);  // this lane's key of the set's dK/dV
+    if (si < nlive && jo < Nk) {
+      float* kp = dk + jo * kHD + h0 * kD + dg;
+      float* vp = dv + jo * kHD + h0 * kD + dg;
+      store4(kp, make_float4(st.dk0[0] * rs, st.dk0[1] * rs, st.dk0[2] * rs, st.dk0[3] * rs), 0);
+      store4(kp + kD, make_float4(st.dk1[0] * rs, st.dk1[1] * rs, st.dk1[2] * rs, st.dk1[3] * rs), 0);
+      store4(vp, make_float4(st.dv0[0], st.dv0[1], st.dv0[2], st.dv0[3]), 0);
+      store4(vp + kD, make_float4(st.dv1[0], st.dv1[1], st.dv1[2], st.dv1[3]), 0);
+    }
   }
   if (NB > kFusedBins && over != 0u) *flag = 1u;  // every writer stores the same value
+  // the wave's bins cover both its 32-key blocks: their sum goes to the first block's
+  // partial row, zeros to the second's
   for (int x = lane; x < 2 * NB; x += 64) {
     const int hl = x / NB, b = x - hl * NB;
     float sum = 0.f;
@@ -948,6 +1019,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
       sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
     partial[((jw / 32) * kH + h0 + hl) * NB + b] = sum;
+    partial[((jw / 32 + 1) * kH + h0 + hl) * NB + b] = 0.f;
   }
 }
 
@@ -1073,8 +1145,8 @@ int64_t mfma_npad(int64_t N) { return (N + 31) / 32 * 32; }
 // dtable partial rows: one per 32-key block (padded to whole one-pass workgroups)
 int64_t mfma_kv_blocks(int64_t Nk) { return kv_row_blocks(mfma_npad(Nk) / 32); }
 
-// dQ partials of the one-pass backward: one per workgroup's 256 keys
-int64_t mfma_fused_dq_parts(int64_t Nk) { return mfma_kv_blocks(Nk) / kFusedWaves; }
+// dQ partials of the one-pass backward: one per workgroup's 512 keys
+int64_t mfma_fused_dq_parts(int64_t Nk) { return mfma_kv_blocks(Nk) / kFusedBlocks; }
 
 size_t mfma_ops_bytes(int64_t N, int64_t Nk) {
   const size_t npq = static_cast<size_t>(mfma_npad(N)), npk = static_cast<size_t>(mfma_npad(Nk));

@@ -338,7 +338,7 @@ BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtyp
   w.dq_off = w.dkv_off + dkv;
   const size_t dq = w.q.S > 1 ? up256(static_cast<size_t>(w.q.S) * N * H * D * f) : 0;
   w.dqf_off = w.dq_off + dq;
-  // the one-pass backward's dQ partials: one [N][H][D] array per workgroup's 256 keys
+  // the one-pass backward's dQ partials: one [N][H][D] array per workgroup's 512 keys
   const size_t dqf = w.fused ? up256(static_cast<size_t>(mfma_fused_dq_parts(Nk)) * N * H * D * f) : 0;
   w.flag_off = w.dqf_off + dqf;  // one device word the kernels of a call share (code-range flag)
   w.bytes = w.flag_off + 256;

@@ -107,9 +107,9 @@ def test_split_workspaces():
     # too few keys to split: one partial result's room (a block step may merge into out/lse)
     assert L.gt_attn_fwd_block_workspace_bytes(4096, 200, 8, 8, 33, 1) == 4096 * 8 * 8 * 4 + 4096 * 8 * 4
     # the small graph's backward holds split partial gradients on top of the unsplit needs;
-    # at D = 8 (bf16, H = 8) the one-pass backward adds one dQ partial [N, H, D] per 256-key workgroup
+    # at D = 8 (bf16, H = 8) the one-pass backward adds one dQ partial [N, H, D] per 512-key workgroup
     small, big = L.gt_attn_bwd_workspace_bytes(6800, 8, 8, 33, 1), L.gt_attn_bwd_workspace_bytes(32768, 8, 8, 33, 1)
-    dq_partials = (32768 // 256) * 32768 * 8 * 8 * 4
+    dq_partials = (32768 // 512) * 32768 * 8 * 8 * 4
     assert small > 3 * 6800 * 8 * 8 * 4 and dq_partials < big < dq_partials + 40 * 32768 * 8 * 8 * 4
     # the float32 path has no one-pass backward
     assert L.gt_attn_bwd_workspace_bytes(32768, 8, 8, 33, 0) < 40 * 32768 * 8 * 8 * 4
