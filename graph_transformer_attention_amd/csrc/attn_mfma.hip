@@ -859,18 +859,27 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
   constexpr int kCh = 256;  // qa, doa
   s16x8 sr[stage_per_thread<kCh>()];
-  StageCursor<kCh> cursor;
-  cursor.init(src, npad, tid);
-  cursor.load_next(sr, tid);
+  // The sweep starts at query tile rot and wraps around: key blocks on one XCD start at
+  // tiles ntiles / 8 apart, so the code rows they read at one time (rows N bytes apart)
+  // fall at different column offsets, and so in different L2 sets, instead of all at the
+  // same offset. The 4 head pairs of a key block share its rotation, and its code lines.
+  const int64_t rot = static_cast<int64_t>(kb) * ntiles / nkb;
+  auto wrap = [&](int64_t x) { return x < ntiles ? x : x - ntiles; };
+  const uint16_t* sp0 = tid < kCh ? stage_chunk(src, npad, 0, tid) : nullptr;  // this thread's staged chunk
+  auto stage_load = [&](int64_t tt) {
+    if (tid < kCh) sr[0] = load_h8(sp0 + tt * (32 * kH * 16));
+  };
+  auto codes_of = [&](const FusedSet& st, int64_t tt) {
+    return tt < nfull ? codes_at<false, kAligned>(st.crow, tt * 32 + cc, N) : codes_at<true, kAligned>(st.crow, tt * 32 + cc, N);
+  };
+  stage_load(rot);
   stage_store<kCh>(stage, sr, tid);
 #pragma unroll
-  for (int si = 0; si < kFusedSets; ++si)
-    set[si].cw =
-        nfull > 0 ? codes_at<false, kAligned>(set[si].crow, cc, N) : codes_at<true, kAligned>(set[si].crow, cc, N);
+  for (int si = 0; si < kFusedSets; ++si) set[si].cw = codes_of(set[si], rot);
   float* dqw = dqpart + static_cast<int64_t>(kb) * dqstride + (ib + rq) * kHD + (h0 + rh) * kD + rd;
-  // the workgroup's dQ for tile tt from the eight waves' contributions, in wave order
-  auto reduce_dq = [&](int64_t tt) {
-    const float* slot = red + (tt & 1) * kRedFloats + rq * kRedRow + rh * 8 + rd;
+  // the workgroup's dQ for tile tt (iteration t) from the eight waves' contributions, in wave order
+  auto reduce_dq = [&](int64_t tt, int64_t t) {
+    const float* slot = red + (t & 1) * kRedFloats + rq * kRedRow + rh * 8 + rd;
     float acc = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kFusedWaves; ++ww) acc += slot[ww * (32 * kRedRow)];
@@ -953,14 +962,12 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   auto sweep = [&](auto live_tag) __attribute__((always_inline)) {
     constexpr int kLive = decltype(live_tag)::value;
     for (int64_t t = 0; t < ntiles; ++t) {
-      const int64_t i0 = t * 32;
+      const int64_t tt = wrap(t + rot), tn = wrap(t + 1 + rot);  // this tile and the next
       const uint16_t* cur = stage + (t & 1) * kAugStageHalves;
       if (t + 1 < ntiles) {
-        cursor.load_next(sr, tid);
+        stage_load(tn);
 #pragma unroll
-        for (int si = 0; si < kLive; ++si)
-          set[si].cwn = (t + 1 < nfull) ? codes_at<false, kAligned>(set[si].crow, i0 + 32 + cc, N)
-                                        : codes_at<true, kAligned>(set[si].crow, i0 + 32 + cc, N);
+        for (int si = 0; si < kLive; ++si) set[si].cwn = codes_of(set[si], tn);
       }
       // rows 4G .. 4G+3 = head G / 2, d 4 (G % 2) .. +3 of query 16qh + m16: this lane's dQ^T
       f32x4 dq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -977,7 +984,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
 #pragma unroll
       for (int si = 0; si < kLive; ++si) set[si].cw = set[si].cwn;
       __syncthreads();
-      reduce_dq(t);
+      reduce_dq(tt, t);
     }
   };
   if (nlive == 2)
