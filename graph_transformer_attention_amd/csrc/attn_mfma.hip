@@ -859,11 +859,14 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   const int64_t ntiles = (N + 31) / 32, nfull = N / 32;
   constexpr int kCh = 256;  // qa, doa
   s16x8 sr[stage_per_thread<kCh>()];
-  // The sweep starts at query tile rot and wraps around: key blocks on one XCD start at
-  // tiles ntiles / 8 apart, so the code rows they read at one time (rows N bytes apart)
-  // fall at different column offsets, and so in different L2 sets, instead of all at the
-  // same offset. The 4 head pairs of a key block share its rotation, and its code lines.
-  const int64_t rot = static_cast<int64_t>(kb) * ntiles / nkb;
+  // The sweep starts at query tile rot and wraps around. Code rows are N bytes apart, so
+  // the code lines that the key blocks of one XCD read at one time all sat at the same
+  // column offset, in the same few L2 sets, and were fetched again and again. Those key
+  // blocks (kb = 8i + xcd) now start 4 tiles (one 128-byte line) apart, i mod 8: their
+  // lines fall in different sets, while the staged query rows they read stay within a
+  // window of 32 tiles that L2 holds for all of them. The 4 head pairs of a key block share
+  // its rotation, and its code lines.
+  const int64_t rot = static_cast<int64_t>(((kb / kXcds) % 8) * 4) % ntiles;
   auto wrap = [&](int64_t x) { return x < ntiles ? x : x - ntiles; };
   const uint16_t* sp0 = tid < kCh ? stage_chunk(src, npad, 0, tid) : nullptr;  // this thread's staged chunk
   auto stage_load = [&](int64_t tt) {
