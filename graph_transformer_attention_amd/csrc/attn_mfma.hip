@@ -412,17 +412,17 @@ __global__ __launch_bounds__(256) void bwd_prep_mfma_d8_kernel(const uint16_t* _
 constexpr int kBwdWaves = 4;              // waves per backward workgroup: 4 x 32 nodes, one head pair
 constexpr int kKvTable = 64;              // key-outer table entries (codes clamped to NB-1 <= 63)
 constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kFusedWaves = 8;            // waves per one-pass workgroup: 8 x 2 x 32 keys, one head pair
+constexpr int kFusedWaves = 8;            // waves per one-pass workgroup: 8 x (1 or 2) x 32 keys, one head pair
 constexpr int kFusedThreads = 64 * kFusedWaves;
 
-constexpr int kFusedSets = 2;             // 32-key sets per one-pass wave
-constexpr int kFusedBlocks = kFusedWaves * kFusedSets;  // 32-key blocks per one-pass workgroup
+constexpr int kFusedMaxSets = 2;          // 32-key sets per one-pass wave: 1 or 2 (fused_sets)
+constexpr int kFusedMaxBlocks = kFusedWaves * kFusedMaxSets;  // 32-key blocks per one-pass workgroup, at most
 
-// 32-key blocks of dtable partial rows, padded to whole one-pass workgroups (a multiple
-// of 16, so of the 4-wave kernels' blocks too); every key-outer kernel covers them all, a
-// wave past the last key writing zero rows, so each row is defined whichever ran.
+// 32-key blocks of dtable partial rows, padded to whole one-pass workgroups of either size
+// (a multiple of 16, so of the 4-wave kernels' blocks too); every key-outer kernel covers
+// them all, a wave past the last key writing zero rows, so each row is defined whichever ran.
 __host__ __device__ constexpr int64_t kv_row_blocks(int64_t npad32) {
-  return (npad32 + kFusedBlocks - 1) / kFusedBlocks * kFusedBlocks;
+  return (npad32 + kFusedMaxBlocks - 1) / kFusedMaxBlocks * kFusedMaxBlocks;
 }
 
 // One 32-node tile of backward operands of a head pair, staged into LDS: two
@@ -724,12 +724,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_d8_kernel(
 // Backward in one pass (key-outer with dQ): the key-outer kernel's work and, from the
 // same probabilities, the queries' gradient, so the query-outer pass (a third sweep
 // over the codes with a third exp per entry) is not needed. The dK/dV contractions are
-// those of bwd_kv_mfma_d8_kernel, with 8-wave workgroups of 512 keys x one head pair, one
-// workgroup per CU: each wave owns two sets of 32 keys and runs them one after the other on
-// every staged query tile. The tile, its barrier and the cross-wave dQ sum then serve four
-// times the keys of a 4-wave, one-set workgroup, and each workgroup's dQ partial covers 512
-// keys (0.54 GB of partials at N = 32768 instead of 2.1 GB at 128 keys). dK and dV contract
-// on 16x16x32 MFMAs, which leaves the registers for the second set.
+// those of bwd_kv_mfma_d8_kernel, with 8-wave workgroups of one head pair, one workgroup per
+// CU: each wave owns kSets sets of 32 keys and runs them one after the other on every staged
+// query tile (two sets, 512 keys per workgroup, once those workgroups alone fill the GPU;
+// one set, 256 keys, below: fused_sets). The tile, its barrier and the cross-wave dQ sum
+// then serve 2 or 4 times the keys of a 4-wave, one-set workgroup, and each workgroup's dQ
+// partial covers all its keys (0.54 GB of partials at N = 32768 instead of 2.1 GB at 128
+// keys). dK and dV contract on 16x16x32 MFMAs, which leaves the registers for a second set.
 // Only the two augmented row tiles are staged (4 KB per tile): the dK^T and dV^T
 // contractions read Q^T and dO^T from them with ds_read_b64_tr_b16 (tr_aug_base16). Per
 // 32-query tile each of a wave's sets also:
@@ -769,7 +770,7 @@ struct FusedSet {
   u32x4 cw, cwn;             // codes of the current and the next query tile
 };
 
-template <bool kAligned>
+template <bool kAligned, int kSets>
 __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
     const uint8_t* __restrict__ spd_t, const float* __restrict__ table, BwdOps ops, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ partial, float* __restrict__ dqpart, int64_t N, int64_t Nk,
@@ -794,15 +795,16 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   float2* mybins = bins + w * (kFusedBins * 64) + lane;
   uint16_t* mydst = dsbuf + w * kDsHalves;
 
-  const int nkb = static_cast<int>(kv_row_blocks(ops.npk / 32) / kFusedBlocks);
+  constexpr int kBlocks = kFusedWaves * kSets;  // 32-key blocks per workgroup
+  const int nkb = static_cast<int>(kv_row_blocks(ops.npk / 32) / kBlocks);
   int kb, hpair;
   xcd_map(blockIdx.x, nkb, kb, hpair);
   if (kb < 0) return;
   const int c = lane & 31, hp = lane >> 5;
   const int h0 = 2 * hpair;
-  // the wave's keys: set s (s = 0, 1) holds the 32 keys from jw + 32 s
-  const int64_t jw = static_cast<int64_t>(kb) * (32 * kFusedBlocks) + 32 * kFusedSets * w;
-  const int nlive = jw + 32 < ops.npk ? 2 : (jw < ops.npk ? 1 : 0);  // live sets (wave-uniform)
+  // the wave's keys: set s (s < kSets) holds the 32 keys from jw + 32 s
+  const int64_t jw = static_cast<int64_t>(kb) * (32 * kBlocks) + 32 * kSets * w;
+  const int nlive = kSets == 2 && jw + 32 < ops.npk ? 2 : (jw < ops.npk ? 1 : 0);  // live sets (wave-uniform)
   const int64_t npad = ops.npq;
   const float sqd = sqrtf(static_cast<float>(kD));
   const float sc2 = kLog2e / sqd;
@@ -818,9 +820,9 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   // zero where a row's head is not the k-group's, and is the same every tile.
   const int G = lane >> 4, m16 = lane & 15;
   const int64_t cc = 16 * hp;
-  FusedSet set[kFusedSets];
+  FusedSet set[kSets];
 #pragma unroll
-  for (int si = 0; si < kFusedSets; ++si) {
+  for (int si = 0; si < kSets; ++si) {
     FusedSet& st = set[si];
     const int64_t js = jw + 32 * si;
     const bool live = js < ops.npk;
@@ -878,7 +880,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   stage_load(rot);
   stage_store<kCh>(stage, sr, tid);
 #pragma unroll
-  for (int si = 0; si < kFusedSets; ++si) set[si].cw = codes_of(set[si], rot);
+  for (int si = 0; si < kSets; ++si) set[si].cw = codes_of(set[si], rot);
   float* dqw = dqpart + static_cast<int64_t>(kb) * dqstride + (ib + rq) * kHD + (h0 + rh) * kD + rd;
   // the workgroup's dQ for tile tt (iteration t) from the eight waves' contributions, in wave order
   auto reduce_dq = [&](int64_t tt, int64_t t) {
@@ -990,9 +992,9 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
       reduce_dq(tt, t);
     }
   };
-  if (nlive == 2)
-    sweep(std::integral_constant<int, 2>{});
-  else if (nlive == 1)
+  if (kSets == 2 && nlive == 2)
+    sweep(std::integral_constant<int, kSets>{});
+  else if (nlive >= 1)
     sweep(std::integral_constant<int, 1>{});
   else
     sweep(std::integral_constant<int, 0>{});
@@ -1000,7 +1002,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
   const float rs = 1.f / sqd;
   const int dg = 4 * ((lane >> 4) & 1);
 #pragma unroll
-  for (int si = 0; si < kFusedSets; ++si) {
+  for (int si = 0; si < kSets; ++si) {
     const FusedSet& st = set[si];
     const int64_t jo = jw + 32 * si + 16 * hp + (lane & 15);  // this lane's key of the set's dK/dV
     if (si < nlive && jo < Nk) {
@@ -1013,8 +1015,8 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
     }
   }
   if (NB > kFusedBins && over != 0u) *flag = 1u;  // every writer stores the same value
-  // the wave's bins cover both its 32-key blocks: their sum goes to the first block's
-  // partial row, zeros to the second's
+  // the wave's bins cover all its 32-key blocks: their sum goes to the first block's
+  // partial row, zeros to the second's (two sets)
   for (int x = lane; x < 2 * NB; x += 64) {
     const int hl = x / NB, b = x - hl * NB;
     float sum = 0.f;
@@ -1029,7 +1031,7 @@ __global__ __launch_bounds__(kFusedThreads) void bwd_fused_mfma_d8_kernel(
       sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
     partial[((jw / 32) * kH + h0 + hl) * NB + b] = sum;
-    partial[((jw / 32 + 1) * kH + h0 + hl) * NB + b] = 0.f;
+    if (kSets == 2) partial[((jw / 32 + 1) * kH + h0 + hl) * NB + b] = 0.f;
   }
 }
 
@@ -1155,8 +1157,13 @@ int64_t mfma_npad(int64_t N) { return (N + 31) / 32 * 32; }
 // dtable partial rows: one per 32-key block (padded to whole one-pass workgroups)
 int64_t mfma_kv_blocks(int64_t Nk) { return kv_row_blocks(mfma_npad(Nk) / 32); }
 
-// dQ partials of the one-pass backward: one per workgroup's 512 keys
-int64_t mfma_fused_dq_parts(int64_t Nk) { return mfma_kv_blocks(Nk) / kFusedBlocks; }
+// 32-key sets per wave of the one-pass backward: two once the 512-key workgroups alone fill
+// the GPU (64 key blocks x 4 head pairs = 256 CUs), one below, where workgroups of 256 keys
+// give the launch twice as many workgroups for the same query split.
+int fused_sets(int64_t Nk) { return (mfma_npad(Nk) + 511) / 512 >= 64 ? 2 : 1; }
+
+// dQ partials of the one-pass backward: one per workgroup (256 or 512 keys)
+int64_t mfma_fused_dq_parts(int64_t Nk) { return mfma_kv_blocks(Nk) / (kFusedWaves * fused_sets(Nk)); }
 
 size_t mfma_ops_bytes(int64_t N, int64_t Nk) {
   const size_t npq = static_cast<size_t>(mfma_npad(N)), npk = static_cast<size_t>(mfma_npad(Nk));
@@ -1244,12 +1251,11 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t 
     const int nfb = static_cast<int>(mfma_fused_dq_parts(a.Nk));
     const dim3 fgrid(static_cast<unsigned>(xcd_grid(nfb)), static_cast<unsigned>(w.kv.S));
     trace_begin(kTraceBwdFused, s);
-    if (kv_aligned)
-      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<true>, fgrid, dim3(kFusedThreads), 0, s, a.spd_t, a.table, ops,
-                         dkp, dvp, partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
-    else
-      hipLaunchKernelGGL(bwd_fused_mfma_d8_kernel<false>, fgrid, dim3(kFusedThreads), 0, s, a.spd_t, a.table, ops,
-                         dkp, dvp, partial, dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
+    auto fused_kernel = fused_sets(a.Nk) == 2
+                            ? (kv_aligned ? bwd_fused_mfma_d8_kernel<true, 2> : bwd_fused_mfma_d8_kernel<false, 2>)
+                            : (kv_aligned ? bwd_fused_mfma_d8_kernel<true, 1> : bwd_fused_mfma_d8_kernel<false, 1>);
+    hipLaunchKernelGGL(fused_kernel, fgrid, dim3(kFusedThreads), 0, s, a.spd_t, a.table, ops, dkp, dvp, partial,
+                       dqpart, a.N, a.Nk, a.ld_t, a.NB, w.kv.chunk, nk_el, pstride, nq_el, flag);
     e = hipGetLastError();
     trace_end(kTraceBwdFused, s);
     if (e != hipSuccess) return e;

@@ -271,7 +271,10 @@ void trace_end(int kernel_id, hipStream_t s) {
 // least 256 inner nodes). S minimises a time model of the launch in units of one 32-node
 // tile: ceil(W*S / R) rounds of workgroups, each costing a fixed overhead plus its
 // inner tiles, with W workgroups per row (128 outer nodes x one head pair) and R
-// workgroups resident at once (the kernel's occupancy). Measured per-workgroup costs
+// workgroups resident at once (the kernel's occupancy). The one-pass D = 8 backward's
+// workgroups are 8 waves of one or two 32-key sets (256 or 512 keys, fused_sets), one
+// per CU: W counts those, each costing 2 or 4 of the others' workgroups (fixed part and
+// tiles alike). Measured per-workgroup costs
 // are a fixed ~10-20 us plus ~1.7-1.8 us per tile, so the fixed part is about 12 tiles.
 // This both fills the GPU when the outer dimension is short and evens out the last
 // round when W is not a multiple of R.
@@ -288,6 +291,7 @@ constexpr int64_t kFwdTailTenths = 2;
 // D = 8: forward 128 -> 4, key-outer 192-212 -> 2, query-outer 142 -> 3; D = 32: forward 156
 // -> 3, key-outer 238-243 and query-outer 226 -> 2.
 int64_t resident_wgs(int kind, int D) {
+  if (kind == kSplitFused) return 256;
   const int per_cu = D == 32 ? (kind == kSplitFwd ? 3 : 2) : (kind == kSplitFwd ? 4 : kind == kSplitKv ? 2 : 3);
   return 256 * per_cu;
 }
@@ -296,7 +300,9 @@ Split inner_split(int64_t outer, int64_t inner, int H, int D, int dtype, int kin
   Split sp{1, inner};
   if (!mfma_supported(H, D, dtype)) return sp;
   const int64_t R = resident_wgs(kind, D);
-  const int64_t W = (outer + 127) / 128 * (H / 2);
+  const int64_t sets = kind == kSplitFused ? fused_sets(outer) : 0;
+  const int64_t wg_nodes = sets ? 256 * sets : 128, cost = sets ? 2 * sets : 1;
+  const int64_t W = (outer + wg_nodes - 1) / wg_nodes * (H / 2);
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, inner / kSplitMinInner));
   int64_t best_t = -1;
   for (int64_t S = 1; S <= smax; ++S) {
@@ -304,7 +310,7 @@ Split inner_split(int64_t outer, int64_t inner, int H, int D, int dtype, int kin
     const int64_t parts = (inner + chunk - 1) / chunk;
     const int64_t rounds = (W * parts + R - 1) / R;
     const int64_t tiles = (chunk + 31) / 32;
-    const int64_t t = 10 * rounds * (kSplitFixedTiles + tiles) + (kind == kSplitFwd ? kFwdTailTenths * tiles : 0);
+    const int64_t t = 10 * rounds * cost * (kSplitFixedTiles + tiles) + (kind == kSplitFwd ? kFwdTailTenths * tiles : 0);
     if (best_t < 0 || t < best_t) {
       best_t = t;
       sp.S = static_cast<int>(parts);
@@ -327,7 +333,7 @@ BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtyp
   w.fused = fused_ok && mfma && D == 8;
   const int64_t kb = valu_kv_block(H);
   w.n_kv_blocks = mfma ? (D == 32 ? mfma_d32_kv_blocks(Nk) : mfma_kv_blocks(Nk)) : (Nk + kb - 1) / kb;
-  w.kv = inner_split(Nk, N, H, D, dtype, kSplitKv);
+  w.kv = inner_split(Nk, N, H, D, dtype, w.fused ? kSplitFused : kSplitKv);
   w.q = inner_split(N, Nk, H, D, dtype, kSplitQ);
   const size_t f = sizeof(float);
   w.delta_off = 0;
@@ -338,7 +344,7 @@ BwdWorkspace bwd_workspace(int64_t N, int64_t Nk, int H, int D, int NB, int dtyp
   w.dq_off = w.dkv_off + dkv;
   const size_t dq = w.q.S > 1 ? up256(static_cast<size_t>(w.q.S) * N * H * D * f) : 0;
   w.dqf_off = w.dq_off + dq;
-  // the one-pass backward's dQ partials: one [N][H][D] array per workgroup's 512 keys
+  // the one-pass backward's dQ partials: one [N][H][D] array per workgroup (256 or 512 keys)
   const size_t dqf = w.fused ? up256(static_cast<size_t>(mfma_fused_dq_parts(Nk)) * N * H * D * f) : 0;
   w.flag_off = w.dqf_off + dqf;  // one device word the kernels of a call share (code-range flag)
   w.bytes = w.flag_off + 256;

@@ -34,7 +34,7 @@ struct Split {
   int64_t chunk;
 };
 // kind: which matrix-core kernel (its occupancy sets how many workgroups fit at once).
-enum SplitKind { kSplitFwd = 0, kSplitKv = 1, kSplitQ = 2 };
+enum SplitKind { kSplitFwd = 0, kSplitKv = 1, kSplitQ = 2, kSplitFused = 3 };
 Split inner_split(int64_t outer, int64_t inner, int H, int D, int dtype, int kind);
 // block: room for at least one partial result (a block step may merge into out/lse)
 size_t fwd_workspace_bytes(int64_t N, int64_t Nk, int H, int D, int dtype, bool block);
@@ -115,6 +115,7 @@ bool mfma_supported(int H, int D, int dtype);
 int64_t mfma_npad(int64_t N);
 int64_t mfma_kv_blocks(int64_t Nk);
 int64_t mfma_fused_dq_parts(int64_t Nk);
+int fused_sets(int64_t Nk);  // 32-key sets per wave of the one-pass D = 8 backward (1 or 2)
 size_t mfma_ops_bytes(int64_t N, int64_t Nk);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdWorkspace& w, hipStream_t s);
